@@ -1,0 +1,124 @@
+"""Decode attention over packed TQ pages (oracle, fp64, dense).
+
+Follows:
+* TorbuQuant docs, "Current Status" table: diagnostic attention routes (dense, dequantized,
+  direct-QK, packed-V) and a paged decode reference over TQ packed pages; "TQ4 page tensor"
+  figure for slot addressing through a block table.
+* turboquant-pro 1.4.2, "Fused CUDA decode": one decode step over the whole cache computed on
+  the codes equals decompress-then-attend (exact to a few 1e-7 there).
+* tq-kv, "3-Fix for GGUF Models" (the first four tokens stay fp16: sink tokens) and the
+  "Quick Start" calls pre_rotate_query_with_signs / fused_attention_scores (scores on the
+  codes with a rotated query).
+
+Plain definition used here
+--------------------------
+For sequence b with L_b cached tokens and query head h (kv head h_kv = h // G, G = H_q / H_kv):
+  k_p, v_p = the fp16 sink rows for p < n_sink, else the dequantized rows n R^T c[idx]
+             read from page[bt[b][p // bs], p % bs, h_kv, :];
+  s_p = scale * q_h . k_p      (scale = 1/sqrt(D) unless given);
+  o_h = sum_p softmax(s)_p v_p over p in [0, L_b);  L_b = 0 gives o_h = 0.
+Everything is fp64; the query is the fp16 input.
+
+The second route, decode_attention_rotated(), is the fused identity a kernel uses
+(q . (n R^T c) = n (R q) . c and sum_p w_p n_p R^T c_p = R^T sum_p w_p n_p c_p); the tests check
+the two routes against each other by brute force.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import quantize, rotation
+
+
+def _dequantized_sequence(pages, block_table, L, n_sink, layer, k_centroids32, v_centroids32):
+    """Dequantized K, V rows [L - n_sink, H_kv, D] (fp64, plain route) for positions n_sink..L-1."""
+    D, H_kv, bs = layer["D"], layer["H_kv"], layer["block_size"]
+    pos = np.arange(n_sink, L, dtype=np.int64)
+    slots = np.asarray(block_table, dtype=np.int64)[pos // bs] * bs + pos % bs
+    k_idx, k_n, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, layer["k_bits"], layer["v_bits"],
+                                                 layer.get("slot_stride"))
+    K = quantize.dequantize_plain(k_idx, k_n, k_centroids32, layer["seed"])
+    V = quantize.dequantize_plain(v_idx, v_n, v_centroids32, layer["seed"])
+    return K, V
+
+
+def decode_attention(q16, pages, block_tables, seq_lens, layer, k_centroids32, v_centroids32,
+                     sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None):
+    """Dense decode attention, fp64.  Returns out [B, H_q, D] (rows not in `seqs` stay zero).
+
+    layer: dict with D, H_kv, block_size, k_bits, v_bits, seed and optionally slot_stride.
+    q16: [B, H_q, D] fp16.  block_tables: [B, max_blocks] int.  seq_lens: [B] int.
+    sink_k16 / sink_v16: [B, n_sink, H_kv, D] fp16 (or None when n_sink == 0).
+    """
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    B, H_q, D = q.shape
+    H_kv = layer["H_kv"]
+    G = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, H_q, D), dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        ns = min(n_sink, L)
+        Kq, Vq = _dequantized_sequence(pages, block_tables[b], L, ns, layer, k_centroids32, v_centroids32)
+        if ns:
+            Ks = np.asarray(sink_k16[b, :ns], dtype=np.float16).astype(np.float64)
+            Vs = np.asarray(sink_v16[b, :ns], dtype=np.float16).astype(np.float64)
+            K = np.concatenate([Ks, Kq], axis=0)
+            V = np.concatenate([Vs, Vq], axis=0)
+        else:
+            K, V = Kq, Vq
+        for h in range(H_q):
+            hk = h // G
+            s = scale * (K[:, hk, :] @ q[b, h])
+            w = np.exp(s - s.max())
+            w /= w.sum()
+            out[b, h] = w @ V[:, hk, :]
+    return out
+
+
+def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centroids32, v_centroids32,
+                             sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None):
+    """Same result through the rotated domain: scores n_K (R q).c_K, values R^T sum w n_V c_V."""
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    B, H_q, D = q.shape
+    H_kv, bs = layer["H_kv"], layer["block_size"]
+    G = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    R = rotation.rotation_matrix(layer["seed"], D)
+    ck = np.asarray(k_centroids32, np.float32).astype(np.float64)
+    cv = np.asarray(v_centroids32, np.float32).astype(np.float64)
+    out = np.zeros((B, H_q, D), dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        ns = min(n_sink, L)
+        pos = np.arange(ns, L, dtype=np.int64)
+        slots = np.asarray(block_tables[b], dtype=np.int64)[pos // bs] * bs + pos % bs
+        k_idx, k_n, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, layer["k_bits"], layer["v_bits"],
+                                                     layer.get("slot_stride"))
+        for h in range(H_q):
+            hk = h // G
+            qr = R @ q[b, h]
+            s_codes = scale * k_n[:, hk].astype(np.float64) * (ck[k_idx[:, hk, :]] @ qr)
+            if ns:
+                Ks = np.asarray(sink_k16[b, :ns, hk], np.float16).astype(np.float64)
+                s_sink = scale * (Ks @ q[b, h])
+            else:
+                s_sink = np.zeros(0)
+            m = max(s_codes.max() if s_codes.size else -np.inf, s_sink.max() if s_sink.size else -np.inf)
+            w_codes = np.exp(s_codes - m)
+            w_sink = np.exp(s_sink - m)
+            l = w_codes.sum() + w_sink.sum()
+            acc_rot = (w_codes * v_n[:, hk].astype(np.float64)) @ cv[v_idx[:, hk, :]]
+            o = R.T @ acc_rot
+            if ns:
+                Vs = np.asarray(sink_v16[b, :ns, hk], np.float16).astype(np.float64)
+                o = o + w_sink @ Vs
+            out[b, h] = o / l
+    return out
