@@ -213,9 +213,12 @@ def lloyd_max(D: int, bits: int, family: str = "beta", tol: float = 1e-13,
         c = c_new
         if residual <= tol:
             break
-    # Newton polishing of the same fixed point (boundary form), kept symmetric.
-    if residual > tol:
+    # Newton polishing of the same fixed point (boundary form), kept symmetric.  It runs to the
+    # floating-point floor (not just to `tol`) so that independent solvers round the fixed point
+    # to the same fp32 values.
+    if residual > tol or bits >= 3:
         t = midpoints(c)
+        best, stall = residual, 0
         for _ in range(max_newton):
             it += 1
             step = _newton_step(dist, t)
@@ -233,7 +236,11 @@ def lloyd_max(D: int, bits: int, family: str = "beta", tol: float = 1e-13,
             c_chk, _ = centroids_for(dist, midpoints(c_new))
             residual = float(np.max(np.abs(_symmetrize(c_chk) - c_new)))
             c = c_new
-            if residual <= tol:
+            if residual < best:
+                best, stall = residual, 0
+            else:
+                stall += 1
+            if residual <= 1e-17 or stall >= 3:
                 break
     t = midpoints(c)
     t[L // 2 - 1] = 0.0 if L > 1 else t[L // 2 - 1]   # exact by symmetry; removes a +-0 ulp
