@@ -1,0 +1,169 @@
+/*
+ * tq.h — C ABI of the TurboQuant packed-KV library for AMD Instinct MI355X (gfx950).
+ *
+ * Two halves of one hot path, as the pages describe it:
+ *   1. quantize-on-append: randomized Hadamard rotation (sign flip + Walsh-Hadamard transform),
+ *      fp32 L2-norm split, nearest Lloyd-Max centroid per rotated coordinate, and bit packing of
+ *      the indices plus the norm into TQ page slots
+ *      (turboquant-serve 0.1.2, "Architecture"; turboquant-pro 1.4.2, "How It Works";
+ *       tq-kv, "How It Works" step [3]; TorbuQuant docs, "TQ4 page tensor" figure);
+ *   2. fused paged decode attention that reads the packed pages directly: scores on the codes
+ *      with a rotated query, online softmax, values accumulated in the rotated domain and rotated
+ *      back once per output (tq-kv, "Quick Start" pre_rotate_query_with_signs /
+ *      fused_attention_scores and "Custom CUDA Kernel Stack" split-KV flash decode;
+ *      turboquant-pro 1.4.2, "Fused CUDA decode").
+ *
+ * Page layout (TorbuQuant docs, "TQ4 page tensor" figure): a uint8 tensor
+ *   pages[num_blocks][block_size][num_kv_heads][slot_stride]
+ * The slot of token position p of a sequence is slot = block_table[p / block_size] * block_size
+ * + p % block_size, and kv head h of that slot starts at byte (slot * num_kv_heads + h) *
+ * slot_stride.  Each slot holds a K region then a V region; a region is ceil(D * bits / 8) bytes
+ * of indices (LSB-first bitstream: index i occupies bits [i*bits, (i+1)*bits), byte k holds bits
+ * 8k..8k+7) followed by the row's fp32 L2 norm, little-endian.  Bytes from slot_bytes up to
+ * slot_stride are written as zero.
+ *
+ * Conventions for every call below:
+ *   - Pointers marked "device" are device memory of the current HIP device; the caller owns
+ *     them and keeps them alive until the stream has finished the work.  The library never
+ *     allocates or frees device memory and keeps no pointer after a call returns.
+ *   - Calls that take a stream only enqueue work on it and return without waiting.
+ *   - Every argument is validated on the host before anything is enqueued.  A call returns
+ *     TQ_OK (0) or a negative tq_status; on error nothing was enqueued.  No exception crosses
+ *     the ABI.  Device-side contract violations (a block id >= num_blocks, seq_len >
+ *     max_seq_len, a slot >= num_blocks * block_size, duplicate slots in one append,
+ *     non-finite inputs) are undefined behaviour.
+ *   - fp16 means IEEE binary16 stored as uint16; fp32 means IEEE binary32.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* tq_stream_t; /* a hipStream_t; NULL = the default stream */
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1,    /* a null pointer, a negative size, H_q % H_kv != 0, ...       */
+  TQ_ERR_UNSUPPORTED = -2,    /* head_dim or bit width outside what the kernels implement    */
+  TQ_ERR_WORKSPACE = -3,      /* decode workspace smaller than tq_decode_workspace_bytes()   */
+  TQ_ERR_HIP = -4,            /* the HIP runtime reported an error while enqueueing          */
+  TQ_ERR_NO_CONVERGENCE = -5  /* the Lloyd-Max solver did not reach its tolerance            */
+} tq_status;
+
+typedef enum tq_codebook_family {
+  TQ_CODEBOOK_BETA = 0,     /* exact law of one coordinate of a uniform point on S^{D-1}   */
+  TQ_CODEBOOK_GAUSSIAN = 1  /* its N(0, 1/D) approximation                                  */
+} tq_codebook_family;
+
+/* One layer's format.  K and V may use different bit widths (p1 policies q8k-q8v, q8k-int4v;
+ * p4 K8/K4 and V8/V4/V3/V2 formats); a model with boundary-layer protection simply uses a
+ * different descriptor for the protected layers. */
+typedef struct tq_layer_desc {
+  int32_t head_dim;       /* D: 64 or 128                                                     */
+  int32_t num_q_heads;    /* H_q (decode only; multiple of num_kv_heads; G = H_q/H_kv <= 8)   */
+  int32_t num_kv_heads;   /* H_kv >= 1                                                         */
+  int32_t block_size;     /* tokens per page block, >= 1                                       */
+  int32_t k_bits;         /* 2, 3, 4 or 8                                                      */
+  int32_t v_bits;         /* 2, 3, 4 or 8                                                      */
+  int32_t slot_stride;    /* bytes per (token, kv head) slot; 0 means tq_slot_bytes()          */
+  int32_t reserved;       /* must be 0                                                         */
+  uint64_t rht_seed;      /* seed of the SplitMix64 sign vector of the rotation                */
+  const float* k_centroids;   /* device, 2^k_bits ascending fp32 (tq_build_codebook output) */
+  const float* k_boundaries;  /* device, 2^k_bits - 1 ascending fp32                          */
+  const float* v_centroids;   /* device, 2^v_bits                                             */
+  const float* v_boundaries;  /* device, 2^v_bits - 1                                         */
+} tq_layer_desc;
+
+/* Lloyd-Max codebook for one rotated coordinate (host only, pure, no device work).
+ * Follows turboquant-serve 0.1.2, "Architecture" (MSE-optimal codebook for the Beta prior on
+ * rotated unit vectors, fitted once and shared) and the TorbuQuant docs, "Current Status" table
+ * (exact Beta-sphere and Gaussian-approximation codebooks).  Solves the midpoint and centroid
+ * conditions in fp64 to a centroid residual <= 1e-13, exactly symmetric, and rounds centroids
+ * and boundaries to fp32 independently.
+ *   D            head dimension, 2..65536
+ *   bits         1..8
+ *   family       tq_codebook_family
+ *   centroids    host out, 2^bits fp32 (ascending)
+ *   boundaries   host out, 2^bits - 1 fp32 (ascending; the middle one is exactly 0)
+ *   centroids_f64, boundaries_f64, mse   optional host outs (NULL to skip): the fp64 fixed
+ *                point and the mean squared error per coordinate. */
+int tq_build_codebook(int32_t D, int32_t bits, int32_t family, float* centroids, float* boundaries,
+                      double* centroids_f64, double* boundaries_f64, double* mse);
+
+/* The rotation's sign vector (host only): signs[i] = -1 when bit 63 of the i-th SplitMix64
+ * draw from `seed` is set, else +1 (tq-kv, "Quick Start": generate_signs(dim, seed)).
+ * out: host, D int8 values. */
+int tq_rht_signs(int32_t D, uint64_t seed, int8_t* out);
+
+/* Bytes of one slot: (ceil(D*k_bits/8) + 4) + (ceil(D*v_bits/8) + 4) (TorbuQuant docs,
+ * "TQ4 page tensor" figure).  Returns a negative tq_status for unsupported arguments. */
+int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits);
+
+/* Quantize-on-append (turboquant-serve 0.1.2, "Architecture" update(); TorbuQuant docs,
+ * "TQ4 page tensor" figure; turboquant-pro 1.4.2, "How It Works" per-vector flow).
+ *   k, v          device fp16 [n_tok][num_kv_heads][D], contiguous
+ *   slot_mapping  device int64 [n_tok]: destination slot of each token; a negative slot skips
+ *                 the token (padding).  Slots must be distinct and < num_blocks * block_size.
+ *   pages         device uint8 [num_blocks][block_size][num_kv_heads][slot_stride] (written)
+ * For each (token, kv head) and for K and V: n = fp32 norm of the fp16 row (exact squares,
+ * stride-halving fp32 tree, correctly rounded sqrt); u = R x / n; index = number of fp32
+ * boundaries <= u (all indices 2^bits/2 when n == 0); pack; store. */
+int tq_quantize_append(const tq_layer_desc* layer, const void* k, const void* v,
+                       const int64_t* slot_mapping, int64_t n_tok, void* pages, int64_t num_blocks,
+                       tq_stream_t stream);
+
+/* Workspace bytes tq_paged_decode_attention needs for these sizes.  The workspace holds
+ * split-K partial results and per-(sequence, kv head) arrival counters.  The counter region
+ * must be zero before the first call that uses a workspace (zero the whole buffer once after
+ * allocating it); every call leaves it zero again.  Calls sharing a workspace must be ordered
+ * on one stream. */
+size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs, int32_t max_seq_len);
+
+/* Fused paged decode attention over packed pages, one query token per sequence.
+ * (tq-kv, "Custom CUDA Kernel Stack": split-KV flash decode with online softmax and TQ fused
+ *  attention on compressed KV; "3-Fix for GGUF Models": sink tokens kept fp16;
+ *  turboquant-pro 1.4.2, "Fused CUDA decode": split-K decode on the codes.)
+ *   q             device fp16 [num_seqs][num_q_heads][D]
+ *   pages         device uint8 page tensor (read only)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]: cached tokens of each sequence, sinks included;
+ *                 each <= max_seq_len (a host value used to size the grid)
+ *   sink_k, sink_v device fp16 [num_seqs][n_sink][num_kv_heads][D], or NULL when n_sink == 0.
+ *                 Positions p < min(n_sink, seq_len) are read from these arrays; their page
+ *                 slots are ignored.
+ *   scale         softmax scale; <= 0 selects 1/sqrt(D)
+ *   out           device fp32 [num_seqs][num_q_heads][D] (written; seq_len == 0 gives zeros)
+ *   workspace     device, >= tq_decode_workspace_bytes(layer, num_seqs, max_seq_len)
+ * Query head h reads kv head h / G (G = num_q_heads / num_kv_heads).  Computes, for every
+ * sequence and query head, softmax(scale * q . k_p) weighted sum of v_p over p < seq_len, where
+ * k_p, v_p are the sinks or the dequantized rows n R^T c[idx]; scores use n (R q) . c[idx] and
+ * values are summed as n c[idx] in the rotated domain and rotated back once. */
+int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q, const void* pages,
+                              int64_t num_blocks, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t max_seq_len, const void* sink_k, const void* sink_v,
+                              int32_t n_sink, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, tq_stream_t stream);
+
+/* Dequantize whole slots (turboquant-serve 0.1.2, "Architecture" _decode(): unpack, Lloyd-Max
+ * decode, restore magnitude, rotate back).  Bit-exact definition: c_i = centroid[idx_i] (fp32);
+ * z = H c computed exactly (fp64); g = fp32(n * fp32(1/sqrt(D))); x_i = s_i * fp32(fp32(z_i) * g).
+ *   slots         device int64 [n]: slot ids (< num_blocks * block_size)
+ *   k_out, v_out  device fp32 [n][num_kv_heads][D] (written) */
+int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages, int64_t num_blocks,
+                       const int64_t* slots, int64_t n, float* k_out, float* v_out,
+                       tq_stream_t stream);
+
+/* Static description of a status code. */
+const char* tq_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,75 @@
+"""TurboQuant packed-KV hot path on AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library libtq.so (include/tq.h).  This package is its thin Python
+binding: `_lib` mirrors the C ABI one function per entry point; `LayerFormat` builds a layer
+descriptor with its device codebooks; `workloads` generates the seeded synthetic inputs.
+
+PyTorch provides device memory and streams only.  Nothing here computes any step of the method.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    TqError,
+    tq_build_codebook,
+    tq_decode_workspace_bytes,
+    tq_dequantize_rows,
+    tq_layer_desc,
+    tq_paged_decode_attention,
+    tq_quantize_append,
+    tq_rht_signs,
+    tq_slot_bytes,
+    tq_status_str,
+)
+
+_CODEBOOKS: dict = {}
+
+
+def host_codebook(D: int, bits: int, family: str = "beta"):
+    """fp32 (centroids, boundaries) from tq_build_codebook, memoised per (D, bits, family)."""
+    key = (D, bits, family)
+    if key not in _CODEBOOKS:
+        c, t, _, _, _ = tq_build_codebook(D, bits, family)
+        _CODEBOOKS[key] = (c, t)
+    return _CODEBOOKS[key]
+
+
+class LayerFormat:
+    """One layer's TQ format (head_dim, heads, bits, block size, slot stride, rotation seed)
+    plus its fp32 codebooks on the device.  Keeps the device arrays alive for `desc`."""
+
+    def __init__(self, head_dim: int, num_q_heads: int, num_kv_heads: int, k_bits: int,
+                 v_bits: int, block_size: int = 16, rht_seed: int = 0, family: str = "beta",
+                 slot_stride: int = 0, device="cuda", k_codebook=None, v_codebook=None):
+        import torch
+        self.head_dim, self.num_q_heads, self.num_kv_heads = head_dim, num_q_heads, num_kv_heads
+        self.k_bits, self.v_bits, self.block_size = k_bits, v_bits, block_size
+        self.rht_seed, self.family = rht_seed, family
+        self.slot_bytes = tq_slot_bytes(head_dim, k_bits, v_bits)
+        self.slot_stride = slot_stride or self.slot_bytes
+        kc, kt = k_codebook if k_codebook is not None else host_codebook(head_dim, k_bits, family)
+        vc, vt = v_codebook if v_codebook is not None else host_codebook(head_dim, v_bits, family)
+        as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        self.k_centroids, self.k_boundaries = as_dev(kc), as_dev(kt)
+        self.v_centroids, self.v_boundaries = as_dev(vc), as_dev(vt)
+        self.desc = tq_layer_desc(
+            head_dim=head_dim, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+            block_size=block_size, k_bits=k_bits, v_bits=v_bits, slot_stride=slot_stride,
+            reserved=0, rht_seed=rht_seed,
+            k_centroids=self.k_centroids.data_ptr(), k_boundaries=self.k_boundaries.data_ptr(),
+            v_centroids=self.v_centroids.data_ptr(), v_boundaries=self.v_boundaries.data_ptr())
+
+    def new_pages(self, num_blocks: int, device="cuda"):
+        import torch
+        return torch.zeros((num_blocks, self.block_size, self.num_kv_heads, self.slot_stride),
+                           dtype=torch.uint8, device=device)
+
+    def new_workspace(self, num_seqs: int, max_seq_len: int, device="cuda"):
+        """Zeroed decode workspace (the arrival counters must start at zero)."""
+        import torch
+        n = tq_decode_workspace_bytes(self.desc, num_seqs, max_seq_len)
+        return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)

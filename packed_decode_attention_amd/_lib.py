@@ -1,0 +1,166 @@
+"""ctypes binding of libtq.so (the HIP library).  Argument marshalling only.
+
+Every entry point of include/tq.h has a Python function of the same name here.  Tensors are
+torch tensors on the current HIP device; only their data pointers and the current stream cross
+the boundary.  There is no fallback: if libtq.so is missing or fails to load, import of the
+functions that need it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("TQ_LIB", os.path.join(_HERE, "libtq.so"))
+
+TQ_OK = 0
+TQ_ERR_INVALID_ARG = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_WORKSPACE = -3
+TQ_ERR_HIP = -4
+TQ_ERR_NO_CONVERGENCE = -5
+
+FAMILIES = {"beta": 0, "gaussian": 1}
+
+EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_quantize_append",
+           "tq_decode_workspace_bytes", "tq_paged_decode_attention", "tq_dequantize_rows",
+           "tq_status_str")
+
+
+class TqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({_lib().tq_status_str(status).decode()})")
+
+
+class tq_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("k_bits", ctypes.c_int32),
+        ("v_bits", ctypes.c_int32),
+        ("slot_stride", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rht_seed", ctypes.c_uint64),
+        ("k_centroids", ctypes.c_void_p),
+        ("k_boundaries", ctypes.c_void_p),
+        ("v_centroids", ctypes.c_void_p),
+        ("v_boundaries", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
+                               "`python -m packed_decode_attention_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        D = ctypes.POINTER(tq_layer_desc)
+        lib.tq_build_codebook.argtypes = [I32, I32, I32, P, P, P, P, P]
+        lib.tq_build_codebook.restype = ctypes.c_int
+        lib.tq_rht_signs.argtypes = [I32, ctypes.c_uint64, P]
+        lib.tq_rht_signs.restype = ctypes.c_int
+        lib.tq_slot_bytes.argtypes = [I32, I32, I32]
+        lib.tq_slot_bytes.restype = I32
+        lib.tq_quantize_append.argtypes = [D, P, P, P, I64, P, I64, P]
+        lib.tq_quantize_append.restype = ctypes.c_int
+        lib.tq_decode_workspace_bytes.argtypes = [D, I32, I32]
+        lib.tq_decode_workspace_bytes.restype = SZ
+        lib.tq_paged_decode_attention.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P, I32,
+                                                  ctypes.c_float, P, P, SZ, P]
+        lib.tq_paged_decode_attention.restype = ctypes.c_int
+        lib.tq_dequantize_rows.argtypes = [D, P, I64, P, I64, P, P, P]
+        lib.tq_dequantize_rows.restype = ctypes.c_int
+        lib.tq_status_str.argtypes = [ctypes.c_int]
+        lib.tq_status_str.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def _check(fn: str, status: int):
+    if status != TQ_OK:
+        raise TqError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------------------------
+# Host-only calls
+# ---------------------------------------------------------------------------------------------
+def tq_build_codebook(D: int, bits: int, family: str = "beta"):
+    """Returns (centroids fp32, boundaries fp32, centroids fp64, boundaries fp64, mse)."""
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(L - 1, np.float32)
+    c64 = np.zeros(L, np.float64)
+    t64 = np.zeros(L - 1, np.float64)
+    mse = ctypes.c_double(0.0)
+    st = _lib().tq_build_codebook(D, bits, FAMILIES[family], c.ctypes.data, t.ctypes.data,
+                                  c64.ctypes.data, t64.ctypes.data, ctypes.addressof(mse))
+    _check("tq_build_codebook", st)
+    return c, t, c64, t64, mse.value
+
+
+def tq_rht_signs(D: int, seed: int) -> np.ndarray:
+    out = np.zeros(D, np.int8)
+    _check("tq_rht_signs", _lib().tq_rht_signs(D, seed, out.ctypes.data))
+    return out
+
+
+def tq_slot_bytes(D: int, k_bits: int, v_bits: int) -> int:
+    r = _lib().tq_slot_bytes(D, k_bits, v_bits)
+    _check("tq_slot_bytes", min(r, 0))
+    return r
+
+
+def tq_status_str(status: int) -> str:
+    return _lib().tq_status_str(status).decode()
+
+
+# ---------------------------------------------------------------------------------------------
+# Device calls (enqueue on the current torch stream unless a stream is given)
+# ---------------------------------------------------------------------------------------------
+def tq_quantize_append(desc, k, v, slot_mapping, pages, num_blocks: int, stream=None) -> None:
+    st = _lib().tq_quantize_append(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping),
+                                   slot_mapping.numel(), _ptr(pages), num_blocks, _stream(stream))
+    _check("tq_quantize_append", st)
+
+
+def tq_decode_workspace_bytes(desc, num_seqs: int, max_seq_len: int) -> int:
+    return int(_lib().tq_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_seq_len))
+
+
+def tq_paged_decode_attention(desc, q, pages, num_blocks: int, block_tables, seq_lens,
+                              max_seq_len: int, out, workspace, sink_k=None, sink_v=None,
+                              n_sink: int = 0, scale: float = 0.0, stream=None) -> None:
+    num_seqs = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    st = _lib().tq_paged_decode_attention(
+        ctypes.byref(desc), _ptr(q), _ptr(pages), num_blocks, _ptr(block_tables), max_blocks,
+        _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, scale,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_paged_decode_attention", st)
+
+
+def tq_dequantize_rows(desc, pages, num_blocks: int, slots, k_out, v_out, stream=None) -> None:
+    st = _lib().tq_dequantize_rows(ctypes.byref(desc), _ptr(pages), num_blocks, _ptr(slots),
+                                   slots.numel(), _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check("tq_dequantize_rows", st)

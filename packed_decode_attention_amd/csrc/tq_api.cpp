@@ -1,0 +1,142 @@
+// C ABI entry points: argument validation on the host, rotation sign mask, split geometry, and
+// the kernel launches.  Nothing here allocates device memory.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool bits_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
+int code_bytes(int D, int bits) { return (D * bits + 7) / 8; }
+
+// Fill a TqLayer from the public descriptor.  need_q: decode also checks num_q_heads.
+int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
+  if (d == nullptr) return TQ_ERR_INVALID_ARG;
+  if (d->reserved != 0) return TQ_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return TQ_ERR_UNSUPPORTED;
+  if (!bits_ok(d->k_bits) || !bits_ok(d->v_bits)) return TQ_ERR_UNSUPPORTED;
+  if (d->num_kv_heads < 1 || d->block_size < 1) return TQ_ERR_INVALID_ARG;
+  if (d->k_centroids == nullptr || d->k_boundaries == nullptr || d->v_centroids == nullptr ||
+      d->v_boundaries == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  const int sb = tq_slot_bytes(d->head_dim, d->k_bits, d->v_bits);
+  const int stride = d->slot_stride == 0 ? sb : d->slot_stride;
+  if (stride < sb || (stride & 3) != 0) return TQ_ERR_INVALID_ARG;
+  int G = 1;
+  if (need_q) {
+    if (d->num_q_heads < 1 || d->num_q_heads % d->num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+    G = d->num_q_heads / d->num_kv_heads;
+    if (G > 8) return TQ_ERR_UNSUPPORTED;
+  }
+  L->D = d->head_dim;
+  L->Hq = need_q ? d->num_q_heads : d->num_kv_heads;
+  L->Hkv = d->num_kv_heads;
+  L->G = G;
+  L->bs = d->block_size;
+  L->kb = d->k_bits;
+  L->vb = d->v_bits;
+  L->stride = stride;
+  L->slot_bytes = sb;
+  L->kcode_bytes = code_bytes(d->head_dim, d->k_bits);
+  L->vcode_bytes = code_bytes(d->head_dim, d->v_bits);
+  uint64_t words[2];
+  tq_sign_words(d->head_dim, d->rht_seed, words, 2);
+  L->signs.w[0] = (uint32_t)words[0];
+  L->signs.w[1] = (uint32_t)(words[0] >> 32);
+  L->signs.w[2] = (uint32_t)words[1];
+  L->signs.w[3] = (uint32_t)(words[1] >> 32);
+  L->kc = d->k_centroids;
+  L->kt = d->k_boundaries;
+  L->vc = d->v_centroids;
+  L->vt = d->v_boundaries;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits) {
+  if (D < 1 || D > 65536 || k_bits < 1 || k_bits > 8 || v_bits < 1 || v_bits > 8)
+    return TQ_ERR_INVALID_ARG;
+  return (code_bytes(D, k_bits) + 4) + (code_bytes(D, v_bits) + 4);
+}
+
+extern "C" int tq_quantize_append(const tq_layer_desc* layer, const void* k, const void* v,
+                                  const int64_t* slot_mapping, int64_t n_tok, void* pages,
+                                  int64_t num_blocks, tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, false, &L);
+  if (st != TQ_OK) return st;
+  if (n_tok < 0 || num_blocks < 0) return TQ_ERR_INVALID_ARG;
+  if (n_tok == 0) return TQ_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || pages == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (n_tok > (int64_t)1 << 40) return TQ_ERR_INVALID_ARG;
+  return tq_launch_quantize(L, k, v, slot_mapping, n_tok, pages, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+extern "C" size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs,
+                                            int32_t max_seq_len) {
+  TqLayer L;
+  if (make_layer(layer, true, &L) != TQ_OK || num_seqs < 0 || max_seq_len < 0) return 0;
+  return tq_decode_ws_bytes(L, num_seqs, tq_decode_split(L, num_seqs, max_seq_len));
+}
+
+extern "C" int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q,
+                                         const void* pages, int64_t num_blocks,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, int32_t num_seqs,
+                                         int32_t max_seq_len, const void* sink_k,
+                                         const void* sink_v, int32_t n_sink, float scale,
+                                         float* out, void* workspace, size_t workspace_bytes,
+                                         tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, true, &L);
+  if (st != TQ_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || n_sink < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return TQ_ERR_UNSUPPORTED;
+  if (n_sink > TQ_MAX_SINKS) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return TQ_OK;
+  if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
+    return TQ_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  const TqSplit sp = tq_decode_split(L, num_seqs, max_seq_len);
+  if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) return TQ_ERR_WORKSPACE;
+  return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
+                          sink_k, sink_v, n_sink, scale, out, workspace, stream) == 0
+             ? TQ_OK
+             : TQ_ERR_HIP;
+}
+
+extern "C" int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages, int64_t num_blocks,
+                                  const int64_t* slots, int64_t n, float* k_out, float* v_out,
+                                  tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, false, &L);
+  if (st != TQ_OK) return st;
+  if (n < 0 || num_blocks < 0) return TQ_ERR_INVALID_ARG;
+  if (n == 0) return TQ_OK;
+  if (pages == nullptr || slots == nullptr || k_out == nullptr || v_out == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  return tq_launch_dequant(L, pages, slots, n, k_out, v_out, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+extern "C" const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported head_dim, bit width or size";
+    case TQ_ERR_WORKSPACE: return "decode workspace too small";
+    case TQ_ERR_HIP: return "HIP runtime error while enqueueing";
+    case TQ_ERR_NO_CONVERGENCE: return "Lloyd-Max solver did not converge";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,50 @@
+// Internal declarations shared by the C ABI layer (tq_api.cpp), the host set-up code
+// (tq_codebook.cpp) and the kernels (tq_kernels.hip).  Not part of the public ABI.
+#ifndef TQ_INTERNAL_H_
+#define TQ_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+// Sign bits of the rotation for head dimension D (bit i set: s_i = -1), nwords 64-bit words.
+void tq_sign_words(int32_t D, uint64_t seed, uint64_t* words, int nwords);
+
+// Largest n_sink the decode kernel accepts (sink scores live in LDS).
+#define TQ_MAX_SINKS 128
+
+// Sign bits as passed to the kernels by value (D <= 128).
+struct TqSigns {
+  uint32_t w[4];
+};
+
+// Validated launch parameters shared by the launchers.
+struct TqLayer {
+  int D, Hq, Hkv, G, bs, kb, vb;
+  int stride;          // slot stride in bytes
+  int slot_bytes;      // K region + V region
+  int kcode_bytes;     // ceil(D * kb / 8)
+  int vcode_bytes;     // ceil(D * vb / 8)
+  TqSigns signs;
+  const float *kc, *kt, *vc, *vt;
+};
+
+// Decode split geometry chosen on the host.
+struct TqSplit {
+  int chunk;      // page tokens per split
+  int max_split;  // splits per (sequence, kv head) at max_seq_len
+};
+
+TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len);
+size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp);
+
+// Launchers: return a hipError_t value (0 on success).
+int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,
+                       int64_t n_tok, void* pages, void* stream);
+int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
+                     int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
+                     const void* sink_k, const void* sink_v, int n_sink, float scale, float* out,
+                     void* workspace, void* stream);
+int tq_launch_dequant(const TqLayer& L, const void* pages, const int64_t* slots, int64_t n,
+                      float* k_out, float* v_out, void* stream);
+
+#endif  // TQ_INTERNAL_H_

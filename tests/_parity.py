@@ -1,0 +1,150 @@
+"""Shared helpers of the GPU parity tests: build one seeded case, run the HIP path through the C ABI
+and the CPU oracle on the same inputs, and compare at the three levels (packed bytes, dequantized
+rows, attention output)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import attention as oatt
+from oracle import codebook as ocb
+from oracle import quantize as oq
+
+# Attention tolerance (fp32 accumulation on the GPU vs fp64 oracle): max-abs and relative L2.
+ATOL = 1e-3
+REL_L2 = 1e-4
+
+
+def check_attention(got: np.ndarray, want: np.ndarray, seqs=None):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    if seqs is not None:
+        got, want = got[seqs], want[seqs]
+    err = np.abs(got - want)
+    max_abs = float(err.max()) if err.size else 0.0
+    denom = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(got - want) / denom) if denom > 0 else float(np.linalg.norm(got))
+    assert np.all(np.isfinite(got)), "non-finite attention output"
+    assert max_abs <= ATOL, f"max-abs {max_abs:.3e} > {ATOL}"
+    assert rel <= REL_L2, f"relative L2 {rel:.3e} > {REL_L2}"
+    return max_abs, rel
+
+
+def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D: int, kb: int,
+                  vb: int, stride: int, k_tie: np.ndarray, v_tie: np.ndarray) -> int:
+    """Packed bytes must be identical except for indices at oracle-listed ties (|u - t_j| <= 1e-6),
+    where the neighbouring index is accepted.  Returns the number of accepted tie differences.
+
+    slots: [n] slot of each token row (k_tie/v_tie are [n, H, D]); negative slots are skipped.
+    """
+    keep = slots >= 0
+    slots, k_tie, v_tie = slots[keep], k_tie[keep], v_tie[keep]
+    g = gpu.reshape(-1, H, stride)[slots]
+    r = ref.reshape(-1, H, stride)[slots]
+    if np.array_equal(g, r):
+        return 0
+    sb = oq.slot_bytes(D, kb, vb)
+    kr = oq.region_bytes(D, kb)
+    assert np.array_equal(g[:, :, sb:], r[:, :, sb:]), "padding bytes differ"
+    ties = 0
+    for lo, hi, bits, tie in ((0, kr, kb, k_tie), (kr, sb, vb, v_tie)):
+        gi, gn = oq.unpack_regions(g[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
+        ri, rn = oq.unpack_regions(r[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
+        assert np.array_equal(gn.view(np.uint32), rn.view(np.uint32)), "stored norms differ"
+        bad = gi != ri
+        t = tie.reshape(-1, D)
+        assert np.all(t[bad]), f"{int(np.sum(bad & ~t))} index differences outside the tie band"
+        assert np.all(np.abs(gi[bad] - ri[bad]) == 1)
+        ties += int(bad.sum())
+    return ties
+
+
+def oracle_codebooks(D, kb, vb, family="beta"):
+    k = ocb.codebook(D, kb, family)
+    v = ocb.codebook(D, vb, family)
+    return (k.centroids32, k.boundaries32), (v.centroids32, v.boundaries32)
+
+
+class Case:
+    """One seeded decode case: per-sequence K/V for every cached position, queries, sinks,
+    block tables, and the oracle's pages."""
+
+    def __init__(self, w, layer=0, lens=None, slack=0, family="beta", slot_stride=0):
+        import torch
+        from packed_decode_attention_amd import workloads as wl
+        self.w = w
+        kb, vb = w.bits(layer)
+        self.kb, self.vb = kb, vb
+        self.D, self.H, self.Hq = w.head_dim, w.num_kv_heads, w.num_q_heads
+        self.lens = np.asarray(wl.seq_lens(w) if lens is None else lens, np.int32)
+        self.bt, self.num_blocks = wl.block_tables(w, np.maximum(self.lens, 1), slack)
+        self.family = family
+        self.slot_stride = slot_stride or oq.slot_bytes(self.D, kb, vb)
+        n_tok = int(self.lens.sum())
+        self.k = wl.kv_values(w, layer, n_tok, "k")
+        self.v = wl.kv_values(w, layer, n_tok, "v")
+        slots = [wl.token_slots(self.bt, b, np.arange(L), w.block_size) for b, L in enumerate(self.lens)]
+        self.slots = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+        self.q = wl.queries(w, layer)
+        self.sink_k, self.sink_v = wl.sinks(w, layer)
+        (kc, kt), (vc, vt) = oracle_codebooks(self.D, kb, vb, family)
+        self.kcb, self.vcb = (kc, kt), (vc, vt)
+        self.layer_dict = dict(D=self.D, H_kv=self.H, block_size=w.block_size, k_bits=kb, v_bits=vb,
+                               seed=0, slot_stride=self.slot_stride)
+        self.pages_ref = np.zeros(self.num_blocks * w.block_size * self.H * self.slot_stride, np.uint8)
+        self.k_tie, self.v_tie = oq.append_rows_fast(
+            self.pages_ref, self.k.numpy(), self.v.numpy(), self.slots, kt, vt, kb, vb, 0,
+            self.slot_stride)
+        self._torch = torch
+
+    # ---- HIP path -------------------------------------------------------------------------
+    def fmt(self):
+        from packed_decode_attention_amd import LayerFormat
+        return LayerFormat(self.D, self.Hq, self.H, self.kb, self.vb, self.w.block_size, 0,
+                           self.family, slot_stride=self.slot_stride if self.slot_stride !=
+                           oq.slot_bytes(self.D, self.kb, self.vb) else 0,
+                           k_codebook=self.kcb, v_codebook=self.vcb)
+
+    def gpu_quantize(self, fmt):
+        import packed_decode_attention_amd as tq
+        torch = self._torch
+        pages = torch.full((self.num_blocks, self.w.block_size, self.H, self.slot_stride), 0x5A,
+                           dtype=torch.uint8, device="cuda")
+        tq.tq_quantize_append(fmt.desc, self.k.cuda(), self.v.cuda(),
+                              torch.from_numpy(self.slots).cuda(), pages, self.num_blocks)
+        torch.cuda.synchronize()
+        return pages
+
+    def gpu_decode(self, fmt, pages_dev, workspace=None, scale=0.0):
+        import packed_decode_attention_amd as tq
+        torch = self._torch
+        B = len(self.lens)
+        max_len = int(self.lens.max()) if B else 0
+        ws = fmt.new_workspace(B, max_len) if workspace is None else workspace
+        out = torch.full((B, self.Hq, self.D), float("nan"), dtype=torch.float32, device="cuda")
+        sk = None if self.sink_k is None else self.sink_k.cuda()
+        sv = None if self.sink_v is None else self.sink_v.cuda()
+        tq.tq_paged_decode_attention(fmt.desc, self.q.cuda(), pages_dev, self.num_blocks,
+                                     torch.from_numpy(self.bt).cuda(),
+                                     torch.from_numpy(self.lens).cuda(), max_len, out, ws,
+                                     sk, sv, self.w.n_sink, scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), ws
+
+    def ref_pages_on_gpu(self):
+        torch = self._torch
+        return torch.from_numpy(self.pages_ref).cuda().reshape(
+            self.num_blocks, self.w.block_size, self.H, self.slot_stride)
+
+    # ---- oracle -----------------------------------------------------------------------------
+    def oracle_decode(self, seqs=None, scale=None):
+        sk = None if self.sink_k is None else self.sink_k.numpy()
+        sv = None if self.sink_v is None else self.sink_v.numpy()
+        return oatt.decode_attention(self.q.numpy(), self.pages_ref, self.bt, self.lens, self.layer_dict,
+                                     self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink, scale=scale, seqs=seqs)
+
+    def oracle_dequant(self, slots):
+        k_idx, k_n, v_idx, v_n = oq.read_slots(self.pages_ref, slots, self.H, self.D, self.kb, self.vb,
+                                               self.slot_stride)
+        return (oq.dequantize_spec(k_idx, k_n, self.kcb[0], 0),
+                oq.dequantize_spec(v_idx, v_n, self.vcb[0], 0))

@@ -1,0 +1,143 @@
+"""CPU-only checks of the HIP library: it loads, exports every declared symbol, and its host-side
+set-up (slot bytes, rotation signs, Lloyd-Max codebooks, argument validation) matches the oracle.
+No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import codebook as ocb
+from oracle import quantize as oq
+from oracle import rotation as orot
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import packed_decode_attention_amd._lib as L
+    return L
+
+
+def test_library_exports_every_declared_symbol(lib):
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", header))
+    assert declared == set(lib.EXPORTS)
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+def test_slot_bytes(lib):
+    for D in (64, 128, 256, 1024):
+        for kb in range(1, 9):
+            for vb in range(1, 9):
+                assert lib.tq_slot_bytes(D, kb, vb) == oq.slot_bytes(D, kb, vb)
+    with pytest.raises(lib.TqError):
+        lib.tq_slot_bytes(128, 9, 4)
+
+
+def test_rht_signs_match_oracle(lib):
+    for D in (64, 128, 1000):
+        for seed in (0, 1, 12345, 2 ** 63 + 7):
+            assert lib.tq_rht_signs(D, seed).tolist() == orot.signs(seed, D).astype(int).tolist()
+
+
+@pytest.mark.parametrize("family", ["beta", "gaussian"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
+def test_build_codebook_matches_oracle(lib, family, D, bits):
+    c, t, c64, t64, mse = lib.tq_build_codebook(D, bits, family)
+    ref = ocb.codebook(D, bits, family)
+    np.testing.assert_allclose(c64, ref.centroids, atol=1e-10, rtol=0)
+    np.testing.assert_allclose(t64, ref.boundaries, atol=1e-10, rtol=0)
+    assert abs(mse - ref.mse) < 1e-12
+    # The fp32 arrays the kernels use equal the oracle's, except where the fp64 fixed point lies
+    # so close to an fp32 rounding midpoint that the two independent fp64 solves (which agree to
+    # about 1e-11 at 256 levels) round to neighbouring floats.  Those rounding ties are 1 ulp apart.
+    for got, want64 in ((c, ref.centroids), (t, ref.boundaries)):
+        want = want64.astype(np.float32)
+        diff = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+        for i in diff:
+            a, b = sorted((float(got[i]), float(want[i])))
+            assert np.nextafter(np.float32(a), np.float32(np.inf)) == np.float32(b)
+            assert abs(want64[i] - 0.5 * (a + b)) < 5e-11
+        assert len(diff) <= 4
+
+
+def test_build_codebook_rejects_bad_arguments(lib):
+    with pytest.raises(lib.TqError):
+        lib.tq_build_codebook(128, 9, "beta")
+    so = lib._lib()
+    buf = np.zeros(16, np.float32)
+    assert so.tq_build_codebook(128, 4, 7, buf.ctypes.data, buf.ctypes.data, None, None, None) == lib.TQ_ERR_INVALID_ARG
+    assert so.tq_build_codebook(128, 4, 0, None, buf.ctypes.data, None, None, None) == lib.TQ_ERR_INVALID_ARG
+
+
+def _desc(lib, **kw):
+    fake = 0x10000  # never dereferenced: validation fails before anything is enqueued
+    d = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, block_size=16, k_bits=4, v_bits=4,
+             slot_stride=0, reserved=0, rht_seed=0, k_centroids=fake, k_boundaries=fake,
+             v_centroids=fake, v_boundaries=fake)
+    d.update(kw)
+    return lib.tq_layer_desc(**d)
+
+
+def test_argument_validation_before_launch(lib):
+    so = lib._lib()
+    P = ctypes.c_void_p(0x20000)
+    E = lib
+    q = lambda d, n=4, **kw: so.tq_quantize_append(ctypes.byref(d), kw.get("k", P), kw.get("v", P),
+                                                    kw.get("sm", P), n, kw.get("pages", P), 10, None)
+    assert q(_desc(lib, head_dim=96)) == E.TQ_ERR_UNSUPPORTED
+    assert q(_desc(lib, k_bits=5)) == E.TQ_ERR_UNSUPPORTED
+    assert q(_desc(lib, v_bits=1)) == E.TQ_ERR_UNSUPPORTED
+    assert q(_desc(lib, slot_stride=100)) == E.TQ_ERR_INVALID_ARG      # < 136
+    assert q(_desc(lib, slot_stride=138)) == E.TQ_ERR_INVALID_ARG      # not a multiple of 4
+    assert q(_desc(lib, reserved=1)) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib, num_kv_heads=0)) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib, block_size=0)) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib, k_centroids=0)) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib), k=None) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib), n=-1) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib), n=0, k=None) == E.TQ_OK                       # nothing to do
+    assert so.tq_quantize_append(None, P, P, P, 1, P, 1, None) == E.TQ_ERR_INVALID_ARG
+
+    def dec(d, ws_bytes=1 << 40, n_sink=0, sk=None, B=4, max_len=100, bt=P, mb=7):
+        return so.tq_paged_decode_attention(ctypes.byref(d), P, P, 100, bt, mb, P, B, max_len, sk, sk,
+                                            n_sink, 0.0, P, P, ws_bytes, None)
+    assert dec(_desc(lib, num_q_heads=30)) == E.TQ_ERR_INVALID_ARG      # 30 % 8 != 0
+    assert dec(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED      # G = 9 > 8
+    assert dec(_desc(lib), ws_bytes=16) == E.TQ_ERR_WORKSPACE
+    assert dec(_desc(lib), n_sink=4) == E.TQ_ERR_INVALID_ARG            # sinks without arrays
+    assert dec(_desc(lib), n_sink=129, sk=P) == E.TQ_ERR_UNSUPPORTED
+    assert dec(_desc(lib), mb=6) == E.TQ_ERR_INVALID_ARG                # 6 * 16 < 100 tokens
+    assert dec(_desc(lib), bt=None) == E.TQ_ERR_INVALID_ARG
+    assert dec(_desc(lib), B=0) == E.TQ_OK
+    assert dec(_desc(lib), B=-1) == E.TQ_ERR_INVALID_ARG
+
+    dq = lambda d, n=3: so.tq_dequantize_rows(ctypes.byref(d), P, 10, P, n, P, P, None)
+    assert dq(_desc(lib, head_dim=256)) == E.TQ_ERR_UNSUPPORTED
+    assert dq(_desc(lib), n=-2) == E.TQ_ERR_INVALID_ARG
+    assert dq(_desc(lib), n=0) == E.TQ_OK
+    assert so.tq_dequantize_rows(ctypes.byref(_desc(lib)), None, 10, P, 3, P, P, None) == E.TQ_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(lib):
+    d = _desc(lib)
+    so = lib._lib()
+    a = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 32769)
+    b = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 100)
+    assert a >= b > 0
+    # counters (one per sequence and kv head) + split partials (G * (D + 2) floats each)
+    assert a >= 16 * 8 * 4 + 16 * 8 * 4 * 130 * 4
+    assert so.tq_decode_workspace_bytes(ctypes.byref(_desc(lib, head_dim=80)), 16, 100) == 0
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(lib.tq_status_str(s), str) and lib.tq_status_str(s)
