@@ -1,0 +1,280 @@
+"""Benchmark of the packed-KV decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: for every layer, quantize-on-append of
+one new token per sequence into the packed pages, then fused paged decode attention over all
+cached tokens.  Inputs (pages filled by a bulk quantize of the context, queries, new tokens) are
+resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama3-8b] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-KV decode attention: KV tokens/s + achieved HBM GB/s vs peak, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BULK_CHUNK = 1 << 18  # tokens per bulk-fill quantize call
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def describe(w):
+    pol = f"K{w.k_bits}/V{w.v_bits}"
+    if w.protected:
+        pol += " (layers " + ",".join(str(k) for k in sorted(w.protected)) + " K8/V8)"
+    ctx = f"{w.context}+1" if w.ragged is None else f"U[{w.ragged[0]},{w.ragged[1]}]+1"
+    s = (f"{w.name}: {w.layers} layers, {w.num_seqs} seqs x {ctx} tokens, {w.num_q_heads}/"
+         f"{w.num_kv_heads} heads, D={w.head_dim}, {pol} TQ pages bs{w.block_size}")
+    if w.n_sink:
+        s += f", {w.n_sink} fp16 sinks"
+    return s
+
+
+class LayerState:
+    def __init__(self, fmt, pages, num_blocks):
+        self.fmt, self.pages, self.num_blocks = fmt, pages, num_blocks
+
+
+def setup(w, torch, tq, wl, n_steps_total):
+    lens = wl.seq_lens(w)                       # includes the token appended each step
+    bt_np, num_blocks = wl.block_tables(w, lens)
+    dev = "cuda"
+    bt = torch.from_numpy(bt_np).to(dev)
+    seq_lens = torch.from_numpy(lens).to(dev)
+    B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
+    # slots of the context (bulk fill) and of the appended position, per sequence
+    ctx_slots = [wl.token_slots(bt_np, b, np.arange(lens[b] - 1), w.block_size) for b in range(B)]
+    ctx_slots = torch.from_numpy(np.concatenate(ctx_slots)).to(dev)
+    new_slots = torch.from_numpy(np.array([wl.token_slots(bt_np, b, [lens[b] - 1], w.block_size)[0]
+                                           for b in range(B)], np.int64)).to(dev)
+    fmts = {}
+    layers = []
+    bulk_ms, bulk_rows = [], 0
+    n_ctx = int(ctx_slots.numel())
+    for l in range(w.layers):
+        kb, vb = w.bits(l)
+        if (kb, vb) not in fmts:
+            fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0)
+        fmt = fmts[(kb, vb)]
+        pages = fmt.new_pages(num_blocks)
+        gk = wl.generator(w.seed * 1000003 + l * 31, dev)
+        gv = wl.generator(w.seed * 1000003 + l * 31 + 1, dev)
+        t_layer = 0.0
+        for s0 in range(0, n_ctx, BULK_CHUNK):
+            n = min(BULK_CHUNK, n_ctx - s0)
+            k = wl.kv_values(w, l, n, "k", dev, gen=gk)
+            v = wl.kv_values(w, l, n, "v", dev, gen=gv)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tq.tq_quantize_append(fmt.desc, k, v, ctx_slots[s0:s0 + n], pages, num_blocks)
+            e1.record()
+            e1.synchronize()
+            t_layer += e0.elapsed_time(e1)
+            del k, v
+        if l > 0:  # layer 0 includes first-launch costs
+            bulk_ms.append(t_layer)
+        bulk_rows = n_ctx * H
+        layers.append(LayerState(fmt, pages, num_blocks))
+    torch.cuda.synchronize()
+    # per-step inputs: queries and one new K/V token per sequence and layer
+    qs = [wl.queries(w, l, 0, dev) for l in range(w.layers)]
+    gnew = wl.generator(w.seed * 99991 + 17, dev)
+    new_k = wl.kv_values(w, 0, n_steps_total * w.layers * B, "k", dev, gen=gnew).reshape(
+        n_steps_total, w.layers, B, H, D)
+    new_v = wl.kv_values(w, 0, n_steps_total * w.layers * B, "v", dev, gen=gnew).reshape(
+        n_steps_total, w.layers, B, H, D)
+    sink_k, sink_v = wl.sinks(w, 0, dev)
+    max_len = int(lens.max())
+    ws = fmts[(w.k_bits, w.v_bits)].new_workspace(B, max_len)
+    for f in fmts.values():
+        assert tq.tq_decode_workspace_bytes(f.desc, B, max_len) <= ws.numel()
+    out = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device=dev)
+    return dict(lens=lens, bt=bt, seq_lens=seq_lens, new_slots=new_slots, layers=layers, qs=qs,
+                new_k=new_k, new_v=new_v, sink_k=sink_k, sink_v=sink_v, max_len=max_len, ws=ws,
+                out=out, bulk_ms=bulk_ms, bulk_rows=bulk_rows, n_ctx=n_ctx, num_blocks=num_blocks)
+
+
+def run_step(w, S, tq, step, ev=None):
+    for l, L in enumerate(S["layers"]):
+        if ev is not None:
+            ev["a0"][l].record()
+        tq.tq_quantize_append(L.fmt.desc, S["new_k"][step, l], S["new_v"][step, l], S["new_slots"],
+                              L.pages, L.num_blocks)
+        if ev is not None:
+            ev["a1"][l].record()
+        tq.tq_paged_decode_attention(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
+                                     S["seq_lens"], S["max_len"], S["out"], S["ws"],
+                                     S["sink_k"], S["sink_v"], w.n_sink)
+        if ev is not None:
+            ev["d1"][l].record()
+
+
+def algorithmic_bytes(w, lens, tq):
+    """Bytes the decode of one layer must move, and the bytes of one bulk-fill row pair."""
+    B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
+    per_layer = []
+    for l in range(w.layers):
+        kb, vb = w.bits(l)
+        sb = tq.tq_slot_bytes(D, kb, vb)
+        page_tok = np.maximum(lens - w.n_sink, 0)
+        b = int(page_tok.sum()) * H * sb                                  # packed slots
+        b += int(np.sum((lens + w.block_size - 1) // w.block_size)) * 4   # block tables
+        b += B * w.num_q_heads * D * 2 + B * w.num_q_heads * D * 4 + B * 4  # q, out, seq_lens
+        b += B * w.n_sink * H * D * 2 * 2                                 # fp16 sinks
+        per_layer.append(b)
+    return per_layer
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle as it stands, on a bounded sample: one layer, the first sequences in turn until
+    about `budget_s` seconds of decode work have been timed; pages built by the oracle itself."""
+    import threadpoolctl
+    import torch
+    from oracle import attention as oatt
+    from oracle import codebook as ocb
+    from oracle import quantize as oq
+    from packed_decode_attention_amd import workloads as wl
+
+    lens = wl.seq_lens(w)
+    l = 0
+    kb, vb = w.bits(l)
+    ck, cv = ocb.codebook(w.head_dim, kb), ocb.codebook(w.head_dim, vb)
+    layer = dict(D=w.head_dim, H_kv=w.num_kv_heads, block_size=w.block_size, k_bits=kb, v_bits=vb, seed=0)
+    q = wl.queries(w, l).numpy()
+    sk, sv = wl.sinks(w, l)
+    sk = None if sk is None else sk.numpy()
+    sv = None if sv is None else sv.numpy()
+    tokens, t_dec, t_q, rows_q, seqs = 0, 0.0, 0.0, 0, []
+    for b in range(w.num_seqs):
+        L = int(lens[b])
+        one = wl.scaled(w, num_seqs=1)
+        bt1, nblk = wl.block_tables(one, np.array([L]))
+        pages = np.zeros(nblk * w.block_size * w.num_kv_heads * oq.slot_bytes(w.head_dim, kb, vb), np.uint8)
+        k = wl.kv_values(w, l, L, "k").numpy()
+        v = wl.kv_values(w, l, L, "v").numpy()
+        slots = wl.token_slots(bt1, 0, np.arange(L), w.block_size)
+        t0 = time.perf_counter()
+        oq.append_rows_fast(pages, k, v, slots, ck.boundaries32, cv.boundaries32, kb, vb, 0)
+        t1 = time.perf_counter()
+        oatt.decode_attention(q[b:b + 1], pages, bt1, np.array([L]), layer, ck.centroids32, cv.centroids32,
+                              None if sk is None else sk[b:b + 1], None if sv is None else sv[b:b + 1], w.n_sink)
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        rows_q += L * w.num_kv_heads
+        t_dec += t2 - t1
+        tokens += L
+        seqs.append(b)
+        if t_dec + t_q > budget_s:
+            break
+    threads = max([p["num_threads"] for p in threadpoolctl.threadpool_info()] + [1])
+    return {"value": tokens / t_dec, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"layer 0 decode of sequences {seqs} ({tokens} KV tokens, {w.num_kv_heads} kv heads, "
+                       f"{w.num_q_heads} q heads) with fp64 NumPy oracle on {os.cpu_count()} host cores; "
+                       f"oracle quantize of the same {rows_q} rows took {t_q:.1f}s ({rows_q / t_q:.0f} rows/s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3-8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import packed_decode_attention_amd as tq
+    from packed_decode_attention_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    log(f"workload {describe(w)}")
+    total = args.warmup + args.steps
+    t0 = time.time()
+    S = setup(w, torch, tq, wl, total)
+    log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
+
+    for s in range(args.warmup):
+        run_step(w, S, tq, s)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(w.layers * args.steps)]
+          for k in ("a0", "a1", "d1")}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        sub = {k: v[s * w.layers:(s + 1) * w.layers] for k, v in ev.items()}
+        run_step(w, S, tq, args.warmup + s, sub)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    n = w.layers * args.steps
+    dec_ms = np.array([ev["a1"][i].elapsed_time(ev["d1"][i]) for i in range(n)])
+    app_ms = np.array([ev["a0"][i].elapsed_time(ev["a1"][i]) for i in range(n)])
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; decode {dec_ms.mean() * 1e3:.1f} us/layer "
+        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
+        f"append {app_ms.mean() * 1e3:.1f} us/layer")
+
+    lens = S["lens"]
+    kv_tokens_step = int(lens.sum()) * w.layers
+    value = kv_tokens_step / (ms_per_step / 1e3)
+    per_layer_bytes = algorithmic_bytes(w, lens, tq)
+    layer_ids = np.arange(n) % w.layers
+    dec_bytes = np.array([per_layer_bytes[i] for i in layer_ids], np.float64)
+    achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
+    bulk_ms = float(np.mean(S["bulk_ms"])) if S["bulk_ms"] else float("nan")
+    kb, vb = w.bits(1 % w.layers)
+    bulk_bytes = S["n_ctx"] * w.num_kv_heads * (4 * w.head_dim + tq.tq_slot_bytes(w.head_dim, kb, vb)) + S["n_ctx"] * 8
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "kv_tokens_per_layer": int(lens.sum()),
+                   "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tq_decode_kernel", "bytes_per_launch": float(np.mean(dec_bytes)),
+                     "avg_launch_us": float(dec_ms.mean() * 1e3)},
+        "append": {"step_us_per_layer": float(app_ms.mean() * 1e3),
+                   "bulk_fill_us_per_layer": bulk_ms * 1e3,
+                   "bulk_fill_GBps": bulk_bytes / (bulk_ms / 1e3) / 1e9,
+                   "bulk_fill_frac": bulk_bytes / (bulk_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                   "bulk_rows": S["bulk_rows"]},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,11 +117,9 @@ int tq_quantize_append(const tq_layer_desc* layer, const void* k, const void* v,
                        const int64_t* slot_mapping, int64_t n_tok, void* pages, int64_t num_blocks,
                        tq_stream_t stream);
 
-/* Workspace bytes tq_paged_decode_attention needs for these sizes.  The workspace holds
- * split-K partial results and per-(sequence, kv head) arrival counters.  The counter region
- * must be zero before the first call that uses a workspace (zero the whole buffer once after
- * allocating it); every call leaves it zero again.  Calls sharing a workspace must be ordered
- * on one stream. */
+/* Workspace bytes tq_paged_decode_attention needs for these sizes: the split-K partial results
+ * (running max, sum and rotated accumulator per sequence, query head and split).  It needs no
+ * initialisation.  Calls sharing a workspace must be ordered on one stream. */
 size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs, int32_t max_seq_len);
 
 /* Fused paged decode attention over packed pages, one query token per sequence.

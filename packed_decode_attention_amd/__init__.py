@@ -69,7 +69,7 @@ class LayerFormat:
                            dtype=torch.uint8, device=device)
 
     def new_workspace(self, num_seqs: int, max_seq_len: int, device="cuda"):
-        """Zeroed decode workspace (the arrival counters must start at zero)."""
+        """Decode workspace for up to num_seqs sequences of at most max_seq_len tokens."""
         import torch
         n = tq_decode_workspace_bytes(self.desc, num_seqs, max_seq_len)
-        return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=device)

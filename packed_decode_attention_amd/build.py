@@ -26,7 +26,8 @@ DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
 
 SOURCES = [
-    ("tq_kernels.hip", "device"),
+    ("tq_quantize.hip", "device"),
+    ("tq_decode.hip", "device"),
     ("tq_api.cpp", "host"),
     ("tq_codebook.cpp", "host"),
 ]

@@ -1,0 +1,458 @@
+// Fused paged decode attention over packed TQ pages, gfx950.
+//
+// Method: scores on the codes with a rotated query, online softmax, values accumulated in the
+// rotated frame and rotated back once per output (tq-kv "Quick Start": pre_rotate_query_with_signs
+// and fused_attention_scores; "Custom CUDA Kernel Stack": split-KV flash decode with online
+// softmax, attention on compressed KV without decompression; "3-Fix for GGUF Models": sink tokens
+// kept fp16; turboquant-pro 1.4.2 "Fused CUDA decode": split-K decode on the codes).  With
+// R = D^(-1/2) H diag(s):  q . (n R^T c) = n (R q) . c  and  sum_p w_p n_p R^T c_p = R^T sum_p w_p n_p c_p.
+//
+// Two launches:
+//  1. tq_decode_split_kernel: one workgroup (4 waves) per (sequence, kv head, split of `chunk` page
+//     tokens).  A token row is held by P lanes (C = D/P coordinates each; P = 8, or 16 for 8 query
+//     heads at D = 128), so a wave covers 64/P tokens per step and the QK dot product needs a
+//     log2(P)-step DPP reduction.  The G query heads that share the kv head are processed
+//     together, so each code is unpacked and looked up once for G heads.  Centroids come from
+//     per-workgroup LDS tables indexed by whole bytes of codes.  Page rows are prefetched
+//     kPrefetch steps ahead into registers; the block-table segment of the split sits in LDS so
+//     no global load waits on another.  The online softmax keeps a running maximum per (row
+//     group, head) and rescales only when it grows.  Writes (m, l, acc[D]) per split.
+//  2. tq_decode_merge_kernel: one workgroup per (sequence, kv head): log-sum-exp merge of the
+//     splits and the fp16 sinks, R^T by Walsh-Hadamard butterflies in LDS, division by the sum.
+//
+// Workgroups of the same (sequence, split) for different kv heads read adjacent bytes of the same
+// page rows; the grid is laid out so that they land on the same XCD (round-robin dispatch puts
+// workgroup i on XCD i % 8) and share its L2.
+
+#include "tq_device.h"
+
+namespace {
+using namespace tqd;
+
+constexpr int kNW = 4;          // waves per split workgroup
+constexpr int kPrefetch = 4;    // page-row steps kept in flight per wave
+constexpr int kMaxBtLds = 1024; // block-table entries staged in LDS per split
+
+// Lanes per token row: 8, or 16 when 8 query heads share a kv head at D = 128, so that the
+// per-lane query and accumulator registers (2 * G * C) still fit.
+template <int D, int GMAX>
+constexpr int lanes_per_row() { return (D == 128 && GMAX == 8) ? 16 : 8; }
+
+struct DecodeArgs {
+  TqLayer L;
+  float rsqrt_d, qscale, sink_scale;
+  const uint16_t* q;
+  const uint8_t* pages;
+  const int32_t* bt;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int chunk, max_split, n_units, bs_shift;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  int n_sink;
+  float* out;
+  float* partials;   // [B][Hkv][max_split][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
+};
+
+// Raw page data of one step for one lane.
+template <int NBK, int NBV>
+struct Step {
+  LaneCodes<NBK> k;
+  LaneCodes<NBV> v;
+  float kn, vn;
+  bool valid;
+};
+
+template <int D, int KB, int VB, int GMAX>
+__global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
+  constexpr int P = lanes_per_row<D, GMAX>();
+  constexpr int C = D / P;
+  constexpr int TPW = 64 / P;           // tokens per wave per step
+  constexpr int TPI = TPW * kNW;        // tokens per workgroup per step
+  constexpr int NBK = C * KB / 8;       // code bytes per lane
+  constexpr int NBV = C * VB / 8;
+  const TqLayer& L = a.L;
+  const int G = L.G;
+
+  // (sequence, split) units with equal index modulo 8 share an XCD across all kv heads
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7;
+  const int rest = lin >> 3;
+  const int h = rest % L.Hkv;
+  const int unit = (rest / L.Hkv) * 8 + xcd;
+  if (unit >= a.n_units) return;
+  const int b = unit / a.max_split;
+  const int split = unit - b * a.max_split;
+  const int seq_len = a.seq_lens[b];
+  const int ns = min(a.n_sink, seq_len);
+  const int npage = seq_len - ns;
+  const int nsplit = npage > 0 ? (npage + a.chunk - 1) / a.chunk : 1;
+  if (split >= nsplit) return;
+
+  __shared__ float s_klut[Lut<KB>::kFloats];
+  __shared__ float s_vlut[Lut<VB>::kFloats];
+  __shared__ float s_part[kNW][GMAX][D + 2];
+  __shared__ int32_t s_bt[kMaxBtLds];
+  build_lut<KB>(s_klut, L.kc, threadIdx.x, kWG);
+  build_lut<VB>(s_vlut, L.vc, threadIdx.x, kWG);
+
+  const int p_begin = ns + split * a.chunk;
+  const int p_end = min(ns + (split + 1) * a.chunk, seq_len);
+  const int n_it = (p_end - p_begin + TPI - 1) / TPI;
+  auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
+  const int blk0 = p_end > p_begin ? block_of(p_begin) : 0;
+  const int nblk = p_end > p_begin ? block_of(p_end - 1) - blk0 + 1 : 0;  // <= kMaxBtLds (host)
+  const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
+  for (int i = threadIdx.x; i < nblk; i += kWG) s_bt[i] = btg[i];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & (P - 1);
+  const int sub = lane / P;
+
+  // Rotated query qscale * H (s * q) for the G heads (qscale = scale * log2(e) / sqrt(D)):
+  // scores come out in the log2 domain.
+  uint32_t sbits = 0;
+#pragma unroll
+  for (int e = 0; e < C; e += 8) sbits |= sign_byte(L.signs, (C * j + e) / 8) << e;
+  float qr[GMAX][C];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g < G) {
+      const uint16_t* qp = a.q + ((int64_t)b * L.Hq + h * G + g) * D + C * j;
+#pragma unroll
+      for (int e = 0; e < C; e += 8) load8_f16(qp + e, &qr[g][e]);
+#pragma unroll
+      for (int e = 0; e < C; ++e) qr[g][e] = ((sbits >> e) & 1u) ? -qr[g][e] : qr[g][e];
+      wht_row<C, P>(qr[g], j);
+#pragma unroll
+      for (int e = 0; e < C; ++e) qr[g][e] *= a.qscale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < C; ++e) qr[g][e] = 0.0f;
+    }
+  }
+
+  float m[GMAX], l[GMAX], acc[GMAX][C];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C; ++e) acc[g][e] = 0.0f;
+  }
+
+  const int voff = L.kcode_bytes + 4;
+  const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
+  const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
+  __syncthreads();  // lookup tables and block-table segment ready
+
+  // Page row of step `it` for this lane's row group; rows past the end re-read the last valid
+  // row and are masked.
+  auto fetch = [&](int it) {
+    Step<NBK, NBV> st;
+    int p = p_begin + it * TPI + wave * TPW + sub;
+    st.valid = p < p_end;
+    p = st.valid ? p : p_end - 1;
+    const int bi = block_of(p);
+    const int64_t slot = (int64_t)s_bt[bi - blk0] * L.bs + (p - bi * L.bs);
+    const uint8_t* base = head_base + slot * row_bytes;
+    st.k = load_lane_codes<NBK>(base, j);
+    st.v = load_lane_codes<NBV>(base + voff, j);
+    st.kn = *reinterpret_cast<const float*>(base + L.kcode_bytes);
+    st.vn = *reinterpret_cast<const float*>(base + voff + L.vcode_bytes);
+    return st;
+  };
+
+  auto consume = [&](const Step<NBK, NBV>& st) {
+    float kf[C];
+    lookup_codes<KB, C>(st.k, s_klut, kf);
+    float s[GMAX];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < C; ++e) d += qr[g][e] * kf[e];
+      d = group_sum<P>(d);
+      s[g] = st.valid ? st.kn * d : -INFINITY;
+    }
+    bool grow = false;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) grow |= s[g] > m[g];
+    if (grow) {
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (s[g] > m[g]) {
+          const float r = __builtin_amdgcn_exp2f(m[g] - s[g]);
+          l[g] *= r;
+#pragma unroll
+          for (int e = 0; e < C; ++e) acc[g][e] *= r;
+          m[g] = s[g];
+        }
+      }
+    }
+    float vf[C];
+    lookup_codes<VB, C>(st.v, s_vlut, vf);
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      const float pw = st.valid ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
+      l[g] += pw;
+      const float w = pw * st.vn;
+#pragma unroll
+      for (int e = 0; e < C; ++e) acc[g][e] += w * vf[e];
+    }
+  };
+
+  // kPrefetch-deep register ring: slot u always holds step it0 + u.
+  Step<NBK, NBV> ring[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+    if (u < n_it) ring[u] = fetch(u);
+  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int it = it0 + u;
+      if (it < n_it) {
+        const Step<NBK, NBV> cur = ring[u];
+        if (it + kPrefetch < n_it) ring[u] = fetch(it + kPrefetch);
+        consume(cur);
+      }
+    }
+  }
+
+  // Merge the row groups of the wave (lanes with equal j hold the same coordinates).
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g < G) {
+#pragma unroll
+      for (int msk = P; msk < 64; msk <<= 1) {
+        const float mo = __shfl_xor(m[g], msk);
+        const float lo = __shfl_xor(l[g], msk);
+        const float M = fmaxf(m[g], mo);
+        const float r = (m[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[g] - M);
+        const float ro = (mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mo - M);
+        l[g] = l[g] * r + lo * ro;
+#pragma unroll
+        for (int e = 0; e < C; ++e) {
+          const float o = __shfl_xor(acc[g][e], msk);
+          acc[g][e] = acc[g][e] * r + o * ro;
+        }
+        m[g] = M;
+      }
+      if (sub == 0) {
+#pragma unroll
+        for (int e = 0; e < C; ++e) s_part[wave][g][2 + C * j + e] = acc[g][e];
+        if (j == 0) {
+          s_part[wave][g][0] = m[g];
+          s_part[wave][g][1] = l[g];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves and publish this split's partial (m, l, acc[D]).
+  const int64_t bh = (int64_t)b * L.Hkv + h;
+  float* part = a.partials + (bh * a.max_split + split) * (int64_t)G * (D + 2);
+  for (int i = threadIdx.x; i < G * (D + 2); i += kWG) {
+    const int g = i / (D + 2), d = i % (D + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_part[w][g][0]);
+    float r;
+    if (d == 0) {
+      r = M;
+    } else {
+      r = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const float mw = s_part[w][g][0];
+        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        r += s_part[w][g][d] * f;
+      }
+    }
+    part[i] = r;
+  }
+}
+
+// One workgroup per (sequence, kv head): merge the splits and the sinks, rotate back, normalise.
+template <int D, int GMAX>
+__global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
+  const TqLayer& L = a.L;
+  const int G = L.G;
+  const int h = blockIdx.x % L.Hkv;
+  const int b = blockIdx.x / L.Hkv;
+  const int seq_len = a.seq_lens[b];
+  const int ns = min(a.n_sink, seq_len);
+  const int npage = seq_len - ns;
+  const int nsplit = npage > 0 ? (npage + a.chunk - 1) / a.chunk : 1;
+  float* outp = a.out + ((int64_t)b * L.Hq + h * G) * D;
+  if (seq_len == 0) {
+    for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
+    return;
+  }
+  __shared__ float s_acc[GMAX * D];              // rotated accumulators
+  __shared__ float s_ml[2 * GMAX];               // max, sum
+  __shared__ float s_sink[GMAX * TQ_MAX_SINKS];  // sink scores, log2 domain
+  for (int i = threadIdx.x; i < G * ns; i += kWG) {
+    const int g = i / ns, pp = i % ns;
+    const uint16_t* qv = a.q + ((int64_t)b * L.Hq + h * G + g) * D;
+    const uint16_t* kv = a.sink_k + (((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D;
+    float dot = 0.0f;
+    for (int d = 0; d < D; ++d) dot += half_bits_to_float(qv[d]) * half_bits_to_float(kv[d]);
+    s_sink[g * ns + pp] = dot * a.sink_scale;
+  }
+  __syncthreads();
+  const int64_t bh = (int64_t)b * L.Hkv + h;
+  const float* pb = a.partials + bh * a.max_split * (int64_t)G * (D + 2);
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pb[(sp * G + g) * (D + 2)]);
+    for (int pp = 0; pp < ns; ++pp) M = fmaxf(M, s_sink[g * ns + pp]);
+    float sum = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float ms = pb[(sp * G + g) * (D + 2)];
+      if (ms != -INFINITY) sum += pb[(sp * G + g) * (D + 2) + 1] * __builtin_amdgcn_exp2f(ms - M);
+    }
+    for (int pp = 0; pp < ns; ++pp) sum += __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
+    s_ml[g] = M;
+    s_ml[GMAX + g] = sum;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += kWG) {
+    const int g = i / D, d = i % D;
+    const float M = s_ml[g];
+    float acc_d = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float ms = pb[(sp * G + g) * (D + 2)];
+      if (ms != -INFINITY) acc_d += pb[(sp * G + g) * (D + 2) + 2 + d] * __builtin_amdgcn_exp2f(ms - M);
+    }
+    s_acc[g * D + d] = acc_d;
+  }
+  __syncthreads();
+  // R^T a = D^(-1/2) diag(s) H a: Walsh-Hadamard butterflies in LDS.
+  for (int hb = 1; hb < D; hb <<= 1) {
+    for (int i = threadIdx.x; i < G * D / 2; i += kWG) {
+      const int g = i / (D / 2), r = i % (D / 2);
+      const int lo = (r / hb) * 2 * hb + (r % hb);
+      const float x0 = s_acc[g * D + lo], x1 = s_acc[g * D + lo + hb];
+      s_acc[g * D + lo] = x0 + x1;
+      s_acc[g * D + lo + hb] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < G * D; i += kWG) {
+    const int g = i / D, d = i % D;
+    const bool neg = (L.signs.w[d >> 5] >> (d & 31)) & 1u;
+    float o = s_acc[g * D + d] * a.rsqrt_d;
+    if (neg) o = -o;
+    const float M = s_ml[g];
+    for (int pp = 0; pp < ns; ++pp) {
+      const float w = __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
+      o += w * half_bits_to_float(a.sink_v[(((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D + d]);
+    }
+    outp[g * D + d] = o / s_ml[GMAX + g];
+  }
+}
+
+template <int D, int KB, int VB, int GMAX>
+void launch_t(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+  hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX>), grid, dim3(kWG), 0, st, a);
+  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(kWG), 0, st, a);
+}
+
+template <int D, int KB, int VB>
+void launch_g(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+  const int G = a.L.G;
+  if (G <= 1) launch_t<D, KB, VB, 1>(a, grid, mgrid, st);
+  else if (G <= 2) launch_t<D, KB, VB, 2>(a, grid, mgrid, st);
+  else if (G <= 4) launch_t<D, KB, VB, 4>(a, grid, mgrid, st);
+  else launch_t<D, KB, VB, 8>(a, grid, mgrid, st);
+}
+
+template <int D, int KB>
+void launch_v(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+  switch (a.L.vb) {
+    case 2: launch_g<D, KB, 2>(a, grid, mgrid, st); break;
+    case 3: launch_g<D, KB, 3>(a, grid, mgrid, st); break;
+    case 4: launch_g<D, KB, 4>(a, grid, mgrid, st); break;
+    default: launch_g<D, KB, 8>(a, grid, mgrid, st); break;
+  }
+}
+
+template <int D>
+void launch_k(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+  switch (a.L.kb) {
+    case 2: launch_v<D, 2>(a, grid, mgrid, st); break;
+    case 3: launch_v<D, 3>(a, grid, mgrid, st); break;
+    case 4: launch_v<D, 4>(a, grid, mgrid, st); break;
+    default: launch_v<D, 8>(a, grid, mgrid, st); break;
+  }
+}
+
+int ilog2_exact(int v) {
+  for (int s = 0; s < 31; ++s)
+    if ((1 << s) == v) return s;
+  return -1;
+}
+
+}  // namespace
+
+// Split geometry: page tokens per split are a multiple of 32 (the tokens a workgroup covers per
+// step), span at most kMaxBtLds page blocks, and give enough workgroups to fill 256 CUs several
+// times over.
+TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
+  const long bh = (long)num_seqs * L.Hkv;
+  const long tokens = (long)(max_seq_len > 0 ? max_seq_len : 1);
+  const long target_wgs = 4096;
+  long chunk = (tokens * bh + target_wgs - 1) / target_wgs;
+  if (chunk < 256) chunk = 256;
+  if (chunk > 4096) chunk = 4096;
+  const long bt_cap = ((long)(kMaxBtLds - 2) * L.bs / 32) * 32;  // blocks a split may touch
+  if (chunk > bt_cap) chunk = bt_cap;
+  chunk = ((chunk + 31) / 32) * 32;
+  TqSplit sp;
+  sp.chunk = (int)chunk;
+  sp.max_split = (int)((tokens + chunk - 1) / chunk);
+  if (sp.max_split < 1) sp.max_split = 1;
+  return sp;
+}
+
+size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
+  const size_t bh = (size_t)num_seqs * L.Hkv;
+  return bh * (size_t)sp.max_split * L.G * (L.D + 2) * sizeof(float);
+}
+
+int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
+                     int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
+                     const void* sink_k, const void* sink_v, int n_sink, float scale, float* out,
+                     void* workspace, void* stream) {
+  if (num_seqs == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  DecodeArgs a;
+  a.L = L;
+  a.rsqrt_d = (float)(1.0 / __builtin_sqrt((double)L.D));
+  a.qscale = scale * kLog2e * a.rsqrt_d;
+  a.sink_scale = scale * kLog2e;
+  a.q = (const uint16_t*)q;
+  a.pages = (const uint8_t*)pages;
+  a.bt = block_tables;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.chunk = sp.chunk;
+  a.max_split = sp.max_split;
+  a.n_units = num_seqs * sp.max_split;
+  a.bs_shift = ilog2_exact(L.bs);
+  a.sink_k = (const uint16_t*)sink_k;
+  a.sink_v = (const uint16_t*)sink_v;
+  a.n_sink = n_sink;
+  a.out = out;
+  a.partials = (float*)workspace;
+  const long groups = (a.n_units + 7) / 8;
+  const dim3 grid((unsigned)(groups * 8 * L.Hkv));
+  const dim3 mgrid((unsigned)(num_seqs * L.Hkv));
+  if (L.D == 128) launch_k<128>(a, grid, mgrid, st);
+  else launch_k<64>(a, grid, mgrid, st);
+  return (int)hipGetLastError();
+}
