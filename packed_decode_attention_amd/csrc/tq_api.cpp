@@ -24,7 +24,10 @@ int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
     return TQ_ERR_INVALID_ARG;
   const int sb = tq_slot_bytes(d->head_dim, d->k_bits, d->v_bits);
   const int stride = d->slot_stride == 0 ? sb : d->slot_stride;
-  if (stride < sb || (stride & 3) != 0) return TQ_ERR_INVALID_ARG;
+  if (stride < sb || (stride & 3) != 0 || stride > 4096) return TQ_ERR_INVALID_ARG;
+  if (d->num_kv_heads > 64 || d->block_size > 65536) return TQ_ERR_UNSUPPORTED;
+  // one page block's bytes must fit in 31 bits (row offsets inside a block are 32-bit)
+  if ((int64_t)d->block_size * d->num_kv_heads * stride > ((int64_t)1 << 31)) return TQ_ERR_UNSUPPORTED;
   int G = 1;
   if (need_q) {
     if (d->num_q_heads < 1 || d->num_q_heads % d->num_kv_heads != 0) return TQ_ERR_INVALID_ARG;

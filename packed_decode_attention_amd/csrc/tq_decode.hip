@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   __shared__ float s_klut[Lut<KB>::kFloats];
   __shared__ float s_vlut[Lut<VB>::kFloats];
   __shared__ float s_part[kNW][GMAX][D + 2];
-  __shared__ int32_t s_bt[kMaxBtLds];
+  __shared__ int64_t s_boff[kMaxBtLds];  // byte offset of each page block's first row
   build_lut<KB>(s_klut, L.kc, threadIdx.x, kWG);
   build_lut<VB>(s_vlut, L.vc, threadIdx.x, kWG);
 
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   const int blk0 = p_end > p_begin ? block_of(p_begin) : 0;
   const int nblk = p_end > p_begin ? block_of(p_end - 1) - blk0 + 1 : 0;  // <= kMaxBtLds (host)
   const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
-  for (int i = threadIdx.x; i < nblk; i += kWG) s_bt[i] = btg[i];
+  const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
+  for (int i = threadIdx.x; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   }
 
   const int voff = L.kcode_bytes + 4;
-  const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
+  const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   __syncthreads();  // lookup tables and block-table segment ready
 
@@ -155,8 +156,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     st.valid = p < p_end;
     p = st.valid ? p : p_end - 1;
     const int bi = block_of(p);
-    const int64_t slot = (int64_t)s_bt[bi - blk0] * L.bs + (p - bi * L.bs);
-    const uint8_t* base = head_base + slot * row_bytes;
+    const uint8_t* base = head_base + s_boff[bi - blk0] + __umul24((uint32_t)(p - bi * L.bs), row_bytes32);
     st.k = load_lane_codes<NBK>(base, j);
     st.v = load_lane_codes<NBV>(base + voff, j);
     st.kn = *reinterpret_cast<const float*>(base + L.kcode_bytes);
