@@ -54,6 +54,12 @@ struct DecodeArgs {
   float* partials;   // [B][Hkv][max_split][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
 };
 
+// Splits cover absolute positions [split * chunk, (split + 1) * chunk) of a sequence; positions
+// below n_sink are read from the sink arrays instead and are masked out of the splits.
+__device__ __forceinline__ int num_splits(int seq_len, int chunk) {
+  return seq_len > 0 ? (seq_len + chunk - 1) / chunk : 1;
+}
+
 // Raw page data of one step for one lane.
 template <int NBK, int NBV>
 struct Step {
@@ -85,8 +91,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   const int split = unit - b * a.max_split;
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
-  const int npage = seq_len - ns;
-  const int nsplit = npage > 0 ? (npage + a.chunk - 1) / a.chunk : 1;
+  const int nsplit = num_splits(seq_len, a.chunk);
   if (split >= nsplit) return;
 
   __shared__ float s_klut[Lut<KB>::kFloats];
@@ -96,9 +101,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   build_lut<KB>(s_klut, L.kc, threadIdx.x, kWG);
   build_lut<VB>(s_vlut, L.vc, threadIdx.x, kWG);
 
-  const int p_begin = ns + split * a.chunk;
-  const int p_end = min(ns + (split + 1) * a.chunk, seq_len);
-  const int n_it = (p_end - p_begin + TPI - 1) / TPI;
+  const int p_begin = max(ns, split * a.chunk);
+  const int p_end = min((split + 1) * a.chunk, seq_len);
+  const int n_it = p_end > p_begin ? (p_end - p_begin + TPI - 1) / TPI : 0;
   auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
   const int blk0 = p_end > p_begin ? block_of(p_begin) : 0;
   const int nblk = p_end > p_begin ? block_of(p_end - 1) - blk0 + 1 : 0;  // <= kMaxBtLds (host)
@@ -275,6 +280,385 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   }
 }
 
+
+// =============================================================================================
+// Matrix-core split kernel for 4-bit K and V codes at D = 128.
+//
+// Per wave, tiles of 32 page positions.  QK^T and PV run on v_mfma_f32_16x16x32_f16:
+//  * QK: A = rotated queries (rows 2g / 2g+1 = fp16 high / low part of head g, zero rows for
+//    g >= G), B = centroids of 16 tokens (K dimension = 32 coordinates per step; lane group q
+//    owns coordinates 32q..32q+31, so its B data is one 16-byte load per token).  The B operand
+//    is used twice, with the fp16 high and low parts of the centroids, so every product of the
+//    two-part query with the two-part centroid is accumulated in fp32 (about 22 significant
+//    bits per factor instead of 11).  Scores for head g are rows 2g + 2g+1 of the result.
+//  * PV: A = softmax weights w = p * n_V (fp16 high / low rows per head), B = value centroids
+//    with the K dimension running over 32 tokens; the 4-bit value codes of 8 tokens are
+//    gathered per lane through a small LDS tile and paired by nibble so that one byte-indexed
+//    lookup yields the fp16 pair (token a, token b) of one coordinate.
+// All fp16 operands are pre-scaled by powers of two into the normal fp16 range (queries per
+// head, centroid tables by 2^8, weights by 2^15); the scales are removed in fp32.  Weights use
+// their own running maximum of score + log2(n_V), so they stay in (0, 1] before scaling.
+// =============================================================================================
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLutShift = 8;    // centroid tables hold c * 2^8
+constexpr int kWShift = 15;     // weights enter the PV product as w * 2^15
+constexpr int kVRow = 18;       // dwords per token row of the per-wave value-code tile
+
+__device__ __forceinline__ float4_t mfma_f16(const uint4& a, const uint4& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// fp16 high and low parts of x: hi = fp16(x), lo = fp16(x - hi); hi + lo carries ~22 bits of x.
+__device__ __forceinline__ void split_f16(float x, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = (_Float16)x;
+  const _Float16 l = (_Float16)(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// Byte e of 4-bit codes -> (hi(c[e & 15]) | hi(c[e >> 4]) << 16, lo(..) | lo(..) << 16), c scaled.
+__device__ __forceinline__ void build_pair_lut4(uint2* t, const float* __restrict__ c, int tid) {
+  for (int e = tid; e < 256; e += kWG) {
+    uint32_t h0, l0, h1, l1;
+    split_f16(ldexpf(c[e & 15], kLutShift), h0, l0);
+    split_f16(ldexpf(c[e >> 4], kLutShift), h1, l1);
+    t[e] = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
+  }
+}
+
+template <int DPPCTRL>
+__device__ __forceinline__ float dpp_max_step(float x) { return fmaxf(x, dpp<DPPCTRL>(x)); }
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = dpp_max_step<kDppQuadXor1>(x);
+  x = dpp_max_step<kDppQuadXor2>(x);
+  x = dpp_max_step<kDppHalfRowMirror>(x);
+  x = dpp_max_step<kDppRowMirror>(x);
+  return x;
+}
+
+// One 32-position tile of page data for one lane: lane (t, q) reads tokens t and 16 + t.
+struct MTile {
+  uint4 k[2];     // K code bytes 16q..16q+15 of tokens t, 16+t
+  uint4 v[2];     // V code bytes 16q..16q+15 of tokens t, 16+t
+  float kn[2], vn[2];
+};
+
+__global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  const TqLayer& L = a.L;
+  const int G = L.G;
+
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7;
+  const int rest = lin >> 3;
+  const int h = rest % L.Hkv;
+  const int unit = (rest / L.Hkv) * 8 + xcd;
+  if (unit >= a.n_units) return;
+  const int b = unit / a.max_split;
+  const int split = unit - b * a.max_split;
+  const int seq_len = a.seq_lens[b];
+  const int ns = min(a.n_sink, seq_len);
+  const int nsplit = num_splits(seq_len, a.chunk);
+  if (split >= nsplit) return;
+
+  __shared__ uint2 s_klut[256];
+  __shared__ uint2 s_vlut[256];
+  __shared__ float s_q[8][D];
+  __shared__ float s_qmax[8];
+  __shared__ int64_t s_boff[kMaxBtLds];
+  __shared__ uint16_t s_w[kNW][16][32];
+  __shared__ uint32_t s_v[kNW][32][kVRow];
+  __shared__ float s_part[kNW][8][D + 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  build_pair_lut4(s_klut, L.kc, tid);
+  build_pair_lut4(s_vlut, L.vc, tid);
+
+  const int p0 = split * a.chunk;
+  const int p_end = min(p0 + a.chunk, seq_len);
+  auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
+  const int blk0 = block_of(p0);
+  const int nblk = p_end > p0 ? block_of(p_end - 1) - blk0 + 1 : 0;
+  const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
+  const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
+  for (int i = tid; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
+
+  // Rotated queries qscale * H (s * q), then a power-of-two scale per head into fp16 range.
+  for (int i = tid; i < G * D; i += kWG) {
+    const int g = i / D, d = i % D;
+    const float v = half_bits_to_float(a.q[((int64_t)b * L.Hq + h * G + g) * D + d]);
+    const bool neg = (L.signs.w[d >> 5] >> (d & 31)) & 1u;
+    s_q[g][d] = neg ? -v : v;
+  }
+  __syncthreads();
+  for (int hb = 1; hb < D; hb <<= 1) {
+    for (int i = tid; i < G * D / 2; i += kWG) {
+      const int g = i / (D / 2), r = i % (D / 2);
+      const int lo = (r / hb) * 2 * hb + (r % hb);
+      const float x0 = s_q[g][lo], x1 = s_q[g][lo + hb];
+      s_q[g][lo] = x0 + x1;
+      s_q[g][lo + hb] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  if (tid < 64 * 2) {  // per-head max |q'| (two waves, 32 lanes per head group of 4 values)
+    for (int g = tid >> 4; g < G; g += 8) {
+      float mx = 0.0f;
+      for (int d = tid & 15; d < D; d += 16) mx = fmaxf(mx, fabsf(s_q[g][d]));
+      mx = fmaxf(mx, dpp<kDppQuadXor1>(mx));
+      mx = fmaxf(mx, dpp<kDppQuadXor2>(mx));
+      mx = fmaxf(mx, dpp<kDppHalfRowMirror>(mx));
+      mx = fmaxf(mx, dpp<kDppRowMirror>(mx));
+      if ((tid & 15) == 0) s_qmax[g] = mx * a.qscale;
+    }
+  }
+  __syncthreads();
+
+  // A operand of QK: lane (m = t16, q4) holds rows m of coordinates 32 q4 + 8 s + 0..7, s = 0..3.
+  uint4 aq[4];
+  {
+    const int g = t16 >> 1;
+    const bool lo_part = t16 & 1;
+    const bool live = g < G;
+    const float qm = live ? s_qmax[g] : 0.0f;
+    const int e = (live && qm > 0.0f) ? 13 - ilogbf(qm) : 0;
+    const float f = ldexpf(a.qscale, e);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t pr[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float x = live ? s_q[g][32 * q4 + 8 * st + 2 * i + k] * f : 0.0f;
+          uint32_t hi, lo;
+          split_f16(x, hi, lo);
+          pr[k] = lo_part ? lo : hi;
+        }
+        w[i] = pr[0] | (pr[1] << 16);
+      }
+      aq[st] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  // Score factors of the two heads whose rows this lane holds in the QK result: 2^-(e + 8).
+  const int g0 = 2 * q4, g1 = 2 * q4 + 1;
+  auto head_factor = [&](int g) {
+    if (g >= G) return 0.0f;
+    const float qm = s_qmax[g];
+    const int e = qm > 0.0f ? 13 - ilogbf(qm) : 0;
+    return ldexpf(1.0f, -(e + kLutShift));
+  };
+  const float f0 = head_factor(g0), f1 = head_factor(g1);
+  const bool live0 = g0 < G, live1 = g1 < G;
+
+  const int voff = L.kcode_bytes + 4;
+  const uint32_t row_bytes32 = (uint32_t)row_bytes;
+  const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
+  const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
+
+  auto row_ptr = [&](int p) {
+    const int pc = min(p, p_end - 1);
+    const int bi = block_of(pc);
+    return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
+  };
+  auto fetch = [&](int tile) {
+    MTile m;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint8_t* r = row_ptr(p0 + 32 * tile + 16 * u + t16);
+      m.k[u] = *reinterpret_cast<const uint4*>(r + 16 * q4);
+      m.v[u] = *reinterpret_cast<const uint4*>(r + voff + 16 * q4);
+      m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
+      m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
+    }
+    return m;
+  };
+
+  float m_s[2] = {-INFINITY, -INFINITY};   // running max of scores (heads g0, g1)
+  float m_w[2] = {-INFINITY, -INFINITY};   // running max of score + log2(n_V)
+  float l_s[2] = {0.0f, 0.0f};             // per-lane partial sums of 2^(s - m_s)
+  float4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  __syncthreads();  // tables, block offsets ready
+  uint16_t* wt = &s_w[wave][0][0];
+  uint32_t* vt = &s_v[wave][0][0];
+
+  MTile cur;
+  int tile = wave;
+  if (tile < n_tiles) cur = fetch(tile);
+  for (; tile < n_tiles; tile += kNW) {
+    MTile nxt = cur;
+    if (tile + kNW < n_tiles) nxt = fetch(tile + kNW);
+
+    // ---- QK on the matrix cores ----
+    float4_t sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const uint32_t kw[4] = {cur.k[u].x, cur.k[u].y, cur.k[u].z, cur.k[u].w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint2 e = s_klut[(kw[st] >> (8 * i)) & 0xffu];
+          hi[i] = e.x;
+          lo[i] = e.y;
+        }
+        sc[u] = mfma_f16(aq[st], make_uint4(hi[0], hi[1], hi[2], hi[3]), sc[u]);
+        sc[u] = mfma_f16(aq[st], make_uint4(lo[0], lo[1], lo[2], lo[3]), sc[u]);
+      }
+    }
+
+    // ---- online softmax on the two heads of this lane group, tokens t16 and 16 + t16 ----
+    const int pbase = p0 + 32 * tile;
+    float s0[2], s1[2], lv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = pbase + 16 * u + t16;
+      const bool valid = p >= ns && p < p_end;
+      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * cur.kn[u] * f0 : -INFINITY;
+      s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * cur.kn[u] * f1 : -INFINITY;
+      lv[u] = __builtin_amdgcn_logf(cur.vn[u]);  // log2(n_V); -inf for a zero row
+    }
+    const float ts0 = row16_max(fmaxf(s0[0], s0[1]));
+    const float ts1 = row16_max(fmaxf(s1[0], s1[1]));
+    const float tw0 = row16_max(fmaxf(s0[0] + lv[0], s0[1] + lv[1]));
+    const float tw1 = row16_max(fmaxf(s1[0] + lv[0], s1[1] + lv[1]));
+    const float ms0 = fmaxf(m_s[0], ts0), ms1 = fmaxf(m_s[1], ts1);
+    const float mw0 = fmaxf(m_w[0], tw0), mw1 = fmaxf(m_w[1], tw1);
+    if (ms0 > m_s[0]) l_s[0] *= __builtin_amdgcn_exp2f(m_s[0] - ms0);
+    if (ms1 > m_s[1]) l_s[1] *= __builtin_amdgcn_exp2f(m_s[1] - ms1);
+    m_s[0] = ms0;
+    m_s[1] = ms1;
+    if (mw0 > m_w[0] || mw1 > m_w[1]) {
+      const float r0 = mw0 > m_w[0] ? __builtin_amdgcn_exp2f(m_w[0] - mw0) : 1.0f;
+      const float r1 = mw1 > m_w[1] ? __builtin_amdgcn_exp2f(m_w[1] - mw1) : 1.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        acc[c][0] *= r0;
+        acc[c][1] *= r0;
+        acc[c][2] *= r1;
+        acc[c][3] *= r1;
+      }
+    }
+    m_w[0] = mw0;
+    m_w[1] = mw1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float p0u = s0[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s0[u] - ms0);
+      const float p1u = s1[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s1[u] - ms1);
+      l_s[0] += p0u;
+      l_s[1] += p1u;
+      const float sw0 = s0[u] + lv[u], sw1 = s1[u] + lv[u];
+      const float w0 = sw0 == -INFINITY ? 0.0f : ldexpf(__builtin_amdgcn_exp2f(sw0 - mw0), kWShift);
+      const float w1 = sw1 == -INFINITY ? 0.0f : ldexpf(__builtin_amdgcn_exp2f(sw1 - mw1), kWShift);
+      uint32_t h0, l0, h1, l1;
+      split_f16(w0, h0, l0);
+      split_f16(w1, h1, l1);
+      const int col = 16 * u + t16;
+      wt[(4 * q4 + 0) * 32 + col] = (uint16_t)h0;
+      wt[(4 * q4 + 1) * 32 + col] = (uint16_t)l0;
+      wt[(4 * q4 + 2) * 32 + col] = (uint16_t)h1;
+      wt[(4 * q4 + 3) * 32 + col] = (uint16_t)l1;
+      // value codes of token 16u + t16, coordinates 32 q4 .. 32 q4 + 31 (dwords 4 q4 .. 4 q4 + 3)
+      uint32_t* vrow = vt + (16 * u + t16) * kVRow + 4 * q4;
+      *reinterpret_cast<uint2*>(vrow) = make_uint2(cur.v[u].x, cur.v[u].y);
+      *reinterpret_cast<uint2*>(vrow + 2) = make_uint2(cur.v[u].z, cur.v[u].w);
+    }
+
+    // ---- PV on the matrix cores: lane (n = t16, q4) handles tokens 8 q4 .. 8 q4 + 7 ----
+    const uint4 aw = *reinterpret_cast<const uint4*>(wt + t16 * 32 + 8 * q4);
+    uint32_t vd[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) vd[kk] = vt[(8 * q4 + kk) * kVRow + t16];
+    uint32_t eo[8];  // E_i, O_i: bytes (nibble c of token 2i, nibble c of token 2i+1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      eo[2 * i] = (vd[2 * i] & 0x0f0f0f0fu) | ((vd[2 * i + 1] << 4) & 0xf0f0f0f0u);
+      eo[2 * i + 1] = ((vd[2 * i] >> 4) & 0x0f0f0f0fu) | (vd[2 * i + 1] & 0xf0f0f0f0u);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // coordinate 8 t16 + c: even c -> byte c/2 of E_i, odd c -> byte c/2 of O_i
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint2 e = s_vlut[(eo[2 * i + (c & 1)] >> (8 * (c >> 1))) & 0xffu];
+        hi[i] = e.x;
+        lo[i] = e.y;
+      }
+      acc[c] = mfma_f16(aw, make_uint4(hi[0], hi[1], hi[2], hi[3]), acc[c]);
+      acc[c] = mfma_f16(aw, make_uint4(lo[0], lo[1], lo[2], lo[3]), acc[c]);
+    }
+    cur = nxt;
+  }
+
+  // ---- wave result: heads g0, g1 at coordinates 8 t16 + c, in the score-max frame ----
+  l_s[0] += dpp<kDppQuadXor1>(l_s[0]);
+  l_s[0] += dpp<kDppQuadXor2>(l_s[0]);
+  l_s[0] += dpp<kDppHalfRowMirror>(l_s[0]);
+  l_s[0] += dpp<kDppRowMirror>(l_s[0]);
+  l_s[1] += dpp<kDppQuadXor1>(l_s[1]);
+  l_s[1] += dpp<kDppQuadXor2>(l_s[1]);
+  l_s[1] += dpp<kDppHalfRowMirror>(l_s[1]);
+  l_s[1] += dpp<kDppRowMirror>(l_s[1]);
+  const float vscale = ldexpf(1.0f, -(kWShift + kLutShift));
+  const float c0 = m_w[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[0] - m_s[0]) * vscale;
+  const float c1 = m_w[1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
+  if (live0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s_part[wave][g0][2 + 8 * t16 + c] = (acc[c][0] + acc[c][1]) * c0;
+    if (t16 == 0) {
+      s_part[wave][g0][0] = m_s[0];
+      s_part[wave][g0][1] = l_s[0];
+    }
+  }
+  if (live1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s_part[wave][g1][2 + 8 * t16 + c] = (acc[c][2] + acc[c][3]) * c1;
+    if (t16 == 0) {
+      s_part[wave][g1][0] = m_s[1];
+      s_part[wave][g1][1] = l_s[1];
+    }
+  }
+  __syncthreads();
+
+  const int64_t bh = (int64_t)b * L.Hkv + h;
+  float* part = a.partials + (bh * a.max_split + split) * (int64_t)G * (D + 2);
+  for (int i = tid; i < G * (D + 2); i += kWG) {
+    const int g = i / (D + 2), d = i % (D + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_part[w][g][0]);
+    float r;
+    if (d == 0) {
+      r = M;
+    } else {
+      r = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const float mw = s_part[w][g][0];
+        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        r += s_part[w][g][d] * f;
+      }
+    }
+    part[i] = r;
+  }
+}
+
 // One workgroup per (sequence, kv head): merge the splits and the sinks, rotate back, normalise.
 template <int D, int GMAX>
 __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
@@ -284,8 +668,7 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const int b = blockIdx.x / L.Hkv;
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
-  const int npage = seq_len - ns;
-  const int nsplit = npage > 0 ? (npage + a.chunk - 1) / a.chunk : 1;
+  const int nsplit = num_splits(seq_len, a.chunk);
   float* outp = a.out + ((int64_t)b * L.Hq + h * G) * D;
   if (seq_len == 0) {
     for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
@@ -383,6 +766,14 @@ void launch_v(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
 
 template <int D>
 void launch_k(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+  if (D == 128 && a.L.kb == 4 && a.L.vb == 4) {
+    hipLaunchKernelGGL(tq_decode_mfma_k4v4_kernel, grid, dim3(kWG), 0, st, a);
+    if (a.L.G <= 1) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 1>), mgrid, dim3(kWG), 0, st, a);
+    else if (a.L.G <= 2) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 2>), mgrid, dim3(kWG), 0, st, a);
+    else if (a.L.G <= 4) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 4>), mgrid, dim3(kWG), 0, st, a);
+    else hipLaunchKernelGGL((tq_decode_merge_kernel<128, 8>), mgrid, dim3(kWG), 0, st, a);
+    return;
+  }
   switch (a.L.kb) {
     case 2: launch_v<D, 2>(a, grid, mgrid, st); break;
     case 3: launch_v<D, 3>(a, grid, mgrid, st); break;
