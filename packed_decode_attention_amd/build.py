@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libtq.so")
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fno-strict-aliasing", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]

@@ -347,8 +347,17 @@ struct MTile {
   float kn[2], vn[2];
 };
 
+// MFMA operand of 8 fp16 in the interleaved order used by both products: for a pair of
+// lookups e0, e1 (each = (high parts of two values, low parts of the same two values)) the
+// operand is [hi(x0), hi(x1), lo(x0), lo(x1), hi(x2), hi(x3), lo(x2), lo(x3)], so the K dimension
+// runs over (value, part).  The other operand repeats its value for both parts.
+__device__ __forceinline__ uint4 quad_of(const uint2& e0, const uint2& e1) {
+  return make_uint4(e0.x, e0.y, e1.x, e1.y);
+}
+
 __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs a) {
   constexpr int D = 128;
+  constexpr int kRing = 1;  // tiles in flight per wave (register ring)
   const TqLayer& L = a.L;
   const int G = L.G;
 
@@ -410,7 +419,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     }
     __syncthreads();
   }
-  if (tid < 64 * 2) {  // per-head max |q'| (two waves, 32 lanes per head group of 4 values)
+  if (tid < 128) {  // max |q'| per head: one 16-lane row per head
     for (int g = tid >> 4; g < G; g += 8) {
       float mx = 0.0f;
       for (int d = tid & 15; d < D; d += 16) mx = fmaxf(mx, fabsf(s_q[g][d]));
@@ -423,43 +432,37 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   }
   __syncthreads();
 
-  // A operand of QK: lane (m = t16, q4) holds rows m of coordinates 32 q4 + 8 s + 0..7, s = 0..3.
-  uint4 aq[4];
+  auto head_exp = [&](int g) {
+    const float qm = s_qmax[g];
+    return qm > 0.0f ? 13 - ilogbf(qm) : 0;
+  };
+  // A operand of QK: lane (m = t16, q4), step st = 0..7 covers coordinates 32 q4 + 4 st + 0..3 as
+  // [q(c0), q(c1), q(c0), q(c1), q(c2), q(c3), q(c2), q(c3)] of row m (fp16 high or low part).
+  uint4 aq[8];
   {
     const int g = t16 >> 1;
     const bool lo_part = t16 & 1;
     const bool live = g < G;
-    const float qm = live ? s_qmax[g] : 0.0f;
-    const int e = (live && qm > 0.0f) ? 13 - ilogbf(qm) : 0;
-    const float f = ldexpf(a.qscale, e);
+    const float f = live ? ldexpf(a.qscale, head_exp(g)) : 0.0f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint32_t w[4];
+    for (int st = 0; st < 8; ++st) {
+      uint32_t pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t pr[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float x = live ? s_q[g][32 * q4 + 8 * st + 2 * i + k] * f : 0.0f;
-          uint32_t hi, lo;
-          split_f16(x, hi, lo);
-          pr[k] = lo_part ? lo : hi;
-        }
-        w[i] = pr[0] | (pr[1] << 16);
+        const float x = live ? s_q[g][32 * q4 + 4 * st + i] * f : 0.0f;
+        uint32_t hi, lo;
+        split_f16(x, hi, lo);
+        pr[i] = lo_part ? lo : hi;
       }
-      aq[st] = make_uint4(w[0], w[1], w[2], w[3]);
+      const uint32_t d01 = pr[0] | (pr[1] << 16), d23 = pr[2] | (pr[3] << 16);
+      aq[st] = make_uint4(d01, d01, d23, d23);
     }
   }
   // Score factors of the two heads whose rows this lane holds in the QK result: 2^-(e + 8).
   const int g0 = 2 * q4, g1 = 2 * q4 + 1;
-  auto head_factor = [&](int g) {
-    if (g >= G) return 0.0f;
-    const float qm = s_qmax[g];
-    const int e = qm > 0.0f ? 13 - ilogbf(qm) : 0;
-    return ldexpf(1.0f, -(e + kLutShift));
-  };
-  const float f0 = head_factor(g0), f1 = head_factor(g1);
   const bool live0 = g0 < G, live1 = g1 < G;
+  const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
+  const float f1 = live1 ? ldexpf(1.0f, -(head_exp(g1) + kLutShift)) : 0.0f;
 
   const int voff = L.kcode_bytes + 4;
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
@@ -471,8 +474,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     const int bi = block_of(pc);
     return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
   };
-  auto fetch = [&](int tile) {
-    MTile m;
+  auto fetch = [&](int tile, MTile& m) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint8_t* r = row_ptr(p0 + 32 * tile + 16 * u + t16);
@@ -481,7 +483,6 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
       m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
       m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
     }
-    return m;
   };
 
   float m_s[2] = {-INFINITY, -INFINITY};   // running max of scores (heads g0, g1)
@@ -495,31 +496,23 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   uint16_t* wt = &s_w[wave][0][0];
   uint32_t* vt = &s_v[wave][0][0];
 
-  MTile cur;
-  int tile = wave;
-  if (tile < n_tiles) cur = fetch(tile);
-  for (; tile < n_tiles; tile += kNW) {
-    MTile nxt = cur;
-    if (tile + kNW < n_tiles) nxt = fetch(tile + kNW);
-
+  auto process = [&](const MTile& cur, int tile) {
     // ---- QK on the matrix cores ----
     float4_t sc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      sc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      // all 16 lookups of the sub-tile first, so their LDS latency overlaps
       const uint32_t kw[4] = {cur.k[u].x, cur.k[u].y, cur.k[u].z, cur.k[u].w};
+      uint2 ek[16];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        uint32_t hi[4], lo[4];
+      for (int i = 0; i < 16; ++i) ek[i] = s_klut[(kw[i >> 2] >> (8 * (i & 3))) & 0xffu];
+      float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, sb = sa;  // two independent MFMA chains
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint2 e = s_klut[(kw[st] >> (8 * i)) & 0xffu];
-          hi[i] = e.x;
-          lo[i] = e.y;
-        }
-        sc[u] = mfma_f16(aq[st], make_uint4(hi[0], hi[1], hi[2], hi[3]), sc[u]);
-        sc[u] = mfma_f16(aq[st], make_uint4(lo[0], lo[1], lo[2], lo[3]), sc[u]);
+      for (int st = 0; st < 8; st += 2) {
+        sa = mfma_f16(aq[st], quad_of(ek[2 * st], ek[2 * st + 1]), sa);
+        sb = mfma_f16(aq[st + 1], quad_of(ek[2 * st + 2], ek[2 * st + 3]), sb);
       }
+      sc[u] = sa + sb;
     }
 
     // ---- online softmax on the two heads of this lane group, tokens t16 and 16 + t16 ----
@@ -580,7 +573,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     }
 
     // ---- PV on the matrix cores: lane (n = t16, q4) handles tokens 8 q4 .. 8 q4 + 7 ----
-    const uint4 aw = *reinterpret_cast<const uint4*>(wt + t16 * 32 + 8 * q4);
+    // The tiles written above are read back by other lanes of this wave: order the LDS accesses.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     uint32_t vd[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) vd[kk] = vt[(8 * q4 + kk) * kVRow + t16];
@@ -591,30 +585,47 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
       eo[2 * i + 1] = ((vd[2 * i] >> 4) & 0x0f0f0f0fu) | (vd[2 * i + 1] & 0xf0f0f0f0u);
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int j = 0; j < 2; ++j) {
+      // weights of tokens 8 q4 + 4 j + 0..3 as [w0, w1, w0, w1, w2, w3, w2, w3] (row t16)
+      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wt + t16 * 32 + 8 * q4 + 4 * j);
+      const uint32_t w01 = wrow[0], w23 = wrow[1];
+      const uint4 aw = make_uint4(w01, w01, w23, w23);
       // coordinate 8 t16 + c: even c -> byte c/2 of E_i, odd c -> byte c/2 of O_i
-      uint32_t hi[4], lo[4];
+      uint2 ev[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint2 e = s_vlut[(eo[2 * i + (c & 1)] >> (8 * (c >> 1))) & 0xffu];
-        hi[i] = e.x;
-        lo[i] = e.y;
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sh = 8 * (c >> 1);
+        ev[2 * c] = s_vlut[(eo[2 * (2 * j) + (c & 1)] >> sh) & 0xffu];
+        ev[2 * c + 1] = s_vlut[(eo[2 * (2 * j + 1) + (c & 1)] >> sh) & 0xffu];
       }
-      acc[c] = mfma_f16(aw, make_uint4(hi[0], hi[1], hi[2], hi[3]), acc[c]);
-      acc[c] = mfma_f16(aw, make_uint4(lo[0], lo[1], lo[2], lo[3]), acc[c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, quad_of(ev[2 * c], ev[2 * c + 1]), acc[c]);
     }
-    cur = nxt;
+  };
+
+  MTile ring[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r)
+    if (wave + r * kNW < n_tiles) fetch(wave + r * kNW, ring[r]);
+  for (int base = wave; base < n_tiles; base += kRing * kNW) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      const int tile = base + r * kNW;
+      if (tile < n_tiles) {
+        process(ring[r], tile);
+        if (tile + kRing * kNW < n_tiles) fetch(tile + kRing * kNW, ring[r]);
+      }
+    }
   }
 
   // ---- wave result: heads g0, g1 at coordinates 8 t16 + c, in the score-max frame ----
-  l_s[0] += dpp<kDppQuadXor1>(l_s[0]);
-  l_s[0] += dpp<kDppQuadXor2>(l_s[0]);
-  l_s[0] += dpp<kDppHalfRowMirror>(l_s[0]);
-  l_s[0] += dpp<kDppRowMirror>(l_s[0]);
-  l_s[1] += dpp<kDppQuadXor1>(l_s[1]);
-  l_s[1] += dpp<kDppQuadXor2>(l_s[1]);
-  l_s[1] += dpp<kDppHalfRowMirror>(l_s[1]);
-  l_s[1] += dpp<kDppRowMirror>(l_s[1]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    l_s[i] += dpp<kDppQuadXor1>(l_s[i]);
+    l_s[i] += dpp<kDppQuadXor2>(l_s[i]);
+    l_s[i] += dpp<kDppHalfRowMirror>(l_s[i]);
+    l_s[i] += dpp<kDppRowMirror>(l_s[i]);
+  }
   const float vscale = ldexpf(1.0f, -(kWShift + kLutShift));
   const float c0 = m_w[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[0] - m_s[0]) * vscale;
   const float c1 = m_w[1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
@@ -791,15 +802,16 @@ int ilog2_exact(int v) {
 }  // namespace
 
 // Split geometry: page tokens per split are a multiple of 32 (the tokens a workgroup covers per
-// step), span at most kMaxBtLds page blocks, and give enough workgroups to fill 256 CUs several
-// times over.
+// step) and span at most kMaxBtLds page blocks.  About three workgroups per CU: each workgroup
+// pays a fixed prologue (rotated query, lookup tables, block offsets) and writes one partial, so
+// fewer, longer splits win as long as every CU still holds a few of them.
 TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
   const long bh = (long)num_seqs * L.Hkv;
   const long tokens = (long)(max_seq_len > 0 ? max_seq_len : 1);
-  const long target_wgs = 4096;
+  const long target_wgs = 768;
   long chunk = (tokens * bh + target_wgs - 1) / target_wgs;
   if (chunk < 256) chunk = 256;
-  if (chunk > 4096) chunk = 4096;
+  if (chunk > 16384) chunk = 16384;
   const long bt_cap = ((long)(kMaxBtLds - 2) * L.bs / 32) * 32;  // blocks a split may touch
   if (chunk > bt_cap) chunk = bt_cap;
   chunk = ((chunk + 31) / 32) * 32;
