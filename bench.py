@@ -137,6 +137,47 @@ def algorithmic_bytes(w, lens, tq):
     return per_layer
 
 
+DECODE_SOURCES = ("tq_decode.hip", "tq_device.h", "tq_internal.h")
+
+
+def decode_source_digest():
+    """sha256 over the decode kernels' sources: recorded traffic is only valid for this code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "packed_decode_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(w):
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of
+    this workload, or None when there is none or the decode sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                kv[parts[0]] = parts[1]
+    if kv.get("source_sha256") != decode_source_digest() or "traffic_bytes_per_call" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_call"])
+
+
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of known size, the calibration run for the HBM counters."""
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 4}), flush=True)
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The oracle as it stands, on a bounded sample: one layer, the first sequences in turn until
     about `budget_s` seconds of decode work have been timed; pages built by the oracle itself."""
@@ -193,6 +234,8 @@ def main():
     ap.add_argument("--workload", default="llama3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -204,6 +247,9 @@ def main():
     from packed_decode_attention_amd import workloads as wl
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
     w = wl.WORKLOADS[args.workload]
     log(f"workload {describe(w)}")
     total = args.warmup + args.steps
@@ -261,8 +307,9 @@ def main():
         "config": {"workload": describe(w), "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "tq_decode_kernel", "bytes_per_launch": float(np.mean(dec_bytes)),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w),
+                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits)),
+                     "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},
         "append": {"step_us_per_layer": float(app_ms.mean() * 1e3),
                    "bulk_fill_us_per_layer": bulk_ms * 1e3,

@@ -73,3 +73,11 @@ class LayerFormat:
         import torch
         n = tq_decode_workspace_bytes(self.desc, num_seqs, max_seq_len)
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int):
+    """Names of the kernels one tq_paged_decode_attention call launches for this format, in
+    launch order (as they appear in a kernel trace)."""
+    split = ("tq_decode_mfma_k4v4_kernel" if (head_dim, k_bits, v_bits) == (128, 4, 4)
+             else "tq_decode_split_kernel")
+    return [split, "tq_decode_merge_kernel"]
