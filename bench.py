@@ -47,6 +47,49 @@ class LayerState:
         self.fmt, self.pages, self.num_blocks = fmt, pages, num_blocks
 
 
+def context_slots(w, bt_np, lens, wl):
+    """Slots of every cached position but the last of each sequence (the bulk-filled context), in
+    sequence order, and the slot of each sequence's last position (the decode step's append)."""
+    ctx = [wl.token_slots(bt_np, b, np.arange(lens[b] - 1), w.block_size) for b in range(w.num_seqs)]
+    new = np.array([wl.token_slots(bt_np, b, [lens[b] - 1], w.block_size)[0] for b in range(w.num_seqs)],
+                   np.int64)
+    return np.concatenate(ctx), new
+
+
+def fill_layer(w, l, fmt, pages, ctx_slots, num_blocks, torch, tq, wl, dev="cuda", tap=None):
+    """Bulk quantize-append of layer l's context in chunks of BULK_CHUNK tokens; returns the summed
+    kernel time in ms.  tap(s0, k, v) sees each chunk's fp16 rows (for parity sampling)."""
+    gk = wl.generator(w.seed * 1000003 + l * 31, dev)
+    gv = wl.generator(w.seed * 1000003 + l * 31 + 1, dev)
+    n_ctx = int(ctx_slots.numel())
+    t_layer = 0.0
+    for s0 in range(0, n_ctx, BULK_CHUNK):
+        n = min(BULK_CHUNK, n_ctx - s0)
+        k = wl.kv_values(w, l, n, "k", dev, gen=gk)
+        v = wl.kv_values(w, l, n, "v", dev, gen=gv)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.tq_quantize_append(fmt.desc, k, v, ctx_slots[s0:s0 + n], pages, num_blocks)
+        e1.record()
+        e1.synchronize()
+        t_layer += e0.elapsed_time(e1)
+        if tap is not None:
+            tap(s0, k, v)
+        del k, v
+    return t_layer
+
+
+def new_tokens(w, n_steps_total, wl, dev="cuda"):
+    """fp16 K and V of the token each step appends: [steps, layers, B, H_kv, D] each."""
+    B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
+    gnew = wl.generator(w.seed * 99991 + 17, dev)
+    new_k = wl.kv_values(w, 0, n_steps_total * w.layers * B, "k", dev, gen=gnew).reshape(
+        n_steps_total, w.layers, B, H, D)
+    new_v = wl.kv_values(w, 0, n_steps_total * w.layers * B, "v", dev, gen=gnew).reshape(
+        n_steps_total, w.layers, B, H, D)
+    return new_k, new_v
+
+
 def setup(w, torch, tq, wl, n_steps_total):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
@@ -54,11 +97,9 @@ def setup(w, torch, tq, wl, n_steps_total):
     bt = torch.from_numpy(bt_np).to(dev)
     seq_lens = torch.from_numpy(lens).to(dev)
     B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
-    # slots of the context (bulk fill) and of the appended position, per sequence
-    ctx_slots = [wl.token_slots(bt_np, b, np.arange(lens[b] - 1), w.block_size) for b in range(B)]
-    ctx_slots = torch.from_numpy(np.concatenate(ctx_slots)).to(dev)
-    new_slots = torch.from_numpy(np.array([wl.token_slots(bt_np, b, [lens[b] - 1], w.block_size)[0]
-                                           for b in range(B)], np.int64)).to(dev)
+    ctx_np, new_np = context_slots(w, bt_np, lens, wl)
+    ctx_slots = torch.from_numpy(ctx_np).to(dev)
+    new_slots = torch.from_numpy(new_np).to(dev)
     fmts = {}
     layers = []
     bulk_ms, bulk_rows = [], 0
@@ -69,20 +110,7 @@ def setup(w, torch, tq, wl, n_steps_total):
             fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0)
         fmt = fmts[(kb, vb)]
         pages = fmt.new_pages(num_blocks)
-        gk = wl.generator(w.seed * 1000003 + l * 31, dev)
-        gv = wl.generator(w.seed * 1000003 + l * 31 + 1, dev)
-        t_layer = 0.0
-        for s0 in range(0, n_ctx, BULK_CHUNK):
-            n = min(BULK_CHUNK, n_ctx - s0)
-            k = wl.kv_values(w, l, n, "k", dev, gen=gk)
-            v = wl.kv_values(w, l, n, "v", dev, gen=gv)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            tq.tq_quantize_append(fmt.desc, k, v, ctx_slots[s0:s0 + n], pages, num_blocks)
-            e1.record()
-            e1.synchronize()
-            t_layer += e0.elapsed_time(e1)
-            del k, v
+        t_layer = fill_layer(w, l, fmt, pages, ctx_slots, num_blocks, torch, tq, wl)
         if l > 0:  # layer 0 includes first-launch costs
             bulk_ms.append(t_layer)
         bulk_rows = n_ctx * H
@@ -90,11 +118,7 @@ def setup(w, torch, tq, wl, n_steps_total):
     torch.cuda.synchronize()
     # per-step inputs: queries and one new K/V token per sequence and layer
     qs = [wl.queries(w, l, 0, dev) for l in range(w.layers)]
-    gnew = wl.generator(w.seed * 99991 + 17, dev)
-    new_k = wl.kv_values(w, 0, n_steps_total * w.layers * B, "k", dev, gen=gnew).reshape(
-        n_steps_total, w.layers, B, H, D)
-    new_v = wl.kv_values(w, 0, n_steps_total * w.layers * B, "v", dev, gen=gnew).reshape(
-        n_steps_total, w.layers, B, H, D)
+    new_k, new_v = new_tokens(w, n_steps_total, wl, dev)
     sink_k, sink_v = wl.sinks(w, 0, dev)
     max_len = int(lens.max())
     ws = fmts[(w.k_bits, w.v_bits)].new_workspace(B, max_len)

@@ -1,0 +1,135 @@
+"""Parity at the benchmark's full sizes, in the launch configuration bench.py times.
+
+Each case fills one layer of a full-size workload exactly as the benchmark does (bulk
+quantize-append of the whole context in chunks, then the decode step's one-token append), then runs
+decode over the whole batch.  A few sampled sequences are recomputed by the CPU oracle from the same
+fp16 rows:
+  * their packed page rows must equal the oracle's (indices at listed ties excepted);
+  * with the oracle's bytes written into their page rows (so ties cannot move a key), the decode
+    output of those sequences must match the oracle's dense attention to the attention tolerance.
+The other sequences of the batch still run, so the grid, split geometry and workspace are the
+benchmark's.
+"""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from _parity import check_attention, compare_pages, oracle_codebooks
+from oracle import attention as oatt
+from oracle import quantize as oq
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def _pick(w, lens, which):
+    if which == "extremes":
+        return [int(np.argmax(lens)), int(np.argmin(lens))]
+    return list(which)
+
+
+CASES = [
+    ("llama3-8b", 1, (0, 13)),
+    ("mistral-7b", 2, (1,)),
+    ("ragged", 5, "extremes"),
+    ("qwen2.5-0.5b", 7, (0, 5)),
+]
+
+
+@pytest.mark.parametrize("name,layer,which", CASES, ids=[f"{c[0]}-L{c[1]}" for c in CASES])
+def test_full_size_sampled(name, layer, which):
+    import torch
+    import packed_decode_attention_amd as tq
+    from packed_decode_attention_amd import workloads as wl
+    bench = _bench()
+
+    w = wl.WORKLOADS[name]
+    kb, vb = w.bits(layer)
+    B, H, D, Hq, bs = w.num_seqs, w.num_kv_heads, w.head_dim, w.num_q_heads, w.block_size
+    lens = wl.seq_lens(w)
+    bt_np, num_blocks = wl.block_tables(w, lens)
+    ctx_np, new_np = bench.context_slots(w, bt_np, lens, wl)
+    seqs = _pick(w, lens, which)
+    print(f"[fullsize] {name} layer {layer} K{kb}/V{vb}: B={B} max_len={int(lens.max())} "
+          f"sampled sequences {seqs}", flush=True)
+
+    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0)
+    pages = fmt.new_pages(num_blocks)
+    ctx_off = np.concatenate([[0], np.cumsum(lens - 1)])
+    rows = {b: ([], []) for b in seqs}
+
+    def tap(s0, k, v):
+        n = k.shape[0]
+        for b in seqs:
+            lo, hi = max(int(ctx_off[b]), s0), min(int(ctx_off[b + 1]), s0 + n)
+            if lo < hi:
+                rows[b][0].append(k[lo - s0:hi - s0].cpu())
+                rows[b][1].append(v[lo - s0:hi - s0].cpu())
+
+    bench.fill_layer(w, layer, fmt, pages, torch.from_numpy(ctx_np).cuda(), num_blocks, torch, tq, wl,
+                     tap=tap)
+    new_k, new_v = bench.new_tokens(w, 1, wl)
+    new_slots = torch.from_numpy(new_np).cuda()
+    tq.tq_quantize_append(fmt.desc, new_k[0, layer], new_v[0, layer], new_slots, pages, num_blocks)
+    torch.cuda.synchronize()
+
+    (kc, kt), (vc, vt) = oracle_codebooks(D, kb, vb)
+    stride = fmt.slot_stride
+    flat = pages.view(-1, H, stride)
+    refs = {}
+    for b in seqs:
+        L = int(lens[b])
+        k = torch.cat(rows[b][0] + [new_k[0, layer, b:b + 1].cpu()]).numpy()
+        v = torch.cat(rows[b][1] + [new_v[0, layer, b:b + 1].cpu()]).numpy()
+        assert k.shape == (L, H, D)
+        # oracle pages of this one sequence, identity table
+        one = wl.scaled(w, num_seqs=1, tables="identity")
+        bt1, nblk1 = wl.block_tables(one, np.array([L]))
+        slots1 = wl.token_slots(bt1, 0, np.arange(L), bs)
+        ref = np.zeros(nblk1 * bs * H * stride, np.uint8)
+        k_tie, v_tie = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride)
+        # the GPU's rows of the same positions
+        slots = wl.token_slots(bt_np, b, np.arange(L), bs)
+        gpu_rows = flat[torch.from_numpy(slots).cuda()].cpu().numpy()
+        ref_rows = ref.reshape(-1, H, stride)[slots1]
+        ties = compare_pages(gpu_rows.reshape(-1), ref_rows.reshape(-1), np.arange(L), H, D, kb, vb,
+                             stride, k_tie, v_tie)
+        print(f"[fullsize]   seq {b} (L={L}): page rows match, {ties} tie indices", flush=True)
+        # the oracle's bytes into the GPU pages of this sequence
+        flat[torch.from_numpy(slots).cuda()] = torch.from_numpy(ref_rows).cuda()
+        refs[b] = (ref, bt1, L)
+
+    q = wl.queries(w, layer, 0, "cuda")
+    sink_k, sink_v = wl.sinks(w, 0, "cuda")
+    max_len = int(lens.max())
+    ws = fmt.new_workspace(B, max_len)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_paged_decode_attention(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
+                                 torch.from_numpy(lens).cuda(), max_len, out, ws, sink_k, sink_v,
+                                 w.n_sink)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got)), "non-finite output in the batch"
+    layer_dict = dict(D=D, H_kv=H, block_size=bs, k_bits=kb, v_bits=vb, seed=0, slot_stride=stride)
+    qn = q.cpu().numpy()
+    skn = None if sink_k is None else sink_k.cpu().numpy()
+    svn = None if sink_v is None else sink_v.cpu().numpy()
+    for b in seqs:
+        ref, bt1, L = refs[b]
+        want = oatt.decode_attention(qn[b:b + 1], ref, bt1, np.array([L], np.int32), layer_dict, kc, vc,
+                                     None if skn is None else skn[b:b + 1],
+                                     None if svn is None else svn[b:b + 1], w.n_sink)
+        max_abs, rel = check_attention(got[b:b + 1], want)
+        print(f"[fullsize]   seq {b}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}", flush=True)
