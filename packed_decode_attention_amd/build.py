@@ -3,7 +3,9 @@
     python -m packed_decode_attention_amd.build            # or: python packed_decode_attention_amd/build.py
 
 hipcc cross-compiles the device code for gfx950 without a GPU present.  Packed-fp32 VALU
-instructions are disabled for all device code (-packed-fp32-ops).
+instructions are disabled for all device code (-packed-fp32-ops).  The decode kernels take
+finite inputs by contract and are built with -fno-honor-nans, which lets the running-maximum
+reductions fold into single DPP max instructions.
 """
 
 from __future__ import annotations
@@ -26,10 +28,10 @@ DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fno-strict-aliasing", f"--offloa
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
 
 SOURCES = [
-    ("tq_quantize.hip", "device"),
-    ("tq_decode.hip", "device"),
-    ("tq_api.cpp", "host"),
-    ("tq_codebook.cpp", "host"),
+    ("tq_quantize.hip", "device", []),
+    ("tq_decode.hip", "device", ["-fno-honor-nans"]),
+    ("tq_api.cpp", "host", []),
+    ("tq_codebook.cpp", "host", []),
 ]
 
 
@@ -40,15 +42,20 @@ def _run(cmd):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src, kind in SOURCES:
+    objs, procs = [], []
+    for src, kind, extra in SOURCES:  # compile every source in parallel
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         path = os.path.join(CSRC, src)
         if kind == "device":
-            _run([HIPCC, *DEVICE_FLAGS, "-c", path, "-o", obj])
+            cmd = [HIPCC, *DEVICE_FLAGS, *extra, "-c", path, "-o", obj]
         else:
-            _run(["g++", *HOST_FLAGS, "-c", path, "-o", obj])
+            cmd = ["g++", *HOST_FLAGS, *extra, "-c", path, "-o", obj]
+        print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
         objs.append(obj)
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -305,6 +305,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kLutShift = 8;    // centroid tables hold c * 2^8
 constexpr int kWShift = 15;     // weights enter the PV product as w * 2^15
 constexpr int kVRow = 18;       // dwords per token row of the per-wave value-code tile
+constexpr int kWRow = 34;       // fp16 per weight row of the per-wave weight tile (padded: the
+                                // four lane groups write different LDS banks)
+constexpr float kSent = -1.0e30f;  // finite stand-in for minus infinity in the running maxima
 
 __device__ __forceinline__ float4_t mfma_f16(const uint4& a, const uint4& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -355,9 +358,9 @@ __device__ __forceinline__ uint4 quad_of(const uint2& e0, const uint2& e1) {
   return make_uint4(e0.x, e0.y, e1.x, e1.y);
 }
 
+template <bool G8, bool UBLK>
 __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int kRing = 1;  // tiles in flight per wave (register ring)
   const TqLayer& L = a.L;
   const int G = L.G;
 
@@ -379,13 +382,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   __shared__ float s_q[8][D];
   __shared__ float s_qmax[8];
   __shared__ int64_t s_boff[kMaxBtLds];
-  __shared__ uint16_t s_w[kNW][16][32];
+  __shared__ uint16_t s_w[kNW][16][kWRow];
   __shared__ uint32_t s_v[kNW][32][kVRow];
   __shared__ float s_part[kNW][8][D + 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t16 = lane & 15;
   const int q4 = lane >> 4;
 
@@ -396,51 +399,45 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   const int p_end = min(p0 + a.chunk, seq_len);
   auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
   const int blk0 = block_of(p0);
-  const int nblk = p_end > p0 ? block_of(p_end - 1) - blk0 + 1 : 0;
+  const int blk_last = p_end > p0 ? block_of(p_end - 1) : blk0;
+  const int nblk = p_end > p0 ? blk_last - blk0 + 1 : 0;
   const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
   const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
   for (int i = tid; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
 
-  // Rotated queries qscale * H (s * q), then a power-of-two scale per head into fp16 range.
-  for (int i = tid; i < G * D; i += kWG) {
-    const int g = i / D, d = i % D;
-    const float v = half_bits_to_float(a.q[((int64_t)b * L.Hq + h * G + g) * D + d]);
-    const bool neg = (L.signs.w[d >> 5] >> (d & 31)) & 1u;
-    s_q[g][d] = neg ? -v : v;
-  }
-  __syncthreads();
-  for (int hb = 1; hb < D; hb <<= 1) {
-    for (int i = tid; i < G * D / 2; i += kWG) {
-      const int g = i / (D / 2), r = i % (D / 2);
-      const int lo = (r / hb) * 2 * hb + (r % hb);
-      const float x0 = s_q[g][lo], x1 = s_q[g][lo + hb];
-      s_q[g][lo] = x0 + x1;
-      s_q[g][lo + hb] = x0 - x1;
+  // Rotated queries H (s * q): one 16-lane DPP row per head, 8 coordinates per lane; the
+  // largest |q'| of each head sets its power-of-two scale into fp16 range below.
+  if (tid < 16 * G) {
+    const int g = tid >> 4, j = tid & 15;
+    float x[8];
+    load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, x);
+    const uint32_t sb = sign_byte(L.signs, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((sb >> e) & 1u) x[e] = -x[e];
+    wht_row8_dpp<16>(x, j);
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_q[g][8 * j + e] = x[e];
+      mx = fmaxf(mx, fabsf(x[e]));
     }
-    __syncthreads();
-  }
-  if (tid < 128) {  // max |q'| per head: one 16-lane row per head
-    for (int g = tid >> 4; g < G; g += 8) {
-      float mx = 0.0f;
-      for (int d = tid & 15; d < D; d += 16) mx = fmaxf(mx, fabsf(s_q[g][d]));
-      mx = fmaxf(mx, dpp<kDppQuadXor1>(mx));
-      mx = fmaxf(mx, dpp<kDppQuadXor2>(mx));
-      mx = fmaxf(mx, dpp<kDppHalfRowMirror>(mx));
-      mx = fmaxf(mx, dpp<kDppRowMirror>(mx));
-      if ((tid & 15) == 0) s_qmax[g] = mx * a.qscale;
-    }
+    mx = row16_max(mx);
+    if (j == 0) s_qmax[g] = mx * a.qscale;
   }
   __syncthreads();
 
-  auto head_exp = [&](int g) {
+auto head_exp = [&](int g) {
     const float qm = s_qmax[g];
     return qm > 0.0f ? 13 - ilogbf(qm) : 0;
   };
+  // Rows of both products: row m <-> head (m >> 2) + 4 ((m >> 1) & 1), fp16 part m & 1, so the
+  // result rows 4 q + i of lane group q are head q (i = 0, 1) and head q + 4 (i = 2, 3).
   // A operand of QK: lane (m = t16, q4), step st = 0..7 covers coordinates 32 q4 + 4 st + 0..3 as
-  // [q(c0), q(c1), q(c0), q(c1), q(c2), q(c3), q(c2), q(c3)] of row m (fp16 high or low part).
+  // [q(c0), q(c1), q(c0), q(c1), q(c2), q(c3), q(c2), q(c3)] of row m.
   uint4 aq[8];
   {
-    const int g = t16 >> 1;
+    const int g = (t16 >> 2) + 4 * ((t16 >> 1) & 1);
     const bool lo_part = t16 & 1;
     const bool live = g < G;
     const float f = live ? ldexpf(a.qscale, head_exp(g)) : 0.0f;
@@ -458,9 +455,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
       aq[st] = make_uint4(d01, d01, d23, d23);
     }
   }
-  // Score factors of the two heads whose rows this lane holds in the QK result: 2^-(e + 8).
-  const int g0 = 2 * q4, g1 = 2 * q4 + 1;
-  const bool live0 = g0 < G, live1 = g1 < G;
+  const int g0 = q4, g1 = q4 + 4;
+  const bool live0 = g0 < G, live1 = G8 && g1 < G;
+  // Score factors of the heads this lane holds: 2^-(e + 8).
   const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
   const float f1 = live1 ? ldexpf(1.0f, -(head_exp(g1) + kLutShift)) : 0.0f;
 
@@ -468,8 +465,27 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
+  // Per-lane byte offsets inside a run of 16 page rows (token t16, code bytes 16 q4..16 q4+15).
+  const uint32_t lane_row = __umul24((uint32_t)t16, row_bytes32);
+  const uint32_t off_k = lane_row + 16 * q4, off_v = off_k + voff;
+  const uint32_t off_kn = lane_row + L.kcode_bytes, off_vn = lane_row + voff + L.vcode_bytes;
 
-  auto row_ptr = [&](int p) {
+  // Row base of the 16 positions starting at pu (a multiple of 16).  With a block size that is a
+  // multiple of 16 the 16 rows lie in one page block, so the base is the same for the whole wave;
+  // past the split's last position the last block is reused (rows in bounds, masked later).
+  auto run_base = [&](int pu) {
+    int bi = block_of(pu);
+    int r0 = pu - bi * L.bs;
+    if (bi > blk_last) {
+      bi = blk_last;
+      r0 = 0;
+    }
+    const int64_t boff = s_boff[bi - blk0];
+    const int64_t o = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(boff & 0xffffffff)) |
+                      ((int64_t)__builtin_amdgcn_readfirstlane((int)(boff >> 32)) << 32);
+    return head_base + o + (int64_t)r0 * row_bytes;
+  };
+  auto row_ptr = [&](int p) {  // any block size: one lane's row
     const int pc = min(p, p_end - 1);
     const int bi = block_of(pc);
     return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
@@ -477,24 +493,43 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   auto fetch = [&](int tile, MTile& m) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint8_t* r = row_ptr(p0 + 32 * tile + 16 * u + t16);
-      m.k[u] = *reinterpret_cast<const uint4*>(r + 16 * q4);
-      m.v[u] = *reinterpret_cast<const uint4*>(r + voff + 16 * q4);
-      m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
-      m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
+      const int pu = p0 + 32 * tile + 16 * u;
+      if (UBLK) {
+        const uint8_t* rb = run_base(pu);
+        m.k[u] = *reinterpret_cast<const uint4*>(rb + off_k);
+        m.v[u] = *reinterpret_cast<const uint4*>(rb + off_v);
+        m.kn[u] = *reinterpret_cast<const float*>(rb + off_kn);
+        m.vn[u] = *reinterpret_cast<const float*>(rb + off_vn);
+      } else {
+        const uint8_t* r = row_ptr(pu + t16);
+        m.k[u] = *reinterpret_cast<const uint4*>(r + 16 * q4);
+        m.v[u] = *reinterpret_cast<const uint4*>(r + voff + 16 * q4);
+        m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
+        m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
+      }
     }
   };
 
-  float m_s[2] = {-INFINITY, -INFINITY};   // running max of scores (heads g0, g1)
-  float m_w[2] = {-INFINITY, -INFINITY};   // running max of score + log2(n_V)
-  float l_s[2] = {0.0f, 0.0f};             // per-lane partial sums of 2^(s - m_s)
+  // Online-softmax state.  kSent is a finite "minus infinity": masked positions score kSent, so
+  // no exp2 ever sees -inf - -inf; anything accumulated while the maximum is still kSent is
+  // scaled by exp2(kSent - m) = 0 as soon as a real score arrives.
+  float m_s[2] = {kSent, kSent};   // running max of scores (heads g0, g1)
+  float m_w[2] = {kSent, kSent};   // running max of score + log2(n_V)
+  float l_s[2] = {0.0f, 0.0f};     // per-lane partial sums of 2^(s - m_s)
   float4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  __syncthreads();  // tables, block offsets ready
   uint16_t* wt = &s_w[wave][0][0];
   uint32_t* vt = &s_v[wave][0][0];
+  if (!G8) {  // weight rows of heads 4..7 stay zero
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      wt[(4 * q4 + 2) * kWRow + 16 * u + t16] = 0;
+      wt[(4 * q4 + 3) * kWRow + 16 * u + t16] = 0;
+    }
+  }
+  __syncthreads();  // tables, block offsets, zero rows ready
 
   auto process = [&](const MTile& cur, int tile) {
     // ---- QK on the matrix cores ----
@@ -515,57 +550,66 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
       sc[u] = sa + sb;
     }
 
-    // ---- online softmax on the two heads of this lane group, tokens t16 and 16 + t16 ----
+    // ---- online softmax, tokens t16 and 16 + t16 ----
     const int pbase = p0 + 32 * tile;
     float s0[2], s1[2], lv[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p = pbase + 16 * u + t16;
       const bool valid = p >= ns && p < p_end;
-      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * cur.kn[u] * f0 : -INFINITY;
-      s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * cur.kn[u] * f1 : -INFINITY;
+      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * cur.kn[u] * f0 : kSent;
+      if (G8) s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * cur.kn[u] * f1 : kSent;
       lv[u] = __builtin_amdgcn_logf(cur.vn[u]);  // log2(n_V); -inf for a zero row
     }
-    const float ts0 = row16_max(fmaxf(s0[0], s0[1]));
-    const float ts1 = row16_max(fmaxf(s1[0], s1[1]));
-    const float tw0 = row16_max(fmaxf(s0[0] + lv[0], s0[1] + lv[1]));
-    const float tw1 = row16_max(fmaxf(s1[0] + lv[0], s1[1] + lv[1]));
-    const float ms0 = fmaxf(m_s[0], ts0), ms1 = fmaxf(m_s[1], ts1);
-    const float mw0 = fmaxf(m_w[0], tw0), mw1 = fmaxf(m_w[1], tw1);
+    const float ms0 = fmaxf(m_s[0], row16_max(fmaxf(s0[0], s0[1])));
+    const float mw0 = fmaxf(m_w[0], row16_max(fmaxf(s0[0] + lv[0], s0[1] + lv[1])));
+    float ms1 = kSent, mw1 = kSent;
+    if (G8) {
+      ms1 = fmaxf(m_s[1], row16_max(fmaxf(s1[0], s1[1])));
+      mw1 = fmaxf(m_w[1], row16_max(fmaxf(s1[0] + lv[0], s1[1] + lv[1])));
+    }
     if (ms0 > m_s[0]) l_s[0] *= __builtin_amdgcn_exp2f(m_s[0] - ms0);
-    if (ms1 > m_s[1]) l_s[1] *= __builtin_amdgcn_exp2f(m_s[1] - ms1);
     m_s[0] = ms0;
-    m_s[1] = ms1;
-    if (mw0 > m_w[0] || mw1 > m_w[1]) {
-      const float r0 = mw0 > m_w[0] ? __builtin_amdgcn_exp2f(m_w[0] - mw0) : 1.0f;
-      const float r1 = mw1 > m_w[1] ? __builtin_amdgcn_exp2f(m_w[1] - mw1) : 1.0f;
+    if (G8) {
+      if (ms1 > m_s[1]) l_s[1] *= __builtin_amdgcn_exp2f(m_s[1] - ms1);
+      m_s[1] = ms1;
+    }
+    const bool grow0 = mw0 > m_w[0], grow1 = G8 && mw1 > m_w[1];
+    if (grow0 || grow1) {
+      const float r0 = grow0 ? __builtin_amdgcn_exp2f(m_w[0] - mw0) : 1.0f;
+      const float r1 = grow1 ? __builtin_amdgcn_exp2f(m_w[1] - mw1) : 1.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         acc[c][0] *= r0;
         acc[c][1] *= r0;
-        acc[c][2] *= r1;
-        acc[c][3] *= r1;
+        if (G8) {
+          acc[c][2] *= r1;
+          acc[c][3] *= r1;
+        }
       }
     }
     m_w[0] = mw0;
-    m_w[1] = mw1;
+    if (G8) m_w[1] = mw1;
+    // weights enter the product scaled by 2^kWShift: fold the shift into the reference maximum
+    const float mw0s = mw0 - (float)kWShift, mw1s = mw1 - (float)kWShift;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // last tile's tile reads are done
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const float p0u = s0[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s0[u] - ms0);
-      const float p1u = s1[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s1[u] - ms1);
-      l_s[0] += p0u;
-      l_s[1] += p1u;
-      const float sw0 = s0[u] + lv[u], sw1 = s1[u] + lv[u];
-      const float w0 = sw0 == -INFINITY ? 0.0f : ldexpf(__builtin_amdgcn_exp2f(sw0 - mw0), kWShift);
-      const float w1 = sw1 == -INFINITY ? 0.0f : ldexpf(__builtin_amdgcn_exp2f(sw1 - mw1), kWShift);
-      uint32_t h0, l0, h1, l1;
+      l_s[0] += __builtin_amdgcn_exp2f(s0[u] - ms0);
+      const float w0 = __builtin_amdgcn_exp2f(s0[u] + lv[u] - mw0s);
+      uint32_t h0, l0;
       split_f16(w0, h0, l0);
-      split_f16(w1, h1, l1);
       const int col = 16 * u + t16;
-      wt[(4 * q4 + 0) * 32 + col] = (uint16_t)h0;
-      wt[(4 * q4 + 1) * 32 + col] = (uint16_t)l0;
-      wt[(4 * q4 + 2) * 32 + col] = (uint16_t)h1;
-      wt[(4 * q4 + 3) * 32 + col] = (uint16_t)l1;
+      wt[(4 * q4 + 0) * kWRow + col] = (uint16_t)h0;
+      wt[(4 * q4 + 1) * kWRow + col] = (uint16_t)l0;
+      if (G8) {
+        l_s[1] += __builtin_amdgcn_exp2f(s1[u] - ms1);
+        const float w1 = __builtin_amdgcn_exp2f(s1[u] + lv[u] - mw1s);
+        uint32_t h1, l1;
+        split_f16(w1, h1, l1);
+        wt[(4 * q4 + 2) * kWRow + col] = (uint16_t)h1;
+        wt[(4 * q4 + 3) * kWRow + col] = (uint16_t)l1;
+      }
       // value codes of token 16u + t16, coordinates 32 q4 .. 32 q4 + 31 (dwords 4 q4 .. 4 q4 + 3)
       uint32_t* vrow = vt + (16 * u + t16) * kVRow + 4 * q4;
       *reinterpret_cast<uint2*>(vrow) = make_uint2(cur.v[u].x, cur.v[u].y);
@@ -587,7 +631,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       // weights of tokens 8 q4 + 4 j + 0..3 as [w0, w1, w0, w1, w2, w3, w2, w3] (row t16)
-      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wt + t16 * 32 + 8 * q4 + 4 * j);
+      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wt + t16 * kWRow + 8 * q4 + 4 * j);
       const uint32_t w01 = wrow[0], w23 = wrow[1];
       const uint4 aw = make_uint4(w01, w01, w23, w23);
       // coordinate 8 t16 + c: even c -> byte c/2 of E_i, odd c -> byte c/2 of O_i
@@ -603,19 +647,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     }
   };
 
-  MTile ring[kRing];
-#pragma unroll
-  for (int r = 0; r < kRing; ++r)
-    if (wave + r * kNW < n_tiles) fetch(wave + r * kNW, ring[r]);
-  for (int base = wave; base < n_tiles; base += kRing * kNW) {
-#pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      const int tile = base + r * kNW;
-      if (tile < n_tiles) {
-        process(ring[r], tile);
-        if (tile + kRing * kNW < n_tiles) fetch(tile + kRing * kNW, ring[r]);
-      }
-    }
+  MTile cur;
+  if (wave < n_tiles) fetch(wave, cur);
+  for (int tile = wave; tile < n_tiles; tile += kNW) {
+    MTile nxt;
+    if (tile + kNW < n_tiles) fetch(tile + kNW, nxt);
+    process(cur, tile);
+    cur = nxt;
   }
 
   // ---- wave result: heads g0, g1 at coordinates 8 t16 + c, in the score-max frame ----
@@ -627,8 +665,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     l_s[i] += dpp<kDppRowMirror>(l_s[i]);
   }
   const float vscale = ldexpf(1.0f, -(kWShift + kLutShift));
-  const float c0 = m_w[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[0] - m_s[0]) * vscale;
-  const float c1 = m_w[1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
+  const float c0 = __builtin_amdgcn_exp2f(m_w[0] - m_s[0]) * vscale;
+  const float c1 = __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
   if (live0) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) s_part[wave][g0][2 + 8 * t16 + c] = (acc[c][0] + acc[c][1]) * c0;
@@ -651,7 +689,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   float* part = a.partials + (bh * a.max_split + split) * (int64_t)G * (D + 2);
   for (int i = tid; i < G * (D + 2); i += kWG) {
     const int g = i / (D + 2), d = i % (D + 2);
-    float M = -INFINITY;
+    float M = kSent;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_part[w][g][0]);
     float r;
@@ -660,11 +698,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
     } else {
       r = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        const float mw = s_part[w][g][0];
-        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        r += s_part[w][g][d] * f;
-      }
+      for (int w = 0; w < kNW; ++w) r += s_part[w][g][d] * __builtin_amdgcn_exp2f(s_part[w][g][0] - M);
     }
     part[i] = r;
   }
@@ -685,7 +719,7 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
     for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
     return;
   }
-  __shared__ float s_acc[GMAX * D];              // rotated accumulators
+  __shared__ float s_acc[GMAX * D];              // merged rotated accumulators
   __shared__ float s_ml[2 * GMAX];               // max, sum
   __shared__ float s_sink[GMAX * TQ_MAX_SINKS];  // sink scores, log2 domain
   for (int i = threadIdx.x; i < G * ns; i += kWG) {
@@ -697,56 +731,72 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
     s_sink[g * ns + pp] = dot * a.sink_scale;
   }
   __syncthreads();
+
+  // Online log-sum-exp merge of the splits, one (head, coordinate) per thread.  Partials are
+  // loaded eight splits at a time so their loads are in flight together.  Empty partials carry a
+  // maximum of -inf or kSent and contribute exp2(. - M) = 0 once a real score is in M.
   const int64_t bh = (int64_t)b * L.Hkv + h;
   const float* pb = a.partials + bh * a.max_split * (int64_t)G * (D + 2);
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pb[(sp * G + g) * (D + 2)]);
+  for (int i = threadIdx.x; i < G * D; i += kWG) {
+    const int g = i / D, d = i % D;
+    float M = kSent;
     for (int pp = 0; pp < ns; ++pp) M = fmaxf(M, s_sink[g * ns + pp]);
-    float sum = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ms = pb[(sp * G + g) * (D + 2)];
-      if (ms != -INFINITY) sum += pb[(sp * G + g) * (D + 2) + 1] * __builtin_amdgcn_exp2f(ms - M);
+    float l = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float ms[8], ls[8], as[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool in = s0 + k < nsplit;
+        const float* e = pb + ((int64_t)(in ? s0 + k : 0) * G + g) * (D + 2);
+        ms[k] = in ? e[0] : -INFINITY;
+        ls[k] = in ? e[1] : 0.0f;
+        as[k] = in ? e[2 + d] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float Mn = fmaxf(M, ms[k]);
+        const float fo = __builtin_amdgcn_exp2f(M - Mn), fn = __builtin_amdgcn_exp2f(ms[k] - Mn);
+        l = l * fo + ls[k] * fn;
+        acc = acc * fo + as[k] * fn;
+        M = Mn;
+      }
     }
-    for (int pp = 0; pp < ns; ++pp) sum += __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
-    s_ml[g] = M;
-    s_ml[GMAX + g] = sum;
+    for (int pp = 0; pp < ns; ++pp) l += __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
+    s_acc[g * D + d] = acc;
+    if (d == 0) {
+      s_ml[g] = M;
+      s_ml[GMAX + g] = l;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kWG) {
-    const int g = i / D, d = i % D;
-    const float M = s_ml[g];
-    float acc_d = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ms = pb[(sp * G + g) * (D + 2)];
-      if (ms != -INFINITY) acc_d += pb[(sp * G + g) * (D + 2) + 2 + d] * __builtin_amdgcn_exp2f(ms - M);
+
+  // R^T a = D^(-1/2) diag(s) H a, then the sinks' values, then the division by the sum: D/8
+  // lanes of one DPP row per head, 8 coordinates per lane.
+  constexpr int LPH = D / 8;
+  if (threadIdx.x < LPH * G) {
+    const int g = threadIdx.x / LPH, j = threadIdx.x % LPH;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = s_acc[g * D + 8 * j + e];
+    wht_row8_dpp<LPH>(x, j);
+    const uint32_t sb = sign_byte(L.signs, j);
+    const float M = s_ml[g], inv_l = 1.0f / s_ml[GMAX + g];
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = x[e] * a.rsqrt_d;
+      if ((sb >> e) & 1u) o[e] = -o[e];
     }
-    s_acc[g * D + d] = acc_d;
-  }
-  __syncthreads();
-  // R^T a = D^(-1/2) diag(s) H a: Walsh-Hadamard butterflies in LDS.
-  for (int hb = 1; hb < D; hb <<= 1) {
-    for (int i = threadIdx.x; i < G * D / 2; i += kWG) {
-      const int g = i / (D / 2), r = i % (D / 2);
-      const int lo = (r / hb) * 2 * hb + (r % hb);
-      const float x0 = s_acc[g * D + lo], x1 = s_acc[g * D + lo + hb];
-      s_acc[g * D + lo] = x0 + x1;
-      s_acc[g * D + lo + hb] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  for (int i = threadIdx.x; i < G * D; i += kWG) {
-    const int g = i / D, d = i % D;
-    const bool neg = (L.signs.w[d >> 5] >> (d & 31)) & 1u;
-    float o = s_acc[g * D + d] * a.rsqrt_d;
-    if (neg) o = -o;
-    const float M = s_ml[g];
     for (int pp = 0; pp < ns; ++pp) {
       const float w = __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
-      o += w * half_bits_to_float(a.sink_v[(((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D + d]);
+      float sv[8];
+      load8_f16(a.sink_v + (((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D + 8 * j, sv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += w * sv[e];
     }
-    outp[g * D + d] = o / s_ml[GMAX + g];
+    float4* o4 = reinterpret_cast<float4*>(outp + g * D + 8 * j);
+    o4[0] = make_float4(o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l);
+    o4[1] = make_float4(o[4] * inv_l, o[5] * inv_l, o[6] * inv_l, o[7] * inv_l);
   }
 }
 
@@ -778,7 +828,14 @@ void launch_v(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
 template <int D>
 void launch_k(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
   if (D == 128 && a.L.kb == 4 && a.L.vb == 4) {
-    hipLaunchKernelGGL(tq_decode_mfma_k4v4_kernel, grid, dim3(kWG), 0, st, a);
+    const bool ublk = a.L.bs % 16 == 0;
+    if (a.L.G > 4) {
+      if (ublk) hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<true, true>), grid, dim3(kWG), 0, st, a);
+      else hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<true, false>), grid, dim3(kWG), 0, st, a);
+    } else {
+      if (ublk) hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<false, true>), grid, dim3(kWG), 0, st, a);
+      else hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<false, false>), grid, dim3(kWG), 0, st, a);
+    }
     if (a.L.G <= 1) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 1>), mgrid, dim3(kWG), 0, st, a);
     else if (a.L.G <= 2) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 2>), mgrid, dim3(kWG), 0, st, a);
     else if (a.L.G <= 4) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 4>), mgrid, dim3(kWG), 0, st, a);

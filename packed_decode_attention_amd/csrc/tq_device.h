@@ -87,6 +87,44 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+constexpr int kDppRowRor8 = 0x128;        // lane i <- lane (i + 8) mod 16 within each 16-lane row
+
+// x of lane (i XOR M) within each 16-lane row, M = 1, 2, 4 or 8, by one or two DPP moves.
+template <int M>
+__device__ __forceinline__ float dpp_xor(float x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP xor partner");
+  if constexpr (M == 1) return dpp<kDppQuadXor1>(x);
+  if constexpr (M == 2) return dpp<kDppQuadXor2>(x);
+  if constexpr (M == 4) return dpp<kDppQuadRev>(dpp<kDppHalfRowMirror>(x));  // 7-i, then quad reversal
+  return dpp<kDppRowRor8>(x);
+}
+
+// Walsh-Hadamard transform (Sylvester order) of a row of 8*P floats held by P <= 16 lanes of one
+// DPP row, 8 per lane (lane j holds elements 8j .. 8j+7): in-lane butterflies, then DPP partners.
+template <int P>
+__device__ __forceinline__ void wht_row8_dpp(float (&x)[8], int j) {
+#pragma unroll
+  for (int hb = 1; hb < 8; hb <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!(e & hb)) {
+        const float a = x[e], b = x[e | hb];
+        x[e] = a + b;
+        x[e | hb] = a - b;
+      }
+    }
+  }
+  auto level = [&](auto partner, int m) {
+    const float sgn = (j & m) ? -1.0f : 1.0f;  // lower lane: x + p, upper lane: p - x
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(x[e], sgn, partner(x[e]));
+  };
+  if constexpr (P >= 2) level([](float v) { return dpp_xor<1>(v); }, 1);
+  if constexpr (P >= 4) level([](float v) { return dpp_xor<2>(v); }, 2);
+  if constexpr (P >= 8) level([](float v) { return dpp_xor<4>(v); }, 4);
+  if constexpr (P >= 16) level([](float v) { return dpp_xor<8>(v); }, 8);
+}
+
 // Sum over aligned groups of P lanes (P = 1, 2, 4, 8, 16), result in every lane of the group.
 template <int P>
 __device__ __forceinline__ float group_sum(float x) {
