@@ -78,6 +78,6 @@ class LayerFormat:
 def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int):
     """Names of the kernels one tq_paged_decode_attention call launches for this format, in
     launch order (as they appear in a kernel trace)."""
-    split = ("tq_decode_mfma_k4v4_kernel" if (head_dim, k_bits, v_bits) == (128, 4, 4)
-             else "tq_decode_split_kernel")
-    return [split, "tq_decode_merge_kernel"]
+    mfma = ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
+            (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
+    return ["tq_decode_mfma_kernel" if mfma else "tq_decode_split_kernel", "tq_decode_merge_kernel"]

@@ -8,8 +8,9 @@
 // R = D^(-1/2) H diag(s):  q . (n R^T c) = n (R q) . c  and  sum_p w_p n_p R^T c_p = R^T sum_p w_p n_p c_p.
 //
 // Two launches:
-//  1. tq_decode_split_kernel: one workgroup (4 waves) per (sequence, kv head, split of `chunk` page
-//     tokens).  A token row is held by P lanes (C = D/P coordinates each; P = 8, or 16 for 8 query
+//  1. a split kernel, one workgroup (4 waves) per (sequence, kv head, split of `chunk` page
+//     tokens): tq_decode_mfma_kernel (matrix cores, further below) for the formats it covers,
+//     else tq_decode_split_kernel (vector ALUs), described here.  A token row is held by P lanes (C = D/P coordinates each; P = 8, or 16 for 8 query
 //     heads at D = 128), so a wave covers 64/P tokens per step and the QK dot product needs a
 //     log2(P)-step DPP reduction.  The G query heads that share the kv head are processed
 //     together, so each code is unpacked and looked up once for G heads.  Centroids come from
@@ -282,19 +283,26 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 
 
 // =============================================================================================
-// Matrix-core split kernel for 4-bit K and V codes at D = 128.
+// Matrix-core split kernel: D = 128 with K codes of 2, 3, 4 or 8 bits and V codes of 2, 4 or 8
+// bits, and D = 64 with 4- or 8-bit K and V codes.
 //
-// Per wave, tiles of 32 page positions.  QK^T and PV run on v_mfma_f32_16x16x32_f16:
-//  * QK: A = rotated queries (rows 2g / 2g+1 = fp16 high / low part of head g, zero rows for
-//    g >= G), B = centroids of 16 tokens (K dimension = 32 coordinates per step; lane group q
-//    owns coordinates 32q..32q+31, so its B data is one 16-byte load per token).  The B operand
-//    is used twice, with the fp16 high and low parts of the centroids, so every product of the
-//    two-part query with the two-part centroid is accumulated in fp32 (about 22 significant
-//    bits per factor instead of 11).  Scores for head g are rows 2g + 2g+1 of the result.
-//  * PV: A = softmax weights w = p * n_V (fp16 high / low rows per head), B = value centroids
-//    with the K dimension running over 32 tokens; the 4-bit value codes of 8 tokens are
-//    gathered per lane through a small LDS tile and paired by nibble so that one byte-indexed
-//    lookup yields the fp16 pair (token a, token b) of one coordinate.
+// Per wave, tiles of 32 page positions (two sub-tiles of 16).  QK^T and PV run on
+// v_mfma_f32_16x16x32_f16 (A: 16 rows x 32, B: 32 x 16 columns, fp32 accumulate):
+//  * Rows of both products: row m <-> query head (m >> 2) + 4 ((m >> 1) & 1), fp16 part m & 1
+//    (high, low), so result rows 4q + i of lane group q hold head q (i = 0, 1) and head q + 4
+//    (i = 2, 3); with G <= 4 every lane group carries one head and rows of heads >= G are zero.
+//  * QK: A = rotated query (two fp16 parts per head), B = key centroids of 16 tokens.  Lane
+//    group q owns coordinates (D/4) q .. (D/4) q + D/4 - 1 of every token, one contiguous run of
+//    code bytes.  A code index (one byte; six bits for 3-bit codes) selects from an LDS table the
+//    fp16 high and low parts of one, two or four centroids, already in MFMA operand order; the
+//    query operand repeats its values in the matching pattern, so every product of the two-part
+//    query with the two-part centroid is accumulated in fp32 (about 22 significant bits per
+//    factor instead of 11).
+//  * PV: A = softmax weights w = p * n_V (two fp16 parts per head), B = value centroids with the
+//    contraction running over tokens.  Value codes of the tile go through a per-wave LDS tile so
+//    that lane (n, q) can gather the codes of coordinates (D/16) n .. (D/16) n + D/16 - 1 for
+//    tokens 8q .. 8q + 7; 4-bit codes of two tokens (or 2-bit codes of four) are merged into one
+//    byte per coordinate, so one table read yields the operand values of several tokens.
 // All fp16 operands are pre-scaled by powers of two into the normal fp16 range (queries per
 // head, centroid tables by 2^8, weights by 2^15); the scales are removed in fp32.  Weights use
 // their own running maximum of score + log2(n_V), so they stay in (0, 1] before scaling.
@@ -304,10 +312,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLutShift = 8;    // centroid tables hold c * 2^8
 constexpr int kWShift = 15;     // weights enter the PV product as w * 2^15
-constexpr int kVRow = 18;       // dwords per token row of the per-wave value-code tile
-constexpr int kWRow = 34;       // fp16 per weight row of the per-wave weight tile (padded: the
-                                // four lane groups write different LDS banks)
 constexpr float kSent = -1.0e30f;  // finite stand-in for minus infinity in the running maxima
+
+// Formats the matrix-core kernel implements (everything else runs on tq_decode_split_kernel).
+constexpr bool mfma_format(int D, int KB, int VB) {
+  return (D == 128 && (KB == 2 || KB == 3 || KB == 4 || KB == 8) && (VB == 2 || VB == 4 || VB == 8)) ||
+         (D == 64 && (KB == 4 || KB == 8) && (VB == 4 || VB == 8));
+}
 
 __device__ __forceinline__ float4_t mfma_f16(const uint4& a, const uint4& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -322,45 +333,129 @@ __device__ __forceinline__ void split_f16(float x, uint32_t& hi, uint32_t& lo) {
   lo = __builtin_bit_cast(uint16_t, l);
 }
 
-// Byte e of 4-bit codes -> (hi(c[e & 15]) | hi(c[e >> 4]) << 16, lo(..) | lo(..) << 16), c scaled.
-__device__ __forceinline__ void build_pair_lut4(uint2* t, const float* __restrict__ c, int tid) {
-  for (int e = tid; e < 256; e += kWG) {
-    uint32_t h0, l0, h1, l1;
-    split_f16(ldexpf(c[e & 15], kLutShift), h0, l0);
-    split_f16(ldexpf(c[e >> 4], kLutShift), h1, l1);
-    t[e] = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
+// Operand tables.  Index e holds the codes of V consecutive values (value v in bits
+// [BITS v, BITS (v + 1)) of e); the entry is the 8 fp16 of an MFMA operand fragment for them:
+//   V = 1 (8-bit codes): uint32 {hi, lo}                                  -> [h0 l0]
+//   V = 2 (3-, 4-bit):   uint2  {hi0 hi1, lo0 lo1}                        -> [h0 h1 l0 l1]
+//   V = 4 (2-bit):       uint4  {hi0 hi1, hi2 hi3, lo0 lo1, lo2 lo3}      -> [h0 h1 h2 h3 l0 l1 l2 l3]
+// The other operand repeats its values to match: [x0 x0 x1 x1 ..], [x0 x1 x0 x1 ..] or
+// [x0 x1 x2 x3 x0 x1 x2 x3].
+template <int BITS> struct OpTable;
+template <> struct OpTable<8> { using E = uint32_t; static constexpr int N = 256, V = 1; };
+template <> struct OpTable<4> { using E = uint2; static constexpr int N = 256, V = 2; };
+template <> struct OpTable<3> { using E = uint2; static constexpr int N = 64, V = 2; };
+template <> struct OpTable<2> { using E = uint4; static constexpr int N = 256, V = 4; };
+
+template <int BITS>
+__device__ __forceinline__ void build_op_table(typename OpTable<BITS>::E* t, const float* __restrict__ c,
+                                               int tid) {
+  constexpr int V = OpTable<BITS>::V, M = (1 << BITS) - 1;
+  for (int e = tid; e < OpTable<BITS>::N; e += kWG) {
+    uint32_t hi[V], lo[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) split_f16(ldexpf(c[(e >> (BITS * v)) & M], kLutShift), hi[v], lo[v]);
+    if constexpr (V == 1) t[e] = hi[0] | (lo[0] << 16);
+    if constexpr (V == 2) t[e] = make_uint2(hi[0] | (hi[1] << 16), lo[0] | (lo[1] << 16));
+    if constexpr (V == 4)
+      t[e] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), lo[0] | (lo[1] << 16),
+                        lo[2] | (lo[3] << 16));
   }
 }
+
+// The other operand for four fp16 values given as x01 = x0 | x1 << 16 and x23 = x2 | x3 << 16.
+template <int V>
+__device__ __forceinline__ uint4 repeat_operand(uint32_t x01, uint32_t x23) {
+  if constexpr (V == 2) return make_uint4(x01, x01, x23, x23);
+  if constexpr (V == 4) return make_uint4(x01, x23, x01, x23);
+  const uint32_t l01 = x01 & 0xffffu, l23 = x23 & 0xffffu;
+  return make_uint4(l01 | (l01 << 16), (x01 >> 16) | (x01 & 0xffff0000u), l23 | (l23 << 16),
+                    (x23 >> 16) | (x23 & 0xffff0000u));
+}
+
+// N consecutive dwords from a 4-byte aligned address.
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t (&w)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = x.x;
+      w[4 * i + 1] = x.y;
+      w[4 * i + 2] = x.z;
+      w[4 * i + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+  }
+}
+
+template <int D, int KB, int VB>
+struct MfmaCfg {
+  static constexpr int QC = D / 4;              // coordinates per lane group in QK
+  static constexpr int NMQ = D / 16;            // QK MFMAs per 16-token sub-tile
+  static constexpr int PC = D / 16;             // coordinates per lane in PV (= PV MFMAs)
+  static constexpr int KW = D * KB / 128;       // dwords of K codes per lane and token
+  static constexpr int VW = D * VB / 128;       // dwords of V codes per lane and token
+  static constexpr int VROW = D * VB / 32 + 2;  // dwords per token row of the value tile (padded)
+  static constexpr int VK = OpTable<KB>::V, VV = OpTable<VB>::V;
+  // weight tile: fp16 per token, or fp16 pairs (w, w) for 8-bit values (rows of 16-byte
+  // multiples so a lane reads four pairs at once); rows padded against bank conflicts
+  static constexpr int WROW = VV == 1 ? 36 : 18;  // dwords per weight row
+};
+
+template <int D, int KB, int VB>
+struct MfmaTile {
+  uint32_t k[2][MfmaCfg<D, KB, VB>::KW];  // K codes of tokens t16, 16 + t16 (lane group's run)
+  uint32_t v[2][MfmaCfg<D, KB, VB>::VW];  // V codes of the same tokens and coordinates
+  float kn[2], vn[2];
+};
 
 template <int DPPCTRL>
 __device__ __forceinline__ float dpp_max_step(float x) { return fmaxf(x, dpp<DPPCTRL>(x)); }
 
-__device__ __forceinline__ float row16_max(float x) {
+// Maximum over aligned groups of P = 8 or 16 lanes, result in every lane of the group.
+template <int P>
+__device__ __forceinline__ float lanes_max(float x) {
   x = dpp_max_step<kDppQuadXor1>(x);
   x = dpp_max_step<kDppQuadXor2>(x);
   x = dpp_max_step<kDppHalfRowMirror>(x);
-  x = dpp_max_step<kDppRowMirror>(x);
+  if constexpr (P == 16) x = dpp_max_step<kDppRowMirror>(x);
   return x;
 }
+__device__ __forceinline__ float row16_max(float x) { return lanes_max<16>(x); }
 
-// One 32-position tile of page data for one lane: lane (t, q) reads tokens t and 16 + t.
-struct MTile {
-  uint4 k[2];     // K code bytes 16q..16q+15 of tokens t, 16+t
-  uint4 v[2];     // V code bytes 16q..16q+15 of tokens t, 16+t
-  float kn[2], vn[2];
-};
-
-// MFMA operand of 8 fp16 in the interleaved order used by both products: for a pair of
-// lookups e0, e1 (each = (high parts of two values, low parts of the same two values)) the
-// operand is [hi(x0), hi(x1), lo(x0), lo(x1), hi(x2), hi(x3), lo(x2), lo(x3)], so the K dimension
-// runs over (value, part).  The other operand repeats its value for both parts.
-__device__ __forceinline__ uint4 quad_of(const uint2& e0, const uint2& e1) {
-  return make_uint4(e0.x, e0.y, e1.x, e1.y);
+// B operand of QK step st (coordinates 4 st .. 4 st + 3 of the lane's run) from its code words.
+template <int KB>
+__device__ __forceinline__ uint4 k_operand(const typename OpTable<KB>::E* tab, const uint32_t* kw, int st) {
+  if constexpr (KB == 8) {
+    const uint32_t w = kw[st];
+    return make_uint4(tab[w & 0xffu], tab[(w >> 8) & 0xffu], tab[(w >> 16) & 0xffu], tab[w >> 24]);
+  } else if constexpr (KB == 4) {
+    const uint32_t w = kw[st >> 1] >> (16 * (st & 1));
+    const uint2 e0 = tab[w & 0xffu], e1 = tab[(w >> 8) & 0xffu];
+    return make_uint4(e0.x, e0.y, e1.x, e1.y);
+  } else if constexpr (KB == 3) {
+    const int bit = 12 * st;  // two 6-bit indices at bits [12 st, 12 st + 12) of the run
+    const int wi = bit >> 5, sh = bit & 31;
+    const uint32_t f = sh <= 20 ? (kw[wi] >> sh) : __builtin_amdgcn_alignbit(kw[wi + 1], kw[wi], sh);
+    const uint2 e0 = tab[f & 63u], e1 = tab[(f >> 6) & 63u];
+    return make_uint4(e0.x, e0.y, e1.x, e1.y);
+  } else {
+    return tab[(kw[st >> 2] >> (8 * (st & 3))) & 0xffu];
+  }
 }
 
-template <bool G8, bool UBLK>
-__global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs a) {
-  constexpr int D = 128;
+template <int D, int KB, int VB, bool G8, bool UBLK>
+__global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
+  using C = MfmaCfg<D, KB, VB>;
+  using KE = typename OpTable<KB>::E;
+  using VE = typename OpTable<VB>::E;
+  using Tile = MfmaTile<D, KB, VB>;
   const TqLayer& L = a.L;
   const int G = L.G;
 
@@ -377,14 +472,17 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   const int nsplit = num_splits(seq_len, a.chunk);
   if (split >= nsplit) return;
 
-  __shared__ uint2 s_klut[256];
-  __shared__ uint2 s_vlut[256];
-  __shared__ float s_q[8][D];
-  __shared__ float s_qmax[8];
+  __shared__ KE s_ktab[OpTable<KB>::N];
+  __shared__ VE s_vtab[OpTable<VB>::N];
   __shared__ int64_t s_boff[kMaxBtLds];
-  __shared__ uint16_t s_w[kNW][16][kWRow];
-  __shared__ uint32_t s_v[kNW][32][kVRow];
-  __shared__ float s_part[kNW][8][D + 2];
+  __shared__ float s_qmax[8];
+  constexpr int H8 = G8 ? 8 : 4;  // query heads per kv head this instance handles at most
+  __shared__ __align__(16) uint32_t s_w[kNW][16][C::WROW];
+  __shared__ __align__(16) uint32_t s_v[kNW][32][C::VROW];
+  // rotated queries (prologue) and the per-wave partial results (epilogue) share one buffer
+  __shared__ __align__(16) float s_qp[kNW * H8 * (D + 2)];
+  float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_qp);
+  float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_qp);  // [wave * H8 + head]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,8 +490,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   const int t16 = lane & 15;
   const int q4 = lane >> 4;
 
-  build_pair_lut4(s_klut, L.kc, tid);
-  build_pair_lut4(s_vlut, L.vc, tid);
+  build_op_table<KB>(s_ktab, L.kc, tid);
+  build_op_table<VB>(s_vtab, L.vc, tid);
 
   const int p0 = split * a.chunk;
   const int p_end = min(p0 + a.chunk, seq_len);
@@ -405,54 +503,52 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_k4v4_kernel(DecodeArgs 
   const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
   for (int i = tid; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
 
-  // Rotated queries H (s * q): one 16-lane DPP row per head, 8 coordinates per lane; the
+  // Rotated queries H (s * q): D/8 lanes of one DPP row per head, 8 coordinates per lane; the
   // largest |q'| of each head sets its power-of-two scale into fp16 range below.
-  if (tid < 16 * G) {
-    const int g = tid >> 4, j = tid & 15;
+  constexpr int LPH = D / 8;
+  if (tid < LPH * G) {
+    const int g = tid / LPH, j = tid % LPH;
     float x[8];
     load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, x);
     const uint32_t sb = sign_byte(L.signs, j);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if ((sb >> e) & 1u) x[e] = -x[e];
-    wht_row8_dpp<16>(x, j);
+    wht_row8_dpp<LPH>(x, j);
     float mx = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       s_q[g][8 * j + e] = x[e];
       mx = fmaxf(mx, fabsf(x[e]));
     }
-    mx = row16_max(mx);
+    mx = lanes_max<LPH>(mx);
     if (j == 0) s_qmax[g] = mx * a.qscale;
   }
   __syncthreads();
 
-auto head_exp = [&](int g) {
+  auto head_exp = [&](int g) {
     const float qm = s_qmax[g];
     return qm > 0.0f ? 13 - ilogbf(qm) : 0;
   };
-  // Rows of both products: row m <-> head (m >> 2) + 4 ((m >> 1) & 1), fp16 part m & 1, so the
-  // result rows 4 q + i of lane group q are head q (i = 0, 1) and head q + 4 (i = 2, 3).
-  // A operand of QK: lane (m = t16, q4), step st = 0..7 covers coordinates 32 q4 + 4 st + 0..3 as
-  // [q(c0), q(c1), q(c0), q(c1), q(c2), q(c3), q(c2), q(c3)] of row m.
-  uint4 aq[8];
+  // A operand of QK, step st: coordinates QC q4 + 4 st + 0..3 of row m = t16 (one fp16 part),
+  // repeated in the pattern of the key table.
+  uint4 aq[C::NMQ];
   {
     const int g = (t16 >> 2) + 4 * ((t16 >> 1) & 1);
     const bool lo_part = t16 & 1;
     const bool live = g < G;
     const float f = live ? ldexpf(a.qscale, head_exp(g)) : 0.0f;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < C::NMQ; ++st) {
       uint32_t pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = live ? s_q[g][32 * q4 + 4 * st + i] * f : 0.0f;
+        const float x = live ? s_q[g][C::QC * q4 + 4 * st + i] * f : 0.0f;
         uint32_t hi, lo;
         split_f16(x, hi, lo);
         pr[i] = lo_part ? lo : hi;
       }
-      const uint32_t d01 = pr[0] | (pr[1] << 16), d23 = pr[2] | (pr[3] << 16);
-      aq[st] = make_uint4(d01, d01, d23, d23);
+      aq[st] = repeat_operand<C::VK>(pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16));
     }
   }
   const int g0 = q4, g1 = q4 + 4;
@@ -465,9 +561,9 @@ auto head_exp = [&](int g) {
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
-  // Per-lane byte offsets inside a run of 16 page rows (token t16, code bytes 16 q4..16 q4+15).
+  // Per-lane byte offsets inside a run of 16 page rows (token t16, code run of lane group q4).
   const uint32_t lane_row = __umul24((uint32_t)t16, row_bytes32);
-  const uint32_t off_k = lane_row + 16 * q4, off_v = off_k + voff;
+  const uint32_t off_k = lane_row + 4 * C::KW * q4, off_v = lane_row + voff + 4 * C::VW * q4;
   const uint32_t off_kn = lane_row + L.kcode_bytes, off_vn = lane_row + voff + L.vcode_bytes;
 
   // Row base of the 16 positions starting at pu (a multiple of 16).  With a block size that is a
@@ -490,23 +586,29 @@ auto head_exp = [&](int g) {
     const int bi = block_of(pc);
     return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
   };
-  auto fetch = [&](int tile, MTile& m) {
+  auto fetch = [&](int tile, Tile& m) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int pu = p0 + 32 * tile + 16 * u;
+      const uint8_t* r;
+      uint32_t ok, ov, okn, ovn;
       if (UBLK) {
-        const uint8_t* rb = run_base(pu);
-        m.k[u] = *reinterpret_cast<const uint4*>(rb + off_k);
-        m.v[u] = *reinterpret_cast<const uint4*>(rb + off_v);
-        m.kn[u] = *reinterpret_cast<const float*>(rb + off_kn);
-        m.vn[u] = *reinterpret_cast<const float*>(rb + off_vn);
+        r = run_base(pu);
+        ok = off_k;
+        ov = off_v;
+        okn = off_kn;
+        ovn = off_vn;
       } else {
-        const uint8_t* r = row_ptr(pu + t16);
-        m.k[u] = *reinterpret_cast<const uint4*>(r + 16 * q4);
-        m.v[u] = *reinterpret_cast<const uint4*>(r + voff + 16 * q4);
-        m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
-        m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
+        r = row_ptr(pu + t16);
+        ok = 4 * C::KW * q4;
+        ov = voff + 4 * C::VW * q4;
+        okn = L.kcode_bytes;
+        ovn = voff + L.vcode_bytes;
       }
+      load_words<C::KW>(r + ok, m.k[u]);
+      load_words<C::VW>(r + ov, m.v[u]);
+      m.kn[u] = *reinterpret_cast<const float*>(r + okn);
+      m.vn[u] = *reinterpret_cast<const float*>(r + ovn);
     }
   };
 
@@ -516,36 +618,40 @@ auto head_exp = [&](int g) {
   float m_s[2] = {kSent, kSent};   // running max of scores (heads g0, g1)
   float m_w[2] = {kSent, kSent};   // running max of score + log2(n_V)
   float l_s[2] = {0.0f, 0.0f};     // per-lane partial sums of 2^(s - m_s)
-  float4_t acc[8];
+  float4_t acc[C::PC];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < C::PC; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint16_t* wt = &s_w[wave][0][0];
+  uint32_t* wt = &s_w[wave][0][0];
   uint32_t* vt = &s_v[wave][0][0];
+  uint16_t* wt16 = reinterpret_cast<uint16_t*>(wt);
+  // weight of row m, token col: a fp16 at [m][col], or the pair (w, w) at dword [m][col]
+  auto put_w = [&](int m, int col, uint32_t w) {
+    if constexpr (C::VV == 1) wt[m * C::WROW + col] = w | (w << 16);
+    else wt16[m * 2 * C::WROW + col] = (uint16_t)w;
+  };
   if (!G8) {  // weight rows of heads 4..7 stay zero
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      wt[(4 * q4 + 2) * kWRow + 16 * u + t16] = 0;
-      wt[(4 * q4 + 3) * kWRow + 16 * u + t16] = 0;
+      put_w(4 * q4 + 2, 16 * u + t16, 0);
+      put_w(4 * q4 + 3, 16 * u + t16, 0);
     }
   }
   __syncthreads();  // tables, block offsets, zero rows ready
 
-  auto process = [&](const MTile& cur, int tile) {
+  auto process = [&](const Tile& cur, int tile) {
     // ---- QK on the matrix cores ----
     float4_t sc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // all 16 lookups of the sub-tile first, so their LDS latency overlaps
-      const uint32_t kw[4] = {cur.k[u].x, cur.k[u].y, cur.k[u].z, cur.k[u].w};
-      uint2 ek[16];
+      uint4 kop[C::NMQ];  // all table reads of the sub-tile first, so their latency overlaps
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ek[i] = s_klut[(kw[i >> 2] >> (8 * (i & 3))) & 0xffu];
+      for (int st = 0; st < C::NMQ; ++st) kop[st] = k_operand<KB>(s_ktab, cur.k[u], st);
       float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, sb = sa;  // two independent MFMA chains
 #pragma unroll
-      for (int st = 0; st < 8; st += 2) {
-        sa = mfma_f16(aq[st], quad_of(ek[2 * st], ek[2 * st + 1]), sa);
-        sb = mfma_f16(aq[st + 1], quad_of(ek[2 * st + 2], ek[2 * st + 3]), sb);
+      for (int st = 0; st < C::NMQ; st += 2) {
+        sa = mfma_f16(aq[st], kop[st], sa);
+        sb = mfma_f16(aq[st + 1], kop[st + 1], sb);
       }
       sc[u] = sa + sb;
     }
@@ -579,7 +685,7 @@ auto head_exp = [&](int g) {
       const float r0 = grow0 ? __builtin_amdgcn_exp2f(m_w[0] - mw0) : 1.0f;
       const float r1 = grow1 ? __builtin_amdgcn_exp2f(m_w[1] - mw1) : 1.0f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < C::PC; ++c) {
         acc[c][0] *= r0;
         acc[c][1] *= r0;
         if (G8) {
@@ -595,68 +701,115 @@ auto head_exp = [&](int g) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // last tile's tile reads are done
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      l_s[0] += __builtin_amdgcn_exp2f(s0[u] - ms0);
-      const float w0 = __builtin_amdgcn_exp2f(s0[u] + lv[u] - mw0s);
-      uint32_t h0, l0;
-      split_f16(w0, h0, l0);
       const int col = 16 * u + t16;
-      wt[(4 * q4 + 0) * kWRow + col] = (uint16_t)h0;
-      wt[(4 * q4 + 1) * kWRow + col] = (uint16_t)l0;
+      l_s[0] += __builtin_amdgcn_exp2f(s0[u] - ms0);
+      uint32_t h0, l0;
+      split_f16(__builtin_amdgcn_exp2f(s0[u] + lv[u] - mw0s), h0, l0);
+      put_w(4 * q4 + 0, col, h0);
+      put_w(4 * q4 + 1, col, l0);
       if (G8) {
         l_s[1] += __builtin_amdgcn_exp2f(s1[u] - ms1);
-        const float w1 = __builtin_amdgcn_exp2f(s1[u] + lv[u] - mw1s);
         uint32_t h1, l1;
-        split_f16(w1, h1, l1);
-        wt[(4 * q4 + 2) * kWRow + col] = (uint16_t)h1;
-        wt[(4 * q4 + 3) * kWRow + col] = (uint16_t)l1;
+        split_f16(__builtin_amdgcn_exp2f(s1[u] + lv[u] - mw1s), h1, l1);
+        put_w(4 * q4 + 2, col, h1);
+        put_w(4 * q4 + 3, col, l1);
       }
-      // value codes of token 16u + t16, coordinates 32 q4 .. 32 q4 + 31 (dwords 4 q4 .. 4 q4 + 3)
-      uint32_t* vrow = vt + (16 * u + t16) * kVRow + 4 * q4;
-      *reinterpret_cast<uint2*>(vrow) = make_uint2(cur.v[u].x, cur.v[u].y);
-      *reinterpret_cast<uint2*>(vrow + 2) = make_uint2(cur.v[u].z, cur.v[u].w);
+      // value codes of token col, lane group q4's run of coordinates
+      uint32_t* vrow = vt + col * C::VROW + C::VW * q4;
+#pragma unroll
+      for (int i = 0; i < C::VW; i += 2) *reinterpret_cast<uint2*>(vrow + i) = make_uint2(cur.v[u][i], cur.v[u][i + 1]);
     }
 
-    // ---- PV on the matrix cores: lane (n = t16, q4) handles tokens 8 q4 .. 8 q4 + 7 ----
+    // ---- PV on the matrix cores: lane (n = t16, q4) handles tokens 8 q4 .. 8 q4 + 7 and
+    // coordinates PC t16 .. PC t16 + PC - 1 (MFMA c covers coordinate PC n + c of column n) ----
     // The tiles written above are read back by other lanes of this wave: order the LDS accesses.
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    uint32_t vd[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) vd[kk] = vt[(8 * q4 + kk) * kVRow + t16];
-    uint32_t eo[8];  // E_i, O_i: bytes (nibble c of token 2i, nibble c of token 2i+1)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      eo[2 * i] = (vd[2 * i] & 0x0f0f0f0fu) | ((vd[2 * i + 1] << 4) & 0xf0f0f0f0u);
-      eo[2 * i + 1] = ((vd[2 * i] >> 4) & 0x0f0f0f0fu) | (vd[2 * i + 1] & 0xf0f0f0f0u);
-    }
+    constexpr int VBITS = C::PC * VB;  // code bits of the lane's coordinates per token (8..64)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // weights of tokens 8 q4 + 4 j + 0..3 as [w0, w1, w0, w1, w2, w3, w2, w3] (row t16)
-      const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wt + t16 * kWRow + 8 * q4 + 4 * j);
-      const uint32_t w01 = wrow[0], w23 = wrow[1];
-      const uint4 aw = make_uint4(w01, w01, w23, w23);
-      // coordinate 8 t16 + c: even c -> byte c/2 of E_i, odd c -> byte c/2 of O_i
-      uint2 ev[16];
+      // weights of tokens 8 q4 + 4 j + 0..3 of row t16, in the pattern of the value table
+      uint4 aw;
+      if constexpr (C::VV == 1) {
+        aw = *reinterpret_cast<const uint4*>(wt + t16 * C::WROW + 8 * q4 + 4 * j);
+      } else {
+        const uint32_t* wrow = wt + t16 * C::WROW + 4 * q4 + 2 * j;
+        aw = repeat_operand<C::VV>(wrow[0], wrow[1]);
+      }
+      // codes of the lane's coordinates for the four tokens 8 q4 + 4 j + i
+      uint32_t cw[4][VBITS > 32 ? 2 : 1];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sh = 8 * (c >> 1);
-        ev[2 * c] = s_vlut[(eo[2 * (2 * j) + (c & 1)] >> sh) & 0xffu];
-        ev[2 * c + 1] = s_vlut[(eo[2 * (2 * j + 1) + (c & 1)] >> sh) & 0xffu];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t* src = vt + (8 * q4 + 4 * j + i) * C::VROW;
+        if constexpr (VBITS == 64) {
+          const uint2 x = *reinterpret_cast<const uint2*>(src + 2 * t16);
+          cw[i][0] = x.x;
+          cw[i][1] = x.y;
+        } else if constexpr (VBITS == 32) {
+          cw[i][0] = src[t16];
+        } else if constexpr (VBITS == 16) {
+          cw[i][0] = reinterpret_cast<const uint16_t*>(src)[t16];
+        } else {
+          cw[i][0] = reinterpret_cast<const uint8_t*>(src)[t16];
+        }
+      }
+      uint4 vop[C::PC];
+      if constexpr (VB == 8) {
+        // one byte per (token, coordinate): four single-value reads per operand
+#pragma unroll
+        for (int c = 0; c < C::PC; ++c) {
+          const int wi = c >> 2, sh = 8 * (c & 3);
+          vop[c] = make_uint4(s_vtab[(cw[0][wi] >> sh) & 0xffu], s_vtab[(cw[1][wi] >> sh) & 0xffu],
+                              s_vtab[(cw[2][wi] >> sh) & 0xffu], s_vtab[(cw[3][wi] >> sh) & 0xffu]);
+        }
+      } else if constexpr (VB == 4) {
+        // E, O: bytes (nibble c of token 2i, nibble c of token 2i + 1) for even / odd c
+        uint32_t eo[2][2];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const uint32_t x = cw[2 * pr][0], y = cw[2 * pr + 1][0];
+          eo[pr][0] = (x & 0x0f0f0f0fu) | ((y << 4) & 0xf0f0f0f0u);
+          eo[pr][1] = ((x >> 4) & 0x0f0f0f0fu) | (y & 0xf0f0f0f0u);
+        }
+#pragma unroll
+        for (int c = 0; c < C::PC; ++c) {
+          const uint32_t sh = 8 * (c >> 1);
+          const uint2 e0 = s_vtab[(eo[0][c & 1] >> sh) & 0xffu];
+          const uint2 e1 = s_vtab[(eo[1][c & 1] >> sh) & 0xffu];
+          vop[c] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+        }
+      } else {
+        // VB == 2: bytes (code c of tokens 0, 1, 2, 3 at bits 0, 2, 4, 6) for the 8 coordinates
+        uint32_t pe[2], po[2];  // token pairs (0,1), (2,3): nibbles (code a, code b), even / odd c
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const uint32_t x = cw[2 * pr][0], y = cw[2 * pr + 1][0];
+          pe[pr] = (x & 0x3333u) | ((y & 0x3333u) << 2);
+          po[pr] = ((x >> 2) & 0x3333u) | (y & 0xccccu);
+        }
+        // nibble k of pe = coordinate 2k, of po = coordinate 2k + 1
+        const uint32_t r0 = (pe[0] & 0x0f0fu) | ((pe[1] & 0x0f0fu) << 4);          // c = 0, 4
+        const uint32_t r1 = (po[0] & 0x0f0fu) | ((po[1] & 0x0f0fu) << 4);          // c = 1, 5
+        const uint32_t r2 = ((pe[0] >> 4) & 0x0f0fu) | (pe[1] & 0xf0f0u);          // c = 2, 6
+        const uint32_t r3 = ((po[0] >> 4) & 0x0f0fu) | (po[1] & 0xf0f0u);          // c = 3, 7
+        const uint32_t rr[4] = {r0, r1, r2, r3};
+#pragma unroll
+        for (int c = 0; c < C::PC; ++c) vop[c] = s_vtab[(rr[c & 3] >> (8 * (c >> 2))) & 0xffu];
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = mfma_f16(aw, quad_of(ev[2 * c], ev[2 * c + 1]), acc[c]);
+      for (int c = 0; c < C::PC; ++c) acc[c] = mfma_f16(aw, vop[c], acc[c]);
     }
   };
 
-  MTile cur;
+  Tile cur;
   if (wave < n_tiles) fetch(wave, cur);
   for (int tile = wave; tile < n_tiles; tile += kNW) {
-    MTile nxt;
+    Tile nxt;
     if (tile + kNW < n_tiles) fetch(tile + kNW, nxt);
     process(cur, tile);
     cur = nxt;
   }
 
-  // ---- wave result: heads g0, g1 at coordinates 8 t16 + c, in the score-max frame ----
+  // ---- wave result: heads g0, g1 at coordinates PC t16 + c, in the score-max frame ----
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     l_s[i] += dpp<kDppQuadXor1>(l_s[i]);
@@ -669,18 +822,18 @@ auto head_exp = [&](int g) {
   const float c1 = __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
   if (live0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_part[wave][g0][2 + 8 * t16 + c] = (acc[c][0] + acc[c][1]) * c0;
+    for (int c = 0; c < C::PC; ++c) s_part[wave * H8 + g0][2 + C::PC * t16 + c] = (acc[c][0] + acc[c][1]) * c0;
     if (t16 == 0) {
-      s_part[wave][g0][0] = m_s[0];
-      s_part[wave][g0][1] = l_s[0];
+      s_part[wave * H8 + g0][0] = m_s[0];
+      s_part[wave * H8 + g0][1] = l_s[0];
     }
   }
   if (live1) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_part[wave][g1][2 + 8 * t16 + c] = (acc[c][2] + acc[c][3]) * c1;
+    for (int c = 0; c < C::PC; ++c) s_part[wave * H8 + g1][2 + C::PC * t16 + c] = (acc[c][2] + acc[c][3]) * c1;
     if (t16 == 0) {
-      s_part[wave][g1][0] = m_s[1];
-      s_part[wave][g1][1] = l_s[1];
+      s_part[wave * H8 + g1][0] = m_s[1];
+      s_part[wave * H8 + g1][1] = l_s[1];
     }
   }
   __syncthreads();
@@ -691,14 +844,15 @@ auto head_exp = [&](int g) {
     const int g = i / (D + 2), d = i % (D + 2);
     float M = kSent;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_part[w][g][0]);
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_part[w * H8 + g][0]);
     float r;
     if (d == 0) {
       r = M;
     } else {
       r = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) r += s_part[w][g][d] * __builtin_amdgcn_exp2f(s_part[w][g][0] - M);
+      for (int w = 0; w < kNW; ++w)
+        r += s_part[w * H8 + g][d] * __builtin_amdgcn_exp2f(s_part[w * H8 + g][0] - M);
     }
     part[i] = r;
   }
@@ -800,19 +954,38 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int GMAX>
+void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
+  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(kWG), 0, st, a);
+}
+
+// Split kernel for one format and query-group bound, then the merge.
 template <int D, int KB, int VB, int GMAX>
 void launch_t(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
-  hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX>), grid, dim3(kWG), 0, st, a);
-  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(kWG), 0, st, a);
+  if constexpr (mfma_format(D, KB, VB)) {
+    constexpr bool G8 = GMAX > 4;
+    if (a.L.bs % 16 == 0)
+      hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, true>), grid, dim3(kWG), 0, st, a);
+    else
+      hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false>), grid, dim3(kWG), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX>), grid, dim3(kWG), 0, st, a);
+  }
+  launch_merge<D, GMAX>(a, mgrid, st);
 }
 
 template <int D, int KB, int VB>
 void launch_g(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
   const int G = a.L.G;
-  if (G <= 1) launch_t<D, KB, VB, 1>(a, grid, mgrid, st);
-  else if (G <= 2) launch_t<D, KB, VB, 2>(a, grid, mgrid, st);
-  else if (G <= 4) launch_t<D, KB, VB, 4>(a, grid, mgrid, st);
-  else launch_t<D, KB, VB, 8>(a, grid, mgrid, st);
+  if constexpr (mfma_format(D, KB, VB)) {  // the matrix-core kernel covers G <= 4 in one instance
+    if (G <= 4) launch_t<D, KB, VB, 4>(a, grid, mgrid, st);
+    else launch_t<D, KB, VB, 8>(a, grid, mgrid, st);
+  } else {
+    if (G <= 1) launch_t<D, KB, VB, 1>(a, grid, mgrid, st);
+    else if (G <= 2) launch_t<D, KB, VB, 2>(a, grid, mgrid, st);
+    else if (G <= 4) launch_t<D, KB, VB, 4>(a, grid, mgrid, st);
+    else launch_t<D, KB, VB, 8>(a, grid, mgrid, st);
+  }
 }
 
 template <int D, int KB>
@@ -827,21 +1000,6 @@ void launch_v(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
 
 template <int D>
 void launch_k(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
-  if (D == 128 && a.L.kb == 4 && a.L.vb == 4) {
-    const bool ublk = a.L.bs % 16 == 0;
-    if (a.L.G > 4) {
-      if (ublk) hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<true, true>), grid, dim3(kWG), 0, st, a);
-      else hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<true, false>), grid, dim3(kWG), 0, st, a);
-    } else {
-      if (ublk) hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<false, true>), grid, dim3(kWG), 0, st, a);
-      else hipLaunchKernelGGL((tq_decode_mfma_k4v4_kernel<false, false>), grid, dim3(kWG), 0, st, a);
-    }
-    if (a.L.G <= 1) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 1>), mgrid, dim3(kWG), 0, st, a);
-    else if (a.L.G <= 2) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 2>), mgrid, dim3(kWG), 0, st, a);
-    else if (a.L.G <= 4) hipLaunchKernelGGL((tq_decode_merge_kernel<128, 4>), mgrid, dim3(kWG), 0, st, a);
-    else hipLaunchKernelGGL((tq_decode_merge_kernel<128, 8>), mgrid, dim3(kWG), 0, st, a);
-    return;
-  }
   switch (a.L.kb) {
     case 2: launch_v<D, 2>(a, grid, mgrid, st); break;
     case 3: launch_v<D, 3>(a, grid, mgrid, st); break;

@@ -2,13 +2,13 @@
 
 Each case fills one layer of a full-size workload exactly as the benchmark does (bulk
 quantize-append of the whole context in chunks, then the decode step's one-token append), then runs
-decode over the whole batch.  A few sampled sequences are recomputed by the CPU oracle from the same
-fp16 rows:
+decode over the whole batch.  A few sampled (sequence, kv head) pairs are recomputed by the CPU
+oracle from the same fp16 rows:
   * their packed page rows must equal the oracle's (indices at listed ties excepted);
   * with the oracle's bytes written into their page rows (so ties cannot move a key), the decode
-    output of those sequences must match the oracle's dense attention to the attention tolerance.
-The other sequences of the batch still run, so the grid, split geometry and workspace are the
-benchmark's.
+    output of the query heads of that kv head must match the oracle's dense attention to the
+    attention tolerance.
+The rest of the batch still runs, so the grid, split geometry and workspace are the benchmark's.
 """
 
 from __future__ import annotations
@@ -65,6 +65,8 @@ def test_full_size_sampled(name, layer, which):
     print(f"[fullsize] {name} layer {layer} K{kb}/V{vb}: B={B} max_len={int(lens.max())} "
           f"sampled sequences {seqs}", flush=True)
 
+    heads = {b: (7 * b + layer) % H for b in seqs}  # one kv head per sampled sequence
+    G = Hq // H
     fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0)
     pages = fmt.new_pages(num_blocks)
     ctx_off = np.concatenate([[0], np.cumsum(lens - 1)])
@@ -75,8 +77,9 @@ def test_full_size_sampled(name, layer, which):
         for b in seqs:
             lo, hi = max(int(ctx_off[b]), s0), min(int(ctx_off[b + 1]), s0 + n)
             if lo < hi:
-                rows[b][0].append(k[lo - s0:hi - s0].cpu())
-                rows[b][1].append(v[lo - s0:hi - s0].cpu())
+                hh = heads[b]
+                rows[b][0].append(k[lo - s0:hi - s0, hh:hh + 1].cpu())
+                rows[b][1].append(v[lo - s0:hi - s0, hh:hh + 1].cpu())
 
     bench.fill_layer(w, layer, fmt, pages, torch.from_numpy(ctx_np).cuda(), num_blocks, torch, tq, wl,
                      tap=tap)
@@ -90,25 +93,26 @@ def test_full_size_sampled(name, layer, which):
     flat = pages.view(-1, H, stride)
     refs = {}
     for b in seqs:
-        L = int(lens[b])
-        k = torch.cat(rows[b][0] + [new_k[0, layer, b:b + 1].cpu()]).numpy()
-        v = torch.cat(rows[b][1] + [new_v[0, layer, b:b + 1].cpu()]).numpy()
-        assert k.shape == (L, H, D)
-        # oracle pages of this one sequence, identity table
+        L, hh = int(lens[b]), heads[b]
+        k = torch.cat(rows[b][0] + [new_k[0, layer, b:b + 1, hh:hh + 1].cpu()]).numpy()
+        v = torch.cat(rows[b][1] + [new_v[0, layer, b:b + 1, hh:hh + 1].cpu()]).numpy()
+        assert k.shape == (L, 1, D)
+        # oracle pages of this one (sequence, kv head), identity table
         one = wl.scaled(w, num_seqs=1, tables="identity")
         bt1, nblk1 = wl.block_tables(one, np.array([L]))
         slots1 = wl.token_slots(bt1, 0, np.arange(L), bs)
-        ref = np.zeros(nblk1 * bs * H * stride, np.uint8)
+        ref = np.zeros(nblk1 * bs * stride, np.uint8)
         k_tie, v_tie = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride)
-        # the GPU's rows of the same positions
-        slots = wl.token_slots(bt_np, b, np.arange(L), bs)
-        gpu_rows = flat[torch.from_numpy(slots).cuda()].cpu().numpy()
-        ref_rows = ref.reshape(-1, H, stride)[slots1]
-        ties = compare_pages(gpu_rows.reshape(-1), ref_rows.reshape(-1), np.arange(L), H, D, kb, vb,
+        # the GPU's rows of the same positions and kv head
+        slots = torch.from_numpy(wl.token_slots(bt_np, b, np.arange(L), bs)).cuda()
+        gpu_rows = flat[slots, hh].cpu().numpy()
+        ref_rows = ref.reshape(-1, stride)[slots1]
+        ties = compare_pages(gpu_rows.reshape(-1), ref_rows.reshape(-1), np.arange(L), 1, D, kb, vb,
                              stride, k_tie, v_tie)
-        print(f"[fullsize]   seq {b} (L={L}): page rows match, {ties} tie indices", flush=True)
-        # the oracle's bytes into the GPU pages of this sequence
-        flat[torch.from_numpy(slots).cuda()] = torch.from_numpy(ref_rows).cuda()
+        print(f"[fullsize]   seq {b} kv head {hh} (L={L}): page rows match, {ties} tie indices",
+              flush=True)
+        # the oracle's bytes into the GPU pages of this sequence and kv head
+        flat[slots, hh] = torch.from_numpy(ref_rows).cuda()
         refs[b] = (ref, bt1, L)
 
     q = wl.queries(w, layer, 0, "cuda")
@@ -122,14 +126,17 @@ def test_full_size_sampled(name, layer, which):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got)), "non-finite output in the batch"
-    layer_dict = dict(D=D, H_kv=H, block_size=bs, k_bits=kb, v_bits=vb, seed=0, slot_stride=stride)
+    layer_dict = dict(D=D, H_kv=1, block_size=bs, k_bits=kb, v_bits=vb, seed=0, slot_stride=stride)
     qn = q.cpu().numpy()
     skn = None if sink_k is None else sink_k.cpu().numpy()
     svn = None if sink_v is None else sink_v.cpu().numpy()
     for b in seqs:
         ref, bt1, L = refs[b]
-        want = oatt.decode_attention(qn[b:b + 1], ref, bt1, np.array([L], np.int32), layer_dict, kc, vc,
-                                     None if skn is None else skn[b:b + 1],
-                                     None if svn is None else svn[b:b + 1], w.n_sink)
-        max_abs, rel = check_attention(got[b:b + 1], want)
-        print(f"[fullsize]   seq {b}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}", flush=True)
+        hh = heads[b]
+        qh = slice(hh * G, (hh + 1) * G)  # the query heads that read kv head hh
+        want = oatt.decode_attention(qn[b:b + 1, qh], ref, bt1, np.array([L], np.int32), layer_dict, kc, vc,
+                                     None if skn is None else skn[b:b + 1, :, hh:hh + 1],
+                                     None if svn is None else svn[b:b + 1, :, hh:hh + 1], w.n_sink)
+        max_abs, rel = check_attention(got[b:b + 1, qh], want)
+        print(f"[fullsize]   seq {b} kv head {hh}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}",
+              flush=True)
