@@ -60,9 +60,10 @@ typedef enum tq_codebook_family {
   TQ_CODEBOOK_GAUSSIAN = 1  /* its N(0, 1/D) approximation                                  */
 } tq_codebook_family;
 
-/* One layer's format.  K and V may use different bit widths (p1 policies q8k-q8v, q8k-int4v;
- * p4 K8/K4 and V8/V4/V3/V2 formats); a model with boundary-layer protection simply uses a
- * different descriptor for the protected layers. */
+/* One layer's format.  K and V may use different bit widths (tiny-turboquant 0.12.0.3,
+ * "Current status": q8k-q8v and q8k-int4v policies; TorbuQuant docs, "Current Status": K8/K4 and
+ * V8/V4/V3/V2 formats); a model with boundary-layer protection simply uses a different
+ * descriptor for the protected layers. */
 typedef struct tq_layer_desc {
   int32_t head_dim;       /* D: 64 or 128                                                     */
   int32_t num_q_heads;    /* H_q (decode only; multiple of num_kv_heads; G = H_q/H_kv <= 8)   */
