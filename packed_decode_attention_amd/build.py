@@ -28,7 +28,9 @@ DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-fno-strict-aliasing", f"--offloa
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
 
 SOURCES = [
-    ("tq_quantize.hip", "device", []),
+    # MFMA results straight into VGPRs (no accumulation-register round trip; the quantizer's
+    # products are one-shot, never accumulated across instructions)
+    ("tq_quantize.hip", "device", ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("tq_decode.hip", "device", ["-fno-honor-nans"]),
     ("tq_api.cpp", "host", []),
     ("tq_codebook.cpp", "host", []),

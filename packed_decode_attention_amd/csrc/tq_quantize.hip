@@ -2,28 +2,45 @@
 //
 // Quantize: turboquant-serve 0.1.2 "Architecture" (rotate, normalise, Lloyd-Max encode, bit-pack,
 // store uint8); turboquant-pro 1.4.2 "How It Works" (per-vector flow: norm, normalise, rotate,
-// quantise, pack, norm kept beside the bits); TorbuQuant docs "TQ4 page tensor" (slot layout).
+// quantise, pack, norm kept beside the bits); tq-kv "How It Works" (randomised Hadamard
+// rotation); TorbuQuant docs "TQ4 page tensor" (slot layout).
 // Dequantize: turboquant-serve 0.1.2 "Architecture" _decode (unpack, centroid lookup, restore
 // magnitude, rotate back), with an exact fp64 Walsh-Hadamard transform so the fp32 result has a
 // single fixed rounding chain.
-//
-// Quantize: D/16 lanes per (token, kv head) row, 16 coordinates each.  Dequantize: D/8 lanes per
-// row, lane j holding coordinates 8j..8j+7.
+
+#include <type_traits>
 
 #include "tq_device.h"
 
 namespace {
 using namespace tqd;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 // =============================================================================================
 // Quantize-on-append
 //
-// A row (one token and kv head, K or V) is held by P = D/16 lanes, 16 coordinates each.  Loads,
-// decisions, packing and stores use the contiguous layout (lane j: coordinates 16j .. 16j + 15).
-// The norm and the butterflies of coordinate bits >= log2(P) run in a transposed layout (lane j:
-// coordinates j + P k, k = 0..15) reached through a per-wave LDS buffer: there the first levels of
-// the norm tree (pairs i, i + D/2, then D/4, ...) and those butterflies are in-lane, and only the
-// last log2(P) norm levels cross lanes (DPP).  A second pass through the buffer returns to the
-// contiguous layout for the low-bit butterflies.
+// A wave quantizes 16 rows (token, kv head) at a time, K then V.  Lane (g, c), g = lane / 16,
+// c = lane % 16, loads coordinates 32 b + 8 g .. 32 b + 8 g + 7 of row c for every 32-coordinate
+// block b (NB = D / 32 blocks, 16 bytes each): for each block this is the B operand of
+// v_mfma_f32_16x16x32_f16, contraction index k = 8 g + j over the block's coordinates, one row
+// per column.
+//
+// Rotation.  With i = 32 b + r the Sylvester Hadamard matrix factors as H_D = H_NB (x) H_32.  The
+// matrix cores apply diag(s) followed by H_32 inside each block: the A operand holds the +-1
+// entries of H_32 with the block's signs folded in, exact in fp16 like the fp16 inputs, so every
+// product is exact and only the fp32 sums round.  A's rows are ordered so that result lane (g, c)
+// receives rotated coordinates 8 g .. 8 g + 7 of each block of row c (rows 4 g .. 4 g + 3 of the
+// result tile t hold 8 g + 4 t .. 8 g + 4 t + 3); H_NB across the blocks is then one or two
+// butterfly levels inside the lane, and the lane's codes are NB runs of 8 consecutive coordinates.
+//
+// Norm.  Squares of fp16 values are exact in fp32 and the stride-halving tree (pairs i, i + D/2
+// first, then D/4, ...) fixes every rounding.  The block index holds the top bits of i and sits
+// inside the lane, so the first levels are in-lane (the first one fused with a square: one
+// v_fma_mix each); bits 4 and 3 of i are bits 5 and 4 of the lane id and are reduced with
+// permlane32 / permlane16 swaps, which exchange and transpose at once (each halves the values per
+// lane); bits 2, 1, 0 follow in that order, spread over the lanes after the transposes.
 //
 // Decisions: idx = #{j : t_j <= u}.  With S a power of two no smaller than 1 / (smallest gap between
 // boundaries), the bucket floor(u S) holds at most one boundary; a table gives per bucket the
@@ -37,174 +54,170 @@ constexpr int kQNoTable = -100;   // log2 S marker: binary search
 
 __host__ __device__ constexpr int qtab_entries(int bits) { return bits <= 4 ? kQTabSmall : kQTabLarge; }
 
-// 16 contiguous fp16 of lane j (signs flipped), transposed through the row's LDS buffer, as fp32
-// coordinates j + P k of the row, k = 0..15.
-template <int P>
-__device__ __forceinline__ void to_transposed(const uint32_t (&raw)[8], uint32_t* xr, int j, float (&y)[16]) {
-  // coordinate c = 16 j + m goes to transposed row c % P at column c / P (fp16 positions)
-  if constexpr (P == 8) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m)  // (m, m + 8): one dword of row m, column pair j
-      xr[m * 8 + j] = __builtin_amdgcn_perm(raw[4 + m / 2], raw[m / 2], (m & 1) ? 0x07060302u : 0x05040100u);
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {  // (m, m + 4), (m + 8, m + 12): two dwords of row m, columns 4j..
-      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t w0 = __builtin_amdgcn_perm(raw[m / 2 + 2], raw[m / 2], sel);
-      const uint32_t w1 = __builtin_amdgcn_perm(raw[m / 2 + 6], raw[m / 2 + 4], sel);
-      *reinterpret_cast<uint2*>(xr + m * 8 + 2 * j) = make_uint2(w0, w1);
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  const uint4 a = reinterpret_cast<const uint4*>(xr + 8 * j)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(xr + 8 * j)[1];
-  const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    y[2 * q] = half_bits_to_float(d[q] & 0xffffu);
-    y[2 * q + 1] = half_bits_to_float(d[q] >> 16);
-  }
+__device__ __forceinline__ float4_t mfma_f16(const uint4& a, const uint4& b) {
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), zero, 0, 0, 0);
 }
 
-// One region (K or V) of P lanes' row: norm, rotation, decisions, packing, store.
-template <int D>
-__device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, bool load,
-                                             const uint32_t (&smask)[8], uint32_t* xr, int j, int bits,
-                                             int code_bytes, const float* s_t, const uint2* tab, int sh,
-                                             float rsqrt_d, uint8_t* __restrict__ dst, bool store) {
-  constexpr int P = D / 16;
-  uint32_t raw[8];
-  if (load) {
-    const uint4 a = reinterpret_cast<const uint4*>(src + 16 * j)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(src + 16 * j)[1];
-    raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
-    raw[4] = b.x; raw[5] = b.y; raw[6] = b.z; raw[7] = b.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) raw[i] = 0;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) raw[i] ^= smask[i];  // sign flip on the fp16 sign bits
-  float y[16];
-  to_transposed<P>(raw, xr, j, y);
+// fp16 number j (0..7) of an operand register quadruple, as fp32.
+__device__ __forceinline__ float half_of(const uint4& v, int j) {
+  const uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
+  return half_bits_to_float((j & 1) ? (w >> 16) : (w & 0xffffu));
+}
 
-  // Stored norm: exact fp32 squares, stride-halving tree (pairs i, i + D/2, then D/4, ...: the
-  // first four levels are k, k + 8 / 4 / 2 / 1 in-lane, the rest lane j, j + P/2 ...), correctly
-  // rounded square root.  Contraction off: every level is one rounded fp32 add.
-  const float n = [&] {
+// Transpose-reduce across lanes l and l ^ 32 (M = 32) or l ^ 16 (M = 16): returns, in the lower
+// lane of each pair, a(l) + a(partner), and in the upper lane b(partner) + b(l).
+template <int M>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  const auto r = M == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                         : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 4 x 4 transpose across the lane groups g = lane / 16: on return, lane group g holds in w[j]
+// what lane group j held in w[g] (same lane within the group).  Exchanges across lane bit 5, then
+// bit 4.
+__device__ __forceinline__ void transpose_groups(uint32_t (&w)[4]) {
+  auto swap32 = [](uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  };
+  auto swap16 = [](uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  };
+  swap32(w[0], w[2]);
+  swap32(w[1], w[3]);
+  swap16(w[0], w[1]);
+  swap16(w[2], w[3]);
+}
+
+// Sum of squares of a row by the stride-halving tree, in every lane of the row (see above).
+template <int NB>
+__device__ __forceinline__ float row_sum_squares(const uint4 (&x)[NB], float zero) {
 #pragma clang fp contract(off)
-    float sq[16];
+  float p[8];  // partial sums of coordinates with bits 0..2 = j and bits 3, 4 = this lane's g
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sq[e] = y[e] * y[e];
-#pragma unroll
-    for (int hf = 8; hf >= 1; hf >>= 1) {
-#pragma unroll
-      for (int e = 0; e < hf; ++e) sq[e] = sq[e] + sq[e + hf];
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (NB == 4) {  // pairs (b, b + 2), then (0, 1): bits 6 and 5 of i
+      const float s0 = __builtin_fmaf(half_of(x[0], j), half_of(x[0], j),
+                                      __builtin_fmaf(half_of(x[2], j), half_of(x[2], j), zero));
+      const float s1 = __builtin_fmaf(half_of(x[1], j), half_of(x[1], j),
+                                      __builtin_fmaf(half_of(x[3], j), half_of(x[3], j), zero));
+      p[j] = s0 + s1;
+    } else {  // pair (0, 1): bit 5 of i
+      p[j] = __builtin_fmaf(half_of(x[0], j), half_of(x[0], j),
+                            __builtin_fmaf(half_of(x[1], j), half_of(x[1], j), zero));
     }
-    float s = sq[0];
-    if constexpr (P == 8) s = s + dpp_xor<4>(s);
-    s = s + dpp_xor<2>(s);
-    s = s + dpp_xor<1>(s);
-    return sqrtf(s);
-  }();
+  }
+  // bit 4 (lane bit 5): q[j] = class (g & 1, j + 4 (g >> 1)) summed over bit 4
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = swap_add<32>(p[j], p[j + 4]);
+  // bit 3 (lane bit 4): t[j] = class j + 2 g (bits 0..2) summed over bits 3 and 4
+  const float t0 = swap_add<16>(q[0], q[2]);
+  const float t1 = swap_add<16>(q[1], q[3]);
+  // bit 2: lanes g = 0, 1, 2, 3 hold classes 0, 2, 1, 3 of bits 0..1
+  const float w = swap_add<32>(t0, t1);
+  // bit 1: lanes g < 2 hold class 0 of bit 0, lanes g >= 2 class 1
+  const float y = swap_add<16>(w, w);
+  // bit 0
+  return swap_add<32>(y, y);
+}
 
-  // Butterflies of coordinate bits log2(P) .. log2(D) - 1 (k bits), in-lane.
+// One region (K or V, BITS-bit codes) of the wave's 16 rows: norm, rotation, decisions, packing,
+// store.  TABLE: decisions by the bucket table (resolution 2^sh), else by binary search.
+template <int D, int BITS, bool TABLE>
+__device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const uint4 (&A)[D / 32][2],
+                                                float zero, int g, int code_bytes,
+                                                const float* s_t, const uint2* tab, int sh,
+                                                float rsqrt_d, uint8_t* __restrict__ dst) {
+  constexpr int NB = D / 32;
+  const float n = sqrtf(row_sum_squares<NB>(x, zero));  // correctly rounded
+
+  // H_NB across blocks, scaled to u S = y S / (sqrt(D) n) (u = 0 for a zero row), and decisions.
+  const float inv = n > 0.0f ? (TABLE ? ldexpf(rsqrt_d / n, sh) : rsqrt_d / n) : 0.0f;
+  const uint2* tabp = tab + (TABLE ? (1 << sh) + 1 : 0);
+  uint32_t code[NB][8];  // code[a][e]: rotated coordinate 32 a + 8 g + e
 #pragma unroll
-  for (int hb = 1; hb < 16; hb <<= 1) {
+  for (int t = 0; t < 2; ++t) {
+    float4_t z[NB];  // z[b][i]: H_32 diag(s) of block b at rotated coordinate 8 g + 4 t + i
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (!(e & hb)) {
-        const float a0 = y[e], b0 = y[e | hb];
-        y[e] = a0 + b0;
-        y[e | hb] = a0 - b0;
+    for (int b = 0; b < NB; ++b) z[b] = mfma_f16(A[b][t], x[b]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) y[b] = z[b][i] * inv;
+      if constexpr (NB == 4) {
+        const float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];
+        y[0] = a0 + a2;
+        y[1] = a1 + a3;
+        y[2] = a0 - a2;
+        y[3] = a1 - a3;
+      } else {
+        const float a0 = y[0] + y[1], a1 = y[0] - y[1];
+        y[0] = a0;
+        y[1] = a1;
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        const float us = y[a];
+        if constexpr (TABLE) {
+          const uint2 ent = tabp[(int)floorf(us)];
+          code[a][4 * t + i] = ent.y + (us >= __uint_as_float(ent.x) ? 1u : 0u);
+        } else {
+          int id = 0;
+#pragma unroll
+          for (int st = (1 << BITS) >> 1; st >= 1; st >>= 1)
+            if (s_t[id + st - 1] <= us) id += st;
+          code[a][4 * t + i] = (uint32_t)id;
+        }
       }
     }
   }
-  // Back to the contiguous layout through the same buffer.
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  // Pack: run a (the lane's 8 codes at rotated coordinates 32 a + 8 g ..) is bytes BITS (4 a + g)
+  // .. BITS (4 a + g + 1) - 1 of the region.  The four lanes of a row transpose their runs, so lane
+  // g < NB then holds the whole 4 BITS-byte run g (its pieces from lanes 0..3 in order) and stores
+  // it in one or two instructions; then the norm.  Every lane stores (rows with no slot write to
+  // the discard buffer), so a region issues a fixed number of stores.
+  uint32_t lo[4], hi[4];  // per run: the piece's bits (lo) and, for 8-bit codes, its upper dword
 #pragma unroll
-  for (int e = 0; e < 16; ++e) xr[j + P * e] = __float_as_uint(y[e]);
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  float z[16];
+  for (int a = 0; a < 4; ++a) {
+    lo[a] = 0;
+    hi[a] = 0;
+    if (a < NB) {
+      if constexpr (BITS == 8) {
+        lo[a] = code[a][0] | (code[a][1] << 8) | (code[a][2] << 16) | (code[a][3] << 24);
+        hi[a] = code[a][4] | (code[a][5] << 8) | (code[a][6] << 16) | (code[a][7] << 24);
+      } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 w = reinterpret_cast<const uint4*>(xr + 16 * j)[i];
-    z[4 * i] = __uint_as_float(w.x);
-    z[4 * i + 1] = __uint_as_float(w.y);
-    z[4 * i + 2] = __uint_as_float(w.z);
-    z[4 * i + 3] = __uint_as_float(w.w);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // buffer free for the next row
-  // Butterflies of coordinate bits 0 .. log2(P) - 1, in-lane.
-#pragma unroll
-  for (int hb = 1; hb < P; hb <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (!(e & hb)) {
-        const float a0 = z[e], b0 = z[e | hb];
-        z[e] = a0 + b0;
-        z[e | hb] = a0 - b0;
+        for (int e = 0; e < 8; ++e) lo[a] |= code[a][e] << (BITS * e);
       }
     }
   }
-
-  // Decisions: u = z / (sqrt(D) n); all indices 2^bits / 2 for a zero row (u = 0).
-  const int levels = 1 << bits;
-  uint32_t code[16];
-  if (sh != kQNoTable) {
-    const float inv = n > 0.0f ? ldexpf(rsqrt_d / n, sh) : 0.0f;  // S / (sqrt(D) n)
-    const int off = (1 << sh) + 1;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float us = z[e] * inv;
-      const uint2 ent = tab[(int)floorf(us) + off];
-      code[e] = ent.y + (us >= __uint_as_float(ent.x) ? 1u : 0u);
-    }
-  } else {
-    const float inv = n > 0.0f ? rsqrt_d / n : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float u = z[e] * inv;
-      int idx = 0;
-      for (int st = levels >> 1; st >= 1; st >>= 1)
-        if (s_t[idx + st - 1] <= u) idx += st;
-      code[e] = (uint32_t)idx;
+  transpose_groups(lo);
+  if constexpr (BITS == 8) transpose_groups(hi);
+  if (NB == 4 || g < NB) {
+    uint8_t* run = dst + 4 * BITS * g;
+    if constexpr (BITS == 8) {
+      uint4* o = reinterpret_cast<uint4*>(run);
+      o[0] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+      o[1] = make_uint4(lo[2], hi[2], lo[3], hi[3]);
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint4*>(run) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    } else if constexpr (BITS == 3) {  // four 24-bit pieces: 12 bytes
+      *reinterpret_cast<uint3*>(run) = make_uint3(lo[0] | (lo[1] << 24), (lo[1] >> 8) | (lo[2] << 16),
+                                                  (lo[2] >> 16) | (lo[3] << 8));
+    } else {  // four 16-bit pieces: 8 bytes
+      *reinterpret_cast<uint2*>(run) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
   }
-
-  // Pack: lane j owns bytes [2 bits j, 2 bits (j + 1)) of the LSB-first bitstream.
-  if (store) {
-    uint8_t* c = dst + 2 * bits * j;
-    if (bits == 8) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
-      *reinterpret_cast<uint4*>(c) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else if (bits == 4) {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w0 |= code[e] << (4 * e);
-        w1 |= code[e + 8] << (4 * e);
-      }
-      *reinterpret_cast<uint2*>(c) = make_uint2(w0, w1);
-    } else if (bits == 2) {
-      uint32_t w0 = 0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) w0 |= code[e] << (2 * e);
-      *reinterpret_cast<uint32_t*>(c) = w0;
-    } else {  // 3 bits: 48 bits at byte 6 j (2-byte aligned)
-      uint64_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) w |= (uint64_t)code[e] << (3 * e);
-      uint16_t* c16 = reinterpret_cast<uint16_t*>(c);
-      c16[0] = (uint16_t)w;
-      c16[1] = (uint16_t)(w >> 16);
-      c16[2] = (uint16_t)(w >> 32);
-    }
-    if (j == 0) *reinterpret_cast<float*>(dst + code_bytes) = n;
-  }
+  if (g == 0) *reinterpret_cast<float*>(dst + code_bytes) = n;
 }
 
 // Bucket table of one codebook (see above): entries for buckets k = -(S + 1) .. S, entry
@@ -224,68 +237,138 @@ __device__ __forceinline__ void build_qtab(const float* s_t, int nb, int sh, uin
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kWG) void tq_quantize_kernel(TqLayer L, float rsqrt_d,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          const int64_t* __restrict__ slot_mapping,
-                                                          int64_t n_rows, uint8_t* __restrict__ pages) {
-  constexpr int P = D / 16;    // lanes per row
-  constexpr int RPW = 64 / P;  // rows per wave per step
-  constexpr int XROW = D + 8;  // dwords per row of the transpose buffer (padded)
+// Destination of the stores of rows that have no slot (past the end of the input, or a negative
+// slot id): every lane stores on every tile, so each tile issues a fixed number of stores.
+__device__ __align__(16) uint8_t tq_quant_discard[4096];
+
+// Stores a region issues per tile (two for 8-bit codes, one otherwise, plus the norm), and the
+// s_waitcnt immediate that waits for everything issued before the last n vector memory operations
+// (gfx9 encoding: vmcnt in bits 3..0 and 15..14; expcnt and lgkmcnt at their maxima).
+constexpr int region_stores(int bits) { return (bits == 8 ? 2 : 1) + 1; }
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+
+// Four waves per SIMD (128 VGPRs): the occupancy that keeps a tile of loads in flight per wave;
+// without the attribute the fallback loop's pressure lowers it for the whole kernel.
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void tq_quantize_kernel(
+    TqLayer L, float rsqrt_d, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slot_mapping, int64_t n_rows, uint8_t* __restrict__ pages) {
+  constexpr int NB = D / 32;
   constexpr int kNWQ = kWG / 64;
   __shared__ float s_t[2][256];
   __shared__ int s_sh[2];
-  __shared__ __align__(16) uint32_t s_x[kNWQ][RPW * XROW];
+  // per wave: K blocks, V blocks, then the low and high dwords of the rows' slot ids
+  __shared__ __align__(16) uint8_t s_stage[kNWQ][2 * NB * 1024 + 512];
   extern __shared__ uint2 s_tab[];  // K table (qtab_entries(kb)), then V table
 
   const int tid = threadIdx.x;
-  const int nbk = (1 << L.kb) - 1, nbv = (1 << L.vb) - 1;
+  constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
   for (int i = tid; i < nbk; i += kWG) s_t[0][i] = L.kt[i];
   for (int i = tid; i < nbv; i += kWG) s_t[1][i] = L.vt[i];
   __syncthreads();
   if (tid < 2) {  // table resolution per codebook: S = 2^sh >= 1 / (smallest gap)
     const int nb = tid == 0 ? nbk : nbv;
-    float g = 2.0f;
-    for (int i = 0; i + 1 < nb; ++i) g = fminf(g, s_t[tid][i + 1] - s_t[tid][i]);
-    int sh = g > 0.0f ? -ilogbf(g) : kQNoTable;  // bucket width 2^-sh <= g
+    float gap = 2.0f;
+    for (int i = 0; i + 1 < nb; ++i) gap = fminf(gap, s_t[tid][i + 1] - s_t[tid][i]);
+    int sh = gap > 0.0f ? -ilogbf(gap) : kQNoTable;  // bucket width 2^-sh <= gap
     if (sh < 0) sh = 0;
-    if (g <= 0.0f || 2 * (1 << min(sh, 20)) + 2 > qtab_entries(tid == 0 ? L.kb : L.vb)) sh = kQNoTable;
+    if (gap <= 0.0f || 2 * (1 << min(sh, 20)) + 2 > qtab_entries(tid == 0 ? KB : VB)) sh = kQNoTable;
     s_sh[tid] = sh;
   }
   __syncthreads();
   uint2* tabk = s_tab;
-  uint2* tabv = s_tab + qtab_entries(L.kb);
+  uint2* tabv = s_tab + qtab_entries(KB);
   if (s_sh[0] != kQNoTable) build_qtab(s_t[0], nbk, s_sh[0], tabk, tid);
   if (s_sh[1] != kQNoTable) build_qtab(s_t[1], nbv, s_sh[1], tabv, tid);
   __syncthreads();
   const int shk = s_sh[0], shv = s_sh[1];
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane % P, rr = lane / P;
-  uint32_t* xr = &s_x[wave][rr * XROW];
-  // fp16 sign masks of coordinates 16 j .. 16 j + 15 (bit 15 / 31 of dword i for 2i / 2i + 1)
-  uint32_t smask[8];
-  {
-    const uint32_t sm = (L.signs.w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+  const int c = lane & 15, g = lane >> 4;
+  // A operands: lane (row m = lane % 16, k = 8 (lane / 16) + j) of tile t holds
+  // H_32[8 (m / 4) + 4 t + m % 4][k] * s_{32 b + k} as fp16 +-1.
+  uint4 A[NB][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) smask[i] = (((sm >> (2 * i)) & 1u) << 15) | (((sm >> (2 * i + 1)) & 1u) << 31);
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 8 * (c >> 2) + 4 * t + (c & 3);
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kk = 8 * g + 2 * q + h;
+          const uint32_t neg = (__builtin_popcount(r & kk) + (L.signs.w[b] >> kk)) & 1u;
+          hv[h] = neg ? 0xBC00u : 0x3C00u;
+        }
+        w[q] = hv[0] | (hv[1] << 16);
+      }
+      A[b][t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
-  const int64_t step = (int64_t)gridDim.x * kNWQ * RPW;
-  for (int64_t r0 = ((int64_t)blockIdx.x * kNWQ + wave) * RPW; r0 < n_rows; r0 += step) {
-    const int64_t row = r0 + rr;
-    const bool in = row < n_rows;
-    const int64_t t = in ? row / L.Hkv : 0;
-    const int h = (int)(row - t * L.Hkv);
-    const int64_t slot = in ? slot_mapping[t] : -1;
-    const bool live = slot >= 0;
-    uint8_t* dst = pages + (live ? (slot * L.Hkv + h) * (int64_t)L.stride : 0);
-    quantize_row<D>(k + row * D, in, smask, xr, j, L.kb, L.kcode_bytes, s_t[0], tabk, shk, rsqrt_d, dst, live);
-    quantize_row<D>(v + row * D, in, smask, xr, j, L.vb, L.vcode_bytes, s_t[1], tabv, shv, rsqrt_d,
-                    dst + L.kcode_bytes + 4, live);
-    if (live)
-      for (int i = L.slot_bytes + j; i < L.stride; i += P) dst[i] = 0;
-  }
+  float zero;  // an addend of 0 the compiler cannot fold, so a lone square stays one v_fma_mix
+  asm("v_mov_b32 %0, 0" : "=v"(zero));
+
+  // Each wave stages its next tile in its own LDS buffer (global_load_lds: lane l's 16 bytes of
+  // block b land at b * 1024 + 16 l, the same lane reads them back; the slot id of lane l's row
+  // lands as two dwords) while it works on the current one from registers.  All vector memory
+  // operations share one in-order counter: the next tile's loads are issued before the current
+  // tile's stores, and the wait at the top of an iteration lets exactly those stores stay in
+  // flight.
+  uint8_t* stage = s_stage[wave];
+  const int64_t n_tiles = (n_rows + 15) / 16;
+  const int64_t tstep = (int64_t)gridDim.x * kNWQ;
+  constexpr int kStores = region_stores(KB) + region_stores(VB);
+  auto issue = [&](int64_t T) {
+    const int64_t row = T * 16 + c;
+    const int64_t rr = row < n_rows ? row : n_rows - 1;  // rows past the end load the last row
+    const uint16_t* sk = k + rr * D + 8 * g;
+    const uint16_t* sv = v + rr * D + 8 * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      __builtin_amdgcn_global_load_lds(sk + 32 * b, stage + b * 1024, 16, 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      __builtin_amdgcn_global_load_lds(sv + 32 * b, stage + (NB + b) * 1024, 16, 0, 0);
+    const uint32_t* sl = reinterpret_cast<const uint32_t*>(slot_mapping + rr / L.Hkv);
+    __builtin_amdgcn_global_load_lds(sl, stage + 2 * NB * 1024, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sl + 1, stage + 2 * NB * 1024 + 256, 4, 0, 0);
+  };
+  // Two complete tile loops, one per decision method (a codebook too fine for its table sends
+  // both regions to the binary search), so neither loop carries the other's registers.
+  auto tile_loop = [&](auto use_table) {
+    constexpr bool kTable = decltype(use_table)::value;
+    int64_t T = (int64_t)blockIdx.x * kNWQ + wave;
+    if (T < n_tiles) issue(T);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    for (; T < n_tiles; T += tstep) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStores));  // all but the previous tile's stores
+      uint4 xk[NB], xv[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xk[b] = reinterpret_cast<const uint4*>(stage + b * 1024)[lane];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xv[b] = reinterpret_cast<const uint4*>(stage + (NB + b) * 1024)[lane];
+      const uint32_t slo = reinterpret_cast<const uint32_t*>(stage + 2 * NB * 1024)[lane];
+      const uint32_t shi = reinterpret_cast<const uint32_t*>(stage + 2 * NB * 1024 + 256)[lane];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): buffer read out before it is refilled
+      const int64_t row = T * 16 + c;
+      const int64_t slot = (int64_t)(((uint64_t)shi << 32) | slo);
+      const bool live = row < n_rows && slot >= 0;
+      const int64_t tok = row / L.Hkv;
+      const int h = (int)(row - tok * L.Hkv);
+      uint8_t* dst = live ? pages + (slot * L.Hkv + h) * (int64_t)L.stride : tq_quant_discard;
+      for (int i = L.slot_bytes + g; i < L.stride; i += 4) dst[i] = 0;  // padding, before the loads
+      if (T + tstep < n_tiles) issue(T + tstep);
+
+      quantize_region<D, KB, kTable>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk, rsqrt_d, dst);
+      quantize_region<D, VB, kTable>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv, rsqrt_d,
+                                     dst + L.kcode_bytes + 4);
+    }
+  };
+  if (shk != kQNoTable && shv != kQNoTable) tile_loop(std::true_type{});
+  else tile_loop(std::false_type{});
 }
 
 // =============================================================================================
@@ -344,21 +427,49 @@ __global__ __launch_bounds__(kWG) void tq_dequant_kernel(TqLayer L, float rsqrt_
 
 static float rsqrt_of(int D) { return (float)(1.0 / __builtin_sqrt((double)D)); }
 
+template <int D, int KB, int VB>
+static void launch_quantize(const TqLayer& L, dim3 grid, size_t lds, hipStream_t st, const void* k,
+                            const void* v, const int64_t* slot_mapping, int64_t rows, void* pages) {
+  hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
+                     (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+}
+
+template <int D, int KB>
+static bool dispatch_vb(const TqLayer& L, dim3 grid, size_t lds, hipStream_t st, const void* k,
+                        const void* v, const int64_t* sm, int64_t rows, void* pages) {
+  switch (L.vb) {
+    case 2: launch_quantize<D, KB, 2>(L, grid, lds, st, k, v, sm, rows, pages); return true;
+    case 3: launch_quantize<D, KB, 3>(L, grid, lds, st, k, v, sm, rows, pages); return true;
+    case 4: launch_quantize<D, KB, 4>(L, grid, lds, st, k, v, sm, rows, pages); return true;
+    case 8: launch_quantize<D, KB, 8>(L, grid, lds, st, k, v, sm, rows, pages); return true;
+  }
+  return false;
+}
+
+template <int D>
+static bool dispatch_kb(const TqLayer& L, dim3 grid, size_t lds, hipStream_t st, const void* k,
+                        const void* v, const int64_t* sm, int64_t rows, void* pages) {
+  switch (L.kb) {
+    case 2: return dispatch_vb<D, 2>(L, grid, lds, st, k, v, sm, rows, pages);
+    case 3: return dispatch_vb<D, 3>(L, grid, lds, st, k, v, sm, rows, pages);
+    case 4: return dispatch_vb<D, 4>(L, grid, lds, st, k, v, sm, rows, pages);
+    case 8: return dispatch_vb<D, 8>(L, grid, lds, st, k, v, sm, rows, pages);
+  }
+  return false;
+}
+
 int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,
                        int64_t n_tok, void* pages, void* stream) {
   const int64_t rows = n_tok * L.Hkv;
   if (rows == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  const int64_t rows_per_wg = (kWG / 64) * (64 / (L.D / 16));
+  const int64_t rows_per_wg = (kWG / 64) * 16;  // one 16-row tile per wave
   const int64_t wgs = (rows + rows_per_wg - 1) / rows_per_wg;
-  const dim3 grid((unsigned)(wgs < 2048 ? wgs : 2048));  // workgroups loop over row groups
+  const dim3 grid((unsigned)(wgs < 2048 ? wgs : 2048));  // workgroups loop over tiles
   const size_t tab_bytes = (size_t)(qtab_entries(L.kb) + qtab_entries(L.vb)) * sizeof(uint2);
-  if (L.D == 128)
-    hipLaunchKernelGGL(tq_quantize_kernel<128>, grid, dim3(kWG), tab_bytes, st, L, rsqrt_of(128),
-                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
-  else
-    hipLaunchKernelGGL(tq_quantize_kernel<64>, grid, dim3(kWG), tab_bytes, st, L, rsqrt_of(64),
-                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+  const bool ok = L.D == 128 ? dispatch_kb<128>(L, grid, tab_bytes, st, k, v, slot_mapping, rows, pages)
+                             : dispatch_kb<64>(L, grid, tab_bytes, st, k, v, slot_mapping, rows, pages);
+  if (!ok) return (int)hipErrorInvalidValue;  // bit widths are validated by the API layer
   return (int)hipGetLastError();
 }
 
