@@ -224,16 +224,19 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
 // {S t_base as bits, base} with base = #{t < k / S}.
 __device__ __forceinline__ void build_qtab(const float* s_t, int nb, int sh, uint2* tab, int tid) {
   const int S = 1 << sh;
-  for (int i = tid; i < 2 * S + 2; i += kWG) {
-    const float edge = ldexpf((float)(i - (S + 1)), -sh);
-    int lo = 0, hi = nb;  // first boundary >= edge
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s_t[mid] < edge) lo = mid + 1;
-      else hi = mid;
+  constexpr int kPer = (kQTabLarge + kWG - 1) / kWG;  // entries per thread at most
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {  // unrolled: the threads' searches overlap
+    const int i = tid + r * kWG;
+    if (i < 2 * S + 2) {
+      const float edge = ldexpf((float)(i - (S + 1)), -sh);
+      int lo = 0;  // #{t < edge}: branchless lower bound over the (at most 255) sorted boundaries
+#pragma unroll
+      for (int st = 128; st >= 1; st >>= 1)
+        if (lo + st <= nb && s_t[lo + st - 1] < edge) lo += st;
+      const float next = lo < nb ? ldexpf(s_t[lo], sh) : 3.0e38f;
+      tab[i] = make_uint2(__float_as_uint(next), (uint32_t)lo);
     }
-    const float next = lo < nb ? ldexpf(s_t[lo], sh) : 3.0e38f;
-    tab[i] = make_uint2(__float_as_uint(next), (uint32_t)lo);
   }
 }
 
@@ -257,19 +260,34 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
   constexpr int kNWQ = kWG / 64;
   __shared__ float s_t[2][256];
   __shared__ int s_sh[2];
+  __shared__ float s_gap[kNWQ][2];
   // per wave: K blocks, V blocks, then the low and high dwords of the rows' slot ids
   __shared__ __align__(16) uint8_t s_stage[kNWQ][2 * NB * 1024 + 512];
   extern __shared__ uint2 s_tab[];  // K table (qtab_entries(kb)), then V table
 
   const int tid = threadIdx.x;
   constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
+  static_assert(nbk < kWG && nbv < kWG, "one boundary gap per thread");
   for (int i = tid; i < nbk; i += kWG) s_t[0][i] = L.kt[i];
   for (int i = tid; i < nbv; i += kWG) s_t[1][i] = L.vt[i];
   __syncthreads();
+  {  // smallest gap between consecutive boundaries, one gap per thread (at most 254 of them)
+    float gk = tid + 1 < nbk ? s_t[0][tid + 1] - s_t[0][tid] : 2.0f;
+    float gv = tid + 1 < nbv ? s_t[1][tid + 1] - s_t[1][tid] : 2.0f;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      gk = fminf(gk, __shfl_xor(gk, m));
+      gv = fminf(gv, __shfl_xor(gv, m));
+    }
+    if ((tid & 63) == 0) {
+      s_gap[tid >> 6][0] = gk;
+      s_gap[tid >> 6][1] = gv;
+    }
+  }
+  __syncthreads();
   if (tid < 2) {  // table resolution per codebook: S = 2^sh >= 1 / (smallest gap)
-    const int nb = tid == 0 ? nbk : nbv;
     float gap = 2.0f;
-    for (int i = 0; i + 1 < nb; ++i) gap = fminf(gap, s_t[tid][i + 1] - s_t[tid][i]);
+    for (int w = 0; w < kNWQ; ++w) gap = fminf(gap, s_gap[w][tid]);
     int sh = gap > 0.0f ? -ilogbf(gap) : kQNoTable;  // bucket width 2^-sh <= gap
     if (sh < 0) sh = 0;
     if (gap <= 0.0f || 2 * (1 << min(sh, 20)) + 2 > qtab_entries(tid == 0 ? KB : VB)) sh = kQNoTable;
