@@ -6,15 +6,22 @@ Follows:
   figure for slot addressing through a block table.
 * turboquant-pro 1.4.2, "Fused CUDA decode": one decode step over the whole cache computed on
   the codes equals decompress-then-attend (exact to a few 1e-7 there).
-* tq-kv, "3-Fix for GGUF Models" (the first four tokens stay fp16: sink tokens) and the
-  "Quick Start" calls pre_rotate_query_with_signs / fused_attention_scores (scores on the
-  codes with a rotated query).
+* tq-kv, "3-Fix for GGUF Models" (the first four tokens stay fp16: sink tokens; the current
+  token is kept lossless) and the "Quick Start" calls pre_rotate_query_with_signs /
+  fused_attention_scores (scores on the codes with a rotated query).
+* turboquant-pro 1.4.2, "Streaming cache" (an uncompressed hot window of recent tokens in front
+  of the bit-packed older ones) and "Fused CUDA decode" (the fp16 hot window is merged with the
+  packed segment by online softmax).
 
 Plain definition used here
 --------------------------
-For sequence b with L_b cached tokens and query head h (kv head h_kv = h // G, G = H_q / H_kv):
-  k_p, v_p = the fp16 sink rows for p < n_sink, else the dequantized rows n R^T c[idx]
-             read from page[bt[b][p // bs], p % bs, h_kv, :];
+For sequence b with L_b cached tokens and query head h (kv head h_kv = h // G, G = H_q / H_kv),
+with ns = min(n_sink, L_b) sinks and the last w_b = win_lens[b] positions in the hot window
+(0 <= w_b <= L_b - ns):
+  k_p, v_p = the fp16 sink rows for p < ns,
+             the fp16 window rows for p >= L_b - w_b (held in any order: attention does not
+             depend on the order of its tokens),
+             else the dequantized rows n R^T c[idx] read from page[bt[b][p // bs], p % bs, h_kv, :];
   s_p = scale * q_h . k_p      (scale = 1/sqrt(D) unless given);
   o_h = sum_p softmax(s)_p v_p over p in [0, L_b);  L_b = 0 gives o_h = 0.
 Everything is fp64; the query is the fp16 input.
@@ -31,10 +38,10 @@ import numpy as np
 from . import quantize, rotation
 
 
-def _dequantized_sequence(pages, block_table, L, n_sink, layer, k_centroids32, v_centroids32):
-    """Dequantized K, V rows [L - n_sink, H_kv, D] (fp64, plain route) for positions n_sink..L-1."""
+def _dequantized_sequence(pages, block_table, end, n_sink, layer, k_centroids32, v_centroids32):
+    """Dequantized K, V rows [end - n_sink, H_kv, D] (fp64, plain route), positions n_sink..end-1."""
     D, H_kv, bs = layer["D"], layer["H_kv"], layer["block_size"]
-    pos = np.arange(n_sink, L, dtype=np.int64)
+    pos = np.arange(n_sink, end, dtype=np.int64)
     slots = np.asarray(block_table, dtype=np.int64)[pos // bs] * bs + pos % bs
     k_idx, k_n, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, layer["k_bits"], layer["v_bits"],
                                                  layer.get("slot_stride"))
@@ -43,13 +50,22 @@ def _dequantized_sequence(pages, block_table, L, n_sink, layer, k_centroids32, v
     return K, V
 
 
+def _window_len(win_lens, b, L, ns):
+    w = 0 if win_lens is None else int(win_lens[b])
+    assert 0 <= w <= L - ns, "the hot window holds at most the tokens after the sinks"
+    return w
+
+
 def decode_attention(q16, pages, block_tables, seq_lens, layer, k_centroids32, v_centroids32,
-                     sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None):
+                     sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None,
+                     win_k16=None, win_v16=None, win_lens=None):
     """Dense decode attention, fp64.  Returns out [B, H_q, D] (rows not in `seqs` stay zero).
 
     layer: dict with D, H_kv, block_size, k_bits, v_bits, seed and optionally slot_stride.
     q16: [B, H_q, D] fp16.  block_tables: [B, max_blocks] int.  seq_lens: [B] int.
     sink_k16 / sink_v16: [B, n_sink, H_kv, D] fp16 (or None when n_sink == 0).
+    win_k16 / win_v16: [B, win_cap, H_kv, D] fp16 and win_lens [B]: rows 0 .. win_lens[b] - 1 are
+    the hot window of sequence b (None: no window).
     """
     q = np.asarray(q16, dtype=np.float16).astype(np.float64)
     B, H_q, D = q.shape
@@ -63,14 +79,14 @@ def decode_attention(q16, pages, block_tables, seq_lens, layer, k_centroids32, v
         if L == 0:
             continue
         ns = min(n_sink, L)
-        Kq, Vq = _dequantized_sequence(pages, block_tables[b], L, ns, layer, k_centroids32, v_centroids32)
-        if ns:
-            Ks = np.asarray(sink_k16[b, :ns], dtype=np.float16).astype(np.float64)
-            Vs = np.asarray(sink_v16[b, :ns], dtype=np.float16).astype(np.float64)
-            K = np.concatenate([Ks, Kq], axis=0)
-            V = np.concatenate([Vs, Vq], axis=0)
-        else:
-            K, V = Kq, Vq
+        w = _window_len(win_lens, b, L, ns)
+        Kq, Vq = _dequantized_sequence(pages, block_tables[b], L - w, ns, layer, k_centroids32, v_centroids32)
+        Ks = np.asarray(sink_k16[b, :ns], dtype=np.float16).astype(np.float64) if ns else Kq[:0]
+        Vs = np.asarray(sink_v16[b, :ns], dtype=np.float16).astype(np.float64) if ns else Vq[:0]
+        Kw = np.asarray(win_k16[b, :w], dtype=np.float16).astype(np.float64) if w else Kq[:0]
+        Vw = np.asarray(win_v16[b, :w], dtype=np.float16).astype(np.float64) if w else Vq[:0]
+        K = np.concatenate([Ks, Kq, Kw], axis=0)
+        V = np.concatenate([Vs, Vq, Vw], axis=0)
         for h in range(H_q):
             hk = h // G
             s = scale * (K[:, hk, :] @ q[b, h])
@@ -81,8 +97,10 @@ def decode_attention(q16, pages, block_tables, seq_lens, layer, k_centroids32, v
 
 
 def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centroids32, v_centroids32,
-                             sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None):
-    """Same result through the rotated domain: scores n_K (R q).c_K, values R^T sum w n_V c_V."""
+                             sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None,
+                             win_k16=None, win_v16=None, win_lens=None):
+    """Same result through the rotated domain: scores n_K (R q).c_K, values R^T sum w n_V c_V; the
+    fp16 rows (sinks, hot window) are scored and summed as they are."""
     q = np.asarray(q16, dtype=np.float16).astype(np.float64)
     B, H_q, D = q.shape
     H_kv, bs = layer["H_kv"], layer["block_size"]
@@ -98,7 +116,8 @@ def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centro
         if L == 0:
             continue
         ns = min(n_sink, L)
-        pos = np.arange(ns, L, dtype=np.int64)
+        w = _window_len(win_lens, b, L, ns)
+        pos = np.arange(ns, L - w, dtype=np.int64)
         slots = np.asarray(block_tables[b], dtype=np.int64)[pos // bs] * bs + pos % bs
         k_idx, k_n, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, layer["k_bits"], layer["v_bits"],
                                                      layer.get("slot_stride"))
@@ -106,19 +125,21 @@ def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centro
             hk = h // G
             qr = R @ q[b, h]
             s_codes = scale * k_n[:, hk].astype(np.float64) * (ck[k_idx[:, hk, :]] @ qr)
+            # the fp16 rows: sinks, then the hot window
+            K16 = np.zeros((0, D))
+            V16 = np.zeros((0, D))
             if ns:
-                Ks = np.asarray(sink_k16[b, :ns, hk], np.float16).astype(np.float64)
-                s_sink = scale * (Ks @ q[b, h])
-            else:
-                s_sink = np.zeros(0)
-            m = max(s_codes.max() if s_codes.size else -np.inf, s_sink.max() if s_sink.size else -np.inf)
+                K16 = np.asarray(sink_k16[b, :ns, hk], np.float16).astype(np.float64)
+                V16 = np.asarray(sink_v16[b, :ns, hk], np.float16).astype(np.float64)
+            if w:
+                K16 = np.concatenate([K16, np.asarray(win_k16[b, :w, hk], np.float16).astype(np.float64)])
+                V16 = np.concatenate([V16, np.asarray(win_v16[b, :w, hk], np.float16).astype(np.float64)])
+            s_16 = scale * (K16 @ q[b, h])
+            m = max(s_codes.max() if s_codes.size else -np.inf, s_16.max() if s_16.size else -np.inf)
             w_codes = np.exp(s_codes - m)
-            w_sink = np.exp(s_sink - m)
-            l = w_codes.sum() + w_sink.sum()
+            w_16 = np.exp(s_16 - m)
+            l = w_codes.sum() + w_16.sum()
             acc_rot = (w_codes * v_n[:, hk].astype(np.float64)) @ cv[v_idx[:, hk, :]]
-            o = R.T @ acc_rot
-            if ns:
-                Vs = np.asarray(sink_v16[b, :ns, hk], np.float16).astype(np.float64)
-                o = o + w_sink @ Vs
+            o = R.T @ acc_rot + w_16 @ V16
             out[b, h] = o / l
     return out

@@ -443,3 +443,97 @@ def test_attention_identical_keys_and_shift(rng):
     _, _, v_idx, v_n = quantize.read_slots(pages, slots, 1, D, 4, 4)
     vhat = quantize.dequantize_plain(v_idx, v_n, cv.centroids32, 0)
     np.testing.assert_allclose(o[0, 0], vhat[:, 0].mean(0), atol=1e-12)
+
+
+# ============================================================================================
+# Hot window (turboquant-pro 1.4.2, "Streaming cache" and "Fused CUDA decode"; tq-kv, "3-Fix for
+# GGUF Models": the current token kept lossless): the last w positions come from fp16 rows.
+# ============================================================================================
+def _window_rows(rng, w_cap, H_kv, D, B=1):
+    wk = rng.standard_normal((B, w_cap, H_kv, D)).astype(np.float16)
+    wv = rng.standard_normal((B, w_cap, H_kv, D)).astype(np.float16)
+    return wk, wv
+
+
+@pytest.mark.parametrize("D, H_kv, G, kb, vb, L, ns, w", [
+    (64, 1, 1, 4, 4, 1, 0, 1), (64, 2, 2, 8, 8, 37, 0, 5), (128, 1, 4, 4, 4, 50, 4, 16),
+    (128, 2, 3, 3, 2, 17, 2, 15), (64, 1, 1, 2, 2, 5, 5, 0), (128, 1, 8, 8, 4, 64, 0, 63)])
+def test_attention_routes_agree_with_window(D, H_kv, G, kb, vb, L, ns, w, rng):
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, kb, vb, L)
+    q = rng.standard_normal((1, H_kv * G, D)).astype(np.float16)
+    sk = rng.standard_normal((1, max(ns, 1), H_kv, D)).astype(np.float16)
+    sv = rng.standard_normal((1, max(ns, 1), H_kv, D)).astype(np.float16)
+    wk, wv = _window_rows(rng, max(w, 1) + 3, H_kv, D)
+    args = (q, pages, bt[None], np.array([L]), layer, ck.centroids32, cv.centroids32, sk, sv, ns)
+    kw = dict(win_k16=wk, win_v16=wv, win_lens=np.array([w]))
+    a = attention.decode_attention(*args, **kw)
+    b = attention.decode_attention_rotated(*args, **kw)
+    np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+
+
+def test_attention_sinks_and_window_cover_everything_is_textbook(rng):
+    import torch
+    D, H_kv, G, L, ns = 64, 2, 3, 11, 3
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, 4, 4, L)
+    q = rng.standard_normal((1, H_kv * G, D)).astype(np.float16)
+    sk = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    sv = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    wk, wv = _window_rows(rng, L - ns + 2, H_kv, D)
+    o = attention.decode_attention(q, pages, bt[None], np.array([L]), layer, ck.centroids32,
+                                   cv.centroids32, sk, sv, n_sink=ns, win_k16=wk, win_v16=wv,
+                                   win_lens=np.array([L - ns]))
+    Kall = np.concatenate([sk[0], wk[0, :L - ns]]).astype(np.float64)   # [L, H_kv, D]
+    Vall = np.concatenate([sv[0], wv[0, :L - ns]]).astype(np.float64)
+    Q = torch.from_numpy(q.astype(np.float64)).reshape(1, H_kv * G, 1, D)
+    K = torch.from_numpy(Kall).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    V = torch.from_numpy(Vall).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V).reshape(1, H_kv * G, D).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def test_attention_window_order_and_ignored_slots(rng):
+    D, H_kv, G, L, ns, w = 128, 1, 4, 45, 2, 9
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, 4, 4, L)
+    q = rng.standard_normal((1, G, D)).astype(np.float16)
+    sk = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    sv = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    wk, wv = _window_rows(rng, w, H_kv, D)
+    run = lambda pg, wk_, wv_: attention.decode_attention(
+        q, pg, bt[None], np.array([L]), layer, ck.centroids32, cv.centroids32, sk, sv, ns,
+        win_k16=wk_, win_v16=wv_, win_lens=np.array([w]))
+    o = run(pages, wk, wv)
+    perm = rng.permutation(w)
+    np.testing.assert_allclose(run(pages, wk[:, perm], wv[:, perm]), o, atol=1e-13)
+    # overwrite the page slots of the window positions (and the sink positions): no effect
+    sb = quantize.slot_bytes(D, 4, 4)
+    pg = pages.copy()
+    for p in list(range(ns)) + list(range(L - w, L)):
+        s = bt[p // 16] * 16 + p % 16
+        pg[s * H_kv * sb:(s + 1) * H_kv * sb] = rng.integers(0, 256, H_kv * sb, dtype=np.uint8)
+    np.testing.assert_allclose(run(pg, wk, wv), o, atol=0)
+    # but a packed position just below the window does matter
+    s = bt[(L - w - 1) // 16] * 16 + (L - w - 1) % 16
+    pg[s * H_kv * sb:(s + 1) * H_kv * sb] = rng.integers(0, 256, H_kv * sb, dtype=np.uint8)
+    assert np.abs(run(pg, wk, wv) - o).max() > 1e-6
+
+
+def test_attention_zero_query_averages_every_segment(rng):
+    D, H_kv, G, L, ns, w = 64, 2, 2, 30, 3, 7
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, 8, 4, L)
+    sk = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    sv = rng.standard_normal((1, ns, H_kv, D)).astype(np.float16)
+    wk, wv = _window_rows(rng, w + 4, H_kv, D)
+    q0 = np.zeros((1, H_kv * G, D), np.float16)
+    o = attention.decode_attention(q0, pages, bt[None], np.array([L]), layer, ck.centroids32,
+                                   cv.centroids32, sk, sv, ns, win_k16=wk, win_v16=wv,
+                                   win_lens=np.array([w]))
+    pos = np.arange(ns, L - w)
+    slots = bt[pos // 16] * 16 + pos % 16
+    _, _, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, 8, 4)
+    vhat = quantize.dequantize_plain(v_idx, v_n, cv.centroids32, 0)      # [L - ns - w, H_kv, D]
+    for h in range(H_kv * G):
+        hk = h // G
+        rows = np.concatenate([sv[0, :, hk].astype(np.float64), vhat[:, hk],
+                               wv[0, :w, hk].astype(np.float64)])
+        assert rows.shape[0] == L
+        np.testing.assert_allclose(o[0, h], rows.mean(0), atol=1e-12)
