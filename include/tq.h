@@ -149,6 +149,29 @@ int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q, const v
                               int32_t n_sink, float scale, float* out, void* workspace,
                               size_t workspace_bytes, tq_stream_t stream);
 
+/* The same decode with an fp16 hot window: the most recent tokens of each sequence kept
+ * uncompressed and merged with the packed tokens by online softmax.
+ * (turboquant-pro 1.4.2, "Streaming cache": an uncompressed hot window of recent tokens in front of
+ *  the bit-packed older ones; "Fused CUDA decode": the fp16 hot window merged via online softmax;
+ *  tq-kv, "3-Fix for GGUF Models": the current token kept lossless.)
+ *   win_k, win_v  device fp16 [num_seqs][win_cap][num_kv_heads][D]: rows 0 .. win_lens[b] - 1 of
+ *                 sequence b are its last win_lens[b] positions, in any order (attention does not
+ *                 depend on the order of its tokens); their page slots are ignored
+ *   win_lens      device int32 [num_seqs]: 0 <= win_lens[b] <= min(win_cap,
+ *                 seq_lens[b] - min(n_sink, seq_lens[b])); values outside are clamped to it
+ *   win_cap       rows per sequence in win_k / win_v, 0 .. 1024 (0: no window; then the window
+ *                 pointers may be NULL)
+ * Every other argument, the workspace size included, is as for tq_paged_decode_attention.  The
+ * packed positions of sequence b are n_sink .. seq_lens[b] - win_lens[b] - 1. */
+int tq_paged_decode_attention_window(const tq_layer_desc* layer, const void* q, const void* pages,
+                                     int64_t num_blocks, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t num_seqs, int32_t max_seq_len, const void* sink_k,
+                                     const void* sink_v, int32_t n_sink, const void* win_k,
+                                     const void* win_v, const int32_t* win_lens, int32_t win_cap,
+                                     float scale, float* out, void* workspace,
+                                     size_t workspace_bytes, tq_stream_t stream);
+
 /* Dequantize whole slots (turboquant-serve 0.1.2, "Architecture" _decode(): unpack, Lloyd-Max
  * decode, restore magnitude, rotate back).  Bit-exact definition: c_i = centroid[idx_i] (fp32);
  * z = H c computed exactly (fp64); g = fp32(n * fp32(1/sqrt(D))); x_i = s_i * fp32(fp32(z_i) * g).

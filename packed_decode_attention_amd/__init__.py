@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     tq_dequantize_rows,
     tq_layer_desc,
     tq_paged_decode_attention,
+    tq_paged_decode_attention_window,
     tq_quantize_append,
     tq_rht_signs,
     tq_slot_bytes,

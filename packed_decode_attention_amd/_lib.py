@@ -26,8 +26,8 @@ TQ_ERR_NO_CONVERGENCE = -5
 FAMILIES = {"beta": 0, "gaussian": 1}
 
 EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_quantize_append",
-           "tq_decode_workspace_bytes", "tq_paged_decode_attention", "tq_dequantize_rows",
-           "tq_status_str")
+           "tq_decode_workspace_bytes", "tq_paged_decode_attention",
+           "tq_paged_decode_attention_window", "tq_dequantize_rows", "tq_status_str")
 
 
 class TqError(RuntimeError):
@@ -79,6 +79,10 @@ def _lib():
         lib.tq_paged_decode_attention.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P, I32,
                                                   ctypes.c_float, P, P, SZ, P]
         lib.tq_paged_decode_attention.restype = ctypes.c_int
+        lib.tq_paged_decode_attention_window.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P,
+                                                         I32, P, P, P, I32, ctypes.c_float, P, P,
+                                                         SZ, P]
+        lib.tq_paged_decode_attention_window.restype = ctypes.c_int
         lib.tq_dequantize_rows.argtypes = [D, P, I64, P, I64, P, P, P]
         lib.tq_dequantize_rows.restype = ctypes.c_int
         lib.tq_status_str.argtypes = [ctypes.c_int]
@@ -158,6 +162,23 @@ def tq_paged_decode_attention(desc, q, pages, num_blocks: int, block_tables, seq
         _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, scale,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_paged_decode_attention", st)
+
+
+def tq_paged_decode_attention_window(desc, q, pages, num_blocks: int, block_tables, seq_lens,
+                                     max_seq_len: int, out, workspace, win_k, win_v, win_lens,
+                                     sink_k=None, sink_v=None, n_sink: int = 0, scale: float = 0.0,
+                                     stream=None) -> None:
+    """Decode with an fp16 hot window: win_k / win_v [B, win_cap, H_kv, D] fp16, win_lens [B]
+    int32 (rows 0 .. win_lens[b] - 1 hold the last win_lens[b] positions of sequence b)."""
+    num_seqs = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    win_cap = win_k.shape[1] if win_k is not None else 0
+    st = _lib().tq_paged_decode_attention_window(
+        ctypes.byref(desc), _ptr(q), _ptr(pages), num_blocks, _ptr(block_tables), max_blocks,
+        _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(win_k),
+        _ptr(win_v), _ptr(win_lens), win_cap, scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_paged_decode_attention_window", st)
 
 
 def tq_dequantize_rows(desc, pages, num_blocks: int, slots, k_out, v_out, stream=None) -> None:

@@ -87,6 +87,40 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t 
   return tq_decode_ws_bytes(L, num_seqs, tq_decode_split(L, num_seqs, max_seq_len));
 }
 
+static int paged_decode(const tq_layer_desc* layer, const void* q, const void* pages,
+                        int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                        const void* sink_k, const void* sink_v, int32_t n_sink, const void* win_k,
+                        const void* win_v, const int32_t* win_lens, int32_t win_cap, float scale,
+                        float* out, void* workspace, size_t workspace_bytes, tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, true, &L);
+  if (st != TQ_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || n_sink < 0 || max_blocks_per_seq < 0 || num_blocks < 0 ||
+      win_cap < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return TQ_ERR_UNSUPPORTED;
+  if (n_sink > TQ_MAX_SINKS || win_cap > TQ_MAX_WINDOW) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return TQ_OK;
+  if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
+    return TQ_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (win_cap > 0 && (win_k == nullptr || win_v == nullptr || win_lens == nullptr))
+    return TQ_ERR_INVALID_ARG;
+  if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  const TqSplit sp = tq_decode_split(L, num_seqs, max_seq_len);
+  if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) return TQ_ERR_WORKSPACE;
+  return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
+                          sink_k, sink_v, n_sink, win_k, win_v, win_lens, win_cap, scale, out,
+                          workspace, stream) == 0
+             ? TQ_OK
+             : TQ_ERR_HIP;
+}
+
 extern "C" int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q,
                                          const void* pages, int64_t num_blocks,
                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -95,28 +129,20 @@ extern "C" int tq_paged_decode_attention(const tq_layer_desc* layer, const void*
                                          const void* sink_v, int32_t n_sink, float scale,
                                          float* out, void* workspace, size_t workspace_bytes,
                                          tq_stream_t stream) {
-  TqLayer L;
-  const int st = make_layer(layer, true, &L);
-  if (st != TQ_OK) return st;
-  if (num_seqs < 0 || max_seq_len < 0 || n_sink < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
-    return TQ_ERR_INVALID_ARG;
-  if (num_seqs > 65535) return TQ_ERR_UNSUPPORTED;
-  if (n_sink > TQ_MAX_SINKS) return TQ_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return TQ_OK;
-  if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
-    return TQ_ERR_INVALID_ARG;
-  if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
-    return TQ_ERR_INVALID_ARG;
-  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
-  if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
-  if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
-  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
-  const TqSplit sp = tq_decode_split(L, num_seqs, max_seq_len);
-  if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) return TQ_ERR_WORKSPACE;
-  return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
-                          sink_k, sink_v, n_sink, scale, out, workspace, stream) == 0
-             ? TQ_OK
-             : TQ_ERR_HIP;
+  return paged_decode(layer, q, pages, num_blocks, block_tables, max_blocks_per_seq, seq_lens,
+                      num_seqs, max_seq_len, sink_k, sink_v, n_sink, nullptr, nullptr, nullptr, 0,
+                      scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int tq_paged_decode_attention_window(
+    const tq_layer_desc* layer, const void* q, const void* pages, int64_t num_blocks,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t num_seqs, int32_t max_seq_len, const void* sink_k, const void* sink_v, int32_t n_sink,
+    const void* win_k, const void* win_v, const int32_t* win_lens, int32_t win_cap, float scale,
+    float* out, void* workspace, size_t workspace_bytes, tq_stream_t stream) {
+  return paged_decode(layer, q, pages, num_blocks, block_tables, max_blocks_per_seq, seq_lens,
+                      num_seqs, max_seq_len, sink_k, sink_v, n_sink, win_k, win_v, win_lens,
+                      win_cap, scale, out, workspace, workspace_bytes, stream);
 }
 
 extern "C" int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages, int64_t num_blocks,

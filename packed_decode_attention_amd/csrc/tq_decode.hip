@@ -51,14 +51,25 @@ struct DecodeArgs {
   const uint16_t* sink_k;
   const uint16_t* sink_v;
   int n_sink;
+  const uint16_t* win_k;     // hot window rows [B][win_cap][Hkv][D] fp16 (NULL: no window)
+  const uint16_t* win_v;
+  const int32_t* win_lens;   // [B]: valid window rows, the last positions of the sequence
+  int win_cap;
   float* out;
   float* partials;   // [B][Hkv][max_split][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
 };
 
-// Splits cover absolute positions [split * chunk, (split + 1) * chunk) of a sequence; positions
-// below n_sink are read from the sink arrays instead and are masked out of the splits.
+// Splits cover absolute positions [split * chunk, (split + 1) * chunk) of a sequence, up to the
+// packed end; positions below n_sink are read from the sink arrays instead and are masked out of
+// the splits, positions from the packed end on come from the hot window.
 __device__ __forceinline__ int num_splits(int seq_len, int chunk) {
   return seq_len > 0 ? (seq_len + chunk - 1) / chunk : 1;
+}
+
+// Hot-window rows of sequence b (clamped to [0, min(win_cap, seq_len - ns)]).
+__device__ __forceinline__ int window_len(const DecodeArgs& a, int b, int seq_len, int ns) {
+  if (a.win_lens == nullptr) return 0;
+  return max(0, min(a.win_lens[b], min(a.win_cap, seq_len - ns)));
 }
 
 // Raw page data of one step for one lane.
@@ -92,7 +103,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   const int split = unit - b * a.max_split;
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
-  const int nsplit = num_splits(seq_len, a.chunk);
+  const int packed_end = seq_len - window_len(a, b, seq_len, ns);
+  const int nsplit = num_splits(packed_end, a.chunk);
   if (split >= nsplit) return;
 
   __shared__ float s_klut[Lut<KB>::kFloats];
@@ -103,7 +115,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   build_lut<VB>(s_vlut, L.vc, threadIdx.x, kWG);
 
   const int p_begin = max(ns, split * a.chunk);
-  const int p_end = min((split + 1) * a.chunk, seq_len);
+  const int p_end = min((split + 1) * a.chunk, packed_end);
   const int n_it = p_end > p_begin ? (p_end - p_begin + TPI - 1) / TPI : 0;
   auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
   const int blk0 = p_end > p_begin ? block_of(p_begin) : 0;
@@ -469,7 +481,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const int split = unit - b * a.max_split;
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
-  const int nsplit = num_splits(seq_len, a.chunk);
+  const int packed_end = seq_len - window_len(a, b, seq_len, ns);
+  const int nsplit = num_splits(packed_end, a.chunk);
   if (split >= nsplit) return;
 
   __shared__ KE s_ktab[OpTable<KB>::N];
@@ -494,7 +507,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   build_op_table<VB>(s_vtab, L.vc, tid);
 
   const int p0 = split * a.chunk;
-  const int p_end = min(p0 + a.chunk, seq_len);
+  const int p_end = min(p0 + a.chunk, packed_end);
   auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
   const int blk0 = block_of(p0);
   const int blk_last = p_end > p0 ? block_of(p_end - 1) : blk0;
@@ -858,7 +871,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (sequence, kv head): merge the splits and the sinks, rotate back, normalise.
+// One workgroup per (sequence, kv head): merge the splits with the fp16 rows (sinks and hot
+// window), rotate back, normalise.
 template <int D, int GMAX>
 __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
@@ -867,34 +881,81 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const int b = blockIdx.x / L.Hkv;
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
-  const int nsplit = num_splits(seq_len, a.chunk);
+  const int nw = window_len(a, b, seq_len, ns);
+  const int nf = ns + nw;  // fp16 rows: sinks 0 .. ns - 1, then window rows
+  const int packed_end = seq_len - nw;
+  const int nsplit = num_splits(packed_end, a.chunk);
   float* outp = a.out + ((int64_t)b * L.Hq + h * G) * D;
   if (seq_len == 0) {
     for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
     return;
   }
-  __shared__ float s_acc[GMAX * D];              // merged rotated accumulators
-  __shared__ float s_ml[2 * GMAX];               // max, sum
-  __shared__ float s_sink[GMAX * TQ_MAX_SINKS];  // sink scores, log2 domain
-  for (int i = threadIdx.x; i < G * ns; i += kWG) {
-    const int g = i / ns, pp = i % ns;
-    const uint16_t* qv = a.q + ((int64_t)b * L.Hq + h * G + g) * D;
-    const uint16_t* kv = a.sink_k + (((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D;
-    float dot = 0.0f;
-    for (int d = 0; d < D; ++d) dot += half_bits_to_float(qv[d]) * half_bits_to_float(kv[d]);
-    s_sink[g * ns + pp] = dot * a.sink_scale;
+  constexpr int FMAX = TQ_MAX_SINKS + TQ_MAX_WINDOW;
+  constexpr int LPH = D / 8;                 // lanes per row, 8 coordinates each
+  __shared__ float s_acc[GMAX * D];          // merged rotated accumulators
+  __shared__ float s_ml[2 * GMAX];           // max, sum
+  __shared__ float s_fmax[GMAX], s_fsum[GMAX];
+  __shared__ float s_f[GMAX * FMAX];         // scores of the fp16 rows, log2 domain
+  __shared__ float s_fv[GMAX][D];            // weighted sums of the fp16 value rows
+  __shared__ float s_red[(kWG / LPH) * (D + 1)];  // per (row part, head): partial sums
+
+  auto krow = [&](int i) {  // key / value row i of the fp16 segment
+    return i < ns ? (((int64_t)b * a.n_sink + i) * L.Hkv + h) * D
+                  : (((int64_t)b * a.win_cap + (i - ns)) * L.Hkv + h) * D;
+  };
+  auto kptr = [&](int i) { return (i < ns ? a.sink_k : a.win_k) + krow(i); };
+  auto vptr = [&](int i) { return (i < ns ? a.sink_v : a.win_v) + krow(i); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane % LPH;      // coordinates 8 j .. 8 j + 7
+  const int slot = lane / LPH;   // row slot within the wave
+  constexpr int RPW = 64 / LPH;  // rows per wave step
+  // Scores of the fp16 rows: each row is held by LPH lanes of one DPP row (or half row).
+  if (nf > 0) {
+    float qv[GMAX][8];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g < G) load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, qv[g]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][e] = 0.0f;
+    }
+    for (int i = wave * RPW + slot; i < nf; i += kNW * RPW) {
+      float kx[8];
+      load8_f16(kptr(i) + 8 * j, kx);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[g][e], kx[e], d);
+        d = group_sum<LPH>(d);
+        if (g < G && j == 0) s_f[g * FMAX + i] = d * a.sink_scale;
+      }
+    }
+  }
+  __syncthreads();
+  // Largest fp16-row score per head: 32 lanes per head.
+  if (tid < 32 * GMAX) {
+    const int g = tid >> 5;
+    float m = kSent;
+    if (g < G)
+      for (int i = tid & 31; i < nf; i += 32) m = fmaxf(m, s_f[g * FMAX + i]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+    if ((tid & 31) == 0) s_fmax[g] = m;
   }
   __syncthreads();
 
-  // Online log-sum-exp merge of the splits, one (head, coordinate) per thread.  Partials are
-  // loaded eight splits at a time so their loads are in flight together.  Empty partials carry a
-  // maximum of -inf or kSent and contribute exp2(. - M) = 0 once a real score is in M.
+  // Online log-sum-exp merge of the splits, one (head, coordinate) per thread, starting from the
+  // fp16 rows' maximum.  Partials are loaded eight splits at a time so their loads are in flight
+  // together.  Empty partials carry a maximum of -inf or kSent and contribute exp2(. - M) = 0
+  // once a real score is in M.
   const int64_t bh = (int64_t)b * L.Hkv + h;
   const float* pb = a.partials + bh * a.max_split * (int64_t)G * (D + 2);
-  for (int i = threadIdx.x; i < G * D; i += kWG) {
+  for (int i = tid; i < G * D; i += kWG) {
     const int g = i / D, d = i % D;
-    float M = kSent;
-    for (int pp = 0; pp < ns; ++pp) M = fmaxf(M, s_sink[g * ns + pp]);
+    float M = s_fmax[g];
     float l = 0.0f, acc = 0.0f;
     for (int s0 = 0; s0 < nsplit; s0 += 8) {
       float ms[8], ls[8], as[8];
@@ -915,7 +976,6 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
         M = Mn;
       }
     }
-    for (int pp = 0; pp < ns; ++pp) l += __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
     s_acc[g * D + d] = acc;
     if (d == 0) {
       s_ml[g] = M;
@@ -924,29 +984,66 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // R^T a = D^(-1/2) diag(s) H a, then the sinks' values, then the division by the sum: D/8
-  // lanes of one DPP row per head, 8 coordinates per lane.
-  constexpr int LPH = D / 8;
-  if (threadIdx.x < LPH * G) {
-    const int g = threadIdx.x / LPH, j = threadIdx.x % LPH;
+  // Weighted sums of the fp16 value rows: thread (part, g, j) takes rows part, part + NP, ... of
+  // head g, coordinates 8 j .. 8 j + 7; the parts are added up below.
+  constexpr int TPH = LPH;                     // threads per head and part
+  const int np = kWG / (TPH * G);              // parts
+  if (nf > 0) {
+    const int part = tid / (TPH * G);
+    const int g = (tid / TPH) % G;
+    float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float ls = 0.0f;
+    if (part < np) {
+      const float M = s_ml[g];
+      for (int i = part; i < nf; i += np) {
+        const float w = __builtin_amdgcn_exp2f(s_f[g * FMAX + i] - M);
+        float v[8];
+        load8_f16(vptr(i) + 8 * j, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, v[e], o[e]);
+        ls += w;
+      }
+    }
+    // sum over parts: first to LDS, then part 0 adds
+    __syncthreads();
+    float* red = s_red;
+    if (part < np) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(part * G + g) * (D + 1) + 8 * j + e] = o[e];
+      if (j == 0) red[(part * G + g) * (D + 1) + D] = ls;
+    }
+    __syncthreads();
+    if (tid < TPH * G) {
+      for (int pp = 1; pp < np; ++pp) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += red[(pp * G + g) * (D + 1) + 8 * j + e];
+        ls += red[(pp * G + g) * (D + 1) + D];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_fv[g][8 * j + e] = o[e];
+      if (j == 0) s_fsum[g] = ls;
+    }
+  } else if (tid < GMAX) {
+    s_fsum[tid] = 0.0f;
+  }
+  __syncthreads();
+
+  // R^T a = D^(-1/2) diag(s) H a, plus the fp16 rows' values, divided by the sum: D/8 lanes of
+  // one DPP row per head, 8 coordinates per lane.
+  if (tid < LPH * G) {
+    const int g = tid / LPH;
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s_acc[g * D + 8 * j + e];
     wht_row8_dpp<LPH>(x, j);
     const uint32_t sb = sign_byte(L.signs, j);
-    const float M = s_ml[g], inv_l = 1.0f / s_ml[GMAX + g];
+    const float inv_l = 1.0f / (s_ml[GMAX + g] + s_fsum[g]);
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       o[e] = x[e] * a.rsqrt_d;
       if ((sb >> e) & 1u) o[e] = -o[e];
-    }
-    for (int pp = 0; pp < ns; ++pp) {
-      const float w = __builtin_amdgcn_exp2f(s_sink[g * ns + pp] - M);
-      float sv[8];
-      load8_f16(a.sink_v + (((int64_t)b * a.n_sink + pp) * L.Hkv + h) * D + 8 * j, sv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += w * sv[e];
+      if (nf > 0) o[e] += s_fv[g][8 * j + e];
     }
     float4* o4 = reinterpret_cast<float4*>(outp + g * D + 8 * j);
     o4[0] = make_float4(o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l);
@@ -1044,8 +1141,9 @@ size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
 
 int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                      int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
-                     const void* sink_k, const void* sink_v, int n_sink, float scale, float* out,
-                     void* workspace, void* stream) {
+                     const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
+                     const void* win_v, const int32_t* win_lens, int win_cap, float scale,
+                     float* out, void* workspace, void* stream) {
   if (num_seqs == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
   DecodeArgs a;
@@ -1065,6 +1163,10 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.sink_k = (const uint16_t*)sink_k;
   a.sink_v = (const uint16_t*)sink_v;
   a.n_sink = n_sink;
+  a.win_k = (const uint16_t*)win_k;
+  a.win_v = (const uint16_t*)win_v;
+  a.win_lens = win_cap > 0 ? win_lens : nullptr;
+  a.win_cap = win_cap;
   a.out = out;
   a.partials = (float*)workspace;
   const long groups = (a.n_units + 7) / 8;

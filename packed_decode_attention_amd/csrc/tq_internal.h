@@ -9,8 +9,9 @@
 // Sign bits of the rotation for head dimension D (bit i set: s_i = -1), nwords 64-bit words.
 void tq_sign_words(int32_t D, uint64_t seed, uint64_t* words, int nwords);
 
-// Largest n_sink the decode kernel accepts (sink scores live in LDS).
+// Largest n_sink and hot-window capacity the decode kernel accepts (their scores live in LDS).
 #define TQ_MAX_SINKS 128
+#define TQ_MAX_WINDOW 1024
 
 // Sign bits as passed to the kernels by value (D <= 128).
 struct TqSigns {
@@ -42,8 +43,9 @@ int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int
                        int64_t n_tok, void* pages, void* stream);
 int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                      int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
-                     const void* sink_k, const void* sink_v, int n_sink, float scale, float* out,
-                     void* workspace, void* stream);
+                     const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
+                     const void* win_v, const int32_t* win_lens, int win_cap, float scale,
+                     float* out, void* workspace, void* stream);
 int tq_launch_dequant(const TqLayer& L, const void* pages, const int64_t* slots, int64_t n,
                       float* k_out, float* v_out, void* stream);
 

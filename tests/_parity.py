@@ -131,6 +131,46 @@ class Case:
         torch.cuda.synchronize()
         return out.cpu().numpy(), ws
 
+    def window(self, win_lens, win_cap, seed=0):
+        """fp16 hot-window rows [B, win_cap, H, D]: rows 0 .. w_b - 1 of sequence b are its last w_b
+        positions' K / V rows in a shuffled order; the rows past w_b hold large values a correct
+        kernel never reads."""
+        torch = self._torch
+        rng = np.random.default_rng(seed)
+        B = len(self.lens)
+        wk = torch.full((B, win_cap, self.H, self.D), 300.0, dtype=torch.float16)
+        wv = torch.full((B, win_cap, self.H, self.D), -300.0, dtype=torch.float16)
+        offs = np.concatenate([[0], np.cumsum(self.lens)])
+        for b, w in enumerate(win_lens):
+            rows = offs[b] + int(self.lens[b]) - w + rng.permutation(w)
+            wk[b, :w] = self.k[torch.from_numpy(rows)]
+            wv[b, :w] = self.v[torch.from_numpy(rows)]
+        return wk, wv, np.asarray(win_lens, np.int32)
+
+    def gpu_decode_window(self, fmt, pages_dev, wk, wv, wl_):
+        import packed_decode_attention_amd as tq
+        torch = self._torch
+        B = len(self.lens)
+        max_len = int(self.lens.max()) if B else 0
+        ws = fmt.new_workspace(B, max_len)
+        out = torch.full((B, self.Hq, self.D), float("nan"), dtype=torch.float32, device="cuda")
+        sk = None if self.sink_k is None else self.sink_k.cuda()
+        sv = None if self.sink_v is None else self.sink_v.cuda()
+        tq.tq_paged_decode_attention_window(fmt.desc, self.q.cuda(), pages_dev, self.num_blocks,
+                                            torch.from_numpy(self.bt).cuda(),
+                                            torch.from_numpy(self.lens).cuda(), max_len, out, ws,
+                                            wk.cuda(), wv.cuda(), torch.from_numpy(wl_).cuda(),
+                                            sk, sv, self.w.n_sink)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle_decode_window(self, wk, wv, wl_, seqs=None):
+        sk = None if self.sink_k is None else self.sink_k.numpy()
+        sv = None if self.sink_v is None else self.sink_v.numpy()
+        return oatt.decode_attention(self.q.numpy(), self.pages_ref, self.bt, self.lens, self.layer_dict,
+                                     self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink, seqs=seqs,
+                                     win_k16=wk.numpy(), win_v16=wv.numpy(), win_lens=wl_)
+
     def ref_pages_on_gpu(self):
         torch = self._torch
         return torch.from_numpy(self.pages_ref).cuda().reshape(

@@ -107,6 +107,39 @@ def test_decode_attention(cases, name):
     assert np.all(got[zero] == 0)
 
 
+# Hot-window lengths per sequence (each <= L - min(n_sink, L)) and the window capacity: a window
+# per case shape, including windows that hold every non-sink token (no packed tokens left), a
+# one-token window (the current token only) and the largest capacity.
+WINDOWS = {
+    "tiny": ([1], 8),
+    "qwen-small": ([200, 517, 0], 600),
+    "llama-small": ([64, 0], 100),
+    "mistral-small": ([512, 0, 126], 1024),
+    "ragged-small": ([1, 100, 0, 65, 17, 128], 130),
+    "edges": ([0, 0, 0, 1, 13, 196], 200),
+    "gaussian-g5": ([300, 0, 1], 301),
+}
+
+
+@pytest.mark.parametrize("name", list(WINDOWS))
+def test_decode_attention_hot_window(cases, name):
+    c = get(cases, name)
+    fmt = c.fmt()
+    lens_w, cap = WINDOWS[name]
+    print(f"[parity] decode with hot window {name}: lens={c.lens.tolist()} windows={lens_w} cap={cap}",
+          flush=True)
+    wk, wv, wl_ = c.window(lens_w, cap)
+    want = c.oracle_decode_window(wk, wv, wl_)
+    got = c.gpu_decode_window(fmt, c.ref_pages_on_gpu(), wk, wv, wl_)
+    check_attention(got, want)
+    # a window of length 0 everywhere is the plain decode
+    if name == "llama-small":
+        z = np.zeros_like(wl_)
+        plain, _ = c.gpu_decode(fmt, c.ref_pages_on_gpu())
+        none = c.gpu_decode_window(fmt, c.ref_pages_on_gpu(), wk, wv, z)
+        assert np.array_equal(plain.view(np.uint32), none.view(np.uint32))
+
+
 def test_decode_explicit_scale(cases):
     c = get(cases, "llama-small")
     fmt = c.fmt()

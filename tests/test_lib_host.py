@@ -120,6 +120,16 @@ def test_argument_validation_before_launch(lib):
     assert dec(_desc(lib), B=0) == E.TQ_OK
     assert dec(_desc(lib), B=-1) == E.TQ_ERR_INVALID_ARG
 
+    def decw(d, cap=16, wk=P, wl=P, B=4):
+        return so.tq_paged_decode_attention_window(ctypes.byref(d), P, P, 100, P, 7, P, B, 100, None,
+                                                   None, 0, wk, wk, wl, cap, 0.0, P, P, 1 << 40, None)
+    assert decw(_desc(lib), cap=1025) == E.TQ_ERR_UNSUPPORTED            # capacity above 1024
+    assert decw(_desc(lib), cap=-1) == E.TQ_ERR_INVALID_ARG
+    assert decw(_desc(lib), wk=None) == E.TQ_ERR_INVALID_ARG             # window without arrays
+    assert decw(_desc(lib), wl=None) == E.TQ_ERR_INVALID_ARG
+    assert decw(_desc(lib), cap=0, wk=None, wl=None, B=0) == E.TQ_OK     # no window, nothing to do
+    assert decw(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
+
     dq = lambda d, n=3: so.tq_dequantize_rows(ctypes.byref(d), P, 10, P, n, P, P, None)
     assert dq(_desc(lib, head_dim=256)) == E.TQ_ERR_UNSUPPORTED
     assert dq(_desc(lib), n=-2) == E.TQ_ERR_INVALID_ARG
