@@ -31,6 +31,7 @@ namespace {
 using namespace tqd;
 
 constexpr int kNW = 4;          // waves per split workgroup
+constexpr float kSent = -1.0e30f;  // finite stand-in for minus infinity in the running maxima
 constexpr int kPrefetch = 4;    // page-row steps kept in flight per wave
 constexpr int kMaxBtLds = 1024; // block-table entries staged in LDS per split
 
@@ -48,6 +49,9 @@ struct DecodeArgs {
   int max_blocks;
   const int32_t* seq_lens;
   int chunk, max_split, n_units, bs_shift;
+  int part_stride;   // partials per (sequence, kv head): max_split packed splits, then row chunks
+  int row_chunks;    // fp16-row chunks launched per (sequence, kv head)
+  int rows_blocks;   // workgroups of fp16-row chunks at the front of the split grid
   const uint16_t* sink_k;
   const uint16_t* sink_v;
   int n_sink;
@@ -56,7 +60,7 @@ struct DecodeArgs {
   const int32_t* win_lens;   // [B]: valid window rows, the last positions of the sequence
   int win_cap;
   float* out;
-  float* partials;   // [B][Hkv][max_split][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
+  float* partials;   // [B][Hkv][part_stride][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
 };
 
 // Splits cover absolute positions [split * chunk, (split + 1) * chunk) of a sequence, up to the
@@ -71,6 +75,183 @@ __device__ __forceinline__ int window_len(const DecodeArgs& a, int b, int seq_le
   if (a.win_lens == nullptr) return 0;
   return max(0, min(a.win_lens[b], min(a.win_cap, seq_len - ns)));
 }
+
+// fp16 rows (sinks, then hot-window rows) of a sequence, kRowChunk at a time.
+constexpr int kRowChunk = 128;
+constexpr int kMaxRowChunks = (TQ_MAX_SINKS + TQ_MAX_WINDOW + kRowChunk - 1) / kRowChunk;
+
+__device__ __forceinline__ int fp16_rows(const DecodeArgs& a, int b, int seq_len) {
+  const int ns = min(a.n_sink, seq_len);
+  return ns + window_len(a, b, seq_len, ns);
+}
+
+// Element offset of fp16 row i of (sequence b, kv head h): sink i, or window row i - ns.
+template <int D>
+__device__ __forceinline__ const uint16_t* fp16_row(const DecodeArgs& a, bool value, int b, int h,
+                                                    int ns, int i) {
+  if (i < ns) return (value ? a.sink_v : a.sink_k) + (((int64_t)b * a.n_sink + i) * a.L.Hkv + h) * D;
+  return (value ? a.win_v : a.win_k) + (((int64_t)b * a.win_cap + (i - ns)) * a.L.Hkv + h) * D;
+}
+
+// One workgroup per (sequence, kv head, chunk of kRowChunk fp16 rows): a split partial of the same
+// form as the packed splits' (maximum, sum, accumulator), the value sum u rotated into the frame
+// of the packed accumulators once: R u = D^(-1/2) H (s * u) (R is linear, so the merge's R^T
+// returns u).  LPH lanes of one DPP row hold a row, 8 coordinates each; every K and V row of the
+// chunk is loaded at the start.  These workgroups lead the split kernels' grids (see fp16_chunk),
+// so they run alongside the packed splits.
+template <int D, int GMAX>
+__device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk) {
+  const TqLayer& L = a.L;
+  const int G = L.G;
+  const int rc = blk % a.row_chunks;
+  const int bh = blk / a.row_chunks;
+  const int h = bh % L.Hkv, b = bh / L.Hkv;
+  const int seq_len = a.seq_lens[b];
+  const int ns = min(a.n_sink, seq_len);
+  const int r0 = rc * kRowChunk;
+  const int nr = min(fp16_rows(a, b, seq_len) - r0, kRowChunk);
+  if (nr <= 0) return;  // the merge reads the chunks below ceil(rows / kRowChunk) only
+  constexpr int LPH = D / 8;      // lanes per row
+  constexpr int RPW = 64 / LPH;   // rows per wave step
+  constexpr int NP = kWG / LPH;   // value-sum parts
+  constexpr int UK = kRowChunk / (kNW * RPW);  // key rows per lane group
+  constexpr int UV = kRowChunk / NP;           // value rows per part
+  __shared__ float s_s[GMAX][kRowChunk];
+  __shared__ float s_m[GMAX];
+  __shared__ float s_red[kNW][GMAX][D + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane % LPH, slot = lane / LPH;
+  const int part = tid / LPH;
+
+  uint4 kraw[UK], vraw[UV];  // all rows in flight together
+#pragma unroll
+  for (int u = 0; u < UK; ++u) {
+    const int r = (u * kNW + wave) * RPW + slot;
+    if (r < nr) kraw[u] = *reinterpret_cast<const uint4*>(fp16_row<D>(a, false, b, h, ns, r0 + r) + 8 * j);
+  }
+#pragma unroll
+  for (int u = 0; u < UV; ++u) {
+    const int r = part + u * NP;
+    if (r < nr) vraw[u] = *reinterpret_cast<const uint4*>(fp16_row<D>(a, true, b, h, ns, r0 + r) + 8 * j);
+  }
+  auto unpack = [](const uint4& w, float (&x)[8]) {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = half_bits_to_float(d[i] & 0xffffu);
+      x[2 * i + 1] = half_bits_to_float(d[i] >> 16);
+    }
+  };
+  {  // scores, log2 domain
+    float qv[GMAX][8];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g < G) load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, qv[g]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][e] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int r = (u * kNW + wave) * RPW + slot;
+      if (r < nr) {
+        float kx[8];
+        unpack(kraw[u], kx);
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+          float d = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(qv[g][e], kx[e], d);
+          d = group_sum<LPH>(d);
+          if (g < G && j == 0) s_s[g][r] = d * a.sink_scale;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 32 * GMAX) {  // maximum per head, 32 lanes each
+    const int g = tid >> 5;
+    float m = kSent;
+    if (g < G)
+      for (int r = tid & 31; r < nr; r += 32) m = fmaxf(m, s_s[g][r]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+    if ((tid & 31) == 0) s_m[g] = m;
+  }
+  __syncthreads();
+
+  // value sums: thread (part, j) takes rows part, part + NP, ... and coordinates 8 j .. 8 j + 7 of
+  // every head
+  float o[GMAX][8], ls[GMAX];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    ls[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < UV; ++u) {
+    const int r = part + u * NP;
+    if (r < nr) {
+      float v[8];
+      unpack(vraw[u], v);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+          const float w = __builtin_amdgcn_exp2f(s_s[g][r] - s_m[g]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[g][e] = fmaf(w, v[e], o[g][e]);
+          ls[g] += w;
+        }
+      }
+    }
+  }
+  // parts of a wave by lane exchanges, then the waves through LDS
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g < G) {
+#pragma unroll
+      for (int m = LPH; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] += __shfl_xor(o[g][e], m);
+        ls[g] += __shfl_xor(ls[g], m);
+      }
+      if (lane < LPH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_red[wave][g][8 * j + e] = o[g][e];
+        if (j == 0) s_red[wave][g][D] = ls[g];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < LPH * G) {  // R u for head g, written as the chunk's partial
+    const int g = tid / LPH;
+    float x[8];
+    float l = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    for (int w = 0; w < kNW; ++w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] += s_red[w][g][8 * j + e];
+      l += s_red[w][g][D];
+    }
+    const uint32_t sb = sign_byte(L.signs, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((sb >> e) & 1u) x[e] = -x[e];
+    wht_row8_dpp<LPH>(x, j);
+    float* part_out = a.partials + ((int64_t)bh * a.part_stride + a.max_split + rc) * G * (D + 2) +
+                      (int64_t)g * (D + 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part_out[2 + 8 * j + e] = x[e] * a.rsqrt_d;
+    if (j == 0) {
+      part_out[0] = s_m[g];
+      part_out[1] = l;
+    }
+  }
+}
+
 
 // Raw page data of one step for one lane.
 template <int NBK, int NBV>
@@ -92,8 +273,12 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
   const int G = L.G;
 
+  if ((int)blockIdx.x < a.rows_blocks) {  // fp16-row chunks lead the grid
+    fp16_chunk<D, GMAX>(a, blockIdx.x);
+    return;
+  }
   // (sequence, split) units with equal index modulo 8 share an XCD across all kv heads
-  const int lin = blockIdx.x;
+  const int lin = blockIdx.x - a.rows_blocks;
   const int xcd = lin & 7;
   const int rest = lin >> 3;
   const int h = rest % L.Hkv;
@@ -271,7 +456,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 
   // Merge the waves and publish this split's partial (m, l, acc[D]).
   const int64_t bh = (int64_t)b * L.Hkv + h;
-  float* part = a.partials + (bh * a.max_split + split) * (int64_t)G * (D + 2);
+  float* part = a.partials + (bh * a.part_stride + split) * (int64_t)G * (D + 2);
   for (int i = threadIdx.x; i < G * (D + 2); i += kWG) {
     const int g = i / (D + 2), d = i % (D + 2);
     float M = -INFINITY;
@@ -324,7 +509,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLutShift = 8;    // centroid tables hold c * 2^8
 constexpr int kWShift = 15;     // weights enter the PV product as w * 2^15
-constexpr float kSent = -1.0e30f;  // finite stand-in for minus infinity in the running maxima
 
 // Formats the matrix-core kernel implements (everything else runs on tq_decode_split_kernel).
 constexpr bool mfma_format(int D, int KB, int VB) {
@@ -471,7 +655,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
   const int G = L.G;
 
-  const int lin = blockIdx.x;
+  if constexpr (!G8) {  // fp16-row chunks lead the grid (with 8 query heads: their own kernel)
+    if ((int)blockIdx.x < a.rows_blocks) {
+      fp16_chunk<D, 4>(a, blockIdx.x);
+      return;
+    }
+  }
+  const int lin = blockIdx.x - a.rows_blocks;
   const int xcd = lin & 7;
   const int rest = lin >> 3;
   const int h = rest % L.Hkv;
@@ -852,7 +1042,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t bh = (int64_t)b * L.Hkv + h;
-  float* part = a.partials + (bh * a.max_split + split) * (int64_t)G * (D + 2);
+  float* part = a.partials + (bh * a.part_stride + split) * (int64_t)G * (D + 2);
   for (int i = tid; i < G * (D + 2); i += kWG) {
     const int g = i / (D + 2), d = i % (D + 2);
     float M = kSent;
@@ -871,8 +1061,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (sequence, kv head): merge the splits with the fp16 rows (sinks and hot
-// window), rotate back, normalise.
+// One workgroup per (sequence, kv head): merge the packed splits and the fp16-row chunks, rotate
+// back, normalise.
 template <int D, int GMAX>
 __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
@@ -880,89 +1070,36 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const int h = blockIdx.x % L.Hkv;
   const int b = blockIdx.x / L.Hkv;
   const int seq_len = a.seq_lens[b];
-  const int ns = min(a.n_sink, seq_len);
-  const int nw = window_len(a, b, seq_len, ns);
-  const int nf = ns + nw;  // fp16 rows: sinks 0 .. ns - 1, then window rows
-  const int packed_end = seq_len - nw;
-  const int nsplit = num_splits(packed_end, a.chunk);
+  const int nf = fp16_rows(a, b, seq_len);
+  const int nsplit = num_splits(seq_len - (nf - min(a.n_sink, seq_len)), a.chunk);
+  const int nrc = (nf + kRowChunk - 1) / kRowChunk;
+  const int nparts = nsplit + nrc;
   float* outp = a.out + ((int64_t)b * L.Hq + h * G) * D;
   if (seq_len == 0) {
     for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
     return;
   }
-  constexpr int FMAX = TQ_MAX_SINKS + TQ_MAX_WINDOW;
-  constexpr int LPH = D / 8;                 // lanes per row, 8 coordinates each
-  __shared__ float s_acc[GMAX * D];          // merged rotated accumulators
-  __shared__ float s_ml[2 * GMAX];           // max, sum
-  __shared__ float s_fmax[GMAX], s_fsum[GMAX];
-  __shared__ float s_f[GMAX * FMAX];         // scores of the fp16 rows, log2 domain
-  __shared__ float s_fv[GMAX][D];            // weighted sums of the fp16 value rows
-  __shared__ float s_red[(kWG / LPH) * (D + 1)];  // per (row part, head): partial sums
+  __shared__ float s_acc[GMAX * D];  // merged rotated accumulators
+  __shared__ float s_ml[2 * GMAX];   // max, sum
 
-  auto krow = [&](int i) {  // key / value row i of the fp16 segment
-    return i < ns ? (((int64_t)b * a.n_sink + i) * L.Hkv + h) * D
-                  : (((int64_t)b * a.win_cap + (i - ns)) * L.Hkv + h) * D;
-  };
-  auto kptr = [&](int i) { return (i < ns ? a.sink_k : a.win_k) + krow(i); };
-  auto vptr = [&](int i) { return (i < ns ? a.sink_v : a.win_v) + krow(i); };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int j = lane % LPH;      // coordinates 8 j .. 8 j + 7
-  const int slot = lane / LPH;   // row slot within the wave
-  constexpr int RPW = 64 / LPH;  // rows per wave step
-  // Scores of the fp16 rows: each row is held by LPH lanes of one DPP row (or half row).
-  if (nf > 0) {
-    float qv[GMAX][8];
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g < G) load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, qv[g]);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[g][e] = 0.0f;
-    }
-    for (int i = wave * RPW + slot; i < nf; i += kNW * RPW) {
-      float kx[8];
-      load8_f16(kptr(i) + 8 * j, kx);
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        float d = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[g][e], kx[e], d);
-        d = group_sum<LPH>(d);
-        if (g < G && j == 0) s_f[g * FMAX + i] = d * a.sink_scale;
-      }
-    }
-  }
-  __syncthreads();
-  // Largest fp16-row score per head: 32 lanes per head.
-  if (tid < 32 * GMAX) {
-    const int g = tid >> 5;
-    float m = kSent;
-    if (g < G)
-      for (int i = tid & 31; i < nf; i += 32) m = fmaxf(m, s_f[g * FMAX + i]);
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-    if ((tid & 31) == 0) s_fmax[g] = m;
-  }
-  __syncthreads();
-
-  // Online log-sum-exp merge of the splits, one (head, coordinate) per thread, starting from the
-  // fp16 rows' maximum.  Partials are loaded eight splits at a time so their loads are in flight
+  // Online log-sum-exp merge of the partials (packed splits, then fp16-row chunks), one (head,
+  // coordinate) per thread.  Partials are loaded eight at a time so their loads are in flight
   // together.  Empty partials carry a maximum of -inf or kSent and contribute exp2(. - M) = 0
   // once a real score is in M.
   const int64_t bh = (int64_t)b * L.Hkv + h;
-  const float* pb = a.partials + bh * a.max_split * (int64_t)G * (D + 2);
-  for (int i = tid; i < G * D; i += kWG) {
+  const float* pb = a.partials + bh * a.part_stride * (int64_t)G * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += kWG) {
     const int g = i / D, d = i % D;
-    float M = s_fmax[g];
+    float M = kSent;
     float l = 0.0f, acc = 0.0f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    for (int s0 = 0; s0 < nparts; s0 += 8) {
       float ms[8], ls[8], as[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const bool in = s0 + k < nsplit;
-        const float* e = pb + ((int64_t)(in ? s0 + k : 0) * G + g) * (D + 2);
+        const int pi = s0 + k;
+        const bool in = pi < nparts;
+        const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
+        const float* e = pb + ((int64_t)idx * G + g) * (D + 2);
         ms[k] = in ? e[0] : -INFINITY;
         ls[k] = in ? e[1] : 0.0f;
         as[k] = in ? e[2 + d] : 0.0f;
@@ -984,66 +1121,22 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Weighted sums of the fp16 value rows: thread (part, g, j) takes rows part, part + NP, ... of
-  // head g, coordinates 8 j .. 8 j + 7; the parts are added up below.
-  constexpr int TPH = LPH;                     // threads per head and part
-  const int np = kWG / (TPH * G);              // parts
-  if (nf > 0) {
-    const int part = tid / (TPH * G);
-    const int g = (tid / TPH) % G;
-    float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    float ls = 0.0f;
-    if (part < np) {
-      const float M = s_ml[g];
-      for (int i = part; i < nf; i += np) {
-        const float w = __builtin_amdgcn_exp2f(s_f[g * FMAX + i] - M);
-        float v[8];
-        load8_f16(vptr(i) + 8 * j, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, v[e], o[e]);
-        ls += w;
-      }
-    }
-    // sum over parts: first to LDS, then part 0 adds
-    __syncthreads();
-    float* red = s_red;
-    if (part < np) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[(part * G + g) * (D + 1) + 8 * j + e] = o[e];
-      if (j == 0) red[(part * G + g) * (D + 1) + D] = ls;
-    }
-    __syncthreads();
-    if (tid < TPH * G) {
-      for (int pp = 1; pp < np; ++pp) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += red[(pp * G + g) * (D + 1) + 8 * j + e];
-        ls += red[(pp * G + g) * (D + 1) + D];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_fv[g][8 * j + e] = o[e];
-      if (j == 0) s_fsum[g] = ls;
-    }
-  } else if (tid < GMAX) {
-    s_fsum[tid] = 0.0f;
-  }
-  __syncthreads();
-
-  // R^T a = D^(-1/2) diag(s) H a, plus the fp16 rows' values, divided by the sum: D/8 lanes of
-  // one DPP row per head, 8 coordinates per lane.
-  if (tid < LPH * G) {
-    const int g = tid / LPH;
+  // R^T a = D^(-1/2) diag(s) H a, divided by the sum: D/8 lanes of one DPP row per head, 8
+  // coordinates per lane.
+  constexpr int LPH = D / 8;
+  if (threadIdx.x < LPH * G) {
+    const int g = threadIdx.x / LPH, j = threadIdx.x % LPH;
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s_acc[g * D + 8 * j + e];
     wht_row8_dpp<LPH>(x, j);
     const uint32_t sb = sign_byte(L.signs, j);
-    const float inv_l = 1.0f / (s_ml[GMAX + g] + s_fsum[g]);
+    const float inv_l = 1.0f / s_ml[GMAX + g];
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       o[e] = x[e] * a.rsqrt_d;
       if ((sb >> e) & 1u) o[e] = -o[e];
-      if (nf > 0) o[e] += s_fv[g][8 * j + e];
     }
     float4* o4 = reinterpret_cast<float4*>(outp + g * D + 8 * j);
     o4[0] = make_float4(o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l);
@@ -1051,14 +1144,32 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+// fp16-row chunks on their own (for the split kernel whose LDS budget leaves no room for them).
+template <int D, int GMAX>
+__global__ __launch_bounds__(kWG) void tq_decode_rows_kernel(DecodeArgs a) {
+  fp16_chunk<D, GMAX>(a, blockIdx.x);
+}
+
 template <int D, int GMAX>
 void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
   hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(kWG), 0, st, a);
 }
 
-// Split kernel for one format and query-group bound, then the merge.
+// Split kernel for one format and query-group bound (the fp16-row chunks at the front of its grid,
+// or in a kernel of their own before it), then the merge.  `grid` holds the packed splits only;
+// a.rows_blocks is the number of fp16-row chunk workgroups.
 template <int D, int KB, int VB, int GMAX>
-void launch_t(const DecodeArgs& a, dim3 grid, dim3 mgrid, hipStream_t st) {
+void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
+  DecodeArgs a = a0;
+  constexpr bool separate_rows = mfma_format(D, KB, VB) && GMAX > 4;
+  dim3 grid = sgrid;
+  if (separate_rows) {
+    if (a.rows_blocks > 0)
+      hipLaunchKernelGGL((tq_decode_rows_kernel<D, GMAX>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
+    a.rows_blocks = 0;
+  } else {
+    grid.x += a.rows_blocks;
+  }
   if constexpr (mfma_format(D, KB, VB)) {
     constexpr bool G8 = GMAX > 4;
     if (a.L.bs % 16 == 0)
@@ -1136,7 +1247,8 @@ TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
 
 size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
   const size_t bh = (size_t)num_seqs * L.Hkv;
-  return bh * (size_t)sp.max_split * L.G * (L.D + 2) * sizeof(float);
+  // packed splits, then room for the fp16-row chunks of the largest sink count and window
+  return bh * (size_t)(sp.max_split + kMaxRowChunks) * L.G * (L.D + 2) * sizeof(float);
 }
 
 int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
@@ -1158,6 +1270,9 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.seq_lens = seq_lens;
   a.chunk = sp.chunk;
   a.max_split = sp.max_split;
+  a.part_stride = sp.max_split + kMaxRowChunks;
+  a.row_chunks = (n_sink + win_cap + kRowChunk - 1) / kRowChunk;
+  a.rows_blocks = num_seqs * L.Hkv * a.row_chunks;
   a.n_units = num_seqs * sp.max_split;
   a.bs_shift = ilog2_exact(L.bs);
   a.sink_k = (const uint16_t*)sink_k;
@@ -1170,7 +1285,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.out = out;
   a.partials = (float*)workspace;
   const long groups = (a.n_units + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * L.Hkv));
+  const dim3 grid((unsigned)(groups * 8 * L.Hkv));  // packed splits; launch_t adds the row chunks
   const dim3 mgrid((unsigned)(num_seqs * L.Hkv));
   if (L.D == 128) launch_k<128>(a, grid, mgrid, st);
   else launch_k<64>(a, grid, mgrid, st);
