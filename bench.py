@@ -45,6 +45,7 @@ def describe(w):
 class LayerState:
     def __init__(self, fmt, pages, num_blocks):
         self.fmt, self.pages, self.num_blocks = fmt, pages, num_blocks
+        self.win_k = self.win_v = None  # fp16 hot window [B, W, H_kv, D] (with --hot-window)
 
 
 def context_slots(w, bt_np, lens, wl):
@@ -90,7 +91,7 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
     return new_k, new_v
 
 
-def setup(w, torch, tq, wl, n_steps_total):
+def setup(w, torch, tq, wl, n_steps_total, hot_window=0):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -114,7 +115,13 @@ def setup(w, torch, tq, wl, n_steps_total):
         if l > 0:  # layer 0 includes first-launch costs
             bulk_ms.append(t_layer)
         bulk_rows = n_ctx * H
-        layers.append(LayerState(fmt, pages, num_blocks))
+        st = LayerState(fmt, pages, num_blocks)
+        if hot_window:  # the last hot_window positions as fp16 rows (their page slots are ignored)
+            g = wl.generator(w.seed * 7919 + l, dev)
+            shape = (B, hot_window, H, D)
+            st.win_k = wl.kv_values(w, l, B * hot_window, "k", dev, gen=g).reshape(shape)
+            st.win_v = wl.kv_values(w, l, B * hot_window, "v", dev, gen=g).reshape(shape)
+        layers.append(st)
     torch.cuda.synchronize()
     # per-step inputs: queries and one new K/V token per sequence and layer
     qs = [wl.queries(w, l, 0, dev) for l in range(w.layers)]
@@ -125,7 +132,10 @@ def setup(w, torch, tq, wl, n_steps_total):
     for f in fmts.values():
         assert tq.tq_decode_workspace_bytes(f.desc, B, max_len) <= ws.numel()
     out = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device=dev)
-    return dict(lens=lens, bt=bt, seq_lens=seq_lens, new_slots=new_slots, layers=layers, qs=qs,
+    ns = np.minimum(lens, w.n_sink)
+    win_lens = np.minimum(hot_window, lens - ns).astype(np.int32)
+    return dict(hot_window=hot_window, win_lens_np=win_lens, win_lens=torch.from_numpy(win_lens).to(dev),
+                lens=lens, bt=bt, seq_lens=seq_lens, new_slots=new_slots, layers=layers, qs=qs,
                 new_k=new_k, new_v=new_v, sink_k=sink_k, sink_v=sink_v, max_len=max_len, ws=ws,
                 out=out, bulk_ms=bulk_ms, bulk_rows=bulk_rows, n_ctx=n_ctx, num_blocks=num_blocks)
 
@@ -134,26 +144,40 @@ def run_step(w, S, tq, step, ev=None):
     for l, L in enumerate(S["layers"]):
         if ev is not None:
             ev["a0"][l].record()
+        # with a hot window the quantized token is the one leaving the window, and the new token
+        # takes its row in the window (a ring: row step % W)
         tq.tq_quantize_append(L.fmt.desc, S["new_k"][step, l], S["new_v"][step, l], S["new_slots"],
                               L.pages, L.num_blocks)
+        if L.win_k is not None:
+            r = step % S["hot_window"]
+            L.win_k[:, r].copy_(S["new_k"][step, l])
+            L.win_v[:, r].copy_(S["new_v"][step, l])
         if ev is not None:
             ev["a1"][l].record()
-        tq.tq_paged_decode_attention(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
-                                     S["seq_lens"], S["max_len"], S["out"], S["ws"],
-                                     S["sink_k"], S["sink_v"], w.n_sink)
+        if L.win_k is None:
+            tq.tq_paged_decode_attention(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
+                                         S["seq_lens"], S["max_len"], S["out"], S["ws"],
+                                         S["sink_k"], S["sink_v"], w.n_sink)
+        else:
+            tq.tq_paged_decode_attention_window(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
+                                                S["seq_lens"], S["max_len"], S["out"], S["ws"],
+                                                L.win_k, L.win_v, S["win_lens"], S["sink_k"],
+                                                S["sink_v"], w.n_sink)
         if ev is not None:
             ev["d1"][l].record()
 
 
-def algorithmic_bytes(w, lens, tq):
-    """Bytes the decode of one layer must move, and the bytes of one bulk-fill row pair."""
+def algorithmic_bytes(w, lens, tq, win_lens=None):
+    """Bytes the decode of one layer must move (with a hot window of win_lens[b] fp16 rows)."""
     B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
+    win = np.zeros_like(lens) if win_lens is None else np.asarray(win_lens)
     per_layer = []
     for l in range(w.layers):
         kb, vb = w.bits(l)
         sb = tq.tq_slot_bytes(D, kb, vb)
-        page_tok = np.maximum(lens - w.n_sink, 0)
+        page_tok = np.maximum(lens - w.n_sink - win, 0)
         b = int(page_tok.sum()) * H * sb                                  # packed slots
+        b += int(win.sum()) * H * D * 2 * 2                               # fp16 window rows
         b += int(np.sum((lens + w.block_size - 1) // w.block_size)) * 4   # block tables
         b += B * w.num_q_heads * D * 2 + B * w.num_q_heads * D * 4 + B * 4  # q, out, seq_lens
         b += B * w.n_sink * H * D * 2 * 2                                 # fp16 sinks
@@ -258,6 +282,9 @@ def main():
     ap.add_argument("--workload", default="llama3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--hot-window", type=int, default=0, metavar="W",
+                    help="keep the last W tokens of each sequence as fp16 rows (decode through "
+                         "tq_paged_decode_attention_window)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -278,7 +305,7 @@ def main():
     log(f"workload {describe(w)}")
     total = args.warmup + args.steps
     t0 = time.time()
-    S = setup(w, torch, tq, wl, total)
+    S = setup(w, torch, tq, wl, total, args.hot_window)
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -308,7 +335,7 @@ def main():
     lens = S["lens"]
     kv_tokens_step = int(lens.sum()) * w.layers
     value = kv_tokens_step / (ms_per_step / 1e3)
-    per_layer_bytes = algorithmic_bytes(w, lens, tq)
+    per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None)
     layer_ids = np.arange(n) % w.layers
     dec_bytes = np.array([per_layer_bytes[i] for i in layer_ids], np.float64)
     achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
@@ -328,10 +355,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": describe(w), "kv_tokens_per_layer": int(lens.sum()),
+        "config": {"workload": describe(w) + (f", fp16 hot window of {args.hot_window} tokens"
+                                             if args.hot_window else ""),
+                   "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if args.hot_window else recorded_traffic(w),
                      "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},

@@ -9,6 +9,9 @@ oracle from the same fp16 rows:
     output of the query heads of that kv head must match the oracle's dense attention to the
     attention tolerance.
 The rest of the batch still runs, so the grid, split geometry and workspace are the benchmark's.
+One case adds a hot window (bench.py --hot-window): the last W positions of every sequence also
+come from fp16 rows (the sampled sequences' own rows, random rows elsewhere) and the decode runs
+through tq_paged_decode_attention_window.
 """
 
 from __future__ import annotations
@@ -41,15 +44,17 @@ def _pick(w, lens, which):
 
 
 CASES = [
-    ("llama3-8b", 1, (0, 13)),
-    ("mistral-7b", 2, (1,)),
-    ("ragged", 5, "extremes"),
-    ("qwen2.5-0.5b", 7, (0, 5)),
+    ("llama3-8b", 1, (0, 13), 0),
+    ("mistral-7b", 2, (1,), 0),
+    ("ragged", 5, "extremes", 0),
+    ("qwen2.5-0.5b", 7, (0, 5), 0),
+    ("llama3-8b", 3, (4,), 512),
 ]
 
 
-@pytest.mark.parametrize("name,layer,which", CASES, ids=[f"{c[0]}-L{c[1]}" for c in CASES])
-def test_full_size_sampled(name, layer, which):
+@pytest.mark.parametrize("name,layer,which,window", CASES,
+                         ids=[f"{c[0]}-L{c[1]}" + (f"-W{c[3]}" if c[3] else "") for c in CASES])
+def test_full_size_sampled(name, layer, which, window):
     import torch
     import packed_decode_attention_amd as tq
     from packed_decode_attention_amd import workloads as wl
@@ -113,16 +118,30 @@ def test_full_size_sampled(name, layer, which):
               flush=True)
         # the oracle's bytes into the GPU pages of this sequence and kv head
         flat[slots, hh] = torch.from_numpy(ref_rows).cuda()
-        refs[b] = (ref, bt1, L)
+        refs[b] = (ref, bt1, L, k, v)
 
     q = wl.queries(w, layer, 0, "cuda")
     sink_k, sink_v = wl.sinks(w, 0, "cuda")
     max_len = int(lens.max())
     ws = fmt.new_workspace(B, max_len)
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    tq.tq_paged_decode_attention(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
-                                 torch.from_numpy(lens).cuda(), max_len, out, ws, sink_k, sink_v,
-                                 w.n_sink)
+    win_lens = np.minimum(window, lens - np.minimum(lens, w.n_sink)).astype(np.int32)
+    if window:
+        g = torch.Generator(device="cuda").manual_seed(99)
+        win_k = torch.randn((B, window, H, D), generator=g, device="cuda").half()
+        win_v = torch.randn((B, window, H, D), generator=g, device="cuda").half()
+        for b in seqs:  # the sampled sequences' own last rows, in reverse order
+            _, _, L, k, v = refs[b]
+            nw = int(win_lens[b])
+            win_k[b, :nw, heads[b]] = torch.from_numpy(k[L - nw:L, 0][::-1].copy()).cuda()
+            win_v[b, :nw, heads[b]] = torch.from_numpy(v[L - nw:L, 0][::-1].copy()).cuda()
+        tq.tq_paged_decode_attention_window(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
+                                            torch.from_numpy(lens).cuda(), max_len, out, ws, win_k, win_v,
+                                            torch.from_numpy(win_lens).cuda(), sink_k, sink_v, w.n_sink)
+    else:
+        tq.tq_paged_decode_attention(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
+                                     torch.from_numpy(lens).cuda(), max_len, out, ws, sink_k, sink_v,
+                                     w.n_sink)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got)), "non-finite output in the batch"
@@ -131,12 +150,14 @@ def test_full_size_sampled(name, layer, which):
     skn = None if sink_k is None else sink_k.cpu().numpy()
     svn = None if sink_v is None else sink_v.cpu().numpy()
     for b in seqs:
-        ref, bt1, L = refs[b]
+        ref, bt1, L, k, v = refs[b]
         hh = heads[b]
         qh = slice(hh * G, (hh + 1) * G)  # the query heads that read kv head hh
+        nw = int(win_lens[b])
+        wkw = dict(win_k16=k[L - nw:L][None], win_v16=v[L - nw:L][None], win_lens=np.array([nw])) if window else {}
         want = oatt.decode_attention(qn[b:b + 1, qh], ref, bt1, np.array([L], np.int32), layer_dict, kc, vc,
                                      None if skn is None else skn[b:b + 1, :, hh:hh + 1],
-                                     None if svn is None else svn[b:b + 1, :, hh:hh + 1], w.n_sink)
+                                     None if svn is None else svn[b:b + 1, :, hh:hh + 1], w.n_sink, **wkw)
         max_abs, rel = check_attention(got[b:b + 1, qh], want)
         print(f"[fullsize]   seq {b} kv head {hh}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}",
               flush=True)
