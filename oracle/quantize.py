@@ -27,6 +27,11 @@ Readings taken where the pages are silent (each is also listed in the design not
   slot_bytes and a larger slot stride are zero.
 * Dequantized row (bit-exact route): c_hat_i = c[idx_i] (fp32); z = H c_hat exactly (fp64 is
   exact here, asserted); g = fp32(n * fp32(1/sqrt(D))); x_hat_i = s_i * fp32(fp32(z_i) * g).
+* Norm correction (format flag; tq-kv, "How It Works": "Lloyd-Max codebook + norm correction",
+  output "packed indices + corrected norm"): the stored norm is n' = n / ||c_hat||_2, so the
+  dequantized row n' R^T c_hat keeps the input row's L2 norm.  ||c_hat||^2 is the stride-halving
+  fp32 tree (as for the norm, over rotated coordinates) of fp32(c_hat_i^2), then a correctly
+  rounded fp32 square root and a correctly rounded fp32 division; a zero norm stays 0.
 """
 
 from __future__ import annotations
@@ -89,11 +94,34 @@ def indices_for(u: np.ndarray, boundaries32: np.ndarray):
     return idx, tie
 
 
-def quantize_rows(x16: np.ndarray, boundaries32: np.ndarray, seed: int):
-    """Quantize fp16 rows [..., D]: returns (idx int64 [..., D], norm fp32 [...], tie bool [..., D])."""
+def _tree_sum32(sq32: np.ndarray) -> np.ndarray:
+    """Stride-halving fp32 tree over the last axis: pairs (i, i + D/2) first, then D/4, ..."""
+    sq = np.asarray(sq32, dtype=np.float32)
+    h = sq.shape[-1] // 2
+    while h >= 1:
+        sq = (sq[..., :h] + sq[..., h:2 * h]).astype(np.float32)
+        h //= 2
+    return sq[..., 0]
+
+
+def corrected_norm(n32: np.ndarray, idx: np.ndarray, centroids32: np.ndarray) -> np.ndarray:
+    """Norm correction: n' = fp32(n / fp32(sqrt(tree(fp32(c[idx]^2))))), 0 where n == 0."""
+    c = np.asarray(centroids32, dtype=np.float32)[np.asarray(idx)]
+    r = np.sqrt(_tree_sum32((c * c).astype(np.float32))).astype(np.float32)
+    n = np.asarray(n32, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (n / r).astype(np.float32)
+    return np.where(n > 0, q, np.float32(0)).astype(np.float32)
+
+
+def quantize_rows(x16: np.ndarray, boundaries32: np.ndarray, seed: int, centroids32=None):
+    """Quantize fp16 rows [..., D]: returns (idx int64 [..., D], norm fp32 [...], tie bool [..., D]).
+    With centroids32 the stored norm is the corrected one (norm-correction format)."""
     u = rotated_unit(x16, seed)
     idx, tie = indices_for(u, boundaries32)
     n = norm_fp32(x16)
+    if centroids32 is not None:
+        n = corrected_norm(n, idx, centroids32)
     return idx, n, tie
 
 
@@ -133,18 +161,19 @@ def slot_offset(slot: int, h: int, num_kv_heads: int, slot_stride: int) -> int:
 
 def append_rows(pages: np.ndarray, k16: np.ndarray, v16: np.ndarray, slot_mapping: np.ndarray,
                 k_boundaries32, v_boundaries32, k_bits: int, v_bits: int, seed: int,
-                slot_stride: int | None = None):
+                slot_stride: int | None = None, k_centroids32=None, v_centroids32=None):
     """Quantize-on-append: write the K and V regions of every (token, kv head) into its slot.
 
     pages: flat uint8 array of num_blocks * block_size * H_kv * slot_stride bytes (modified).
     k16, v16: [n_tok, H_kv, D] fp16.  slot_mapping: [n_tok]; a negative slot skips the token.
     Returns the tie masks (k_tie, v_tie), shaped [n_tok, H_kv, D].
+    k_centroids32 / v_centroids32 (both or neither): store corrected norms.
     """
     n_tok, H_kv, D = k16.shape
     sb = slot_bytes(D, k_bits, v_bits)
     stride = sb if slot_stride is None else slot_stride
-    k_idx, k_n, k_tie = quantize_rows(k16, k_boundaries32, seed)
-    v_idx, v_n, v_tie = quantize_rows(v16, v_boundaries32, seed)
+    k_idx, k_n, k_tie = quantize_rows(k16, k_boundaries32, seed, k_centroids32)
+    v_idx, v_n, v_tie = quantize_rows(v16, v_boundaries32, seed, v_centroids32)
     for t in range(n_tok):
         s = int(slot_mapping[t])
         if s < 0:
@@ -236,13 +265,14 @@ def unpack_regions(buf: np.ndarray, D: int, bits: int):
 
 
 def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, v_boundaries32,
-                     k_bits: int, v_bits: int, seed: int, slot_stride: int | None = None):
+                     k_bits: int, v_bits: int, seed: int, slot_stride: int | None = None,
+                     k_centroids32=None, v_centroids32=None):
     """append_rows() with the vectorised packer (same bytes; used for larger test cases)."""
     n_tok, H_kv, D = k16.shape
     sb = slot_bytes(D, k_bits, v_bits)
     stride = sb if slot_stride is None else slot_stride
-    k_idx, k_n, k_tie = quantize_rows(k16, k_boundaries32, seed)
-    v_idx, v_n, v_tie = quantize_rows(v16, v_boundaries32, seed)
+    k_idx, k_n, k_tie = quantize_rows(k16, k_boundaries32, seed, k_centroids32)
+    v_idx, v_n, v_tie = quantize_rows(v16, v_boundaries32, seed, v_centroids32)
     rows = np.zeros((n_tok, H_kv, stride), dtype=np.uint8)
     kr = region_bytes(D, k_bits)
     rows[:, :, :kr] = pack_regions(k_idx.reshape(-1, D), k_n.reshape(-1), k_bits).reshape(n_tok, H_kv, kr)

@@ -537,3 +537,43 @@ def test_attention_zero_query_averages_every_segment(rng):
                                wv[0, :w, hk].astype(np.float64)])
         assert rows.shape[0] == L
         np.testing.assert_allclose(o[0, h], rows.mean(0), atol=1e-12)
+
+
+# ============================================================================================
+# Norm correction (tq-kv, "How It Works": "Lloyd-Max codebook + norm correction", output
+# "corrected norm"): the stored norm n / ||c[idx]|| keeps the dequantized row's norm equal to n.
+# ============================================================================================
+@pytest.mark.parametrize("D, bits", [(64, 2), (128, 4), (128, 3), (64, 8)])
+def test_corrected_norm_preserves_the_row_norm(D, bits, rng):
+    cb = codebook.codebook(D, bits)
+    x = (rng.standard_normal((40, D)) * rng.uniform(0.01, 30, (40, 1))).astype(np.float16)
+    x[3] = 0
+    idx, n, _ = quantize.quantize_rows(x, cb.boundaries32, 0)
+    idx2, nc, _ = quantize.quantize_rows(x, cb.boundaries32, 0, cb.centroids32)
+    assert np.array_equal(idx, idx2)
+    xhat = quantize.dequantize_plain(idx, nc, cb.centroids32, 0)          # fp64, n' R^T c
+    got = np.linalg.norm(xhat, axis=-1)
+    exact = np.linalg.norm(x.astype(np.float64), axis=-1)
+    # n is within 2.5 ulp of the exact norm, ||c|| within 2.5 ulp, the division 0.5 ulp
+    ulp = np.spacing(exact.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= 6 * ulp + 1e-300)
+    assert nc[3] == 0 and n[3] == 0
+    # without the correction the dequantized norm is off by the codebook's norm error
+    plain = np.linalg.norm(quantize.dequantize_plain(idx, n, cb.centroids32, 0), axis=-1)
+    assert np.max(np.abs(plain[exact > 0] / exact[exact > 0] - 1)) > 1e-4
+
+
+def test_corrected_norm_by_brute_force(rng):
+    # the fp32 tree and operations written out element by element for one row
+    D = 16
+    c32 = np.sort(rng.standard_normal(4)).astype(np.float32)
+    idx = rng.integers(0, 4, D)
+    n = np.float32(3.25)
+    vals = [np.float32(c32[i]) * np.float32(c32[i]) for i in idx]
+    h = D // 2
+    while h >= 1:
+        vals = [np.float32(vals[i] + vals[i + h]) for i in range(h)]
+        h //= 2
+    want = np.float32(n / np.float32(np.sqrt(vals[0])))
+    got = quantize.corrected_norm(np.array([n]), idx[None], c32)[0]
+    assert got.view(np.uint32) == want.view(np.uint32)
