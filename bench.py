@@ -91,7 +91,7 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
     return new_k, new_v
 
 
-def setup(w, torch, tq, wl, n_steps_total, hot_window=0):
+def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -108,7 +108,8 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0):
     for l in range(w.layers):
         kb, vb = w.bits(l)
         if (kb, vb) not in fmts:
-            fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0)
+            fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0,
+                                            norm_correction=norm_correction)
         fmt = fmts[(kb, vb)]
         pages = fmt.new_pages(num_blocks)
         t_layer = fill_layer(w, l, fmt, pages, ctx_slots, num_blocks, torch, tq, wl)
@@ -285,6 +286,8 @@ def main():
     ap.add_argument("--hot-window", type=int, default=0, metavar="W",
                     help="keep the last W tokens of each sequence as fp16 rows (decode through "
                          "tq_paged_decode_attention_window)")
+    ap.add_argument("--norm-correction", action="store_true",
+                    help="store corrected norms n / ||c[idx]|| (the norm-correction page format)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -305,7 +308,7 @@ def main():
     log(f"workload {describe(w)}")
     total = args.warmup + args.steps
     t0 = time.time()
-    S = setup(w, torch, tq, wl, total, args.hot_window)
+    S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction)
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -356,7 +359,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": describe(w) + (f", fp16 hot window of {args.hot_window} tokens"
-                                             if args.hot_window else ""),
+                                             if args.hot_window else "")
+                               + (", norm-correction format" if args.norm_correction else ""),
                    "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

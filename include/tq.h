@@ -60,6 +60,16 @@ typedef enum tq_codebook_family {
   TQ_CODEBOOK_GAUSSIAN = 1  /* its N(0, 1/D) approximation                                  */
 } tq_codebook_family;
 
+/* Format flags of tq_layer_desc.flags.
+ *   TQ_FLAG_NORM_CORRECTION  (tq-kv, "How It Works": Lloyd-Max codebook + norm correction, output
+ *   "corrected norm") each region stores n / ||c[idx]||_2 instead of n = ||x||_2, so the
+ *   dequantized row n' R^T c[idx] keeps the input row's L2 norm.  ||c[idx]||^2 is summed in fp32
+ *   by the stride-halving tree over the rotated coordinates (pairs i, i + D/2 first) of the
+ *   fp32-rounded squares; the square root and the division are correctly rounded; a zero row
+ *   keeps a zero norm.  Only tq_quantize_append changes: decode and dequantize read the stored
+ *   norm as it is.  Other bits must be 0. */
+#define TQ_FLAG_NORM_CORRECTION 1
+
 /* One layer's format.  K and V may use different bit widths (tiny-turboquant 0.12.0.3,
  * "Current status": q8k-q8v and q8k-int4v policies; TorbuQuant docs, "Current Status": K8/K4 and
  * V8/V4/V3/V2 formats); a model with boundary-layer protection simply uses a different
@@ -72,7 +82,7 @@ typedef struct tq_layer_desc {
   int32_t k_bits;         /* 2, 3, 4 or 8                                                      */
   int32_t v_bits;         /* 2, 3, 4 or 8                                                      */
   int32_t slot_stride;    /* bytes per (token, kv head) slot; 0 means tq_slot_bytes()          */
-  int32_t reserved;       /* must be 0                                                         */
+  int32_t flags;          /* format flags (TQ_FLAG_*), 0 for the plain format                  */
   uint64_t rht_seed;      /* seed of the SplitMix64 sign vector of the rotation                */
   const float* k_centroids;   /* device, 2^k_bits ascending fp32 (tq_build_codebook output) */
   const float* k_boundaries;  /* device, 2^k_bits - 1 ascending fp32                          */

@@ -27,6 +27,8 @@ from ._lib import (  # noqa: F401
     tq_status_str,
 )
 
+TQ_FLAG_NORM_CORRECTION = 1  # tq_layer_desc.flags: stored norms are n / ||c[idx]|| (include/tq.h)
+
 _CODEBOOKS: dict = {}
 
 
@@ -45,11 +47,13 @@ class LayerFormat:
 
     def __init__(self, head_dim: int, num_q_heads: int, num_kv_heads: int, k_bits: int,
                  v_bits: int, block_size: int = 16, rht_seed: int = 0, family: str = "beta",
-                 slot_stride: int = 0, device="cuda", k_codebook=None, v_codebook=None):
+                 slot_stride: int = 0, device="cuda", k_codebook=None, v_codebook=None,
+                 norm_correction: bool = False):
         import torch
         self.head_dim, self.num_q_heads, self.num_kv_heads = head_dim, num_q_heads, num_kv_heads
         self.k_bits, self.v_bits, self.block_size = k_bits, v_bits, block_size
         self.rht_seed, self.family = rht_seed, family
+        self.norm_correction = norm_correction
         self.slot_bytes = tq_slot_bytes(head_dim, k_bits, v_bits)
         self.slot_stride = slot_stride or self.slot_bytes
         kc, kt = k_codebook if k_codebook is not None else host_codebook(head_dim, k_bits, family)
@@ -60,7 +64,7 @@ class LayerFormat:
         self.desc = tq_layer_desc(
             head_dim=head_dim, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
             block_size=block_size, k_bits=k_bits, v_bits=v_bits, slot_stride=slot_stride,
-            reserved=0, rht_seed=rht_seed,
+            flags=TQ_FLAG_NORM_CORRECTION if norm_correction else 0, rht_seed=rht_seed,
             k_centroids=self.k_centroids.data_ptr(), k_boundaries=self.k_boundaries.data_ptr(),
             v_centroids=self.v_centroids.data_ptr(), v_boundaries=self.v_boundaries.data_ptr())
 

@@ -45,7 +45,7 @@ class tq_layer_desc(ctypes.Structure):
         ("k_bits", ctypes.c_int32),
         ("v_bits", ctypes.c_int32),
         ("slot_stride", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("rht_seed", ctypes.c_uint64),
         ("k_centroids", ctypes.c_void_p),
         ("k_boundaries", ctypes.c_void_p),

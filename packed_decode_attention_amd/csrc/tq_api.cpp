@@ -15,7 +15,7 @@ int code_bytes(int D, int bits) { return (D * bits + 7) / 8; }
 // Fill a TqLayer from the public descriptor.  need_q: decode also checks num_q_heads.
 int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   if (d == nullptr) return TQ_ERR_INVALID_ARG;
-  if (d->reserved != 0) return TQ_ERR_INVALID_ARG;
+  if ((d->flags & ~TQ_FLAG_NORM_CORRECTION) != 0) return TQ_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return TQ_ERR_UNSUPPORTED;
   if (!bits_ok(d->k_bits) || !bits_ok(d->v_bits)) return TQ_ERR_UNSUPPORTED;
   if (d->num_kv_heads < 1 || d->block_size < 1) return TQ_ERR_INVALID_ARG;
@@ -45,6 +45,7 @@ int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   L->slot_bytes = sb;
   L->kcode_bytes = code_bytes(d->head_dim, d->k_bits);
   L->vcode_bytes = code_bytes(d->head_dim, d->v_bits);
+  L->norm_corr = (d->flags & TQ_FLAG_NORM_CORRECTION) != 0;
   uint64_t words[2];
   tq_sign_words(d->head_dim, d->rht_seed, words, 2);
   L->signs.w[0] = (uint32_t)words[0];

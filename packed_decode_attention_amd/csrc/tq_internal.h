@@ -25,6 +25,7 @@ struct TqLayer {
   int slot_bytes;      // K region + V region
   int kcode_bytes;     // ceil(D * kb / 8)
   int vcode_bytes;     // ceil(D * vb / 8)
+  int norm_corr;       // 1: the stored norm is n / ||c[idx]|| (norm-correction format)
   TqSigns signs;
   const float *kc, *kt, *vc, *vt;
 };

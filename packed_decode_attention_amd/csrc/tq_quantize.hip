@@ -47,6 +47,12 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // number of boundaries below it and the next boundary times S, so idx = base + (u S >= S t).  u S
 // scales u exactly, so the decision is the comparison of u with the fp32 boundaries.  A codebook
 // whose boundaries are closer than the table allows falls back to a binary search.
+//
+// Norm correction (tq-kv "How It Works": the quantiser's norm-correction stage and the corrected
+// norm of its output record), a format flag: the stored norm is n / ||c[idx]|| so the dequantized
+// row keeps norm n.  ||c[idx]||^2 follows the same tree over the rotated coordinates, on the fp32
+// squares of the chosen centroids: the lane holds one code per block for the same low bits, so the
+// block levels are in-lane again and the rest reuses the norm's swap network.
 // =============================================================================================
 constexpr int kQTabSmall = 130;   // bucket-table entries for codes of up to 4 bits (S <= 64)
 constexpr int kQTabLarge = 2050;  // for 8-bit codes (S <= 1024)
@@ -95,6 +101,26 @@ __device__ __forceinline__ void transpose_groups(uint32_t (&w)[4]) {
   swap16(w[2], w[3]);
 }
 
+// The tree levels of coordinate bits 4 .. 0, given per lane the partial sums p[j] of coordinates
+// with bits 0..2 = j and bits 3, 4 = this lane's g (bits 5, 6 already summed in-lane); the total
+// ends up in every lane of the row.
+__device__ __forceinline__ float tree_lanes(const float (&p)[8]) {
+#pragma clang fp contract(off)
+  // bit 4 (lane bit 5): q[j] = class (g & 1, j + 4 (g >> 1)) summed over bit 4
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = swap_add<32>(p[j], p[j + 4]);
+  // bit 3 (lane bit 4): t[j] = class j + 2 g (bits 0..2) summed over bits 3 and 4
+  const float t0 = swap_add<16>(q[0], q[2]);
+  const float t1 = swap_add<16>(q[1], q[3]);
+  // bit 2: lanes g = 0, 1, 2, 3 hold classes 0, 2, 1, 3 of bits 0..1
+  const float w = swap_add<32>(t0, t1);
+  // bit 1: lanes g < 2 hold class 0 of bit 0, lanes g >= 2 class 1
+  const float y = swap_add<16>(w, w);
+  // bit 0
+  return swap_add<32>(y, y);
+}
+
 // Sum of squares of a row by the stride-halving tree, in every lane of the row (see above).
 template <int NB>
 __device__ __forceinline__ float row_sum_squares(const uint4 (&x)[NB], float zero) {
@@ -113,28 +139,36 @@ __device__ __forceinline__ float row_sum_squares(const uint4 (&x)[NB], float zer
                             __builtin_fmaf(half_of(x[1], j), half_of(x[1], j), zero));
     }
   }
-  // bit 4 (lane bit 5): q[j] = class (g & 1, j + 4 (g >> 1)) summed over bit 4
-  float q[4];
+  return tree_lanes(p);
+}
+
+// The same tree over fp32 values v[b][j] at coordinates 32 b + 8 g + j: squares rounded to fp32.
+template <int NB>
+__device__ __forceinline__ float row_sum_squares_f32(const float (&v)[NB][8]) {
+#pragma clang fp contract(off)
+  float p[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q[j] = swap_add<32>(p[j], p[j + 4]);
-  // bit 3 (lane bit 4): t[j] = class j + 2 g (bits 0..2) summed over bits 3 and 4
-  const float t0 = swap_add<16>(q[0], q[2]);
-  const float t1 = swap_add<16>(q[1], q[3]);
-  // bit 2: lanes g = 0, 1, 2, 3 hold classes 0, 2, 1, 3 of bits 0..1
-  const float w = swap_add<32>(t0, t1);
-  // bit 1: lanes g < 2 hold class 0 of bit 0, lanes g >= 2 class 1
-  const float y = swap_add<16>(w, w);
-  // bit 0
-  return swap_add<32>(y, y);
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (NB == 4) {
+      const float s0 = v[0][j] * v[0][j] + v[2][j] * v[2][j];
+      const float s1 = v[1][j] * v[1][j] + v[3][j] * v[3][j];
+      p[j] = s0 + s1;
+    } else {
+      p[j] = v[0][j] * v[0][j] + v[1][j] * v[1][j];
+    }
+  }
+  return tree_lanes(p);
 }
 
 // One region (K or V, BITS-bit codes) of the wave's 16 rows: norm, rotation, decisions, packing,
 // store.  TABLE: decisions by the bucket table (resolution 2^sh), else by binary search.
-template <int D, int BITS, bool TABLE>
+// NC: norm-correction format (the stored norm is n / ||c[idx]||; s_c holds the centroids).
+template <int D, int BITS, bool TABLE, bool NC>
 __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const uint4 (&A)[D / 32][2],
                                                 float zero, int g, int code_bytes,
                                                 const float* s_t, const uint2* tab, int sh,
-                                                float rsqrt_d, uint8_t* __restrict__ dst) {
+                                                const float* s_c, float rsqrt_d,
+                                                uint8_t* __restrict__ dst) {
   constexpr int NB = D / 32;
   const float n = sqrtf(row_sum_squares<NB>(x, zero));  // correctly rounded
 
@@ -142,6 +176,7 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
   const float inv = n > 0.0f ? (TABLE ? ldexpf(rsqrt_d / n, sh) : rsqrt_d / n) : 0.0f;
   const uint2* tabp = tab + (TABLE ? (1 << sh) + 1 : 0);
   uint32_t code[NB][8];  // code[a][e]: rotated coordinate 32 a + 8 g + e
+  float csq[8];          // NC: the in-lane tree levels (coordinate bits 6, 5) of fp32(c[code]^2)
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     float4_t z[NB];  // z[b][i]: H_32 diag(s) of block b at rotated coordinate 8 g + 4 t + i
@@ -177,7 +212,24 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
           code[a][4 * t + i] = (uint32_t)id;
         }
       }
+      if constexpr (NC) {
+#pragma clang fp contract(off)
+        float cv[NB];
+#pragma unroll
+        for (int a = 0; a < NB; ++a) cv[a] = s_c[code[a][4 * t + i]];
+        if constexpr (NB == 4) {
+          csq[4 * t + i] = (cv[0] * cv[0] + cv[2] * cv[2]) + (cv[1] * cv[1] + cv[3] * cv[3]);
+        } else {
+          csq[4 * t + i] = cv[0] * cv[0] + cv[1] * cv[1];
+        }
+      }
     }
+  }
+  // Stored norm: n, or with norm correction n / ||c[idx]|| (correctly rounded sqrt and division).
+  float n_store = n;
+  if constexpr (NC) {
+    const float r = sqrtf(tree_lanes(csq));
+    n_store = n > 0.0f ? n / r : 0.0f;
   }
 
   // Pack: run a (the lane's 8 codes at rotated coordinates 32 a + 8 g ..) is bytes BITS (4 a + g)
@@ -217,7 +269,7 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
       *reinterpret_cast<uint2*>(run) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
   }
-  if (g == 0) *reinterpret_cast<float*>(dst + code_bytes) = n;
+  if (g == 0) *reinterpret_cast<float*>(dst + code_bytes) = n_store;
 }
 
 // Bucket table of one codebook (see above): entries for buckets k = -(S + 1) .. S, entry
@@ -252,7 +304,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf
 
 // Four waves per SIMD (128 VGPRs): the occupancy that keeps a tile of loads in flight per wave;
 // without the attribute the fallback loop's pressure lowers it for the whole kernel.
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool NC>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void tq_quantize_kernel(
     TqLayer L, float rsqrt_d, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slot_mapping, int64_t n_rows, uint8_t* __restrict__ pages) {
@@ -261,6 +313,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
   __shared__ float s_t[2][256];
   __shared__ int s_sh[2];
   __shared__ float s_gap[kNWQ][2];
+  __shared__ float s_c[2][NC ? 256 : 1];  // centroids (norm-correction format)
   // per wave: K blocks, V blocks, then the low and high dwords of the rows' slot ids
   __shared__ __align__(16) uint8_t s_stage[kNWQ][2 * NB * 1024 + 512];
   extern __shared__ uint2 s_tab[];  // K table (qtab_entries(kb)), then V table
@@ -270,6 +323,10 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
   static_assert(nbk < kWG && nbv < kWG, "one boundary gap per thread");
   for (int i = tid; i < nbk; i += kWG) s_t[0][i] = L.kt[i];
   for (int i = tid; i < nbv; i += kWG) s_t[1][i] = L.vt[i];
+  if constexpr (NC) {
+    for (int i = tid; i <= nbk; i += kWG) s_c[0][i] = L.kc[i];
+    for (int i = tid; i <= nbv; i += kWG) s_c[1][i] = L.vc[i];
+  }
   __syncthreads();
   {  // smallest gap between consecutive boundaries, one gap per thread (at most 254 of them)
     float gk = tid + 1 < nbk ? s_t[0][tid + 1] - s_t[0][tid] : 2.0f;
@@ -380,9 +437,10 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
       for (int i = L.slot_bytes + g; i < L.stride; i += 4) dst[i] = 0;  // padding, before the loads
       if (T + tstep < n_tiles) issue(T + tstep);
 
-      quantize_region<D, KB, kTable>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk, rsqrt_d, dst);
-      quantize_region<D, VB, kTable>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv, rsqrt_d,
-                                     dst + L.kcode_bytes + 4);
+      quantize_region<D, KB, kTable, NC>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk, s_c[0],
+                                         rsqrt_d, dst);
+      quantize_region<D, VB, kTable, NC>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv, s_c[1],
+                                         rsqrt_d, dst + L.kcode_bytes + 4);
     }
   };
   if (shk != kQNoTable && shv != kQNoTable) tile_loop(std::true_type{});
@@ -448,8 +506,12 @@ static float rsqrt_of(int D) { return (float)(1.0 / __builtin_sqrt((double)D)); 
 template <int D, int KB, int VB>
 static void launch_quantize(const TqLayer& L, dim3 grid, size_t lds, hipStream_t st, const void* k,
                             const void* v, const int64_t* slot_mapping, int64_t rows, void* pages) {
-  hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
-                     (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+  if (L.norm_corr)
+    hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB, true>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
+                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+  else
+    hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB, false>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
+                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
 }
 
 template <int D, int KB>

@@ -31,14 +31,21 @@ def check_attention(got: np.ndarray, want: np.ndarray, seqs=None):
 
 
 def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D: int, kb: int,
-                  vb: int, stride: int, k_tie: np.ndarray, v_tie: np.ndarray) -> int:
+                  vb: int, stride: int, k_tie: np.ndarray, v_tie: np.ndarray,
+                  norm_correction=None) -> int:
     """Packed bytes must be identical except for indices at oracle-listed ties (|u - t_j| <= 1e-6),
     where the neighbouring index is accepted.  Returns the number of accepted tie differences.
 
     slots: [n] slot of each token row (k_tie/v_tie are [n, H, D]); negative slots are skipped.
+    norm_correction: None for the plain format, else ((k_norms, v_norms) [n, H] fp32 plain norms,
+    (k_centroids, v_centroids)); a row whose indices differ at a tie must then store the corrected
+    norm of its own indices.
     """
     keep = slots >= 0
     slots, k_tie, v_tie = slots[keep], k_tie[keep], v_tie[keep]
+    if norm_correction is not None:
+        (kn, vn), cents = norm_correction
+        plain = (np.asarray(kn)[keep].reshape(-1), np.asarray(vn)[keep].reshape(-1))
     g = gpu.reshape(-1, H, stride)[slots]
     r = ref.reshape(-1, H, stride)[slots]
     if np.array_equal(g, r):
@@ -47,11 +54,20 @@ def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D
     kr = oq.region_bytes(D, kb)
     assert np.array_equal(g[:, :, sb:], r[:, :, sb:]), "padding bytes differ"
     ties = 0
-    for lo, hi, bits, tie in ((0, kr, kb, k_tie), (kr, sb, vb, v_tie)):
+    for side, (lo, hi, bits, tie) in enumerate(((0, kr, kb, k_tie), (kr, sb, vb, v_tie))):
         gi, gn = oq.unpack_regions(g[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
         ri, rn = oq.unpack_regions(r[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
-        assert np.array_equal(gn.view(np.uint32), rn.view(np.uint32)), "stored norms differ"
         bad = gi != ri
+        same = gn.view(np.uint32) == rn.view(np.uint32)
+        if norm_correction is None:
+            assert np.all(same), "stored norms differ"
+        else:
+            moved = bad.any(axis=1)
+            assert np.all(same[~moved]), "stored norms differ"
+            if moved.any():
+                want = oq.corrected_norm(plain[side][moved], gi[moved], cents[side])
+                assert np.array_equal(gn[moved].view(np.uint32), want.view(np.uint32)), \
+                    "corrected norm of a row with a tie difference"
         t = tie.reshape(-1, D)
         assert np.all(t[bad]), f"{int(np.sum(bad & ~t))} index differences outside the tie band"
         assert np.all(np.abs(gi[bad] - ri[bad]) == 1)
@@ -69,7 +85,8 @@ class Case:
     """One seeded decode case: per-sequence K/V for every cached position, queries, sinks,
     block tables, and the oracle's pages."""
 
-    def __init__(self, w, layer=0, lens=None, slack=0, family="beta", slot_stride=0):
+    def __init__(self, w, layer=0, lens=None, slack=0, family="beta", slot_stride=0,
+                 norm_correction=False):
         import torch
         from packed_decode_attention_amd import workloads as wl
         self.w = w
@@ -91,10 +108,12 @@ class Case:
         self.kcb, self.vcb = (kc, kt), (vc, vt)
         self.layer_dict = dict(D=self.D, H_kv=self.H, block_size=w.block_size, k_bits=kb, v_bits=vb,
                                seed=0, slot_stride=self.slot_stride)
+        self.norm_correction = norm_correction
         self.pages_ref = np.zeros(self.num_blocks * w.block_size * self.H * self.slot_stride, np.uint8)
         self.k_tie, self.v_tie = oq.append_rows_fast(
             self.pages_ref, self.k.numpy(), self.v.numpy(), self.slots, kt, vt, kb, vb, 0,
-            self.slot_stride)
+            self.slot_stride, k_centroids32=kc if norm_correction else None,
+            v_centroids32=vc if norm_correction else None)
         self._torch = torch
 
     # ---- HIP path -------------------------------------------------------------------------
@@ -103,7 +122,15 @@ class Case:
         return LayerFormat(self.D, self.Hq, self.H, self.kb, self.vb, self.w.block_size, 0,
                            self.family, slot_stride=self.slot_stride if self.slot_stride !=
                            oq.slot_bytes(self.D, self.kb, self.vb) else 0,
-                           k_codebook=self.kcb, v_codebook=self.vcb)
+                           k_codebook=self.kcb, v_codebook=self.vcb,
+                           norm_correction=self.norm_correction)
+
+    def nc_args(self):
+        """compare_pages' norm_correction argument: the oracle's plain norms and the centroids."""
+        if not self.norm_correction:
+            return None
+        return ((oq.norm_fp32(self.k.numpy()), oq.norm_fp32(self.v.numpy())),
+                (self.kcb[0], self.vcb[0]))
 
     def gpu_quantize(self, fmt):
         import packed_decode_attention_amd as tq

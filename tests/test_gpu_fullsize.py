@@ -9,7 +9,8 @@ oracle from the same fp16 rows:
     output of the query heads of that kv head must match the oracle's dense attention to the
     attention tolerance.
 The rest of the batch still runs, so the grid, split geometry and workspace are the benchmark's.
-One case adds a hot window (bench.py --hot-window): the last W positions of every sequence also
+One case uses the norm-correction page format (bench.py --norm-correction).  One case adds a hot
+window (bench.py --hot-window): the last W positions of every sequence also
 come from fp16 rows (the sampled sequences' own rows, random rows elsewhere) and the decode runs
 through tq_paged_decode_attention_window.
 """
@@ -43,18 +44,20 @@ def _pick(w, lens, which):
     return list(which)
 
 
-CASES = [
-    ("llama3-8b", 1, (0, 13), 0),
-    ("mistral-7b", 2, (1,), 0),
-    ("ragged", 5, "extremes", 0),
-    ("qwen2.5-0.5b", 7, (0, 5), 0),
-    ("llama3-8b", 3, (4,), 512),
+CASES = [  # workload, layer, sampled sequences, hot window, norm-correction format
+    ("llama3-8b", 1, (0, 13), 0, False),
+    ("mistral-7b", 2, (1,), 0, False),
+    ("ragged", 5, "extremes", 0, False),
+    ("qwen2.5-0.5b", 7, (0, 5), 0, False),
+    ("llama3-8b", 3, (4,), 512, False),
+    ("llama3-8b", 6, (9,), 0, True),
 ]
 
 
-@pytest.mark.parametrize("name,layer,which,window", CASES,
-                         ids=[f"{c[0]}-L{c[1]}" + (f"-W{c[3]}" if c[3] else "") for c in CASES])
-def test_full_size_sampled(name, layer, which, window):
+@pytest.mark.parametrize("name,layer,which,window,nc", CASES,
+                         ids=[f"{c[0]}-L{c[1]}" + (f"-W{c[3]}" if c[3] else "") + ("-NC" if c[4] else "")
+                              for c in CASES])
+def test_full_size_sampled(name, layer, which, window, nc):
     import torch
     import packed_decode_attention_amd as tq
     from packed_decode_attention_amd import workloads as wl
@@ -72,7 +75,7 @@ def test_full_size_sampled(name, layer, which, window):
 
     heads = {b: (7 * b + layer) % H for b in seqs}  # one kv head per sampled sequence
     G = Hq // H
-    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0)
+    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0, norm_correction=nc)
     pages = fmt.new_pages(num_blocks)
     ctx_off = np.concatenate([[0], np.cumsum(lens - 1)])
     rows = {b: ([], []) for b in seqs}
@@ -107,13 +110,15 @@ def test_full_size_sampled(name, layer, which, window):
         bt1, nblk1 = wl.block_tables(one, np.array([L]))
         slots1 = wl.token_slots(bt1, 0, np.arange(L), bs)
         ref = np.zeros(nblk1 * bs * stride, np.uint8)
-        k_tie, v_tie = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride)
+        cents = dict(k_centroids32=kc, v_centroids32=vc) if nc else {}
+        k_tie, v_tie = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride, **cents)
         # the GPU's rows of the same positions and kv head
         slots = torch.from_numpy(wl.token_slots(bt_np, b, np.arange(L), bs)).cuda()
         gpu_rows = flat[slots, hh].cpu().numpy()
         ref_rows = ref.reshape(-1, stride)[slots1]
+        nc_args = ((oq.norm_fp32(k), oq.norm_fp32(v)), (kc, vc)) if nc else None
         ties = compare_pages(gpu_rows.reshape(-1), ref_rows.reshape(-1), np.arange(L), 1, D, kb, vb,
-                             stride, k_tie, v_tie)
+                             stride, k_tie, v_tie, nc_args)
         print(f"[fullsize]   seq {b} kv head {hh} (L={L}): page rows match, {ties} tie indices",
               flush=True)
         # the oracle's bytes into the GPU pages of this sequence and kv head

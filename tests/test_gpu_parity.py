@@ -27,6 +27,14 @@ CASES = {
     "gaussian-g5": dict(w=wl.Workload("g5", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                       values="student_t", seed=12),
                         lens=[333, 96, 1], family="gaussian"),
+    # norm-correction format (stored norm n / ||c[idx]||), at each register shape and bit width
+    "llama-nc": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], norm_correction=True),
+    "edges-nc": dict(w=wl.Workload("edges-nc", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
+                                   values="normal", tables="fragmented", seed=13),
+                     lens=[0, 1, 3, 5, 66, 200], slot_stride=160, norm_correction=True),
+    "g5-nc": dict(w=wl.Workload("g5-nc", 1, 3, 10, 2, 64, 8, 4, 0, block_size=32,
+                                values="student_t", seed=14),
+                  lens=[333, 96, 1], family="gaussian", norm_correction=True),
 }
 
 
@@ -53,7 +61,8 @@ def test_quantize_bytes(cases, name):
     fmt = c.fmt()
     print(f"[parity] quantize {name}: rows={len(c.slots)} H={c.H} D={c.D} K{c.kb}/V{c.vb}", flush=True)
     pages = c.gpu_quantize(fmt).cpu().numpy().reshape(-1)
-    ties = compare_pages(pages, c.pages_ref, c.slots, c.H, c.D, c.kb, c.vb, c.slot_stride, c.k_tie, c.v_tie)
+    ties = compare_pages(pages, c.pages_ref, c.slots, c.H, c.D, c.kb, c.vb, c.slot_stride, c.k_tie, c.v_tie,
+                         c.nc_args())
     assert ties <= max(4, 1e-4 * c.slots.size * c.H * c.D)
     # untouched slots keep their contents
     used = np.zeros(c.num_blocks * c.w.block_size, bool)

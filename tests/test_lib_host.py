@@ -81,7 +81,7 @@ def test_build_codebook_rejects_bad_arguments(lib):
 def _desc(lib, **kw):
     fake = 0x10000  # never dereferenced: validation fails before anything is enqueued
     d = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, block_size=16, k_bits=4, v_bits=4,
-             slot_stride=0, reserved=0, rht_seed=0, k_centroids=fake, k_boundaries=fake,
+             slot_stride=0, flags=0, rht_seed=0, k_centroids=fake, k_boundaries=fake,
              v_centroids=fake, v_boundaries=fake)
     d.update(kw)
     return lib.tq_layer_desc(**d)
@@ -98,7 +98,8 @@ def test_argument_validation_before_launch(lib):
     assert q(_desc(lib, v_bits=1)) == E.TQ_ERR_UNSUPPORTED
     assert q(_desc(lib, slot_stride=100)) == E.TQ_ERR_INVALID_ARG      # < 136
     assert q(_desc(lib, slot_stride=138)) == E.TQ_ERR_INVALID_ARG      # not a multiple of 4
-    assert q(_desc(lib, reserved=1)) == E.TQ_ERR_INVALID_ARG
+    assert q(_desc(lib, flags=2)) == E.TQ_ERR_INVALID_ARG              # unknown format flag
+    assert q(_desc(lib, flags=-1)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, num_kv_heads=0)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, block_size=0)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, k_centroids=0)) == E.TQ_ERR_INVALID_ARG
