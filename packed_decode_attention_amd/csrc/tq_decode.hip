@@ -99,8 +99,12 @@ __device__ __forceinline__ const uint16_t* fp16_row(const DecodeArgs& a, bool va
 // returns u).  LPH lanes of one DPP row hold a row, 8 coordinates each; every K and V row of the
 // chunk is loaded at the start.  These workgroups lead the split kernels' grids (see fp16_chunk),
 // so they run alongside the packed splits.
+// LDS floats fp16_chunk needs: scores [GMAX][kRowChunk], maxima [GMAX], wave sums [kNW][GMAX][D + 1].
 template <int D, int GMAX>
-__device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk) {
+constexpr int fp16_chunk_lds() { return GMAX * kRowChunk + GMAX + kNW * GMAX * (D + 1); }
+
+template <int D, int GMAX>
+__device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk, float* lds) {
   const TqLayer& L = a.L;
   const int G = L.G;
   const int rc = blk % a.row_chunks;
@@ -116,9 +120,9 @@ __device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk) {
   constexpr int NP = kWG / LPH;   // value-sum parts
   constexpr int UK = kRowChunk / (kNW * RPW);  // key rows per lane group
   constexpr int UV = kRowChunk / NP;           // value rows per part
-  __shared__ float s_s[GMAX][kRowChunk];
-  __shared__ float s_m[GMAX];
-  __shared__ float s_red[kNW][GMAX][D + 1];
+  float(*s_s)[kRowChunk] = reinterpret_cast<float(*)[kRowChunk]>(lds);
+  float* s_m = lds + GMAX * kRowChunk;
+  float(*s_red)[GMAX][D + 1] = reinterpret_cast<float(*)[GMAX][D + 1]>(lds + GMAX * kRowChunk + GMAX);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane % LPH, slot = lane / LPH;
@@ -274,7 +278,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   const int G = L.G;
 
   if ((int)blockIdx.x < a.rows_blocks) {  // fp16-row chunks lead the grid
-    fp16_chunk<D, GMAX>(a, blockIdx.x);
+    __shared__ float s_rows[fp16_chunk_lds<D, GMAX>()];
+    fp16_chunk<D, GMAX>(a, blockIdx.x, s_rows);
     return;
   }
   // (sequence, split) units with equal index modulo 8 share an XCD across all kv heads
@@ -503,6 +508,11 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 // All fp16 operands are pre-scaled by powers of two into the normal fp16 range (queries per
 // head, centroid tables by 2^8, weights by 2^15); the scales are removed in fp32.  Weights use
 // their own running maximum of score + log2(n_V), so they stay in (0, 1] before scaling.
+// Page rows: when page blocks hold whole runs of 16 positions (UBLK) a wave fetches its tile's 32
+// slots as consecutive 16-byte chunks, one tile ahead, and copies them into its own LDS stage,
+// from which the code runs, the norms and the value codes of the PV transpose are read; for other
+// block sizes each lane loads its own code runs and norms and the value codes pass through a
+// per-wave LDS tile.
 // =============================================================================================
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -611,6 +621,21 @@ struct MfmaTile {
   float kn[2], vn[2];
 };
 
+// Page rows of a 32-position tile for one kv head, as fetched when page blocks hold whole runs of
+// 16 positions and slots are unpadded: a slot is N16 16-byte chunks and an 8-byte tail.  Lane l
+// fetches chunk c = 64 i + l of the tile (row c / N16, chunk c % N16) into c[i] and, for l < 32,
+// the tail of row l: consecutive lanes read consecutive bytes of a row, so a wave's load covers
+// 64 / N16 whole slots instead of a 16-byte piece of 16 slots.
+template <int D, int KB, int VB>
+struct MfmaRaw {
+  static constexpr int SB = D * KB / 8 + 4 + D * VB / 8 + 4;  // slot bytes
+  static constexpr int N16 = (SB - 8) / 16;
+  static constexpr int NI = (32 * N16 + 63) / 64;
+  static_assert((SB - 8) % 16 == 0, "slot = whole 16-byte chunks + an 8-byte tail");
+  uint4 c[NI];
+  uint2 t;
+};
+
 template <int DPPCTRL>
 __device__ __forceinline__ float dpp_max_step(float x) { return fmaxf(x, dpp<DPPCTRL>(x)); }
 
@@ -652,12 +677,24 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   using KE = typename OpTable<KB>::E;
   using VE = typename OpTable<VB>::E;
   using Tile = MfmaTile<D, KB, VB>;
+  using Raw = MfmaRaw<D, KB, VB>;
+  constexpr int H8 = G8 ? 8 : 4;  // query heads per kv head this instance handles at most
   const TqLayer& L = a.L;
   const int G = L.G;
 
+  // s_x holds, in turn: the rotated queries (prologue); per wave, the page rows of the current
+  // tile (UBLK) or its value codes; the per-wave partial results (epilogue).  The fp16-row chunk
+  // workgroups use it for their own sums.
+  constexpr int kTileBytes = UBLK ? kNW * 32 * Raw::SB : kNW * 32 * C::VROW * 4;
+  constexpr int kQPBytes = kNW * H8 * (D + 2) * 4;
+  constexpr int kRowsBytes = G8 ? 0 : 4 * fp16_chunk_lds<D, 4>();
+  constexpr int kXBytes = (kTileBytes > kQPBytes ? kTileBytes : kQPBytes) > kRowsBytes
+                              ? (kTileBytes > kQPBytes ? kTileBytes : kQPBytes)
+                              : kRowsBytes;
+  __shared__ __align__(16) uint8_t s_x[kXBytes];
   if constexpr (!G8) {  // fp16-row chunks lead the grid (with 8 query heads: their own kernel)
     if ((int)blockIdx.x < a.rows_blocks) {
-      fp16_chunk<D, 4>(a, blockIdx.x);
+      fp16_chunk<D, 4>(a, blockIdx.x, reinterpret_cast<float*>(s_x));
       return;
     }
   }
@@ -679,13 +716,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   __shared__ VE s_vtab[OpTable<VB>::N];
   __shared__ int64_t s_boff[kMaxBtLds];
   __shared__ float s_qmax[8];
-  constexpr int H8 = G8 ? 8 : 4;  // query heads per kv head this instance handles at most
   __shared__ __align__(16) uint32_t s_w[kNW][16][C::WROW];
-  __shared__ __align__(16) uint32_t s_v[kNW][32][C::VROW];
-  // rotated queries (prologue) and the per-wave partial results (epilogue) share one buffer
-  __shared__ __align__(16) float s_qp[kNW * H8 * (D + 2)];
-  float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_qp);
-  float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_qp);  // [wave * H8 + head]
+  float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_x);
+  float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_x);  // [wave * H8 + head]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -764,10 +797,6 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
-  // Per-lane byte offsets inside a run of 16 page rows (token t16, code run of lane group q4).
-  const uint32_t lane_row = __umul24((uint32_t)t16, row_bytes32);
-  const uint32_t off_k = lane_row + 4 * C::KW * q4, off_v = lane_row + voff + 4 * C::VW * q4;
-  const uint32_t off_kn = lane_row + L.kcode_bytes, off_vn = lane_row + voff + L.vcode_bytes;
 
   // Row base of the 16 positions starting at pu (a multiple of 16).  With a block size that is a
   // multiple of 16 the 16 rows lie in one page block, so the base is the same for the whole wave;
@@ -789,30 +818,57 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     const int bi = block_of(pc);
     return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
   };
+  // Blocks of any size: each lane loads the code runs and norms it works on (rows t16, 16 + t16).
   auto fetch = [&](int tile, Tile& m) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int pu = p0 + 32 * tile + 16 * u;
-      const uint8_t* r;
-      uint32_t ok, ov, okn, ovn;
-      if (UBLK) {
-        r = run_base(pu);
-        ok = off_k;
-        ov = off_v;
-        okn = off_kn;
-        ovn = off_vn;
-      } else {
-        r = row_ptr(pu + t16);
-        ok = 4 * C::KW * q4;
-        ov = voff + 4 * C::VW * q4;
-        okn = L.kcode_bytes;
-        ovn = voff + L.vcode_bytes;
-      }
-      load_words<C::KW>(r + ok, m.k[u]);
-      load_words<C::VW>(r + ov, m.v[u]);
-      m.kn[u] = *reinterpret_cast<const float*>(r + okn);
-      m.vn[u] = *reinterpret_cast<const float*>(r + ovn);
+      const uint8_t* r = row_ptr(p0 + 32 * tile + 16 * u + t16);
+      load_words<C::KW>(r + 4 * C::KW * q4, m.k[u]);
+      load_words<C::VW>(r + voff + 4 * C::VW * q4, m.v[u]);
+      m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
+      m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
     }
+  };
+  // Whole runs of 16 positions per block: the tile's slots as consecutive chunks (see MfmaRaw),
+  // copied into the wave's stage (slot of row r at r * SB; SB / 4 = 2 mod 4, so the code runs of
+  // 16 consecutive rows, and the value codes of rows t and t + 8, fall on distinct banks).
+  constexpr int kFull = 32 * Raw::N16;  // chunks in a tile
+  uint32_t goff[Raw::NI], loff[Raw::NI];
+#pragma unroll
+  for (int i = 0; i < Raw::NI; ++i) {
+    const int c = 64 * i + lane;
+    const int row = c / Raw::N16, col = c - row * Raw::N16;
+    goff[i] = __umul24((uint32_t)(row & 15), row_bytes32) + 16 * col;
+    loff[i] = row * Raw::SB + 16 * col;
+  }
+  const uint32_t goff_t = __umul24((uint32_t)(lane & 15), row_bytes32) + 16 * Raw::N16;
+  auto fetch_raw = [&](int tile, Raw& m) {
+    const int pu = p0 + 32 * tile;
+    const uint8_t* r0 = run_base(pu);
+    const uint8_t* r1 = run_base(pu + 16);
+#pragma unroll
+    for (int i = 0; i < Raw::NI; ++i) {
+      const int clo = 64 * i, chi = 64 * i + 63;
+      if (chi < kFull || lane + clo < kFull) {
+        const uint8_t* base = chi / Raw::N16 < 16 ? r0
+                              : clo / Raw::N16 >= 16 ? r1
+                              : ((lane + clo) / Raw::N16 < 16 ? r0 : r1);
+        m.c[i] = *reinterpret_cast<const uint4*>(base + goff[i]);
+      }
+    }
+    if (lane < 32) m.t = *reinterpret_cast<const uint2*>((lane < 16 ? r0 : r1) + goff_t);
+  };
+  uint8_t* stage = s_x + wave * 32 * Raw::SB;
+  auto stage_raw = [&](const Raw& m) {
+#pragma unroll
+    for (int i = 0; i < Raw::NI; ++i) {
+      if (64 * i + 63 < kFull || lane + 64 * i < kFull) {
+        uint2* d = reinterpret_cast<uint2*>(stage + loff[i]);
+        d[0] = make_uint2(m.c[i].x, m.c[i].y);
+        d[1] = make_uint2(m.c[i].z, m.c[i].w);
+      }
+    }
+    if (lane < 32) *reinterpret_cast<uint2*>(stage + lane * Raw::SB + 16 * Raw::N16) = m.t;
   };
 
   // Online-softmax state.  kSent is a finite "minus infinity": masked positions score kSent, so
@@ -826,7 +882,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   for (int c = 0; c < C::PC; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   uint32_t* wt = &s_w[wave][0][0];
-  uint32_t* vt = &s_v[wave][0][0];
+  uint32_t* vt = reinterpret_cast<uint32_t*>(s_x) + wave * 32 * C::VROW;  // value codes (!UBLK)
   uint16_t* wt16 = reinterpret_cast<uint16_t*>(wt);
   // weight of row m, token col: a fp16 at [m][col], or the pair (w, w) at dword [m][col]
   auto put_w = [&](int m, int col, uint32_t w) {
@@ -842,14 +898,38 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();  // tables, block offsets, zero rows ready
 
+  // cur: the lane's code runs and norms (blocks of any size); with UBLK they come from the stage.
   auto process = [&](const Tile& cur, int tile) {
     // ---- QK on the matrix cores ----
     float4_t sc[2];
+    float kn[2], vn[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      uint32_t kw[C::KW];
+      if constexpr (UBLK) {
+        const uint8_t* row = stage + (16 * u + t16) * Raw::SB;
+        if constexpr (C::KW % 2 == 0) {
+#pragma unroll
+          for (int i = 0; i < C::KW; i += 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(row + 4 * C::KW * q4 + 4 * i);
+            kw[i] = x.x;
+            kw[i + 1] = x.y;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < C::KW; ++i) kw[i] = reinterpret_cast<const uint32_t*>(row + 4 * C::KW * q4)[i];
+        }
+        kn[u] = *reinterpret_cast<const float*>(row + L.kcode_bytes);
+        vn[u] = *reinterpret_cast<const float*>(row + voff + L.vcode_bytes);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::KW; ++i) kw[i] = cur.k[u][i];
+        kn[u] = cur.kn[u];
+        vn[u] = cur.vn[u];
+      }
       uint4 kop[C::NMQ];  // all table reads of the sub-tile first, so their latency overlaps
 #pragma unroll
-      for (int st = 0; st < C::NMQ; ++st) kop[st] = k_operand<KB>(s_ktab, cur.k[u], st);
+      for (int st = 0; st < C::NMQ; ++st) kop[st] = k_operand<KB>(s_ktab, kw, st);
       float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, sb = sa;  // two independent MFMA chains
 #pragma unroll
       for (int st = 0; st < C::NMQ; st += 2) {
@@ -866,9 +946,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     for (int u = 0; u < 2; ++u) {
       const int p = pbase + 16 * u + t16;
       const bool valid = p >= ns && p < p_end;
-      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * cur.kn[u] * f0 : kSent;
-      if (G8) s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * cur.kn[u] * f1 : kSent;
-      lv[u] = __builtin_amdgcn_logf(cur.vn[u]);  // log2(n_V); -inf for a zero row
+      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * kn[u] * f0 : kSent;
+      if (G8) s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * kn[u] * f1 : kSent;
+      lv[u] = __builtin_amdgcn_logf(vn[u]);  // log2(n_V); -inf for a zero row
     }
     const float ms0 = fmaxf(m_s[0], row16_max(fmaxf(s0[0], s0[1])));
     const float mw0 = fmaxf(m_w[0], row16_max(fmaxf(s0[0] + lv[0], s0[1] + lv[1])));
@@ -917,10 +997,12 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         put_w(4 * q4 + 2, col, h1);
         put_w(4 * q4 + 3, col, l1);
       }
-      // value codes of token col, lane group q4's run of coordinates
-      uint32_t* vrow = vt + col * C::VROW + C::VW * q4;
+      if constexpr (!UBLK) {  // value codes of token col, lane group q4's run of coordinates
+        uint32_t* vrow = vt + col * C::VROW + C::VW * q4;
 #pragma unroll
-      for (int i = 0; i < C::VW; i += 2) *reinterpret_cast<uint2*>(vrow + i) = make_uint2(cur.v[u][i], cur.v[u][i + 1]);
+        for (int i = 0; i < C::VW; i += 2)
+          *reinterpret_cast<uint2*>(vrow + i) = make_uint2(cur.v[u][i], cur.v[u][i + 1]);
+      }
     }
 
     // ---- PV on the matrix cores: lane (n = t16, q4) handles tokens 8 q4 .. 8 q4 + 7 and
@@ -942,11 +1024,12 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       uint32_t cw[4][VBITS > 32 ? 2 : 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t* src = vt + (8 * q4 + 4 * j + i) * C::VROW;
-        if constexpr (VBITS == 64) {
-          const uint2 x = *reinterpret_cast<const uint2*>(src + 2 * t16);
-          cw[i][0] = x.x;
-          cw[i][1] = x.y;
+        const int tok = 8 * q4 + 4 * j + i;
+        const uint32_t* src = UBLK ? reinterpret_cast<const uint32_t*>(stage + tok * Raw::SB + voff)
+                                   : vt + tok * C::VROW;
+        if constexpr (VBITS == 64) {  // the stage's value codes are 4-byte aligned only
+          cw[i][0] = src[2 * t16];
+          cw[i][1] = src[2 * t16 + 1];
         } else if constexpr (VBITS == 32) {
           cw[i][0] = src[t16];
         } else if constexpr (VBITS == 16) {
@@ -1003,14 +1086,27 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  Tile cur;
-  if (wave < n_tiles) fetch(wave, cur);
-  for (int tile = wave; tile < n_tiles; tile += kNW) {
-    Tile nxt;
-    if (tile + kNW < n_tiles) fetch(tile + kNW, nxt);
-    process(cur, tile);
-    cur = nxt;
+  if constexpr (UBLK) {
+    Raw raw;  // the next tile in flight while the stage holds the current one
+    if (wave < n_tiles) fetch_raw(wave, raw);
+    for (int tile = wave; tile < n_tiles; tile += kNW) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // last tile's stage reads are done
+      stage_raw(raw);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // stage written: read by other lanes
+      if (tile + kNW < n_tiles) fetch_raw(tile + kNW, raw);
+      process(Tile{}, tile);
+    }
+  } else {
+    Tile cur;
+    if (wave < n_tiles) fetch(wave, cur);
+    for (int tile = wave; tile < n_tiles; tile += kNW) {
+      Tile nxt;
+      if (tile + kNW < n_tiles) fetch(tile + kNW, nxt);
+      process(cur, tile);
+      cur = nxt;
+    }
   }
+  __syncthreads();  // every wave is done with s_x: it takes the partial results
 
   // ---- wave result: heads g0, g1 at coordinates PC t16 + c, in the score-max frame ----
 #pragma unroll
@@ -1147,7 +1243,8 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
 // fp16-row chunks on their own (for the split kernel whose LDS budget leaves no room for them).
 template <int D, int GMAX>
 __global__ __launch_bounds__(kWG) void tq_decode_rows_kernel(DecodeArgs a) {
-  fp16_chunk<D, GMAX>(a, blockIdx.x);
+  __shared__ float s_rows[fp16_chunk_lds<D, GMAX>()];
+  fp16_chunk<D, GMAX>(a, blockIdx.x, s_rows);
 }
 
 template <int D, int GMAX>
