@@ -26,6 +26,12 @@ with ns = min(n_sink, L_b) sinks and the last w_b = win_lens[b] positions in the
   o_h = sum_p softmax(s)_p v_p over p in [0, L_b);  L_b = 0 gives o_h = 0.
 Everything is fp64; the query is the fp16 input.
 
+Several queries per sequence (decode_attention_multi): the last T cached positions of sequence b
+are T new tokens whose rows are already in the cache (a speculative draft being verified, or a
+chunk of a prompt); query j sits at position L_b - T + j and attends positions 0 .. L_b - T + j
+(causal order), which is the single-query definition above with L_b - T + j + 1 cached tokens
+(none when that is <= 0).
+
 The second route, decode_attention_rotated(), is the fused identity a kernel uses
 (q . (n R^T c) = n (R q) . c and sum_p w_p n_p R^T c_p = R^T sum_p w_p n_p c_p); the tests check
 the two routes against each other by brute force.
@@ -142,4 +148,20 @@ def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centro
             acc_rot = (w_codes * v_n[:, hk].astype(np.float64)) @ cv[v_idx[:, hk, :]]
             o = R.T @ acc_rot + w_16 @ V16
             out[b, h] = o / l
+    return out
+
+
+def decode_attention_multi(q16, pages, block_tables, seq_lens, layer, k_centroids32, v_centroids32,
+                           sink_k16=None, sink_v16=None, n_sink=0, scale=None, seqs=None):
+    """T queries per sequence at its last T positions, each causal.  q16: [B, T, H_q, D] fp16.
+    Returns out [B, T, H_q, D] (fp64): out[:, j] is decode_attention() of query j over the first
+    L_b - T + j + 1 positions."""
+    q = np.asarray(q16, dtype=np.float16)
+    B, T, H_q, D = q.shape
+    out = np.zeros((B, T, H_q, D), dtype=np.float64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    for j in range(T):
+        visible = np.maximum(lens - T + j + 1, 0)
+        out[:, j] = decode_attention(q[:, j], pages, block_tables, visible, layer, k_centroids32,
+                                     v_centroids32, sink_k16, sink_v16, n_sink, scale=scale, seqs=seqs)
     return out

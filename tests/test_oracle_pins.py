@@ -577,3 +577,47 @@ def test_corrected_norm_by_brute_force(rng):
     want = np.float32(n / np.float32(np.sqrt(vals[0])))
     got = quantize.corrected_norm(np.array([n]), idx[None], c32)[0]
     assert got.view(np.uint32) == want.view(np.uint32)
+
+
+# ============================================================================================
+# Several queries per sequence (a verified draft or a prompt chunk): the last T positions are the
+# queries, each attending the positions up to its own (causal).  Pinned against the textbook
+# masked attention over the dequantized rows, not against the single-query oracle it calls.
+# ============================================================================================
+@pytest.mark.parametrize("D, H_kv, G, kb, vb, L, T, ns", [
+    (64, 2, 2, 4, 4, 23, 4, 3), (128, 1, 4, 8, 4, 40, 2, 0), (64, 1, 3, 4, 8, 9, 3, 4)])
+def test_multi_query_is_causal_masked_attention(D, H_kv, G, kb, vb, L, T, ns, rng):
+    import torch
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, kb, vb, L)
+    Hq = H_kv * G
+    q = rng.standard_normal((1, T, Hq, D)).astype(np.float16)
+    sk = rng.standard_normal((1, max(ns, 1), H_kv, D)).astype(np.float16)
+    sv = rng.standard_normal((1, max(ns, 1), H_kv, D)).astype(np.float16)
+    o = attention.decode_attention_multi(q, pages, bt[None], np.array([L]), layer, ck.centroids32,
+                                         cv.centroids32, sk, sv, n_sink=ns)
+    pos = np.arange(ns, L)
+    slots = bt[pos // 16] * 16 + pos % 16
+    k_idx, k_n, v_idx, v_n = quantize.read_slots(pages, slots, H_kv, D, kb, vb)
+    Kall = np.concatenate([sk[0, :ns].astype(np.float64), quantize.dequantize_plain(k_idx, k_n, ck.centroids32, 0)])
+    Vall = np.concatenate([sv[0, :ns].astype(np.float64), quantize.dequantize_plain(v_idx, v_n, cv.centroids32, 0)])
+    Q = torch.from_numpy(q[0].astype(np.float64)).permute(1, 0, 2)[None]            # [1, Hq, T, D]
+    K = torch.from_numpy(Kall).permute(1, 0, 2).repeat_interleave(G, 0)[None]       # [1, Hq, L, D]
+    V = torch.from_numpy(Vall).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    qpos = torch.arange(L - T, L)[:, None]
+    mask = torch.arange(L)[None, :] <= qpos                                          # [T, L]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+    np.testing.assert_allclose(o[0], ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_multi_query_more_queries_than_tokens(rng):
+    # queries at negative positions see nothing (zero output); the others are causal as usual
+    D, H_kv, G, L, T = 64, 1, 2, 2, 4
+    layer, pages, bt, k, v, ck, cv = _tiny_cache(rng, D, H_kv, 4, 4, L)
+    q = rng.standard_normal((1, T, H_kv * G, D)).astype(np.float16)
+    o = attention.decode_attention_multi(q, pages, bt[None], np.array([L]), layer, ck.centroids32,
+                                         cv.centroids32)
+    assert np.all(o[0, :2] == 0)
+    _, _, v_idx, v_n = quantize.read_slots(pages, bt[:1] * 16 + np.arange(2), H_kv, D, 4, 4)
+    vhat = quantize.dequantize_plain(v_idx, v_n, cv.centroids32, 0)
+    np.testing.assert_allclose(o[0, 2], np.broadcast_to(vhat[0, 0], (H_kv * G, D)), atol=1e-12)  # one token
+    assert np.abs(o[0, 3] - o[0, 2]).max() > 1e-6
