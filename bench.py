@@ -91,7 +91,7 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
     return new_k, new_v
 
 
-def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False):
+def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, n_queries=1):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -125,20 +125,35 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False):
         layers.append(st)
     torch.cuda.synchronize()
     # per-step inputs: queries and one new K/V token per sequence and layer
-    qs = [wl.queries(w, l, 0, dev) for l in range(w.layers)]
+    if n_queries > 1:  # [B, T, H_q, D]: the queries of the last T positions
+        qs = [torch.stack([wl.queries(w, l, j, dev) for j in range(n_queries)], dim=1)
+              for l in range(w.layers)]
+    else:
+        qs = [wl.queries(w, l, 0, dev) for l in range(w.layers)]
     new_k, new_v = new_tokens(w, n_steps_total, wl, dev)
     sink_k, sink_v = wl.sinks(w, 0, dev)
     max_len = int(lens.max())
-    ws = fmts[(w.k_bits, w.v_bits)].new_workspace(B, max_len)
+    nq = n_queries if n_queries > 1 else 0
+    ws = fmts[(w.k_bits, w.v_bits)].new_workspace(B, max_len, n_queries=nq)
     for f in fmts.values():
-        assert tq.tq_decode_workspace_bytes(f.desc, B, max_len) <= ws.numel()
-    out = torch.empty((B, w.num_q_heads, D), dtype=torch.float32, device=dev)
+        need = (tq.tq_decode_multi_workspace_bytes(f.desc, B, max_len, n_queries) if nq
+                else tq.tq_decode_workspace_bytes(f.desc, B, max_len))
+        assert need <= ws.numel()
+    out_shape = (B, n_queries, w.num_q_heads, D) if nq else (B, w.num_q_heads, D)
+    out = torch.empty(out_shape, dtype=torch.float32, device=dev)
+    # several queries: each step appends T rows per sequence, at its last T positions
+    multi_slots = None
+    if nq:
+        multi_slots = torch.from_numpy(np.concatenate(
+            [wl.token_slots(bt_np, b, np.arange(lens[b] - n_queries, lens[b]), w.block_size)
+             for b in range(B)]).astype(np.int64)).to(dev)
     ns = np.minimum(lens, w.n_sink)
     win_lens = np.minimum(hot_window, lens - ns).astype(np.int32)
     return dict(hot_window=hot_window, win_lens_np=win_lens, win_lens=torch.from_numpy(win_lens).to(dev),
                 lens=lens, bt=bt, seq_lens=seq_lens, new_slots=new_slots, layers=layers, qs=qs,
                 new_k=new_k, new_v=new_v, sink_k=sink_k, sink_v=sink_v, max_len=max_len, ws=ws,
-                out=out, bulk_ms=bulk_ms, bulk_rows=bulk_rows, n_ctx=n_ctx, num_blocks=num_blocks)
+                out=out, bulk_ms=bulk_ms, bulk_rows=bulk_rows, n_ctx=n_ctx, num_blocks=num_blocks,
+                n_queries=n_queries, multi_slots=multi_slots)
 
 
 def run_step(w, S, tq, step, ev=None):
@@ -147,15 +162,25 @@ def run_step(w, S, tq, step, ev=None):
             ev["a0"][l].record()
         # with a hot window the quantized token is the one leaving the window, and the new token
         # takes its row in the window (a ring: row step % W)
-        tq.tq_quantize_append(L.fmt.desc, S["new_k"][step, l], S["new_v"][step, l], S["new_slots"],
-                              L.pages, L.num_blocks)
+        if S["n_queries"] > 1:  # T new rows per sequence (the step's rows, repeated)
+            T = S["n_queries"]
+            tq.tq_quantize_append(L.fmt.desc, S["new_k"][step, l].repeat_interleave(T, 0),
+                                  S["new_v"][step, l].repeat_interleave(T, 0), S["multi_slots"],
+                                  L.pages, L.num_blocks)
+        else:
+            tq.tq_quantize_append(L.fmt.desc, S["new_k"][step, l], S["new_v"][step, l],
+                                  S["new_slots"], L.pages, L.num_blocks)
         if L.win_k is not None:
             r = step % S["hot_window"]
             L.win_k[:, r].copy_(S["new_k"][step, l])
             L.win_v[:, r].copy_(S["new_v"][step, l])
         if ev is not None:
             ev["a1"][l].record()
-        if L.win_k is None:
+        if S["n_queries"] > 1:
+            tq.tq_paged_decode_attention_multi(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
+                                               S["seq_lens"], S["max_len"], S["out"], S["ws"],
+                                               S["sink_k"], S["sink_v"], w.n_sink)
+        elif L.win_k is None:
             tq.tq_paged_decode_attention(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
                                          S["seq_lens"], S["max_len"], S["out"], S["ws"],
                                          S["sink_k"], S["sink_v"], w.n_sink)
@@ -168,8 +193,9 @@ def run_step(w, S, tq, step, ev=None):
             ev["d1"][l].record()
 
 
-def algorithmic_bytes(w, lens, tq, win_lens=None):
-    """Bytes the decode of one layer must move (with a hot window of win_lens[b] fp16 rows)."""
+def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1):
+    """Bytes the decode of one layer must move (with a hot window of win_lens[b] fp16 rows; with
+    n_queries queries per sequence, that many query and output rows)."""
     B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
     win = np.zeros_like(lens) if win_lens is None else np.asarray(win_lens)
     per_layer = []
@@ -180,7 +206,7 @@ def algorithmic_bytes(w, lens, tq, win_lens=None):
         b = int(page_tok.sum()) * H * sb                                  # packed slots
         b += int(win.sum()) * H * D * 2 * 2                               # fp16 window rows
         b += int(np.sum((lens + w.block_size - 1) // w.block_size)) * 4   # block tables
-        b += B * w.num_q_heads * D * 2 + B * w.num_q_heads * D * 4 + B * 4  # q, out, seq_lens
+        b += n_queries * B * w.num_q_heads * D * (2 + 4) + B * 4          # q, out, seq_lens
         b += B * w.n_sink * H * D * 2 * 2                                 # fp16 sinks
         per_layer.append(b)
     return per_layer
@@ -288,6 +314,9 @@ def main():
                          "tq_paged_decode_attention_window)")
     ap.add_argument("--norm-correction", action="store_true",
                     help="store corrected norms n / ||c[idx]|| (the norm-correction page format)")
+    ap.add_argument("--queries", type=int, default=1, metavar="T",
+                    help="decode T causal queries per sequence (its last T positions) per call, "
+                         "through tq_paged_decode_attention_multi")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -308,7 +337,9 @@ def main():
     log(f"workload {describe(w)}")
     total = args.warmup + args.steps
     t0 = time.time()
-    S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction)
+    if args.queries > 1 and args.hot_window:
+        sys.exit("--queries and --hot-window do not combine (the multi-query call has no window)")
+    S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction, args.queries)
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -338,7 +369,8 @@ def main():
     lens = S["lens"]
     kv_tokens_step = int(lens.sum()) * w.layers
     value = kv_tokens_step / (ms_per_step / 1e3)
-    per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None)
+    per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None,
+                                        args.queries)
     layer_ids = np.arange(n) % w.layers
     dec_bytes = np.array([per_layer_bytes[i] for i in layer_ids], np.float64)
     achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
@@ -360,12 +392,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w) + (f", fp16 hot window of {args.hot_window} tokens"
                                              if args.hot_window else "")
-                               + (", norm-correction format" if args.norm_correction else ""),
+                               + (", norm-correction format" if args.norm_correction else "")
+                               + (f", {args.queries} causal queries per sequence" if args.queries > 1 else ""),
                    "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if args.hot_window else recorded_traffic(w),
+                     "traffic": None if (args.hot_window or args.queries > 1) else recorded_traffic(w),
                      "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},

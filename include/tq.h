@@ -182,6 +182,32 @@ int tq_paged_decode_attention_window(const tq_layer_desc* layer, const void* q, 
                                      float scale, float* out, void* workspace,
                                      size_t workspace_bytes, tq_stream_t stream);
 
+/* Decode several query tokens per sequence at once, in causal order: the last n_queries cached
+ * positions of each sequence are the new tokens (their rows already appended), e.g. a draft being
+ * verified or a chunk of a prompt.
+ * (tq-kv, "What's next": attention over more than the single decode token, for prefill, and the
+ *  verification of EAGLE draft tokens.)
+ *   q             device fp16 [num_seqs][n_queries][num_q_heads][D]
+ *   n_queries     1 .. TQ_MAX_QUERIES
+ *   out           device fp32 [num_seqs][n_queries][num_q_heads][D] (written)
+ *   workspace     device, >= tq_decode_multi_workspace_bytes(layer, num_seqs, max_seq_len,
+ *                 n_queries)
+ * Query j of sequence b sits at position seq_lens[b] - n_queries + j and attends positions 0 ..
+ * seq_lens[b] - n_queries + j: the single-query result over that many cached tokens (a query at a
+ * negative position gives zeros).  Sinks are as for tq_paged_decode_attention; there is no hot
+ * window.  The page bytes are read once for up to 8 / G queries (G query heads per kv head) and
+ * once more per further group of queries.  Other arguments as for tq_paged_decode_attention. */
+#define TQ_MAX_QUERIES 64
+size_t tq_decode_multi_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs,
+                                       int32_t max_seq_len, int32_t n_queries);
+int tq_paged_decode_attention_multi(const tq_layer_desc* layer, const void* q, int32_t n_queries,
+                                    const void* pages, int64_t num_blocks,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, int32_t num_seqs,
+                                    int32_t max_seq_len, const void* sink_k, const void* sink_v,
+                                    int32_t n_sink, float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, tq_stream_t stream);
+
 /* Dequantize whole slots (turboquant-serve 0.1.2, "Architecture" _decode(): unpack, Lloyd-Max
  * decode, restore magnitude, rotate back).  Bit-exact definition: c_i = centroid[idx_i] (fp32);
  * z = H c computed exactly (fp64); g = fp32(n * fp32(1/sqrt(D))); x_i = s_i * fp32(fp32(z_i) * g).

@@ -16,10 +16,13 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     TqError,
     tq_build_codebook,
+    TQ_MAX_QUERIES,
+    tq_decode_multi_workspace_bytes,
     tq_decode_workspace_bytes,
     tq_dequantize_rows,
     tq_layer_desc,
     tq_paged_decode_attention,
+    tq_paged_decode_attention_multi,
     tq_paged_decode_attention_window,
     tq_quantize_append,
     tq_rht_signs,
@@ -73,10 +76,14 @@ class LayerFormat:
         return torch.zeros((num_blocks, self.block_size, self.num_kv_heads, self.slot_stride),
                            dtype=torch.uint8, device=device)
 
-    def new_workspace(self, num_seqs: int, max_seq_len: int, device="cuda"):
-        """Decode workspace for up to num_seqs sequences of at most max_seq_len tokens."""
+    def new_workspace(self, num_seqs: int, max_seq_len: int, device="cuda", n_queries: int = 0):
+        """Decode workspace for up to num_seqs sequences of at most max_seq_len tokens (with
+        n_queries > 0: for tq_paged_decode_attention_multi with that many queries)."""
         import torch
-        n = tq_decode_workspace_bytes(self.desc, num_seqs, max_seq_len)
+        if n_queries > 0:
+            n = tq_decode_multi_workspace_bytes(self.desc, num_seqs, max_seq_len, n_queries)
+        else:
+            n = tq_decode_workspace_bytes(self.desc, num_seqs, max_seq_len)
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 

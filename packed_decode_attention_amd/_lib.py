@@ -27,7 +27,9 @@ FAMILIES = {"beta": 0, "gaussian": 1}
 
 EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_quantize_append",
            "tq_decode_workspace_bytes", "tq_paged_decode_attention",
-           "tq_paged_decode_attention_window", "tq_dequantize_rows", "tq_status_str")
+           "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
+           "tq_paged_decode_attention_multi", "tq_dequantize_rows", "tq_status_str")
+TQ_MAX_QUERIES = 64
 
 
 class TqError(RuntimeError):
@@ -83,6 +85,11 @@ def _lib():
                                                          I32, P, P, P, I32, ctypes.c_float, P, P,
                                                          SZ, P]
         lib.tq_paged_decode_attention_window.restype = ctypes.c_int
+        lib.tq_decode_multi_workspace_bytes.argtypes = [D, I32, I32, I32]
+        lib.tq_decode_multi_workspace_bytes.restype = SZ
+        lib.tq_paged_decode_attention_multi.argtypes = [D, P, I32, P, I64, P, I32, P, I32, I32, P,
+                                                        P, I32, ctypes.c_float, P, P, SZ, P]
+        lib.tq_paged_decode_attention_multi.restype = ctypes.c_int
         lib.tq_dequantize_rows.argtypes = [D, P, I64, P, I64, P, P, P]
         lib.tq_dequantize_rows.restype = ctypes.c_int
         lib.tq_status_str.argtypes = [ctypes.c_int]
@@ -179,6 +186,26 @@ def tq_paged_decode_attention_window(desc, q, pages, num_blocks: int, block_tabl
         _ptr(win_v), _ptr(win_lens), win_cap, scale, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_paged_decode_attention_window", st)
+
+
+def tq_decode_multi_workspace_bytes(desc, num_seqs: int, max_seq_len: int, n_queries: int) -> int:
+    return int(_lib().tq_decode_multi_workspace_bytes(ctypes.byref(desc), num_seqs, max_seq_len,
+                                                      n_queries))
+
+
+def tq_paged_decode_attention_multi(desc, q, pages, num_blocks: int, block_tables, seq_lens,
+                                    max_seq_len: int, out, workspace, sink_k=None, sink_v=None,
+                                    n_sink: int = 0, scale: float = 0.0, stream=None) -> None:
+    """Causal decode of the last T positions of every sequence: q [B, T, H_q, D] fp16, out
+    [B, T, H_q, D] fp32."""
+    num_seqs, n_queries = q.shape[0], q.shape[1]
+    max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    st = _lib().tq_paged_decode_attention_multi(
+        ctypes.byref(desc), _ptr(q), n_queries, _ptr(pages), num_blocks, _ptr(block_tables),
+        max_blocks, _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink,
+        scale, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("tq_paged_decode_attention_multi", st)
 
 
 def tq_dequantize_rows(desc, pages, num_blocks: int, slots, k_out, v_out, stream=None) -> None:

@@ -146,6 +146,62 @@ extern "C" int tq_paged_decode_attention_window(
                       win_cap, scale, out, workspace, workspace_bytes, stream);
 }
 
+// Queries per launch of the multi-query decode: up to 8 kernel heads per kv head.
+static int queries_per_launch(const TqLayer& L) { return L.G >= 8 ? 1 : 8 / L.G; }
+
+extern "C" size_t tq_decode_multi_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs,
+                                                  int32_t max_seq_len, int32_t n_queries) {
+  TqLayer L;
+  if (make_layer(layer, true, &L) != TQ_OK || num_seqs < 0 || max_seq_len < 0 || n_queries < 1 ||
+      n_queries > TQ_MAX_QUERIES)
+    return 0;
+  const int per = queries_per_launch(L);
+  L.G *= n_queries < per ? n_queries : per;
+  return tq_decode_ws_bytes(L, num_seqs, tq_decode_split(L, num_seqs, max_seq_len));
+}
+
+extern "C" int tq_paged_decode_attention_multi(
+    const tq_layer_desc* layer, const void* q, int32_t n_queries, const void* pages,
+    int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len, const void* sink_k,
+    const void* sink_v, int32_t n_sink, float scale, float* out, void* workspace,
+    size_t workspace_bytes, tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, true, &L);
+  if (st != TQ_OK) return st;
+  if (n_queries < 1) return TQ_ERR_INVALID_ARG;
+  if (n_queries > TQ_MAX_QUERIES) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_seq_len < 0 || n_sink < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return TQ_ERR_UNSUPPORTED;
+  if (n_sink > TQ_MAX_SINKS) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return TQ_OK;
+  if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
+    return TQ_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
+  if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
+  const int G = L.G;
+  const int per = queries_per_launch(L);
+  TqLayer Lv = L;
+  Lv.G = G * (n_queries < per ? n_queries : per);
+  const TqSplit sp = tq_decode_split(Lv, num_seqs, max_seq_len);
+  if (workspace_bytes < tq_decode_ws_bytes(Lv, num_seqs, sp)) return TQ_ERR_WORKSPACE;
+  // each group of queries is one split + merge launch pair; the pair after it reuses the
+  // workspace in stream order
+  for (int q0 = 0; q0 < n_queries; q0 += per) {
+    Lv.G = G * (n_queries - q0 < per ? n_queries - q0 : per);
+    if (tq_launch_decode(Lv, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
+                         sink_k, sink_v, n_sink, nullptr, nullptr, nullptr, 0, scale, out,
+                         workspace, stream, n_queries, q0, G) != 0)
+      return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
 extern "C" int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages, int64_t num_blocks,
                                   const int64_t* slots, int64_t n, float* k_out, float* v_out,
                                   tq_stream_t stream) {

@@ -25,6 +25,8 @@
 // page rows; the grid is laid out so that they land on the same XCD (round-robin dispatch puts
 // workgroup i on XCD i % 8) and share its L2.
 
+#include <climits>
+
 #include "tq_device.h"
 
 namespace {
@@ -61,7 +63,24 @@ struct DecodeArgs {
   int win_cap;
   float* out;
   float* partials;   // [B][Hkv][part_stride][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
+  // Several queries per sequence: the kernels' G heads of a kv head are G_real query heads for
+  // each of this launch's queries q0 .. q0 + G / G_real - 1 out of nq (one query: nq = 1, q0 = 0,
+  // g_real = G).
+  int nq, q0, g_real;
 };
+
+// Row (in units of D) of q and out for head v of kv head h: query q0 + v / g_real, query head
+// h * g_real + v % g_real.
+__device__ __forceinline__ int64_t q_row(const DecodeArgs& a, int b, int h, int v) {
+  const int jq = v / a.g_real;
+  return ((int64_t)b * a.nq + a.q0 + jq) * a.L.Hq + (int64_t)h * a.g_real + (v - jq * a.g_real);
+}
+
+// Positions below this are visible to head v: query j of nq sits at position seq_len - nq + j
+// and attends causally (one query: seq_len).
+__device__ __forceinline__ int q_limit(const DecodeArgs& a, int seq_len, int v) {
+  return seq_len - a.nq + a.q0 + v / a.g_real + 1;
+}
 
 // Splits cover absolute positions [split * chunk, (split + 1) * chunk) of a sequence, up to the
 // packed end; positions below n_sink are read from the sink arrays instead and are masked out of
@@ -151,7 +170,7 @@ __device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk, float* 
     float qv[GMAX][8];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      if (g < G) load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, qv[g]);
+      if (g < G) load8_f16(a.q + q_row(a, b, h, g) * D + 8 * j, qv[g]);
       else
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[g][e] = 0.0f;
@@ -168,7 +187,8 @@ __device__ __forceinline__ void fp16_chunk(const DecodeArgs& a, int blk, float* 
 #pragma unroll
           for (int e = 0; e < 8; ++e) d = fmaf(qv[g][e], kx[e], d);
           d = group_sum<LPH>(d);
-          if (g < G && j == 0) s_s[g][r] = d * a.sink_scale;
+          // several queries: a sink past a query's position is masked (no window then)
+          if (g < G && j == 0) s_s[g][r] = r0 + r < q_limit(a, seq_len, g) ? d * a.sink_scale : kSent;
         }
       }
     }
@@ -263,7 +283,7 @@ struct Step {
   LaneCodes<NBK> k;
   LaneCodes<NBV> v;
   float kn, vn;
-  bool valid;
+  int pos;  // position, or INT_MAX past the split's end
 };
 
 template <int D, int KB, int VB, int GMAX>
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     if (g < G) {
-      const uint16_t* qp = a.q + ((int64_t)b * L.Hq + h * G + g) * D + C * j;
+      const uint16_t* qp = a.q + q_row(a, b, h, g) * D + C * j;
 #pragma unroll
       for (int e = 0; e < C; e += 8) load8_f16(qp + e, &qr[g][e]);
 #pragma unroll
@@ -343,8 +363,10 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   }
 
   float m[GMAX], l[GMAX], acc[GMAX][C];
+  int lim[GMAX];  // positions visible to each head (the end of the packed segment, or causal)
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
+    lim[g] = min(p_end, q_limit(a, seq_len, g));
     m[g] = -INFINITY;
     l[g] = 0.0f;
 #pragma unroll
@@ -361,8 +383,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   auto fetch = [&](int it) {
     Step<NBK, NBV> st;
     int p = p_begin + it * TPI + wave * TPW + sub;
-    st.valid = p < p_end;
-    p = st.valid ? p : p_end - 1;
+    st.pos = p < p_end ? p : INT_MAX;
+    p = p < p_end ? p : p_end - 1;
     const int bi = block_of(p);
     const uint8_t* base = head_base + s_boff[bi - blk0] + __umul24((uint32_t)(p - bi * L.bs), row_bytes32);
     st.k = load_lane_codes<NBK>(base, j);
@@ -382,7 +404,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < C; ++e) d += qr[g][e] * kf[e];
       d = group_sum<P>(d);
-      s[g] = st.valid ? st.kn * d : -INFINITY;
+      s[g] = st.pos < lim[g] ? st.kn * d : -INFINITY;
     }
     bool grow = false;
 #pragma unroll
@@ -403,7 +425,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     lookup_codes<VB, C>(st.v, s_vlut, vf);
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      const float pw = st.valid ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
+      const float pw = st.pos < lim[g] ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
       l[g] += pw;
       const float w = pw * st.vn;
 #pragma unroll
@@ -745,7 +767,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   if (tid < LPH * G) {
     const int g = tid / LPH, j = tid % LPH;
     float x[8];
-    load8_f16(a.q + ((int64_t)b * L.Hq + h * G + g) * D + 8 * j, x);
+    load8_f16(a.q + q_row(a, b, h, g) * D + 8 * j, x);
     const uint32_t sb = sign_byte(L.signs, j);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -789,6 +811,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
   const int g0 = q4, g1 = q4 + 4;
   const bool live0 = g0 < G, live1 = G8 && g1 < G;
+  // positions visible to heads g0, g1: the split's end, or earlier for causal queries
+  const int lim0 = min(p_end, q_limit(a, seq_len, g0)), lim1 = min(p_end, q_limit(a, seq_len, g1));
   // Score factors of the heads this lane holds: 2^-(e + 8).
   const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
   const float f1 = live1 ? ldexpf(1.0f, -(head_exp(g1) + kLutShift)) : 0.0f;
@@ -945,9 +969,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p = pbase + 16 * u + t16;
-      const bool valid = p >= ns && p < p_end;
-      s0[u] = (valid && live0) ? (sc[u][0] + sc[u][1]) * kn[u] * f0 : kSent;
-      if (G8) s1[u] = (valid && live1) ? (sc[u][2] + sc[u][3]) * kn[u] * f1 : kSent;
+      s0[u] = (p >= ns && p < lim0 && live0) ? (sc[u][0] + sc[u][1]) * kn[u] * f0 : kSent;
+      if (G8) s1[u] = (p >= ns && p < lim1 && live1) ? (sc[u][2] + sc[u][3]) * kn[u] * f1 : kSent;
       lv[u] = __builtin_amdgcn_logf(vn[u]);  // log2(n_V); -inf for a zero row
     }
     const float ms0 = fmaxf(m_s[0], row16_max(fmaxf(s0[0], s0[1])));
@@ -1170,9 +1193,8 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
   const int nsplit = num_splits(seq_len - (nf - min(a.n_sink, seq_len)), a.chunk);
   const int nrc = (nf + kRowChunk - 1) / kRowChunk;
   const int nparts = nsplit + nrc;
-  float* outp = a.out + ((int64_t)b * L.Hq + h * G) * D;
   if (seq_len == 0) {
-    for (int i = threadIdx.x; i < G * D; i += kWG) outp[i] = 0.0f;
+    for (int i = threadIdx.x; i < G * D; i += kWG) a.out[q_row(a, b, h, i / D) * D + i % D] = 0.0f;
     return;
   }
   __shared__ float s_acc[GMAX * D];  // merged rotated accumulators
@@ -1227,14 +1249,15 @@ __global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) x[e] = s_acc[g * D + 8 * j + e];
     wht_row8_dpp<LPH>(x, j);
     const uint32_t sb = sign_byte(L.signs, j);
-    const float inv_l = 1.0f / s_ml[GMAX + g];
+    // a query before the first position (several queries per sequence) sees nothing: zero
+    const float inv_l = q_limit(a, seq_len, g) > 0 ? 1.0f / s_ml[GMAX + g] : 0.0f;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       o[e] = x[e] * a.rsqrt_d;
       if ((sb >> e) & 1u) o[e] = -o[e];
     }
-    float4* o4 = reinterpret_cast<float4*>(outp + g * D + 8 * j);
+    float4* o4 = reinterpret_cast<float4*>(a.out + q_row(a, b, h, g) * D + 8 * j);
     o4[0] = make_float4(o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l);
     o4[1] = make_float4(o[4] * inv_l, o[5] * inv_l, o[6] * inv_l, o[7] * inv_l);
   }
@@ -1352,7 +1375,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
                      int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                      const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
                      const void* win_v, const int32_t* win_lens, int win_cap, float scale,
-                     float* out, void* workspace, void* stream) {
+                     float* out, void* workspace, void* stream, int nq, int q0, int g_real) {
   if (num_seqs == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
   DecodeArgs a;
@@ -1381,6 +1404,9 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.win_cap = win_cap;
   a.out = out;
   a.partials = (float*)workspace;
+  a.nq = nq;
+  a.q0 = q0;
+  a.g_real = g_real > 0 ? g_real : L.G;
   const long groups = (a.n_units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * L.Hkv));  // packed splits; launch_t adds the row chunks
   const dim3 mgrid((unsigned)(num_seqs * L.Hkv));

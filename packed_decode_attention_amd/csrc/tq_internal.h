@@ -46,7 +46,8 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
                      int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                      const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
                      const void* win_v, const int32_t* win_lens, int win_cap, float scale,
-                     float* out, void* workspace, void* stream);
+                     float* out, void* workspace, void* stream, int nq = 1, int q0 = 0,
+                     int g_real = 0);
 int tq_launch_dequant(const TqLayer& L, const void* pages, const int64_t* slots, int64_t n,
                       float* k_out, float* v_out, void* stream);
 

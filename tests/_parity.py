@@ -198,6 +198,33 @@ class Case:
                                      self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink, seqs=seqs,
                                      win_k16=wk.numpy(), win_v16=wv.numpy(), win_lens=wl_)
 
+    def queries_multi(self, T):
+        """fp16 queries [B, T, H_q, D]: the workload's queries of steps 0 .. T - 1."""
+        from packed_decode_attention_amd import workloads as wl
+        return self._torch.stack([wl.queries(self.w, 0, step) for step in range(T)], dim=1)
+
+    def gpu_decode_multi(self, fmt, pages_dev, qm):
+        import packed_decode_attention_amd as tq
+        torch = self._torch
+        B, T = qm.shape[0], qm.shape[1]
+        max_len = int(self.lens.max()) if B else 0
+        ws = fmt.new_workspace(B, max_len, n_queries=T)
+        out = torch.full((B, T, self.Hq, self.D), float("nan"), dtype=torch.float32, device="cuda")
+        sk = None if self.sink_k is None else self.sink_k.cuda()
+        sv = None if self.sink_v is None else self.sink_v.cuda()
+        tq.tq_paged_decode_attention_multi(fmt.desc, qm.cuda(), pages_dev, self.num_blocks,
+                                           torch.from_numpy(self.bt).cuda(),
+                                           torch.from_numpy(self.lens).cuda(), max_len, out, ws,
+                                           sk, sv, self.w.n_sink)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle_decode_multi(self, qm):
+        sk = None if self.sink_k is None else self.sink_k.numpy()
+        sv = None if self.sink_v is None else self.sink_v.numpy()
+        return oatt.decode_attention_multi(qm.numpy(), self.pages_ref, self.bt, self.lens, self.layer_dict,
+                                           self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink)
+
     def ref_pages_on_gpu(self):
         torch = self._torch
         return torch.from_numpy(self.pages_ref).cuda().reshape(

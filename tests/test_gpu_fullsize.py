@@ -9,7 +9,8 @@ oracle from the same fp16 rows:
     output of the query heads of that kv head must match the oracle's dense attention to the
     attention tolerance.
 The rest of the batch still runs, so the grid, split geometry and workspace are the benchmark's.
-One case uses the norm-correction page format (bench.py --norm-correction).  One case adds a hot
+One case uses the norm-correction page format (bench.py --norm-correction), one decodes two
+causal queries per sequence (bench.py --queries 2).  One case adds a hot
 window (bench.py --hot-window): the last W positions of every sequence also
 come from fp16 rows (the sampled sequences' own rows, random rows elsewhere) and the decode runs
 through tq_paged_decode_attention_window.
@@ -44,20 +45,21 @@ def _pick(w, lens, which):
     return list(which)
 
 
-CASES = [  # workload, layer, sampled sequences, hot window, norm-correction format
-    ("llama3-8b", 1, (0, 13), 0, False),
-    ("mistral-7b", 2, (1,), 0, False),
-    ("ragged", 5, "extremes", 0, False),
-    ("qwen2.5-0.5b", 7, (0, 5), 0, False),
-    ("llama3-8b", 3, (4,), 512, False),
-    ("llama3-8b", 6, (9,), 0, True),
+CASES = [  # workload, layer, sampled sequences, hot window, norm-correction format, queries
+    ("llama3-8b", 1, (0, 13), 0, False, 1),
+    ("mistral-7b", 2, (1,), 0, False, 1),
+    ("ragged", 5, "extremes", 0, False, 1),
+    ("qwen2.5-0.5b", 7, (0, 5), 0, False, 1),
+    ("llama3-8b", 3, (4,), 512, False, 1),
+    ("llama3-8b", 6, (9,), 0, True, 1),
+    ("llama3-8b", 2, (3,), 0, False, 2),
 ]
 
 
-@pytest.mark.parametrize("name,layer,which,window,nc", CASES,
+@pytest.mark.parametrize("name,layer,which,window,nc,nq", CASES,
                          ids=[f"{c[0]}-L{c[1]}" + (f"-W{c[3]}" if c[3] else "") + ("-NC" if c[4] else "")
-                              for c in CASES])
-def test_full_size_sampled(name, layer, which, window, nc):
+                              + (f"-Q{c[5]}" if c[5] > 1 else "") for c in CASES])
+def test_full_size_sampled(name, layer, which, window, nc, nq):
     import torch
     import packed_decode_attention_amd as tq
     from packed_decode_attention_amd import workloads as wl
@@ -126,10 +128,12 @@ def test_full_size_sampled(name, layer, which, window, nc):
         refs[b] = (ref, bt1, L, k, v)
 
     q = wl.queries(w, layer, 0, "cuda")
+    if nq > 1:  # [B, T, H_q, D]: the queries of the last T positions
+        q = torch.stack([wl.queries(w, layer, j, "cuda") for j in range(nq)], dim=1)
     sink_k, sink_v = wl.sinks(w, 0, "cuda")
     max_len = int(lens.max())
-    ws = fmt.new_workspace(B, max_len)
-    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = fmt.new_workspace(B, max_len, n_queries=nq if nq > 1 else 0)
+    out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device="cuda")
     win_lens = np.minimum(window, lens - np.minimum(lens, w.n_sink)).astype(np.int32)
     if window:
         g = torch.Generator(device="cuda").manual_seed(99)
@@ -143,6 +147,10 @@ def test_full_size_sampled(name, layer, which, window, nc):
         tq.tq_paged_decode_attention_window(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
                                             torch.from_numpy(lens).cuda(), max_len, out, ws, win_k, win_v,
                                             torch.from_numpy(win_lens).cuda(), sink_k, sink_v, w.n_sink)
+    elif nq > 1:
+        tq.tq_paged_decode_attention_multi(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
+                                           torch.from_numpy(lens).cuda(), max_len, out, ws, sink_k,
+                                           sink_v, w.n_sink)
     else:
         tq.tq_paged_decode_attention(fmt.desc, q, pages, num_blocks, torch.from_numpy(bt_np).cuda(),
                                      torch.from_numpy(lens).cuda(), max_len, out, ws, sink_k, sink_v,
@@ -160,9 +168,15 @@ def test_full_size_sampled(name, layer, which, window, nc):
         qh = slice(hh * G, (hh + 1) * G)  # the query heads that read kv head hh
         nw = int(win_lens[b])
         wkw = dict(win_k16=k[L - nw:L][None], win_v16=v[L - nw:L][None], win_lens=np.array([nw])) if window else {}
-        want = oatt.decode_attention(qn[b:b + 1, qh], ref, bt1, np.array([L], np.int32), layer_dict, kc, vc,
-                                     None if skn is None else skn[b:b + 1, :, hh:hh + 1],
-                                     None if svn is None else svn[b:b + 1, :, hh:hh + 1], w.n_sink, **wkw)
-        max_abs, rel = check_attention(got[b:b + 1, qh], want)
+        sks = None if skn is None else skn[b:b + 1, :, hh:hh + 1]
+        svs = None if svn is None else svn[b:b + 1, :, hh:hh + 1]
+        if nq > 1:
+            want = oatt.decode_attention_multi(qn[b:b + 1, :, qh], ref, bt1, np.array([L], np.int32),
+                                               layer_dict, kc, vc, sks, svs, w.n_sink)
+            max_abs, rel = check_attention(got[b:b + 1, :, qh].reshape(nq, G, D), want.reshape(nq, G, D))
+        else:
+            want = oatt.decode_attention(qn[b:b + 1, qh], ref, bt1, np.array([L], np.int32), layer_dict,
+                                         kc, vc, sks, svs, w.n_sink, **wkw)
+            max_abs, rel = check_attention(got[b:b + 1, qh], want)
         print(f"[fullsize]   seq {b} kv head {hh}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}",
               flush=True)

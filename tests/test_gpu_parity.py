@@ -116,6 +116,31 @@ def test_decode_attention(cases, name):
     assert np.all(got[zero] == 0)
 
 
+# Several causal queries per sequence: (case, T).  T * G <= 8 runs as one launch on the kernels'
+# 8-head instances; more queries take several launches over the same workspace.  The cases cover
+# the matrix-core kernel (G = 4 at T = 1, 2, 3, 5; G = 8; D = 64 with G = 5), the vector kernel
+# (edges: G = 3, 2/3-bit codes, block size 7), sinks, and sequences shorter than T.
+MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
+         ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4)]
+
+
+@pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
+def test_decode_attention_multi_query(cases, name, T):
+    c = get(cases, name)
+    fmt = c.fmt()
+    qm = c.queries_multi(T)
+    print(f"[parity] multi-query {name} T={T}: lens={c.lens.tolist()} Hq={c.Hq} H={c.H}", flush=True)
+    want = c.oracle_decode_multi(qm)
+    got = c.gpu_decode_multi(fmt, c.ref_pages_on_gpu(), qm)
+    check_attention(got.reshape(-1, c.Hq, c.D), want.reshape(-1, c.Hq, c.D))
+    vis = c.lens[:, None] - T + np.arange(T)[None, :] + 1   # positions each query sees
+    assert np.all(got[vis <= 0] == 0)
+    if T == 1:  # one query is the single-query call, bit for bit
+        assert np.array_equal(qm[:, 0].numpy(), c.q.numpy())
+        single, _ = c.gpu_decode(fmt, c.ref_pages_on_gpu())
+        assert np.array_equal(got[:, 0].view(np.uint32), single.view(np.uint32))
+
+
 # Hot-window lengths per sequence (each <= L - min(n_sink, L)) and the window capacity: a window
 # per case shape, including windows that hold every non-sink token (no packed tokens left), a
 # one-token window (the current token only) and the largest capacity.

@@ -131,6 +131,16 @@ def test_argument_validation_before_launch(lib):
     assert decw(_desc(lib), cap=0, wk=None, wl=None, B=0) == E.TQ_OK     # no window, nothing to do
     assert decw(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
 
+    def decm(d, T=2, ws_bytes=1 << 40, B=4, n_sink=0, sk=None):
+        return so.tq_paged_decode_attention_multi(ctypes.byref(d), P, T, P, 100, P, 7, P, B, 100, sk,
+                                                  sk, n_sink, 0.0, P, P, ws_bytes, None)
+    assert decm(_desc(lib), T=0) == E.TQ_ERR_INVALID_ARG
+    assert decm(_desc(lib), T=65) == E.TQ_ERR_UNSUPPORTED                 # above TQ_MAX_QUERIES
+    assert decm(_desc(lib), ws_bytes=16) == E.TQ_ERR_WORKSPACE
+    assert decm(_desc(lib), n_sink=2) == E.TQ_ERR_INVALID_ARG             # sinks without arrays
+    assert decm(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
+    assert decm(_desc(lib), B=0) == E.TQ_OK
+
     dq = lambda d, n=3: so.tq_dequantize_rows(ctypes.byref(d), P, 10, P, n, P, P, None)
     assert dq(_desc(lib, head_dim=256)) == E.TQ_ERR_UNSUPPORTED
     assert dq(_desc(lib), n=-2) == E.TQ_ERR_INVALID_ARG
@@ -147,6 +157,20 @@ def test_workspace_bytes(lib):
     # split partials: (m, l, acc[D]) per sequence, query head and split
     assert a >= 16 * 8 * 4 * 130 * 4 and a % (32 * 130 * 4) == 0
     assert so.tq_decode_workspace_bytes(ctypes.byref(_desc(lib, head_dim=80)), 16, 100) == 0
+
+
+def test_multi_query_workspace_bytes(lib):
+    so = lib._lib()
+    d = _desc(lib)                                       # G = 4: two queries per launch
+    one = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 32769)
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 1) == one
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 2) == 2 * one
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 7) == 2 * one  # launches reuse it
+    g8 = _desc(lib, num_q_heads=64)                      # G = 8: one query per launch
+    assert (so.tq_decode_multi_workspace_bytes(ctypes.byref(g8), 4, 1000, 5) ==
+            so.tq_decode_workspace_bytes(ctypes.byref(g8), 4, 1000))
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 100, 0) == 0
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 100, 65) == 0
 
 
 def test_status_strings(lib):
