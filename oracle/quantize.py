@@ -27,6 +27,14 @@ Readings taken where the pages are silent (each is also listed in the design not
   slot_bytes and a larger slot stride are zero.
 * Dequantized row (bit-exact route): c_hat_i = c[idx_i] (fp32); z = H c_hat exactly (fp64 is
   exact here, asserted); g = fp32(n * fp32(1/sqrt(D))); x_hat_i = s_i * fp32(fp32(z_i) * g).
+* Per-token mean removal (format flag; tq-kv, "How It Works": the quantiser's per-token mean
+  removal stage, and the mean in its output record): mu = fp32(tree(fp32(x_i))) / D (the
+  stride-halving fp32 tree of the row's values; division by the power of two D is exact); the
+  row is centred, d_i = fp32(x_i - mu); the stored norm is n = fp32 sqrt(tree(fp32(d_i^2))); the
+  rotated coordinate is u = R (x - mu 1) / ||x - mu 1|| (fp64); the region gains mu as a second
+  fp32 after the norm; the dequantized row is fp32(x_hat_i + mu) (plain route: n R^T c + mu 1).
+  A constant row has d = 0: it stores norm 0, indices L/2 and mu = its value, and dequantizes
+  exactly.
 * Norm correction (format flag; tq-kv, "How It Works": "Lloyd-Max codebook + norm correction",
   output "packed indices + corrected norm"): the stored norm is n' = n / ||c_hat||_2, so the
   dequantized row n' R^T c_hat keeps the input row's L2 norm.  ||c_hat||^2 is the stride-halving
@@ -48,14 +56,15 @@ TIE_BAND = 1e-6
 # --------------------------------------------------------------------------------------------
 # Sizes.
 # --------------------------------------------------------------------------------------------
-def region_bytes(D: int, bits: int) -> int:
-    """ceil(D * bits / 8) packed index bytes + 4 bytes of fp32 norm (TQ4 page tensor figure)."""
-    return (D * bits + 7) // 8 + 4
+def region_bytes(D: int, bits: int, mean: bool = False) -> int:
+    """ceil(D * bits / 8) packed index bytes + 4 bytes of fp32 norm (TQ4 page tensor figure), + 4
+    bytes of fp32 mean with mean removal."""
+    return (D * bits + 7) // 8 + 4 + (4 if mean else 0)
 
 
-def slot_bytes(D: int, k_bits: int, v_bits: int) -> int:
+def slot_bytes(D: int, k_bits: int, v_bits: int, mean: bool = False) -> int:
     """K region + V region (TQ4 page tensor figure)."""
-    return region_bytes(D, k_bits) + region_bytes(D, v_bits)
+    return region_bytes(D, k_bits, mean) + region_bytes(D, v_bits, mean)
 
 
 # --------------------------------------------------------------------------------------------
@@ -72,9 +81,24 @@ def norm_fp32(x16: np.ndarray) -> np.ndarray:
     return np.sqrt(sq[..., 0]).astype(np.float32)
 
 
-def rotated_unit(x16: np.ndarray, seed: int) -> np.ndarray:
-    """u = R x / ||x|| in fp64 (rows of zeros give u = 0)."""
+def row_mean(x16: np.ndarray) -> np.ndarray:
+    """Mean-removal format: mu = fp32(stride-halving fp32 tree of the fp16 values) / D."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    return (_tree_sum32(x) / np.float32(x.shape[-1])).astype(np.float32)
+
+
+def centered_norm(x16: np.ndarray, mu32: np.ndarray) -> np.ndarray:
+    """Mean-removal format: d_i = fp32(x_i - mu), n = fp32 sqrt(tree(fp32(d_i^2)))."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    d = (x - np.asarray(mu32, np.float32)[..., None]).astype(np.float32)
+    return np.sqrt(_tree_sum32((d * d).astype(np.float32))).astype(np.float32)
+
+
+def rotated_unit(x16: np.ndarray, seed: int, mu32=None) -> np.ndarray:
+    """u = R x / ||x|| in fp64 (rows of zeros give u = 0); with mu32, u = R (x - mu) / ||x - mu||."""
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    if mu32 is not None:
+        x = x - np.asarray(mu32, np.float32).astype(np.float64)[..., None]
     R = rotation.rotation_matrix(seed, x.shape[-1])
     y = x @ R.T
     n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
@@ -114,15 +138,18 @@ def corrected_norm(n32: np.ndarray, idx: np.ndarray, centroids32: np.ndarray) ->
     return np.where(n > 0, q, np.float32(0)).astype(np.float32)
 
 
-def quantize_rows(x16: np.ndarray, boundaries32: np.ndarray, seed: int, centroids32=None):
-    """Quantize fp16 rows [..., D]: returns (idx int64 [..., D], norm fp32 [...], tie bool [..., D]).
-    With centroids32 the stored norm is the corrected one (norm-correction format)."""
-    u = rotated_unit(x16, seed)
+def quantize_rows(x16: np.ndarray, boundaries32: np.ndarray, seed: int, centroids32=None,
+                  mean: bool = False):
+    """Quantize fp16 rows [..., D]: returns (idx int64 [..., D], norm fp32 [...], tie bool [..., D]),
+    and with mean removal also mu fp32 [...] as a fourth value.  With centroids32 the stored norm
+    is the corrected one (norm-correction format)."""
+    mu = row_mean(x16) if mean else None
+    u = rotated_unit(x16, seed, mu)
     idx, tie = indices_for(u, boundaries32)
-    n = norm_fp32(x16)
+    n = centered_norm(x16, mu) if mean else norm_fp32(x16)
     if centroids32 is not None:
         n = corrected_norm(n, idx, centroids32)
-    return idx, n, tie
+    return (idx, n, tie, mu) if mean else (idx, n, tie)
 
 
 # --------------------------------------------------------------------------------------------
@@ -218,8 +245,9 @@ def exact_wht(chat32: np.ndarray) -> np.ndarray:
     return z
 
 
-def dequantize_spec(idx: np.ndarray, norm32, centroids32: np.ndarray, seed: int) -> np.ndarray:
-    """Bit-exact fp32 reconstruction: x_hat_i = s_i * fp32(fp32(z_i) * fp32(n * fp32(1/sqrt(D))))."""
+def dequantize_spec(idx: np.ndarray, norm32, centroids32: np.ndarray, seed: int, mu32=None) -> np.ndarray:
+    """Bit-exact fp32 reconstruction: x_hat_i = s_i * fp32(fp32(z_i) * fp32(n * fp32(1/sqrt(D)))),
+    then fp32(x_hat_i + mu) with mean removal."""
     idx = np.asarray(idx)
     D = idx.shape[-1]
     chat = np.asarray(centroids32, dtype=np.float32)[idx]
@@ -227,29 +255,45 @@ def dequantize_spec(idx: np.ndarray, norm32, centroids32: np.ndarray, seed: int)
     rD = np.float32(1.0 / math.sqrt(D))
     g = (np.asarray(norm32, dtype=np.float32) * rD).astype(np.float32)
     s = rotation.signs(seed, D).astype(np.float32)
-    return (s * (z32 * g[..., None]).astype(np.float32)).astype(np.float32)
+    x = (s * (z32 * g[..., None]).astype(np.float32)).astype(np.float32)
+    if mu32 is not None:
+        x = (x + np.asarray(mu32, np.float32)[..., None]).astype(np.float32)
+    return x
 
 
-def dequantize_plain(idx: np.ndarray, norm32, centroids32: np.ndarray, seed: int) -> np.ndarray:
-    """x_hat = n R^T c_hat, in fp64 (the plain definition)."""
+def dequantize_plain(idx: np.ndarray, norm32, centroids32: np.ndarray, seed: int, mu32=None) -> np.ndarray:
+    """x_hat = n R^T c_hat (+ mu 1 with mean removal), in fp64 (the plain definition)."""
     idx = np.asarray(idx)
     D = idx.shape[-1]
     chat = np.asarray(centroids32, dtype=np.float32).astype(np.float64)[idx]
     R = rotation.rotation_matrix(seed, D)
-    return np.asarray(norm32, dtype=np.float64)[..., None] * (chat @ R)
+    x = np.asarray(norm32, dtype=np.float64)[..., None] * (chat @ R)
+    if mu32 is not None:
+        x = x + np.asarray(mu32, np.float32).astype(np.float64)[..., None]
+    return x
 
 
 # --------------------------------------------------------------------------------------------
 # Vectorised forms of the packer (same bitstream; pinned against the per-row forms above).
 # --------------------------------------------------------------------------------------------
-def pack_regions(idx: np.ndarray, norms: np.ndarray, bits: int) -> np.ndarray:
-    """Pack many rows at once: idx [N, D] -> uint8 [N, region_bytes(D, bits)]."""
+def pack_regions(idx: np.ndarray, norms: np.ndarray, bits: int, means=None) -> np.ndarray:
+    """Pack many rows at once: idx [N, D] -> uint8 [N, region_bytes(D, bits)] (the mean, when
+    given, follows the norm)."""
     idx = np.asarray(idx, dtype=np.int64)
     N, D = idx.shape
     bitplanes = ((idx[:, :, None] >> np.arange(bits)[None, None, :]) & 1).astype(np.uint8)
     body = np.packbits(bitplanes.reshape(N, D * bits), axis=1, bitorder="little")
-    nb = np.asarray(norms, dtype="<f4").reshape(N, 1).view(np.uint8)
-    return np.concatenate([body, nb], axis=1)
+    parts = [body, np.asarray(norms, dtype="<f4").reshape(N, 1).view(np.uint8)]
+    if means is not None:
+        parts.append(np.asarray(means, dtype="<f4").reshape(N, 1).view(np.uint8))
+    return np.concatenate(parts, axis=1)
+
+
+def unpack_means(buf: np.ndarray, D: int, bits: int) -> np.ndarray:
+    """The fp32 means of mean-removal regions uint8 [N, region_bytes(D, bits, True)]."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    nbytes = (D * bits + 7) // 8
+    return np.ascontiguousarray(buf[:, nbytes + 4:nbytes + 8]).view("<f4").reshape(-1).astype(np.float32)
 
 
 def unpack_regions(buf: np.ndarray, D: int, bits: int):
@@ -266,17 +310,21 @@ def unpack_regions(buf: np.ndarray, D: int, bits: int):
 
 def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, v_boundaries32,
                      k_bits: int, v_bits: int, seed: int, slot_stride: int | None = None,
-                     k_centroids32=None, v_centroids32=None):
-    """append_rows() with the vectorised packer (same bytes; used for larger test cases)."""
+                     k_centroids32=None, v_centroids32=None, mean: bool = False):
+    """append_rows() with the vectorised packer (same bytes; used for larger test cases); mean:
+    the mean-removal format."""
     n_tok, H_kv, D = k16.shape
-    sb = slot_bytes(D, k_bits, v_bits)
+    sb = slot_bytes(D, k_bits, v_bits, mean)
     stride = sb if slot_stride is None else slot_stride
-    k_idx, k_n, k_tie = quantize_rows(k16, k_boundaries32, seed, k_centroids32)
-    v_idx, v_n, v_tie = quantize_rows(v16, v_boundaries32, seed, v_centroids32)
+    kq = quantize_rows(k16, k_boundaries32, seed, k_centroids32, mean)
+    vq = quantize_rows(v16, v_boundaries32, seed, v_centroids32, mean)
+    (k_idx, k_n, k_tie), (v_idx, v_n, v_tie) = kq[:3], vq[:3]
+    k_mu = kq[3].reshape(-1) if mean else None
+    v_mu = vq[3].reshape(-1) if mean else None
     rows = np.zeros((n_tok, H_kv, stride), dtype=np.uint8)
-    kr = region_bytes(D, k_bits)
-    rows[:, :, :kr] = pack_regions(k_idx.reshape(-1, D), k_n.reshape(-1), k_bits).reshape(n_tok, H_kv, kr)
-    rows[:, :, kr:sb] = pack_regions(v_idx.reshape(-1, D), v_n.reshape(-1), v_bits).reshape(n_tok, H_kv, sb - kr)
+    kr = region_bytes(D, k_bits, mean)
+    rows[:, :, :kr] = pack_regions(k_idx.reshape(-1, D), k_n.reshape(-1), k_bits, k_mu).reshape(n_tok, H_kv, kr)
+    rows[:, :, kr:sb] = pack_regions(v_idx.reshape(-1, D), v_n.reshape(-1), v_bits, v_mu).reshape(n_tok, H_kv, sb - kr)
     view = pages.reshape(-1, H_kv, stride)
     sm = np.asarray(slot_mapping, dtype=np.int64)
     keep = sm >= 0
@@ -285,15 +333,20 @@ def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, 
 
 
 def read_slots(pages: np.ndarray, slots: np.ndarray, H_kv: int, D: int, k_bits: int, v_bits: int,
-               slot_stride: int | None = None):
-    """Unpack many slots: returns (k_idx, k_n, v_idx, v_n) shaped [n, H_kv, D] / [n, H_kv]."""
-    sb = slot_bytes(D, k_bits, v_bits)
+               slot_stride: int | None = None, mean: bool = False):
+    """Unpack many slots: returns (k_idx, k_n, v_idx, v_n) shaped [n, H_kv, D] / [n, H_kv], and
+    (k_mu, v_mu) [n, H_kv] after them for the mean-removal format."""
+    sb = slot_bytes(D, k_bits, v_bits, mean)
     stride = sb if slot_stride is None else slot_stride
     view = pages.reshape(-1, H_kv, stride)
     rows = view[np.asarray(slots, dtype=np.int64)]            # [n, H_kv, stride]
     n = rows.shape[0]
-    kr = region_bytes(D, k_bits)
-    k_idx, k_n = unpack_regions(rows[:, :, :kr].reshape(n * H_kv, kr), D, k_bits)
-    v_idx, v_n = unpack_regions(rows[:, :, kr:sb].reshape(n * H_kv, sb - kr), D, v_bits)
-    return (k_idx.reshape(n, H_kv, D), k_n.reshape(n, H_kv),
-            v_idx.reshape(n, H_kv, D), v_n.reshape(n, H_kv))
+    kr = region_bytes(D, k_bits, mean)
+    kbuf = rows[:, :, :kr].reshape(n * H_kv, kr)
+    vbuf = rows[:, :, kr:sb].reshape(n * H_kv, sb - kr)
+    k_idx, k_n = unpack_regions(kbuf, D, k_bits)
+    v_idx, v_n = unpack_regions(vbuf, D, v_bits)
+    out = (k_idx.reshape(n, H_kv, D), k_n.reshape(n, H_kv), v_idx.reshape(n, H_kv, D), v_n.reshape(n, H_kv))
+    if mean:
+        out += (unpack_means(kbuf, D, k_bits).reshape(n, H_kv), unpack_means(vbuf, D, v_bits).reshape(n, H_kv))
+    return out

@@ -621,3 +621,87 @@ def test_multi_query_more_queries_than_tokens(rng):
     vhat = quantize.dequantize_plain(v_idx, v_n, cv.centroids32, 0)
     np.testing.assert_allclose(o[0, 2], np.broadcast_to(vhat[0, 0], (H_kv * G, D)), atol=1e-12)  # one token
     assert np.abs(o[0, 3] - o[0, 2]).max() > 1e-6
+
+
+# ============================================================================================
+# Per-token mean removal (tq-kv, "How It Works": the per-token mean removal stage and the mean in
+# the output record): mu is stored after the norm and added back on dequantization.
+# ============================================================================================
+def test_mean_removal_constant_row_is_exact():
+    D, bits = 64, 3
+    cb = codebook.codebook(D, bits)
+    x = np.full((2, D), [[1.375], [-0.046875]], np.float16)
+    idx, n, tie, mu = quantize.quantize_rows(x, cb.boundaries32, 0, mean=True)
+    assert np.all(idx == (1 << bits) // 2) and np.all(n == 0)
+    assert np.array_equal(mu, x[:, 0].astype(np.float32))
+    xhat = quantize.dequantize_spec(idx, n, cb.centroids32, 0, mu)
+    assert np.array_equal(xhat, x.astype(np.float32))
+
+
+def test_mean_removal_shift_moves_only_the_mean(rng):
+    # integer-valued rows: every sum is exact, so a shift by 8 changes mu by exactly 8 and
+    # leaves the centred row, its norm and its indices unchanged
+    D = 128
+    cb = codebook.codebook(D, 4)
+    x = rng.integers(-20, 21, (16, D)).astype(np.float16)
+    a = quantize.quantize_rows(x, cb.boundaries32, 0, mean=True)
+    b = quantize.quantize_rows((x + 8).astype(np.float16), cb.boundaries32, 0, mean=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(b[3], a[3] + np.float32(8))
+
+
+def test_mean_removal_by_brute_force(rng):
+    # the fp32 operations written out element by element for one row
+    D = 16
+    x = (rng.standard_normal(D) * 3).astype(np.float16)
+    vals = [np.float32(v) for v in x]
+    h = D // 2
+    while h >= 1:
+        vals = [np.float32(vals[i] + vals[i + h]) for i in range(h)]
+        h //= 2
+    mu = np.float32(vals[0] / np.float32(D))
+    d = [np.float32(np.float32(v) - mu) for v in x]
+    sq = [np.float32(e * e) for e in d]
+    h = D // 2
+    while h >= 1:
+        sq = [np.float32(sq[i] + sq[i + h]) for i in range(h)]
+        h //= 2
+    n = np.float32(np.sqrt(sq[0]))
+    assert quantize.row_mean(x[None])[0].view(np.uint32) == mu.view(np.uint32)
+    assert quantize.centered_norm(x[None], np.array([mu]))[0].view(np.uint32) == n.view(np.uint32)
+
+
+def test_mean_removal_reconstructs_offset_rows_better(rng):
+    D, bits = 128, 2
+    cb = codebook.codebook(D, bits)
+    x = (rng.standard_normal((64, D)) * 0.3 + 2.0).astype(np.float16)   # a large common offset
+    xf = x.astype(np.float64)
+    cos = lambda a: np.sum(a * xf, -1) / (np.linalg.norm(a, axis=-1) * np.linalg.norm(xf, axis=-1))
+    idx, n, _ = quantize.quantize_rows(x, cb.boundaries32, 0)
+    plain = quantize.dequantize_plain(idx, n, cb.centroids32, 0)
+    idx_m, n_m, _, mu = quantize.quantize_rows(x, cb.boundaries32, 0, mean=True)
+    centred = quantize.dequantize_plain(idx_m, n_m, cb.centroids32, 0, mu)
+    err = lambda a: np.linalg.norm(a - xf, axis=-1) / np.linalg.norm(xf, axis=-1)
+    assert np.median(err(centred)) < 0.5 * np.median(err(plain))
+    assert np.all(cos(centred) > 0.99)
+    # the spec route agrees with the plain one within a few ulp
+    spec = quantize.dequantize_spec(idx_m, n_m, cb.centroids32, 0, mu)
+    np.testing.assert_allclose(spec, centred, rtol=0, atol=4 * np.spacing(np.float32(np.abs(centred).max())))
+
+
+@pytest.mark.parametrize("D, H_kv, G, kb, vb, L, ns", [(64, 2, 2, 4, 8, 37, 0), (128, 1, 4, 2, 3, 50, 4)])
+def test_attention_routes_agree_with_mean_removal(D, H_kv, G, kb, vb, L, ns, rng):
+    ck, cv = codebook.codebook(D, kb), codebook.codebook(D, vb)
+    nb = (L + 15) // 16
+    bt = rng.permutation(nb + 2)[:nb]
+    k = (rng.standard_normal((L, H_kv, D)) + rng.standard_normal((L, H_kv, 1)) * 3).astype(np.float16)
+    v = (rng.standard_normal((L, H_kv, D)) + rng.standard_normal((L, H_kv, 1)) * 3).astype(np.float16)
+    slots = bt[np.arange(L) // 16] * 16 + np.arange(L) % 16
+    pages = np.zeros((nb + 2) * 16 * H_kv * quantize.slot_bytes(D, kb, vb, True), np.uint8)
+    quantize.append_rows_fast(pages, k, v, slots, ck.boundaries32, cv.boundaries32, kb, vb, 0, mean=True)
+    layer = dict(D=D, H_kv=H_kv, block_size=16, k_bits=kb, v_bits=vb, seed=0, mean=True)
+    q = rng.standard_normal((1, H_kv * G, D)).astype(np.float16)
+    sk = rng.standard_normal((1, max(ns, 1), H_kv, D)).astype(np.float16)
+    args = (q, pages, bt[None], np.array([L]), layer, ck.centroids32, cv.centroids32, sk, sk, ns)
+    np.testing.assert_allclose(attention.decode_attention(*args), attention.decode_attention_rotated(*args),
+                               atol=1e-12, rtol=0)
