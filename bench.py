@@ -91,7 +91,8 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
     return new_k, new_v
 
 
-def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, n_queries=1):
+def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, n_queries=1,
+          mean_removal=False):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -109,7 +110,8 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, 
         kb, vb = w.bits(l)
         if (kb, vb) not in fmts:
             fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0,
-                                            norm_correction=norm_correction)
+                                            norm_correction=norm_correction,
+                                            mean_removal=mean_removal)
         fmt = fmts[(kb, vb)]
         pages = fmt.new_pages(num_blocks)
         t_layer = fill_layer(w, l, fmt, pages, ctx_slots, num_blocks, torch, tq, wl)
@@ -193,7 +195,7 @@ def run_step(w, S, tq, step, ev=None):
             ev["d1"][l].record()
 
 
-def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1):
+def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1, flags=0):
     """Bytes the decode of one layer must move (with a hot window of win_lens[b] fp16 rows; with
     n_queries queries per sequence, that many query and output rows)."""
     B, H, D = w.num_seqs, w.num_kv_heads, w.head_dim
@@ -201,7 +203,7 @@ def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1):
     per_layer = []
     for l in range(w.layers):
         kb, vb = w.bits(l)
-        sb = tq.tq_slot_bytes(D, kb, vb)
+        sb = tq.tq_slot_bytes_ex(D, kb, vb, flags)
         page_tok = np.maximum(lens - w.n_sink - win, 0)
         b = int(page_tok.sum()) * H * sb                                  # packed slots
         b += int(win.sum()) * H * D * 2 * 2                               # fp16 window rows
@@ -314,6 +316,8 @@ def main():
                          "tq_paged_decode_attention_window)")
     ap.add_argument("--norm-correction", action="store_true",
                     help="store corrected norms n / ||c[idx]|| (the norm-correction page format)")
+    ap.add_argument("--mean-removal", action="store_true",
+                    help="centre each row and store its mean (the mean-removal page format)")
     ap.add_argument("--queries", type=int, default=1, metavar="T",
                     help="decode T causal queries per sequence (its last T positions) per call, "
                          "through tq_paged_decode_attention_multi")
@@ -339,7 +343,8 @@ def main():
     t0 = time.time()
     if args.queries > 1 and args.hot_window:
         sys.exit("--queries and --hot-window do not combine (the multi-query call has no window)")
-    S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction, args.queries)
+    S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction, args.queries,
+              args.mean_removal)
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -369,14 +374,17 @@ def main():
     lens = S["lens"]
     kv_tokens_step = int(lens.sum()) * w.layers
     value = kv_tokens_step / (ms_per_step / 1e3)
+    fmt_flags = (tq.TQ_FLAG_NORM_CORRECTION if args.norm_correction else 0) | \
+                (tq.TQ_FLAG_MEAN_REMOVAL if args.mean_removal else 0)
     per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None,
-                                        args.queries)
+                                        args.queries, fmt_flags)
     layer_ids = np.arange(n) % w.layers
     dec_bytes = np.array([per_layer_bytes[i] for i in layer_ids], np.float64)
     achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
     bulk_ms = float(np.mean(S["bulk_ms"])) if S["bulk_ms"] else float("nan")
     kb, vb = w.bits(1 % w.layers)
-    bulk_bytes = S["n_ctx"] * w.num_kv_heads * (4 * w.head_dim + tq.tq_slot_bytes(w.head_dim, kb, vb)) + S["n_ctx"] * 8
+    bulk_bytes = (S["n_ctx"] * w.num_kv_heads * (4 * w.head_dim + tq.tq_slot_bytes_ex(w.head_dim, kb, vb, fmt_flags))
+                  + S["n_ctx"] * 8)
     result = {
         "metric": METRIC,
         "value": value,
@@ -393,12 +401,14 @@ def main():
         "config": {"workload": describe(w) + (f", fp16 hot window of {args.hot_window} tokens"
                                              if args.hot_window else "")
                                + (", norm-correction format" if args.norm_correction else "")
+                               + (", mean-removal format" if args.mean_removal else "")
                                + (f", {args.queries} causal queries per sequence" if args.queries > 1 else ""),
                    "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (args.hot_window or args.queries > 1) else recorded_traffic(w),
+                     "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal)
+                                 else recorded_traffic(w)),
                      "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},

@@ -67,8 +67,18 @@ typedef enum tq_codebook_family {
  *   by the stride-halving tree over the rotated coordinates (pairs i, i + D/2 first) of the
  *   fp32-rounded squares; the square root and the division are correctly rounded; a zero row
  *   keeps a zero norm.  Only tq_quantize_append changes: decode and dequantize read the stored
- *   norm as it is.  Other bits must be 0. */
+ *   norm as it is.
+ *   TQ_FLAG_MEAN_REMOVAL  (tq-kv, "How It Works": per-token mean removal, and the mean in the
+ *   output record) each region stores the row mean mu as a second fp32 after the norm (region
+ *   bytes ceil(D*bits/8) + 8; see tq_slot_bytes_ex).  mu is the stride-halving fp32 tree sum of
+ *   the row divided by D; the row is centred, d = fp32(x - mu), n is the norm of d (fp32-rounded
+ *   squares, the same tree, correctly rounded sqrt) and the codes encode R d / n.  The
+ *   dequantized row is fp32(x_hat + mu), so decode adds mu * sum(q) to each score and the
+ *   weighted means to each output.  Combines with TQ_FLAG_NORM_CORRECTION (which then corrects
+ *   the norm of d).
+ * Other bits must be 0. */
 #define TQ_FLAG_NORM_CORRECTION 1
+#define TQ_FLAG_MEAN_REMOVAL 2
 
 /* One layer's format.  K and V may use different bit widths (tiny-turboquant 0.12.0.3,
  * "Current status": q8k-q8v and q8k-int4v policies; TorbuQuant docs, "Current Status": K8/K4 and
@@ -114,6 +124,10 @@ int tq_rht_signs(int32_t D, uint64_t seed, int8_t* out);
 /* Bytes of one slot: (ceil(D*k_bits/8) + 4) + (ceil(D*v_bits/8) + 4) (TorbuQuant docs,
  * "TQ4 page tensor" figure).  Returns a negative tq_status for unsupported arguments. */
 int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits);
+
+/* Bytes of one slot of a format with flags (TQ_FLAG_*): each region gains 4 bytes with
+ * TQ_FLAG_MEAN_REMOVAL.  Returns a negative tq_status for unsupported arguments or flags. */
+int32_t tq_slot_bytes_ex(int32_t D, int32_t k_bits, int32_t v_bits, int32_t flags);
 
 /* Quantize-on-append (turboquant-serve 0.1.2, "Architecture" update(); TorbuQuant docs,
  * "TQ4 page tensor" figure; turboquant-pro 1.4.2, "How It Works" per-vector flow).

@@ -27,10 +27,12 @@ from ._lib import (  # noqa: F401
     tq_quantize_append,
     tq_rht_signs,
     tq_slot_bytes,
+    tq_slot_bytes_ex,
     tq_status_str,
 )
 
 TQ_FLAG_NORM_CORRECTION = 1  # tq_layer_desc.flags: stored norms are n / ||c[idx]|| (include/tq.h)
+TQ_FLAG_MEAN_REMOVAL = 2     # tq_layer_desc.flags: rows centred, the mean stored after the norm
 
 _CODEBOOKS: dict = {}
 
@@ -51,13 +53,15 @@ class LayerFormat:
     def __init__(self, head_dim: int, num_q_heads: int, num_kv_heads: int, k_bits: int,
                  v_bits: int, block_size: int = 16, rht_seed: int = 0, family: str = "beta",
                  slot_stride: int = 0, device="cuda", k_codebook=None, v_codebook=None,
-                 norm_correction: bool = False):
+                 norm_correction: bool = False, mean_removal: bool = False):
         import torch
         self.head_dim, self.num_q_heads, self.num_kv_heads = head_dim, num_q_heads, num_kv_heads
         self.k_bits, self.v_bits, self.block_size = k_bits, v_bits, block_size
         self.rht_seed, self.family = rht_seed, family
-        self.norm_correction = norm_correction
-        self.slot_bytes = tq_slot_bytes(head_dim, k_bits, v_bits)
+        self.norm_correction, self.mean_removal = norm_correction, mean_removal
+        self.flags = ((TQ_FLAG_NORM_CORRECTION if norm_correction else 0)
+                      | (TQ_FLAG_MEAN_REMOVAL if mean_removal else 0))
+        self.slot_bytes = tq_slot_bytes_ex(head_dim, k_bits, v_bits, self.flags)
         self.slot_stride = slot_stride or self.slot_bytes
         kc, kt = k_codebook if k_codebook is not None else host_codebook(head_dim, k_bits, family)
         vc, vt = v_codebook if v_codebook is not None else host_codebook(head_dim, v_bits, family)
@@ -67,7 +71,7 @@ class LayerFormat:
         self.desc = tq_layer_desc(
             head_dim=head_dim, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
             block_size=block_size, k_bits=k_bits, v_bits=v_bits, slot_stride=slot_stride,
-            flags=TQ_FLAG_NORM_CORRECTION if norm_correction else 0, rht_seed=rht_seed,
+            flags=self.flags, rht_seed=rht_seed,
             k_centroids=self.k_centroids.data_ptr(), k_boundaries=self.k_boundaries.data_ptr(),
             v_centroids=self.v_centroids.data_ptr(), v_boundaries=self.v_boundaries.data_ptr())
 

@@ -25,7 +25,7 @@ TQ_ERR_NO_CONVERGENCE = -5
 
 FAMILIES = {"beta": 0, "gaussian": 1}
 
-EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_quantize_append",
+EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_slot_bytes_ex", "tq_quantize_append",
            "tq_decode_workspace_bytes", "tq_paged_decode_attention",
            "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
            "tq_paged_decode_attention_multi", "tq_dequantize_rows", "tq_status_str")
@@ -74,6 +74,8 @@ def _lib():
         lib.tq_rht_signs.restype = ctypes.c_int
         lib.tq_slot_bytes.argtypes = [I32, I32, I32]
         lib.tq_slot_bytes.restype = I32
+        lib.tq_slot_bytes_ex.argtypes = [I32, I32, I32, I32]
+        lib.tq_slot_bytes_ex.restype = I32
         lib.tq_quantize_append.argtypes = [D, P, P, P, I64, P, I64, P]
         lib.tq_quantize_append.restype = ctypes.c_int
         lib.tq_decode_workspace_bytes.argtypes = [D, I32, I32]
@@ -139,6 +141,12 @@ def tq_rht_signs(D: int, seed: int) -> np.ndarray:
 def tq_slot_bytes(D: int, k_bits: int, v_bits: int) -> int:
     r = _lib().tq_slot_bytes(D, k_bits, v_bits)
     _check("tq_slot_bytes", min(r, 0))
+    return r
+
+
+def tq_slot_bytes_ex(D: int, k_bits: int, v_bits: int, flags: int) -> int:
+    r = _lib().tq_slot_bytes_ex(D, k_bits, v_bits, flags)
+    _check("tq_slot_bytes_ex", min(r, 0))
     return r
 
 

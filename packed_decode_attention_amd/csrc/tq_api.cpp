@@ -15,14 +15,14 @@ int code_bytes(int D, int bits) { return (D * bits + 7) / 8; }
 // Fill a TqLayer from the public descriptor.  need_q: decode also checks num_q_heads.
 int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   if (d == nullptr) return TQ_ERR_INVALID_ARG;
-  if ((d->flags & ~TQ_FLAG_NORM_CORRECTION) != 0) return TQ_ERR_INVALID_ARG;
+  if ((d->flags & ~(TQ_FLAG_NORM_CORRECTION | TQ_FLAG_MEAN_REMOVAL)) != 0) return TQ_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return TQ_ERR_UNSUPPORTED;
   if (!bits_ok(d->k_bits) || !bits_ok(d->v_bits)) return TQ_ERR_UNSUPPORTED;
   if (d->num_kv_heads < 1 || d->block_size < 1) return TQ_ERR_INVALID_ARG;
   if (d->k_centroids == nullptr || d->k_boundaries == nullptr || d->v_centroids == nullptr ||
       d->v_boundaries == nullptr)
     return TQ_ERR_INVALID_ARG;
-  const int sb = tq_slot_bytes(d->head_dim, d->k_bits, d->v_bits);
+  const int sb = tq_slot_bytes_ex(d->head_dim, d->k_bits, d->v_bits, d->flags);
   const int stride = d->slot_stride == 0 ? sb : d->slot_stride;
   if (stride < sb || (stride & 3) != 0 || stride > 4096) return TQ_ERR_INVALID_ARG;
   if (d->num_kv_heads > 64 || d->block_size > 65536) return TQ_ERR_UNSUPPORTED;
@@ -46,6 +46,8 @@ int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   L->kcode_bytes = code_bytes(d->head_dim, d->k_bits);
   L->vcode_bytes = code_bytes(d->head_dim, d->v_bits);
   L->norm_corr = (d->flags & TQ_FLAG_NORM_CORRECTION) != 0;
+  L->mean = (d->flags & TQ_FLAG_MEAN_REMOVAL) != 0;
+  L->kreg = L->kcode_bytes + 4 + 4 * L->mean;
   uint64_t words[2];
   tq_sign_words(d->head_dim, d->rht_seed, words, 2);
   L->signs.w[0] = (uint32_t)words[0];
@@ -62,9 +64,15 @@ int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
 }  // namespace
 
 extern "C" int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits) {
+  return tq_slot_bytes_ex(D, k_bits, v_bits, 0);
+}
+
+extern "C" int32_t tq_slot_bytes_ex(int32_t D, int32_t k_bits, int32_t v_bits, int32_t flags) {
   if (D < 1 || D > 65536 || k_bits < 1 || k_bits > 8 || v_bits < 1 || v_bits > 8)
     return TQ_ERR_INVALID_ARG;
-  return (code_bytes(D, k_bits) + 4) + (code_bytes(D, v_bits) + 4);
+  if ((flags & ~(TQ_FLAG_NORM_CORRECTION | TQ_FLAG_MEAN_REMOVAL)) != 0) return TQ_ERR_INVALID_ARG;
+  const int tail = (flags & TQ_FLAG_MEAN_REMOVAL) ? 8 : 4;  // norm (and mean) per region
+  return (code_bytes(D, k_bits) + tail) + (code_bytes(D, v_bits) + tail);
 }
 
 extern "C" int tq_quantize_append(const tq_layer_desc* layer, const void* k, const void* v,

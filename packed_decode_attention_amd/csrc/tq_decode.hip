@@ -283,7 +283,8 @@ struct Step {
   LaneCodes<NBK> k;
   LaneCodes<NBV> v;
   float kn, vn;
-  int pos;  // position, or INT_MAX past the split's end
+  float km, vm;  // row means (mean-removal format; else 0)
+  int pos;       // position, or INT_MAX past the split's end
 };
 
 template <int D, int KB, int VB, int GMAX>
@@ -344,13 +345,19 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   uint32_t sbits = 0;
 #pragma unroll
   for (int e = 0; e < C; e += 8) sbits |= sign_byte(L.signs, (C * j + e) / 8) << e;
-  float qr[GMAX][C];
+  float qr[GMAX][C], qsum[GMAX];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
+    qsum[g] = 0.0f;
     if (g < G) {
       const uint16_t* qp = a.q + q_row(a, b, h, g) * D + C * j;
 #pragma unroll
       for (int e = 0; e < C; e += 8) load8_f16(qp + e, &qr[g][e]);
+      if (L.mean) {  // mean-removal format: scale log2(e) sum(q), the weight of mu_K in a score
+#pragma unroll
+        for (int e = 0; e < C; ++e) qsum[g] += qr[g][e];
+        qsum[g] = group_sum<P>(qsum[g]) * a.sink_scale;
+      }
 #pragma unroll
       for (int e = 0; e < C; ++e) qr[g][e] = ((sbits >> e) & 1u) ? -qr[g][e] : qr[g][e];
       wht_row<C, P>(qr[g], j);
@@ -363,17 +370,19 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   }
 
   float m[GMAX], l[GMAX], acc[GMAX][C];
-  int lim[GMAX];  // positions visible to each head (the end of the packed segment, or causal)
+  float mv[GMAX];  // mean-removal format: sums of 2^(s - m) mu_V
+  int lim[GMAX];   // positions visible to each head (the end of the packed segment, or causal)
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     lim[g] = min(p_end, q_limit(a, seq_len, g));
+    mv[g] = 0.0f;
     m[g] = -INFINITY;
     l[g] = 0.0f;
 #pragma unroll
     for (int e = 0; e < C; ++e) acc[g][e] = 0.0f;
   }
 
-  const int voff = L.kcode_bytes + 4;
+  const int voff = L.kreg;  // V region
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   __syncthreads();  // lookup tables and block-table segment ready
@@ -391,6 +400,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     st.v = load_lane_codes<NBV>(base + voff, j);
     st.kn = *reinterpret_cast<const float*>(base + L.kcode_bytes);
     st.vn = *reinterpret_cast<const float*>(base + voff + L.vcode_bytes);
+    st.km = L.mean ? *reinterpret_cast<const float*>(base + L.kcode_bytes + 4) : 0.0f;
+    st.vm = L.mean ? *reinterpret_cast<const float*>(base + voff + L.vcode_bytes + 4) : 0.0f;
     return st;
   };
 
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < C; ++e) d += qr[g][e] * kf[e];
       d = group_sum<P>(d);
-      s[g] = st.pos < lim[g] ? st.kn * d : -INFINITY;
+      s[g] = st.pos < lim[g] ? st.kn * d + st.km * qsum[g] : -INFINITY;
     }
     bool grow = false;
 #pragma unroll
@@ -415,6 +426,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
         if (s[g] > m[g]) {
           const float r = __builtin_amdgcn_exp2f(m[g] - s[g]);
           l[g] *= r;
+          mv[g] *= r;
 #pragma unroll
           for (int e = 0; e < C; ++e) acc[g][e] *= r;
           m[g] = s[g];
@@ -427,6 +439,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     for (int g = 0; g < GMAX; ++g) {
       const float pw = st.pos < lim[g] ? __builtin_amdgcn_exp2f(s[g] - m[g]) : 0.0f;
       l[g] += pw;
+      mv[g] += pw * st.vm;
       const float w = pw * st.vn;
 #pragma unroll
       for (int e = 0; e < C; ++e) acc[g][e] += w * vf[e];
@@ -448,6 +461,19 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
         consume(cur);
       }
     }
+  }
+
+  // Mean-removal format: the weighted means enter the rotated accumulator as (sum) R 1, which the
+  // merge's R^T turns into (sum) 1; R 1 = D^(-1/2) H s over this lane's coordinates.
+  if (L.mean) {
+    float r1[C];
+#pragma unroll
+    for (int e = 0; e < C; ++e) r1[e] = ((sbits >> e) & 1u) ? -1.0f : 1.0f;
+    wht_row<C, P>(r1, j);
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+      for (int e = 0; e < C; ++e) acc[g][e] += mv[g] * (r1[e] * a.rsqrt_d);
   }
 
   // Merge the row groups of the wave (lanes with equal j hold the same coordinates).
@@ -641,6 +667,7 @@ struct MfmaTile {
   uint32_t k[2][MfmaCfg<D, KB, VB>::KW];  // K codes of tokens t16, 16 + t16 (lane group's run)
   uint32_t v[2][MfmaCfg<D, KB, VB>::VW];  // V codes of the same tokens and coordinates
   float kn[2], vn[2];
+  float km[2], vm[2];  // row means (mean-removal format; else 0)
 };
 
 // Page rows of a 32-position tile for one kv head, as fetched when page blocks hold whole runs of
@@ -738,6 +765,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   __shared__ VE s_vtab[OpTable<VB>::N];
   __shared__ int64_t s_boff[kMaxBtLds];
   __shared__ float s_qmax[8];
+  __shared__ float s_qsum[8];  // mean-removal format: scale log2(e) sum(q) per head
+  __shared__ float s_r1[D];    // mean-removal format: R 1 = D^(-1/2) H s
   __shared__ __align__(16) uint32_t s_w[kNW][16][C::WROW];
   float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_x);
   float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_x);  // [wave * H8 + head]
@@ -768,6 +797,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     const int g = tid / LPH, j = tid % LPH;
     float x[8];
     load8_f16(a.q + q_row(a, b, h, g) * D + 8 * j, x);
+    if (!UBLK && L.mean) {
+      float qs = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs += x[e];
+      qs = group_sum<LPH>(qs);
+      if (j == 0) s_qsum[g] = qs * a.sink_scale;
+    }
     const uint32_t sb = sign_byte(L.signs, j);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -781,6 +817,15 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     }
     mx = lanes_max<LPH>(mx);
     if (j == 0) s_qmax[g] = mx * a.qscale;
+  } else if (!UBLK && L.mean && tid >= 192 && tid < 192 + LPH) {  // R 1, by the last wave (G <= 8 heads
+    const int j = tid - 192;                             // use at most 128 threads above)
+    const uint32_t sb = sign_byte(L.signs, j);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = ((sb >> e) & 1u) ? -1.0f : 1.0f;
+    wht_row8_dpp<LPH>(x, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_r1[8 * j + e] = x[e] * a.rsqrt_d;
   }
   __syncthreads();
 
@@ -817,7 +862,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
   const float f1 = live1 ? ldexpf(1.0f, -(head_exp(g1) + kLutShift)) : 0.0f;
 
-  const int voff = L.kcode_bytes + 4;
+  const int voff = L.kreg;  // V region
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
   const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
@@ -851,6 +896,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       load_words<C::VW>(r + voff + 4 * C::VW * q4, m.v[u]);
       m.kn[u] = *reinterpret_cast<const float*>(r + L.kcode_bytes);
       m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
+      m.km[u] = L.mean ? *reinterpret_cast<const float*>(r + L.kcode_bytes + 4) : 0.0f;
+      m.vm[u] = L.mean ? *reinterpret_cast<const float*>(r + voff + L.vcode_bytes + 4) : 0.0f;
     }
   };
   // Whole runs of 16 positions per block: the tile's slots as consecutive chunks (see MfmaRaw),
@@ -901,6 +948,11 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   float m_s[2] = {kSent, kSent};   // running max of scores (heads g0, g1)
   float m_w[2] = {kSent, kSent};   // running max of score + log2(n_V)
   float l_s[2] = {0.0f, 0.0f};     // per-lane partial sums of 2^(s - m_s)
+  // Mean-removal format (per-lane fetch only: the staged tile layout is the plain slot format).
+  constexpr bool kMean = !UBLK;
+  float mv_s[2] = {0.0f, 0.0f};    // mean-removal format: partial sums of 2^(s - m_s) mu_V
+  const float qsum0 = (kMean && L.mean && live0) ? s_qsum[g0] : 0.0f;  // mu_K term of the scores
+  const float qsum1 = (kMean && L.mean && live1) ? s_qsum[g1] : 0.0f;
   float4_t acc[C::PC];
 #pragma unroll
   for (int c = 0; c < C::PC; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -926,7 +978,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   auto process = [&](const Tile& cur, int tile) {
     // ---- QK on the matrix cores ----
     float4_t sc[2];
-    float kn[2], vn[2];
+    float kn[2], vn[2], km[2] = {0.0f, 0.0f}, vm[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t kw[C::KW];
@@ -950,6 +1002,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < C::KW; ++i) kw[i] = cur.k[u][i];
         kn[u] = cur.kn[u];
         vn[u] = cur.vn[u];
+        km[u] = cur.km[u];
+        vm[u] = cur.vm[u];
       }
       uint4 kop[C::NMQ];  // all table reads of the sub-tile first, so their latency overlaps
 #pragma unroll
@@ -969,8 +1023,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p = pbase + 16 * u + t16;
-      s0[u] = (p >= ns && p < lim0 && live0) ? (sc[u][0] + sc[u][1]) * kn[u] * f0 : kSent;
-      if (G8) s1[u] = (p >= ns && p < lim1 && live1) ? (sc[u][2] + sc[u][3]) * kn[u] * f1 : kSent;
+      float t0 = (sc[u][0] + sc[u][1]) * kn[u] * f0, t1 = (sc[u][2] + sc[u][3]) * kn[u] * f1;
+      if constexpr (kMean) {
+        t0 += km[u] * qsum0;
+        t1 += km[u] * qsum1;
+      }
+      s0[u] = (p >= ns && p < lim0 && live0) ? t0 : kSent;
+      if (G8) s1[u] = (p >= ns && p < lim1 && live1) ? t1 : kSent;
       lv[u] = __builtin_amdgcn_logf(vn[u]);  // log2(n_V); -inf for a zero row
     }
     const float ms0 = fmaxf(m_s[0], row16_max(fmaxf(s0[0], s0[1])));
@@ -980,10 +1039,18 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       ms1 = fmaxf(m_s[1], row16_max(fmaxf(s1[0], s1[1])));
       mw1 = fmaxf(m_w[1], row16_max(fmaxf(s1[0] + lv[0], s1[1] + lv[1])));
     }
-    if (ms0 > m_s[0]) l_s[0] *= __builtin_amdgcn_exp2f(m_s[0] - ms0);
+    if (ms0 > m_s[0]) {
+      const float r = __builtin_amdgcn_exp2f(m_s[0] - ms0);
+      l_s[0] *= r;
+      if constexpr (kMean) mv_s[0] *= r;
+    }
     m_s[0] = ms0;
     if (G8) {
-      if (ms1 > m_s[1]) l_s[1] *= __builtin_amdgcn_exp2f(m_s[1] - ms1);
+      if (ms1 > m_s[1]) {
+        const float r = __builtin_amdgcn_exp2f(m_s[1] - ms1);
+        l_s[1] *= r;
+        if constexpr (kMean) mv_s[1] *= r;
+      }
       m_s[1] = ms1;
     }
     const bool grow0 = mw0 > m_w[0], grow1 = G8 && mw1 > m_w[1];
@@ -1008,13 +1075,17 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int col = 16 * u + t16;
-      l_s[0] += __builtin_amdgcn_exp2f(s0[u] - ms0);
+      const float p0 = __builtin_amdgcn_exp2f(s0[u] - ms0);
+      l_s[0] += p0;
+      if constexpr (kMean) mv_s[0] += p0 * vm[u];
       uint32_t h0, l0;
       split_f16(__builtin_amdgcn_exp2f(s0[u] + lv[u] - mw0s), h0, l0);
       put_w(4 * q4 + 0, col, h0);
       put_w(4 * q4 + 1, col, l0);
       if (G8) {
-        l_s[1] += __builtin_amdgcn_exp2f(s1[u] - ms1);
+        const float p1 = __builtin_amdgcn_exp2f(s1[u] - ms1);
+        l_s[1] += p1;
+        if constexpr (kMean) mv_s[1] += p1 * vm[u];
         uint32_t h1, l1;
         split_f16(__builtin_amdgcn_exp2f(s1[u] + lv[u] - mw1s), h1, l1);
         put_w(4 * q4 + 2, col, h1);
@@ -1138,13 +1209,23 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     l_s[i] += dpp<kDppQuadXor2>(l_s[i]);
     l_s[i] += dpp<kDppHalfRowMirror>(l_s[i]);
     l_s[i] += dpp<kDppRowMirror>(l_s[i]);
+    if constexpr (kMean) {
+      mv_s[i] += dpp<kDppQuadXor1>(mv_s[i]);
+      mv_s[i] += dpp<kDppQuadXor2>(mv_s[i]);
+      mv_s[i] += dpp<kDppHalfRowMirror>(mv_s[i]);
+      mv_s[i] += dpp<kDppRowMirror>(mv_s[i]);
+    }
   }
   const float vscale = ldexpf(1.0f, -(kWShift + kLutShift));
   const float c0 = __builtin_amdgcn_exp2f(m_w[0] - m_s[0]) * vscale;
   const float c1 = __builtin_amdgcn_exp2f(m_w[1] - m_s[1]) * vscale;
+  // mean-removal format: the weighted means sum_p w_p mu_p enter the rotated accumulator as
+  // (sum) R 1, which the merge's R^T turns into (sum) 1
+  auto mean_term = [&](int i, int c) { return kMean && L.mean ? mv_s[i] * s_r1[C::PC * t16 + c] : 0.0f; };
   if (live0) {
 #pragma unroll
-    for (int c = 0; c < C::PC; ++c) s_part[wave * H8 + g0][2 + C::PC * t16 + c] = (acc[c][0] + acc[c][1]) * c0;
+    for (int c = 0; c < C::PC; ++c)
+      s_part[wave * H8 + g0][2 + C::PC * t16 + c] = (acc[c][0] + acc[c][1]) * c0 + mean_term(0, c);
     if (t16 == 0) {
       s_part[wave * H8 + g0][0] = m_s[0];
       s_part[wave * H8 + g0][1] = l_s[0];
@@ -1152,7 +1233,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
   if (live1) {
 #pragma unroll
-    for (int c = 0; c < C::PC; ++c) s_part[wave * H8 + g1][2 + C::PC * t16 + c] = (acc[c][2] + acc[c][3]) * c1;
+    for (int c = 0; c < C::PC; ++c)
+      s_part[wave * H8 + g1][2 + C::PC * t16 + c] = (acc[c][2] + acc[c][3]) * c1 + mean_term(1, c);
     if (t16 == 0) {
       s_part[wave * H8 + g1][0] = m_s[1];
       s_part[wave * H8 + g1][1] = l_s[1];
@@ -1292,7 +1374,7 @@ void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
   }
   if constexpr (mfma_format(D, KB, VB)) {
     constexpr bool G8 = GMAX > 4;
-    if (a.L.bs % 16 == 0)
+    if (a.L.bs % 16 == 0 && !a.L.mean)  // the staged tile layout is the plain slot format
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, true>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false>), grid, dim3(kWG), 0, st, a);

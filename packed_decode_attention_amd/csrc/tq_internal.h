@@ -26,6 +26,8 @@ struct TqLayer {
   int kcode_bytes;     // ceil(D * kb / 8)
   int vcode_bytes;     // ceil(D * vb / 8)
   int norm_corr;       // 1: the stored norm is n / ||c[idx]|| (norm-correction format)
+  int mean;            // 1: each region ends with the row mean (mean-removal format)
+  int kreg;            // K region bytes: codes, norm (and mean); the V region starts here
   TqSigns signs;
   const float *kc, *kt, *vc, *vt;
 };

@@ -60,6 +60,11 @@ constexpr int kQNoTable = -100;   // log2 S marker: binary search
 
 __host__ __device__ constexpr int qtab_entries(int bits) { return bits <= 4 ? kQTabSmall : kQTabLarge; }
 
+__device__ __forceinline__ float4_t mfma_f16_acc(const uint4& a, const uint4& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float4_t mfma_f16(const uint4& a, const uint4& b) {
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -160,17 +165,62 @@ __device__ __forceinline__ float row_sum_squares_f32(const float (&v)[NB][8]) {
   return tree_lanes(p);
 }
 
+// fp16 high and low parts of x: hi = fp16(x), lo = fp16(x - hi).
+__device__ __forceinline__ void split_half(float x, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = (_Float16)x;
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
+}
+
+// Mean-removal format: the row mean mu (the stride-halving fp32 tree of the values over D, an
+// exact power-of-two scaling), the norm of the centred row d = fp32(x - mu) (squares rounded to
+// fp32, the same tree) and d as fp16 high and low parts for the matrix cores: products with the
+// +-1 operand stay exact and hi + lo carries d to about 22 bits, far inside the tie band.
+template <int NB>
+__device__ __forceinline__ void centre_row(const uint4 (&x)[NB], float& mu, float& n,
+                                           uint4 (&xh)[NB], uint4 (&xl)[NB]) {
+#pragma clang fp contract(off)
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (NB == 4) {
+      p[j] = (half_of(x[0], j) + half_of(x[2], j)) + (half_of(x[1], j) + half_of(x[3], j));
+    } else {
+      p[j] = half_of(x[0], j) + half_of(x[1], j);
+    }
+  }
+  mu = tree_lanes(p) * (1.0f / (32 * NB));
+  float d[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[b][j] = half_of(x[b], j) - mu;
+  n = sqrtf(row_sum_squares_f32<NB>(d));
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_half(d[b][j], h[j], l[j]);
+    xh[b] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    xl[b] = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  }
+}
+
 // One region (K or V, BITS-bit codes) of the wave's 16 rows: norm, rotation, decisions, packing,
 // store.  TABLE: decisions by the bucket table (resolution 2^sh), else by binary search.
 // NC: norm-correction format (the stored norm is n / ||c[idx]||; s_c holds the centroids).
-template <int D, int BITS, bool TABLE, bool NC>
+// MEAN: mean-removal format (the centred row is rotated; the mean is stored after the norm).
+template <int D, int BITS, bool TABLE, bool NC, bool MEAN>
 __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const uint4 (&A)[D / 32][2],
                                                 float zero, int g, int code_bytes,
                                                 const float* s_t, const uint2* tab, int sh,
                                                 const float* s_c, float rsqrt_d,
                                                 uint8_t* __restrict__ dst) {
   constexpr int NB = D / 32;
-  const float n = sqrtf(row_sum_squares<NB>(x, zero));  // correctly rounded
+  float n, mu = 0.0f;
+  uint4 xh[NB], xl[NB];
+  if constexpr (MEAN) centre_row<NB>(x, mu, n, xh, xl);
+  else n = sqrtf(row_sum_squares<NB>(x, zero));  // correctly rounded
 
   // H_NB across blocks, scaled to u S = y S / (sqrt(D) n) (u = 0 for a zero row), and decisions.
   const float inv = n > 0.0f ? (TABLE ? ldexpf(rsqrt_d / n, sh) : rsqrt_d / n) : 0.0f;
@@ -181,7 +231,8 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
   for (int t = 0; t < 2; ++t) {
     float4_t z[NB];  // z[b][i]: H_32 diag(s) of block b at rotated coordinate 8 g + 4 t + i
 #pragma unroll
-    for (int b = 0; b < NB; ++b) z[b] = mfma_f16(A[b][t], x[b]);
+    for (int b = 0; b < NB; ++b)
+      z[b] = MEAN ? mfma_f16_acc(A[b][t], xl[b], mfma_f16(A[b][t], xh[b])) : mfma_f16(A[b][t], x[b]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float y[NB];
@@ -269,7 +320,12 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
       *reinterpret_cast<uint2*>(run) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
   }
-  if (g == 0) *reinterpret_cast<float*>(dst + code_bytes) = n_store;
+  if (g == 0) {
+    if constexpr (MEAN)
+      *reinterpret_cast<uint2*>(dst + code_bytes) = make_uint2(__float_as_uint(n_store), __float_as_uint(mu));
+    else
+      *reinterpret_cast<float*>(dst + code_bytes) = n_store;
+  }
 }
 
 // Bucket table of one codebook (see above): entries for buckets k = -(S + 1) .. S, entry
@@ -296,7 +352,8 @@ __device__ __forceinline__ void build_qtab(const float* s_t, int nb, int sh, uin
 // slot id): every lane stores on every tile, so each tile issues a fixed number of stores.
 __device__ __align__(16) uint8_t tq_quant_discard[4096];
 
-// Stores a region issues per tile (two for 8-bit codes, one otherwise, plus the norm), and the
+// Stores a region issues per tile (two for 8-bit codes, one otherwise, plus the norm (and mean)),
+// and the
 // s_waitcnt immediate that waits for everything issued before the last n vector memory operations
 // (gfx9 encoding: vmcnt in bits 3..0 and 15..14; expcnt and lgkmcnt at their maxima).
 constexpr int region_stores(int bits) { return (bits == 8 ? 2 : 1) + 1; }
@@ -304,8 +361,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf
 
 // Four waves per SIMD (128 VGPRs): the occupancy that keeps a tile of loads in flight per wave;
 // without the attribute the fallback loop's pressure lowers it for the whole kernel.
-template <int D, int KB, int VB, bool NC>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void tq_quantize_kernel(
+// 4 waves per SIMD (at most 128 VGPRs); the mean-removal format, which also holds the centred row
+// as fp16 high and low parts, gets 3 (168 VGPRs) so that nothing spills into the tile loop.
+template <int D, int KB, int VB, bool NC, bool MEAN>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 4))) void tq_quantize_kernel(
     TqLayer L, float rsqrt_d, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slot_mapping, int64_t n_rows, uint8_t* __restrict__ pages) {
   constexpr int NB = D / 32;
@@ -437,10 +496,10 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
       for (int i = L.slot_bytes + g; i < L.stride; i += 4) dst[i] = 0;  // padding, before the loads
       if (T + tstep < n_tiles) issue(T + tstep);
 
-      quantize_region<D, KB, kTable, NC>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk, s_c[0],
-                                         rsqrt_d, dst);
-      quantize_region<D, VB, kTable, NC>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv, s_c[1],
-                                         rsqrt_d, dst + L.kcode_bytes + 4);
+      quantize_region<D, KB, kTable, NC, MEAN>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk,
+                                               s_c[0], rsqrt_d, dst);
+      quantize_region<D, VB, kTable, NC, MEAN>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv,
+                                               s_c[1], rsqrt_d, dst + L.kreg);
     }
   };
   if (shk != kQNoTable && shv != kQNoTable) tile_loop(std::true_type{});
@@ -453,7 +512,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4))) void t
 template <int D>
 __device__ __forceinline__ void dequant_region(const uint8_t* __restrict__ region, int bits,
                                                int code_bytes, const float* s_c, uint32_t sbyte,
-                                               int j, float rsqrt_d, float* __restrict__ out) {
+                                               int j, float rsqrt_d, int mean, float* __restrict__ out) {
+#pragma clang fp contract(off)
   constexpr int LPR = D / 8;
   const uint64_t cw = lane_codes(region, bits, j);
   const uint32_t mask = (1u << bits) - 1u;
@@ -464,10 +524,12 @@ __device__ __forceinline__ void dequant_region(const uint8_t* __restrict__ regio
   const float n = *reinterpret_cast<const float*>(region + code_bytes);
   const float g = n * rsqrt_d;
   float o[8];
+  const float mu = mean ? *reinterpret_cast<const float*>(region + code_bytes + 4) : 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float r = (float)z[e] * g;
     o[e] = ((sbyte >> e) & 1u) ? -r : r;
+    if (mean) o[e] = o[e] + mu;  // mean-removal format: fp32(x_hat + mu)
   }
   float4* o4 = reinterpret_cast<float4*>(out + 8 * j);
   o4[0] = make_float4(o[0], o[1], o[2], o[3]);
@@ -494,8 +556,8 @@ __global__ __launch_bounds__(kWG) void tq_dequant_kernel(TqLayer L, float rsqrt_
   const int h = (int)(row - i * L.Hkv);
   const uint8_t* src = pages + (slots[i] * L.Hkv + h) * (int64_t)L.stride;
   const uint32_t sb = sign_byte(L.signs, j);
-  dequant_region<D>(src, L.kb, L.kcode_bytes, s_kc, sb, j, rsqrt_d, k_out + row * D);
-  dequant_region<D>(src + L.kcode_bytes + 4, L.vb, L.vcode_bytes, s_vc, sb, j, rsqrt_d,
+  dequant_region<D>(src, L.kb, L.kcode_bytes, s_kc, sb, j, rsqrt_d, L.mean, k_out + row * D);
+  dequant_region<D>(src + L.kreg, L.vb, L.vcode_bytes, s_vc, sb, j, rsqrt_d, L.mean,
                     v_out + row * D);
 }
 
@@ -506,12 +568,14 @@ static float rsqrt_of(int D) { return (float)(1.0 / __builtin_sqrt((double)D)); 
 template <int D, int KB, int VB>
 static void launch_quantize(const TqLayer& L, dim3 grid, size_t lds, hipStream_t st, const void* k,
                             const void* v, const int64_t* slot_mapping, int64_t rows, void* pages) {
-  if (L.norm_corr)
-    hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB, true>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
-                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
-  else
-    hipLaunchKernelGGL((tq_quantize_kernel<D, KB, VB, false>), grid, dim3(kWG), lds, st, L, rsqrt_of(D),
-                       (const uint16_t*)k, (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kWG), lds, st, L, rsqrt_of(D), (const uint16_t*)k,
+                       (const uint16_t*)v, slot_mapping, rows, (uint8_t*)pages);
+  };
+  if (L.norm_corr && L.mean) go(tq_quantize_kernel<D, KB, VB, true, true>);
+  else if (L.norm_corr) go(tq_quantize_kernel<D, KB, VB, true, false>);
+  else if (L.mean) go(tq_quantize_kernel<D, KB, VB, false, true>);
+  else go(tq_quantize_kernel<D, KB, VB, false, false>);
 }
 
 template <int D, int KB>

@@ -32,7 +32,7 @@ def check_attention(got: np.ndarray, want: np.ndarray, seqs=None):
 
 def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D: int, kb: int,
                   vb: int, stride: int, k_tie: np.ndarray, v_tie: np.ndarray,
-                  norm_correction=None) -> int:
+                  norm_correction=None, mean: bool = False) -> int:
     """Packed bytes must be identical except for indices at oracle-listed ties (|u - t_j| <= 1e-6),
     where the neighbouring index is accepted.  Returns the number of accepted tie differences.
 
@@ -50,13 +50,17 @@ def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D
     r = ref.reshape(-1, H, stride)[slots]
     if np.array_equal(g, r):
         return 0
-    sb = oq.slot_bytes(D, kb, vb)
-    kr = oq.region_bytes(D, kb)
+    sb = oq.slot_bytes(D, kb, vb, mean)
+    kr = oq.region_bytes(D, kb, mean)
     assert np.array_equal(g[:, :, sb:], r[:, :, sb:]), "padding bytes differ"
     ties = 0
     for side, (lo, hi, bits, tie) in enumerate(((0, kr, kb, k_tie), (kr, sb, vb, v_tie))):
-        gi, gn = oq.unpack_regions(g[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
-        ri, rn = oq.unpack_regions(r[:, :, lo:hi].reshape(-1, hi - lo), D, bits)
+        gb, rb = g[:, :, lo:hi].reshape(-1, hi - lo), r[:, :, lo:hi].reshape(-1, hi - lo)
+        gi, gn = oq.unpack_regions(gb, D, bits)
+        ri, rn = oq.unpack_regions(rb, D, bits)
+        if mean:  # the row mean does not depend on the codes: always bit-exact
+            assert np.array_equal(oq.unpack_means(gb, D, bits).view(np.uint32),
+                                  oq.unpack_means(rb, D, bits).view(np.uint32)), "stored means differ"
         bad = gi != ri
         same = gn.view(np.uint32) == rn.view(np.uint32)
         if norm_correction is None:
@@ -86,7 +90,7 @@ class Case:
     block tables, and the oracle's pages."""
 
     def __init__(self, w, layer=0, lens=None, slack=0, family="beta", slot_stride=0,
-                 norm_correction=False):
+                 norm_correction=False, mean_removal=False):
         import torch
         from packed_decode_attention_amd import workloads as wl
         self.w = w
@@ -96,7 +100,8 @@ class Case:
         self.lens = np.asarray(wl.seq_lens(w) if lens is None else lens, np.int32)
         self.bt, self.num_blocks = wl.block_tables(w, np.maximum(self.lens, 1), slack)
         self.family = family
-        self.slot_stride = slot_stride or oq.slot_bytes(self.D, kb, vb)
+        self.mean = mean_removal
+        self.slot_stride = slot_stride or oq.slot_bytes(self.D, kb, vb, mean_removal)
         n_tok = int(self.lens.sum())
         self.k = wl.kv_values(w, layer, n_tok, "k")
         self.v = wl.kv_values(w, layer, n_tok, "v")
@@ -107,13 +112,13 @@ class Case:
         (kc, kt), (vc, vt) = oracle_codebooks(self.D, kb, vb, family)
         self.kcb, self.vcb = (kc, kt), (vc, vt)
         self.layer_dict = dict(D=self.D, H_kv=self.H, block_size=w.block_size, k_bits=kb, v_bits=vb,
-                               seed=0, slot_stride=self.slot_stride)
+                               seed=0, slot_stride=self.slot_stride, mean=mean_removal)
         self.norm_correction = norm_correction
         self.pages_ref = np.zeros(self.num_blocks * w.block_size * self.H * self.slot_stride, np.uint8)
         self.k_tie, self.v_tie = oq.append_rows_fast(
             self.pages_ref, self.k.numpy(), self.v.numpy(), self.slots, kt, vt, kb, vb, 0,
             self.slot_stride, k_centroids32=kc if norm_correction else None,
-            v_centroids32=vc if norm_correction else None)
+            v_centroids32=vc if norm_correction else None, mean=mean_removal)
         self._torch = torch
 
     # ---- HIP path -------------------------------------------------------------------------
@@ -121,16 +126,17 @@ class Case:
         from packed_decode_attention_amd import LayerFormat
         return LayerFormat(self.D, self.Hq, self.H, self.kb, self.vb, self.w.block_size, 0,
                            self.family, slot_stride=self.slot_stride if self.slot_stride !=
-                           oq.slot_bytes(self.D, self.kb, self.vb) else 0,
+                           oq.slot_bytes(self.D, self.kb, self.vb, self.mean) else 0,
                            k_codebook=self.kcb, v_codebook=self.vcb,
-                           norm_correction=self.norm_correction)
+                           norm_correction=self.norm_correction, mean_removal=self.mean)
 
     def nc_args(self):
         """compare_pages' norm_correction argument: the oracle's plain norms and the centroids."""
         if not self.norm_correction:
             return None
-        return ((oq.norm_fp32(self.k.numpy()), oq.norm_fp32(self.v.numpy())),
-                (self.kcb[0], self.vcb[0]))
+        def plain(x):  # the norm before the correction: of the row, or of the centred row
+            return oq.centered_norm(x, oq.row_mean(x)) if self.mean else oq.norm_fp32(x)
+        return (plain(self.k.numpy()), plain(self.v.numpy())), (self.kcb[0], self.vcb[0])
 
     def gpu_quantize(self, fmt):
         import packed_decode_attention_amd as tq
@@ -238,7 +244,8 @@ class Case:
                                      self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink, scale=scale, seqs=seqs)
 
     def oracle_dequant(self, slots):
-        k_idx, k_n, v_idx, v_n = oq.read_slots(self.pages_ref, slots, self.H, self.D, self.kb, self.vb,
-                                               self.slot_stride)
-        return (oq.dequantize_spec(k_idx, k_n, self.kcb[0], 0),
-                oq.dequantize_spec(v_idx, v_n, self.vcb[0], 0))
+        r = oq.read_slots(self.pages_ref, slots, self.H, self.D, self.kb, self.vb, self.slot_stride,
+                          self.mean)
+        k_mu, v_mu = (r[4], r[5]) if self.mean else (None, None)
+        return (oq.dequantize_spec(r[0], r[1], self.kcb[0], 0, k_mu),
+                oq.dequantize_spec(r[2], r[3], self.vcb[0], 0, v_mu))

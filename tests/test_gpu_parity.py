@@ -35,6 +35,16 @@ CASES = {
     "g5-nc": dict(w=wl.Workload("g5-nc", 1, 3, 10, 2, 64, 8, 4, 0, block_size=32,
                                 values="student_t", seed=14),
                   lens=[333, 96, 1], family="gaussian", norm_correction=True),
+    # mean-removal format (the row mean after the norm): matrix-core kernel's per-lane path (G = 4,
+    # G = 8), the vector kernel (2/3-bit codes, block size 7, padded stride), with norm correction
+    "llama-mean": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], mean_removal=True),
+    "ragged-mean": dict(w=wl.scaled(W["ragged"], num_seqs=3), lens=[700, 65, 1], mean_removal=True),
+    "edges-mean": dict(w=wl.Workload("edges-mean", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
+                                     values="normal", tables="fragmented", seed=15),
+                       lens=[0, 1, 3, 5, 66, 200], slot_stride=160, mean_removal=True),
+    "g5-mean-nc": dict(w=wl.Workload("g5-mean-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
+                                     values="student_t", seed=16),
+                       lens=[333, 96, 1], family="gaussian", norm_correction=True, mean_removal=True),
 }
 
 
@@ -62,7 +72,7 @@ def test_quantize_bytes(cases, name):
     print(f"[parity] quantize {name}: rows={len(c.slots)} H={c.H} D={c.D} K{c.kb}/V{c.vb}", flush=True)
     pages = c.gpu_quantize(fmt).cpu().numpy().reshape(-1)
     ties = compare_pages(pages, c.pages_ref, c.slots, c.H, c.D, c.kb, c.vb, c.slot_stride, c.k_tie, c.v_tie,
-                         c.nc_args())
+                         c.nc_args(), c.mean)
     assert ties <= max(4, 1e-4 * c.slots.size * c.H * c.D)
     # untouched slots keep their contents
     used = np.zeros(c.num_blocks * c.w.block_size, bool)
@@ -121,7 +131,8 @@ def test_decode_attention(cases, name):
 # the matrix-core kernel (G = 4 at T = 1, 2, 3, 5; G = 8; D = 64 with G = 5), the vector kernel
 # (edges: G = 3, 2/3-bit codes, block size 7), sinks, and sequences shorter than T.
 MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
-         ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4)]
+         ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
+         ("llama-mean", 2), ("edges-mean", 3)]
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])

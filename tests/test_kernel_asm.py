@@ -36,7 +36,7 @@ def asm(tmp_path_factory):
 
 def _kernels(text):
     for name in re.findall(r"^(_Z\S*tq_quantize_kernel\S*):", text, re.M):
-        m = re.search(r"tq_quantize_kernelILi(\d+)ELi(\d)ELi(\d)ELb(\d)E", name)
+        m = re.search(r"tq_quantize_kernelILi(\d+)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
         i = text.index(name + ":")
         j = text.index(".Lfunc_end", i)
         yield tuple(map(int, m.groups())), [l.strip() for l in text[i:j].split("\n")]
@@ -44,17 +44,17 @@ def _kernels(text):
 
 def test_every_format_is_instantiated(asm):
     found = {fmt for fmt, _ in _kernels(asm)}
-    want = {(d, kb, vb, nc) for d in (64, 128) for kb in (2, 3, 4, 8) for vb in (2, 3, 4, 8)
-            for nc in (0, 1)}
+    want = {(d, kb, vb, nc, mean) for d in (64, 128) for kb in (2, 3, 4, 8) for vb in (2, 3, 4, 8)
+            for nc in (0, 1) for mean in (0, 1)}
     assert found == want
 
 
 def test_tile_loops_issue_the_stores_their_wait_assumes(asm):
-    for (D, KB, VB, NC), body in _kernels(asm):
+    for (D, KB, VB, NC, MEAN), body in _kernels(asm):
         n = _region_stores(KB) + _region_stores(VB)
         wait = f"s_waitcnt vmcnt({n})"
         tops = [k for k, l in enumerate(body) if l == wait]
-        assert len(tops) == 2, (D, KB, VB, NC, "expected one wait per tile loop")  # table, search
+        assert len(tops) == 2, (D, KB, VB, NC, MEAN, "expected one wait per tile loop")  # table, search
         for t in tops:
             seg = body[t + 1:]
             end = next((k for k, l in enumerate(seg)
@@ -62,9 +62,9 @@ def test_tile_loops_issue_the_stores_their_wait_assumes(asm):
                        len(seg))
             seg = seg[:end]
             loads = [k for k, l in enumerate(seg) if l.startswith("global_load_lds")]
-            assert loads, (D, KB, VB, NC)
+            assert loads, (D, KB, VB, NC, MEAN)
             stores = sum(1 for l in seg[loads[-1] + 1:] if l.startswith("global_store"))
-            assert stores >= n, (D, KB, VB, NC, stores, n)
+            assert stores >= n, (D, KB, VB, NC, MEAN, stores, n)
 
 
 def _loop_blocks(body):
@@ -88,11 +88,11 @@ def _loop_blocks(body):
 def test_no_other_vector_memory_waits_in_tile_loops(asm):
     # inside a tile loop the only wait on vector memory is the one at its top: any other (a spill
     # reload, a load result used in the loop) would also wait for the stores in flight
-    for (D, KB, VB, NC), body in _kernels(asm):
+    for (D, KB, VB, NC, MEAN), body in _kernels(asm):
         n = _region_stores(KB) + _region_stores(VB)
         tile_loops = [ls for ls in _loop_blocks(body).values()
                       if any(l == f"s_waitcnt vmcnt({n})" for l in ls)]
-        assert len(tile_loops) == 2, (D, KB, VB, NC)
+        assert len(tile_loops) == 2, (D, KB, VB, NC, MEAN)
         for ls in tile_loops:
             waits = [l for l in ls if l.startswith("s_waitcnt") and "vmcnt" in l]
-            assert waits == [f"s_waitcnt vmcnt({n})"], (D, KB, VB, NC, waits)
+            assert waits == [f"s_waitcnt vmcnt({n})"], (D, KB, VB, NC, MEAN, waits)

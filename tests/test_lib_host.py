@@ -37,8 +37,12 @@ def test_slot_bytes(lib):
         for kb in range(1, 9):
             for vb in range(1, 9):
                 assert lib.tq_slot_bytes(D, kb, vb) == oq.slot_bytes(D, kb, vb)
+                for flags in (0, 1, 2, 3):  # norm correction, mean removal
+                    assert lib.tq_slot_bytes_ex(D, kb, vb, flags) == oq.slot_bytes(D, kb, vb, bool(flags & 2))
     with pytest.raises(lib.TqError):
         lib.tq_slot_bytes(128, 9, 4)
+    with pytest.raises(lib.TqError):
+        lib.tq_slot_bytes_ex(128, 4, 4, 4)
 
 
 def test_rht_signs_match_oracle(lib):
@@ -98,7 +102,8 @@ def test_argument_validation_before_launch(lib):
     assert q(_desc(lib, v_bits=1)) == E.TQ_ERR_UNSUPPORTED
     assert q(_desc(lib, slot_stride=100)) == E.TQ_ERR_INVALID_ARG      # < 136
     assert q(_desc(lib, slot_stride=138)) == E.TQ_ERR_INVALID_ARG      # not a multiple of 4
-    assert q(_desc(lib, flags=2)) == E.TQ_ERR_INVALID_ARG              # unknown format flag
+    assert q(_desc(lib, flags=4)) == E.TQ_ERR_INVALID_ARG              # unknown format flag
+    assert q(_desc(lib, flags=2, slot_stride=136)) == E.TQ_ERR_INVALID_ARG  # < 144 with the mean
     assert q(_desc(lib, flags=-1)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, num_kv_heads=0)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, block_size=0)) == E.TQ_ERR_INVALID_ARG
