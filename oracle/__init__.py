@@ -14,10 +14,11 @@ codebook   Lloyd-Max codebooks for one rotated coordinate (Beta-sphere and Gauss
 rotation   SplitMix64 sign vector and the dense randomized-Hadamard rotation matrix.
 quantize   fp32 norm, nearest-centroid index, LSB-first bit packing, TQ4 page slots, dequantization.
 attention  Dense decode attention over dequantized K/V with GQA, block tables and fp16 sinks.
+qjl        1-bit QJL residual sketch of keys (SRHT signs + residual norm) and its estimator.
 
 Parity pins: every function here is pinned by the CPU tests against closed forms, textbook
 values, printed byte counts on the pages, or brute force.  The one exception is recorded in
 the module that holds it (search for "parity unpinned").
 """
 
-from . import codebook, rotation, quantize, attention  # noqa: F401
+from . import codebook, rotation, quantize, qjl, attention  # noqa: F401

@@ -41,15 +41,18 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import quantize, rotation
+from . import qjl, quantize, rotation
 
 
 def _read(pages, slots, layer):
-    """(k_idx, k_n, v_idx, v_n, k_mu, v_mu) of the slots; the means are None without mean removal."""
-    mean = layer.get("mean", False)
+    """(k_idx, k_n, v_idx, v_n, k_mu, v_mu, k_bits, k_gamma) of the slots; the means are None
+    without mean removal, the QJL sketch bits and residual norms None without the QJL key format."""
+    mean, qjl_on = layer.get("mean", False), layer.get("qjl", False)
     r = quantize.read_slots(pages, slots, layer["H_kv"], layer["D"], layer["k_bits"], layer["v_bits"],
-                            layer.get("slot_stride"), mean)
-    return r if mean else r + (None, None)
+                            layer.get("slot_stride"), mean, qjl_on)
+    if not mean:
+        r = r[:4] + (None, None) + r[4:]
+    return r if qjl_on else r + (None, None)
 
 
 def _dequantized_sequence(pages, block_table, end, n_sink, layer, k_centroids32, v_centroids32):
@@ -57,8 +60,10 @@ def _dequantized_sequence(pages, block_table, end, n_sink, layer, k_centroids32,
     bs = layer["block_size"]
     pos = np.arange(n_sink, end, dtype=np.int64)
     slots = np.asarray(block_table, dtype=np.int64)[pos // bs] * bs + pos % bs
-    k_idx, k_n, v_idx, v_n, k_mu, v_mu = _read(pages, slots, layer)
+    k_idx, k_n, v_idx, v_n, k_mu, v_mu, k_bits, k_gamma = _read(pages, slots, layer)
     K = quantize.dequantize_plain(k_idx, k_n, k_centroids32, layer["seed"], k_mu)
+    if k_bits is not None:  # QJL key format: the key's dequantized residual
+        K = K + qjl.residual_estimate(k_bits, k_gamma, layer["seed"])
     V = quantize.dequantize_plain(v_idx, v_n, v_centroids32, layer["seed"], v_mu)
     return K, V
 
@@ -74,8 +79,8 @@ def decode_attention(q16, pages, block_tables, seq_lens, layer, k_centroids32, v
                      win_k16=None, win_v16=None, win_lens=None):
     """Dense decode attention, fp64.  Returns out [B, H_q, D] (rows not in `seqs` stay zero).
 
-    layer: dict with D, H_kv, block_size, k_bits, v_bits, seed and optionally slot_stride and mean
-    (the mean-removal format).
+    layer: dict with D, H_kv, block_size, k_bits, v_bits, seed and optionally slot_stride, mean
+    (the mean-removal format) and qjl (the QJL key format).
     q16: [B, H_q, D] fp16.  block_tables: [B, max_blocks] int.  seq_lens: [B] int.
     sink_k16 / sink_v16: [B, n_sink, H_kv, D] fp16 (or None when n_sink == 0).
     win_k16 / win_v16: [B, win_cap, H_kv, D] fp16 and win_lens [B]: rows 0 .. win_lens[b] - 1 are
@@ -133,13 +138,15 @@ def decode_attention_rotated(q16, pages, block_tables, seq_lens, layer, k_centro
         w = _window_len(win_lens, b, L, ns)
         pos = np.arange(ns, L - w, dtype=np.int64)
         slots = np.asarray(block_tables[b], dtype=np.int64)[pos // bs] * bs + pos % bs
-        k_idx, k_n, v_idx, v_n, k_mu, v_mu = _read(pages, slots, layer)
+        k_idx, k_n, v_idx, v_n, k_mu, v_mu, k_bits, k_gamma = _read(pages, slots, layer)
         for h in range(H_q):
             hk = h // G
             qr = R @ q[b, h]
             s_codes = scale * k_n[:, hk].astype(np.float64) * (ck[k_idx[:, hk, :]] @ qr)
             if k_mu is not None:  # q . (x_hat + mu 1) = q . x_hat + mu sum(q)
                 s_codes = s_codes + scale * k_mu[:, hk].astype(np.float64) * q[b, h].sum()
+            if k_bits is not None:  # QJL: the residual's estimated part of q . k
+                s_codes = s_codes + scale * qjl.score_term(qr, k_bits[:, hk], k_gamma[:, hk], layer["seed"])
             # the fp16 rows: sinks, then the hot window
             K16 = np.zeros((0, D))
             V16 = np.zeros((0, D))

@@ -1,0 +1,112 @@
+"""1-bit QJL residual on keys (oracle, fp64, dense).  Test infrastructure only.
+
+Follows:
+* tq-kv, "How It Works": step [5], SRHT QJL error correction, optional, O(d log d) (a
+  subsampled-randomized-Hadamard sketch, as the rotation of step [3] is a randomized Hadamard).
+* TorbuQuant docs, "Current Status": a QJL residual, used for vector and inner-product work.
+* The TurboQuant paper (Zandieh et al., arXiv:2504.19874) and the QJL paper (Zandieh, Daliri, Han,
+  arXiv:2406.03482), both in the TorbuQuant page's references: a key is quantized by the MSE
+  quantizer, then the sign bits of a random projection of the residual and the residual's norm
+  are stored, and an inner product with the key is estimated without bias by the MSE part plus
+  sqrt(pi/2) / m * ||r|| * <S q, sign(S r)> (m rows of S; for rows with unit-variance entries,
+  E[<s, q> sign(<s, r>)] = sqrt(2/pi) <q, r> / ||r||).
+
+Readings taken where the pages are silent (each is also listed in the design notes)
+----------------------------------------------------------------------------------
+* Frame: everything happens in the rotated frame of the MSE quantizer.  v = R (x - mu 1) (mu = 0
+  without mean removal) and the residual is r = v - n_s c[idx], with n_s the stored norm (plain,
+  or corrected) and c the fp32 centroids; then n_s R^T c[idx] + R^T r = x - mu 1 exactly.
+* Sketch: S = H_D diag(sigma), the SRHT with m = D rows (no subsampling): rows of +-1, so every
+  row has unit-variance entries as the estimator needs.  sigma = rotation.signs(seed2, D) with
+  seed2 = seed XOR QJL_SEED_XOR (a second, independent SplitMix64 stream of the layer's seed).
+* Bits: b_i = 1 when (S r)_i >= 0, else 0; z_i = 2 b_i - 1.  gamma = fp32(||r||_2).  A zero
+  residual gives gamma = 0 and every bit 1.  |(S r)_i| <= QJL_TIE * ||r|| counts as a tie: either
+  bit is accepted there (fp32 kernels compute r and S r with rounding).
+* Layout: the key region gains, after its norm (and mean), D/8 bytes of sketch bits, LSB-first
+  (bit i in byte i // 8 at position i % 8), then gamma as little-endian fp32.  Values are not
+  sketched.
+* Estimate: the dequantized key gains sqrt(pi/2) / D * gamma * R^T S^T z, so that
+  q . k_tilde = q . k_mse + sqrt(pi/2) / D * gamma * (S R q) . z, the QJL estimator with R q for q.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import rotation
+
+QJL_SEED_XOR = 0x514A4C5F534B4554  # "QJL_SKET"
+QJL_TIE = 1e-4
+KAPPA_NUM = math.sqrt(math.pi / 2.0)  # the estimator's factor is KAPPA_NUM / D
+
+
+def sketch_seed(seed: int) -> int:
+    """Seed of the sketch's sign vector sigma."""
+    return (int(seed) ^ QJL_SEED_XOR) & ((1 << 64) - 1)
+
+
+def sketch_matrix(seed: int, D: int) -> np.ndarray:
+    """S = H_D diag(sigma), dense (entries +-1)."""
+    return rotation.hadamard(D) * rotation.signs(sketch_seed(seed), D)[None, :]
+
+
+def residual(x16: np.ndarray, idx: np.ndarray, n_store32, centroids32: np.ndarray, seed: int,
+             mu32=None) -> np.ndarray:
+    """r = R (x - mu 1) - n_s c[idx] in fp64, shaped like x16."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    if mu32 is not None:
+        x = x - np.asarray(mu32, np.float32).astype(np.float64)[..., None]
+    D = x.shape[-1]
+    v = x @ rotation.rotation_matrix(seed, D).T
+    c = np.asarray(centroids32, np.float32).astype(np.float64)[np.asarray(idx)]
+    return v - np.asarray(n_store32, np.float32).astype(np.float64)[..., None] * c
+
+
+def encode(x16, idx, n_store32, centroids32, seed: int, mu32=None):
+    """(bits uint8 in {0, 1} [..., D], gamma fp32 [...], tie bool [..., D]) of the key rows."""
+    r = residual(x16, idx, n_store32, centroids32, seed, mu32)
+    D = r.shape[-1]
+    y = r @ sketch_matrix(seed, D).T
+    rn = np.sqrt(np.sum(r * r, axis=-1))
+    bits = (y >= 0).astype(np.uint8)
+    tie = np.abs(y) <= QJL_TIE * rn[..., None]
+    return bits, rn.astype(np.float32), tie
+
+
+def pack(bits: np.ndarray, gamma32) -> np.ndarray:
+    """bits [N, D] -> uint8 [N, D/8 + 4]: the sketch bytes LSB-first, then gamma (fp32 LE)."""
+    bits = np.asarray(bits, dtype=np.uint8)
+    N, D = bits.shape
+    body = np.packbits(bits, axis=1, bitorder="little")
+    g = np.asarray(gamma32, dtype="<f4").reshape(N, 1).view(np.uint8)
+    return np.concatenate([body, g], axis=1)
+
+
+def unpack(buf: np.ndarray, D: int):
+    """Inverse of pack: uint8 [N, D/8 + 4] -> (bits uint8 [N, D], gamma fp32 [N])."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    N = buf.shape[0]
+    bits = np.unpackbits(buf[:, :D // 8], axis=1, bitorder="little")[:, :D]
+    gamma = np.ascontiguousarray(buf[:, D // 8:D // 8 + 4]).view("<f4").reshape(N).astype(np.float32)
+    return bits, gamma
+
+
+def residual_estimate(bits, gamma32, seed: int) -> np.ndarray:
+    """The dequantized residual in the original frame: sqrt(pi/2) / D * gamma * R^T S^T z (fp64)."""
+    z = 2.0 * np.asarray(bits, dtype=np.float64) - 1.0
+    D = z.shape[-1]
+    S = sketch_matrix(seed, D)
+    R = rotation.rotation_matrix(seed, D)
+    rot = z @ S                      # S^T z, row-wise
+    return (KAPPA_NUM / D) * np.asarray(gamma32, np.float32).astype(np.float64)[..., None] * (rot @ R)
+
+
+def score_term(qrot: np.ndarray, bits, gamma32, seed: int) -> np.ndarray:
+    """sqrt(pi/2) / D * gamma * (S q') . z for rotated queries q' = R q (fp64): the residual's part
+    of q . k_tilde.  qrot [D]; bits [..., D]; gamma [...]."""
+    z = 2.0 * np.asarray(bits, dtype=np.float64) - 1.0
+    D = z.shape[-1]
+    sq = sketch_matrix(seed, D) @ np.asarray(qrot, dtype=np.float64)
+    return (KAPPA_NUM / D) * np.asarray(gamma32, np.float32).astype(np.float64) * (z @ sq)

@@ -62,9 +62,19 @@ def region_bytes(D: int, bits: int, mean: bool = False) -> int:
     return (D * bits + 7) // 8 + 4 + (4 if mean else 0)
 
 
-def slot_bytes(D: int, k_bits: int, v_bits: int, mean: bool = False) -> int:
+def qjl_bytes(D: int, qjl: bool) -> int:
+    """QJL key format: D/8 bytes of residual sketch bits + 4 bytes of fp32 residual norm."""
+    return D // 8 + 4 if qjl else 0
+
+
+def key_region_bytes(D: int, k_bits: int, mean: bool = False, qjl: bool = False) -> int:
+    """K region: codes, norm (and mean), then the QJL sketch and residual norm."""
+    return region_bytes(D, k_bits, mean) + qjl_bytes(D, qjl)
+
+
+def slot_bytes(D: int, k_bits: int, v_bits: int, mean: bool = False, qjl: bool = False) -> int:
     """K region + V region (TQ4 page tensor figure)."""
-    return region_bytes(D, k_bits, mean) + region_bytes(D, v_bits, mean)
+    return key_region_bytes(D, k_bits, mean, qjl) + region_bytes(D, v_bits, mean)
 
 
 # --------------------------------------------------------------------------------------------
@@ -310,11 +320,14 @@ def unpack_regions(buf: np.ndarray, D: int, bits: int):
 
 def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, v_boundaries32,
                      k_bits: int, v_bits: int, seed: int, slot_stride: int | None = None,
-                     k_centroids32=None, v_centroids32=None, mean: bool = False):
+                     k_centroids32=None, v_centroids32=None, mean: bool = False, qjl_centroids32=None):
     """append_rows() with the vectorised packer (same bytes; used for larger test cases); mean:
-    the mean-removal format."""
+    the mean-removal format; qjl_centroids32 (the K centroids): the QJL key format, and the sketch
+    tie mask [n_tok, H_kv, D] is returned third."""
+    from . import qjl as _qjl
+    qjl = qjl_centroids32 is not None
     n_tok, H_kv, D = k16.shape
-    sb = slot_bytes(D, k_bits, v_bits, mean)
+    sb = slot_bytes(D, k_bits, v_bits, mean, qjl)
     stride = sb if slot_stride is None else slot_stride
     kq = quantize_rows(k16, k_boundaries32, seed, k_centroids32, mean)
     vq = quantize_rows(v16, v_boundaries32, seed, v_centroids32, mean)
@@ -323,30 +336,41 @@ def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, 
     v_mu = vq[3].reshape(-1) if mean else None
     rows = np.zeros((n_tok, H_kv, stride), dtype=np.uint8)
     kr = region_bytes(D, k_bits, mean)
+    kq_end = key_region_bytes(D, k_bits, mean, qjl)
     rows[:, :, :kr] = pack_regions(k_idx.reshape(-1, D), k_n.reshape(-1), k_bits, k_mu).reshape(n_tok, H_kv, kr)
-    rows[:, :, kr:sb] = pack_regions(v_idx.reshape(-1, D), v_n.reshape(-1), v_bits, v_mu).reshape(n_tok, H_kv, sb - kr)
+    q_tie = None
+    if qjl:
+        bits, gamma, q_tie = _qjl.encode(k16, k_idx, k_n, qjl_centroids32, seed, kq[3] if mean else None)
+        rows[:, :, kr:kq_end] = _qjl.pack(bits.reshape(-1, D), gamma.reshape(-1)).reshape(n_tok, H_kv, kq_end - kr)
+    rows[:, :, kq_end:sb] = pack_regions(v_idx.reshape(-1, D), v_n.reshape(-1), v_bits, v_mu).reshape(n_tok, H_kv, sb - kq_end)
     view = pages.reshape(-1, H_kv, stride)
     sm = np.asarray(slot_mapping, dtype=np.int64)
     keep = sm >= 0
     view[sm[keep]] = rows[keep]
-    return k_tie, v_tie
+    return (k_tie, v_tie, q_tie) if qjl else (k_tie, v_tie)
 
 
 def read_slots(pages: np.ndarray, slots: np.ndarray, H_kv: int, D: int, k_bits: int, v_bits: int,
-               slot_stride: int | None = None, mean: bool = False):
-    """Unpack many slots: returns (k_idx, k_n, v_idx, v_n) shaped [n, H_kv, D] / [n, H_kv], and
-    (k_mu, v_mu) [n, H_kv] after them for the mean-removal format."""
-    sb = slot_bytes(D, k_bits, v_bits, mean)
+               slot_stride: int | None = None, mean: bool = False, qjl: bool = False):
+    """Unpack many slots: returns (k_idx, k_n, v_idx, v_n) shaped [n, H_kv, D] / [n, H_kv],
+    (k_mu, v_mu) [n, H_kv] after them for the mean-removal format, then (sketch bits [n, H_kv, D],
+    gamma [n, H_kv]) for the QJL key format."""
+    from . import qjl as _qjl
+    sb = slot_bytes(D, k_bits, v_bits, mean, qjl)
     stride = sb if slot_stride is None else slot_stride
     view = pages.reshape(-1, H_kv, stride)
     rows = view[np.asarray(slots, dtype=np.int64)]            # [n, H_kv, stride]
     n = rows.shape[0]
     kr = region_bytes(D, k_bits, mean)
+    kq_end = key_region_bytes(D, k_bits, mean, qjl)
     kbuf = rows[:, :, :kr].reshape(n * H_kv, kr)
-    vbuf = rows[:, :, kr:sb].reshape(n * H_kv, sb - kr)
+    vbuf = rows[:, :, kq_end:sb].reshape(n * H_kv, sb - kq_end)
     k_idx, k_n = unpack_regions(kbuf, D, k_bits)
     v_idx, v_n = unpack_regions(vbuf, D, v_bits)
     out = (k_idx.reshape(n, H_kv, D), k_n.reshape(n, H_kv), v_idx.reshape(n, H_kv, D), v_n.reshape(n, H_kv))
     if mean:
         out += (unpack_means(kbuf, D, k_bits).reshape(n, H_kv), unpack_means(vbuf, D, v_bits).reshape(n, H_kv))
+    if qjl:
+        bits, gamma = _qjl.unpack(rows[:, :, kr:kq_end].reshape(n * H_kv, kq_end - kr), D)
+        out += (bits.reshape(n, H_kv, D), gamma.reshape(n, H_kv))
     return out
