@@ -76,9 +76,22 @@ typedef enum tq_codebook_family {
  *   dequantized row is fp32(x_hat + mu), so decode adds mu * sum(q) to each score and the
  *   weighted means to each output.  Combines with TQ_FLAG_NORM_CORRECTION (which then corrects
  *   the norm of d).
+ *   TQ_FLAG_QJL  (tq-kv, "How It Works": step [5], SRHT QJL error correction; TorbuQuant docs,
+ *   "Current Status": QJL residual; the TurboQuant and QJL papers in the TorbuQuant references)
+ *   keys of 2, 3 or 4 bits also carry a 1-bit sketch of their quantization residual.  In the
+ *   rotated frame the residual is r = R (x - mu 1) - n_s c[idx] (n_s the stored norm); the key
+ *   region gains, after its norm (and mean), D/8 bytes holding b_i = [(S r)_i >= 0] LSB-first and
+ *   then gamma = ||r||_2 as fp32, where S = H_D diag(sigma2) and sigma2 is the SplitMix64 sign
+ *   vector of rht_seed XOR 0x514A4C5F534B4554.  The dequantized key gains
+ *   sqrt(pi/2) / D * gamma * R^T S^T (2 b - 1), so decode adds
+ *   scale * sqrt(pi/2) / D * gamma * (S R q) . (2 b - 1) to each score.  Values are unchanged.
+ *   The sign bits and gamma come from fp32 arithmetic: a bit whose |(S r)_i| is within about
+ *   1e-4 gamma of 0 may differ from an exact computation.  Decode of this format runs on the
+ *   vector-ALU kernel.  Combines with the other flags.
  * Other bits must be 0. */
 #define TQ_FLAG_NORM_CORRECTION 1
 #define TQ_FLAG_MEAN_REMOVAL 2
+#define TQ_FLAG_QJL 4
 
 /* One layer's format.  K and V may use different bit widths (tiny-turboquant 0.12.0.3,
  * "Current status": q8k-q8v and q8k-int4v policies; TorbuQuant docs, "Current Status": K8/K4 and
@@ -126,7 +139,8 @@ int tq_rht_signs(int32_t D, uint64_t seed, int8_t* out);
 int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits);
 
 /* Bytes of one slot of a format with flags (TQ_FLAG_*): each region gains 4 bytes with
- * TQ_FLAG_MEAN_REMOVAL.  Returns a negative tq_status for unsupported arguments or flags. */
+ * TQ_FLAG_MEAN_REMOVAL, the key region D/8 + 4 bytes with TQ_FLAG_QJL (D a multiple of 8).
+ * Returns a negative tq_status for unsupported arguments or flags. */
 int32_t tq_slot_bytes_ex(int32_t D, int32_t k_bits, int32_t v_bits, int32_t flags);
 
 /* Quantize-on-append (turboquant-serve 0.1.2, "Architecture" update(); TorbuQuant docs,

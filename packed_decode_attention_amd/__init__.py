@@ -33,6 +33,7 @@ from ._lib import (  # noqa: F401
 
 TQ_FLAG_NORM_CORRECTION = 1  # tq_layer_desc.flags: stored norms are n / ||c[idx]|| (include/tq.h)
 TQ_FLAG_MEAN_REMOVAL = 2     # tq_layer_desc.flags: rows centred, the mean stored after the norm
+TQ_FLAG_QJL = 4              # tq_layer_desc.flags: keys carry a 1-bit residual sketch and its norm
 
 _CODEBOOKS: dict = {}
 
@@ -53,14 +54,15 @@ class LayerFormat:
     def __init__(self, head_dim: int, num_q_heads: int, num_kv_heads: int, k_bits: int,
                  v_bits: int, block_size: int = 16, rht_seed: int = 0, family: str = "beta",
                  slot_stride: int = 0, device="cuda", k_codebook=None, v_codebook=None,
-                 norm_correction: bool = False, mean_removal: bool = False):
+                 norm_correction: bool = False, mean_removal: bool = False, qjl: bool = False):
         import torch
         self.head_dim, self.num_q_heads, self.num_kv_heads = head_dim, num_q_heads, num_kv_heads
         self.k_bits, self.v_bits, self.block_size = k_bits, v_bits, block_size
         self.rht_seed, self.family = rht_seed, family
-        self.norm_correction, self.mean_removal = norm_correction, mean_removal
+        self.norm_correction, self.mean_removal, self.qjl = norm_correction, mean_removal, qjl
         self.flags = ((TQ_FLAG_NORM_CORRECTION if norm_correction else 0)
-                      | (TQ_FLAG_MEAN_REMOVAL if mean_removal else 0))
+                      | (TQ_FLAG_MEAN_REMOVAL if mean_removal else 0)
+                      | (TQ_FLAG_QJL if qjl else 0))
         self.slot_bytes = tq_slot_bytes_ex(head_dim, k_bits, v_bits, self.flags)
         self.slot_stride = slot_stride or self.slot_bytes
         kc, kt = k_codebook if k_codebook is not None else host_codebook(head_dim, k_bits, family)
@@ -91,9 +93,9 @@ class LayerFormat:
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int):
+def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int, qjl: bool = False):
     """Names of the kernels one tq_paged_decode_attention call launches for this format, in
     launch order (as they appear in a kernel trace)."""
-    mfma = ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
-            (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
+    mfma = not qjl and ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
+                        (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
     return ["tq_decode_mfma_kernel" if mfma else "tq_decode_split_kernel", "tq_decode_merge_kernel"]

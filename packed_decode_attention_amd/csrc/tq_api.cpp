@@ -10,14 +10,27 @@ namespace {
 
 bool bits_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 8; }
 
+constexpr int32_t kKnownFlags = TQ_FLAG_NORM_CORRECTION | TQ_FLAG_MEAN_REMOVAL | TQ_FLAG_QJL;
+constexpr uint64_t kQjlSeedXor = 0x514A4C5F534B4554ull;  // sketch signs: a second stream of the seed
+
+void fill_signs(int D, uint64_t seed, TqSigns* s) {
+  uint64_t words[2];
+  tq_sign_words(D, seed, words, 2);
+  s->w[0] = (uint32_t)words[0];
+  s->w[1] = (uint32_t)(words[0] >> 32);
+  s->w[2] = (uint32_t)words[1];
+  s->w[3] = (uint32_t)(words[1] >> 32);
+}
+
 int code_bytes(int D, int bits) { return (D * bits + 7) / 8; }
 
 // Fill a TqLayer from the public descriptor.  need_q: decode also checks num_q_heads.
 int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   if (d == nullptr) return TQ_ERR_INVALID_ARG;
-  if ((d->flags & ~(TQ_FLAG_NORM_CORRECTION | TQ_FLAG_MEAN_REMOVAL)) != 0) return TQ_ERR_INVALID_ARG;
+  if ((d->flags & ~kKnownFlags) != 0) return TQ_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return TQ_ERR_UNSUPPORTED;
   if (!bits_ok(d->k_bits) || !bits_ok(d->v_bits)) return TQ_ERR_UNSUPPORTED;
+  if ((d->flags & TQ_FLAG_QJL) && d->k_bits > 4) return TQ_ERR_UNSUPPORTED;  // sketches low-bit keys
   if (d->num_kv_heads < 1 || d->block_size < 1) return TQ_ERR_INVALID_ARG;
   if (d->k_centroids == nullptr || d->k_boundaries == nullptr || d->v_centroids == nullptr ||
       d->v_boundaries == nullptr)
@@ -47,13 +60,11 @@ int make_layer(const tq_layer_desc* d, bool need_q, TqLayer* L) {
   L->vcode_bytes = code_bytes(d->head_dim, d->v_bits);
   L->norm_corr = (d->flags & TQ_FLAG_NORM_CORRECTION) != 0;
   L->mean = (d->flags & TQ_FLAG_MEAN_REMOVAL) != 0;
-  L->kreg = L->kcode_bytes + 4 + 4 * L->mean;
-  uint64_t words[2];
-  tq_sign_words(d->head_dim, d->rht_seed, words, 2);
-  L->signs.w[0] = (uint32_t)words[0];
-  L->signs.w[1] = (uint32_t)(words[0] >> 32);
-  L->signs.w[2] = (uint32_t)words[1];
-  L->signs.w[3] = (uint32_t)(words[1] >> 32);
+  L->qjl = (d->flags & TQ_FLAG_QJL) != 0;
+  L->kqjl = L->kcode_bytes + 4 + 4 * L->mean;
+  L->kreg = L->kqjl + (L->qjl ? d->head_dim / 8 + 4 : 0);
+  fill_signs(d->head_dim, d->rht_seed, &L->signs);
+  fill_signs(d->head_dim, d->rht_seed ^ kQjlSeedXor, &L->signs2);
   L->kc = d->k_centroids;
   L->kt = d->k_boundaries;
   L->vc = d->v_centroids;
@@ -70,9 +81,11 @@ extern "C" int32_t tq_slot_bytes(int32_t D, int32_t k_bits, int32_t v_bits) {
 extern "C" int32_t tq_slot_bytes_ex(int32_t D, int32_t k_bits, int32_t v_bits, int32_t flags) {
   if (D < 1 || D > 65536 || k_bits < 1 || k_bits > 8 || v_bits < 1 || v_bits > 8)
     return TQ_ERR_INVALID_ARG;
-  if ((flags & ~(TQ_FLAG_NORM_CORRECTION | TQ_FLAG_MEAN_REMOVAL)) != 0) return TQ_ERR_INVALID_ARG;
+  if ((flags & ~kKnownFlags) != 0) return TQ_ERR_INVALID_ARG;
+  if ((flags & TQ_FLAG_QJL) && D % 8 != 0) return TQ_ERR_INVALID_ARG;
   const int tail = (flags & TQ_FLAG_MEAN_REMOVAL) ? 8 : 4;  // norm (and mean) per region
-  return (code_bytes(D, k_bits) + tail) + (code_bytes(D, v_bits) + tail);
+  const int sketch = (flags & TQ_FLAG_QJL) ? D / 8 + 4 : 0;  // key residual bits and norm
+  return (code_bytes(D, k_bits) + tail + sketch) + (code_bytes(D, v_bits) + tail);
 }
 
 extern "C" int tq_quantize_append(const tq_layer_desc* layer, const void* k, const void* v,

@@ -284,10 +284,16 @@ struct Step {
   LaneCodes<NBV> v;
   float kn, vn;
   float km, vm;  // row means (mean-removal format; else 0)
+  uint32_t zb;   // QJL key format: the lane's sketch bits (C of them)
+  float kg;      // QJL key format: the key residual's norm gamma
   int pos;       // position, or INT_MAX past the split's end
 };
 
-template <int D, int KB, int VB, int GMAX>
+// QJL key format: a key's score gains gamma * sqrt(pi/2) / D * (S R q) . (2 b - 1) (the QJL
+// estimator of the residual's inner product; tq-kv, "How It Works", step [5]).
+constexpr float kQjlKappa = 1.2533141373155003f;  // sqrt(pi / 2)
+
+template <int D, int KB, int VB, int GMAX, bool QJL = false>
 __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
   constexpr int P = lanes_per_row<D, GMAX>();
   constexpr int C = D / P;
@@ -368,6 +374,26 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
       for (int e = 0; e < C; ++e) qr[g][e] = 0.0f;
     }
   }
+  // QJL key format: qj = sqrt(pi/2) / D * S qr with S = H diag(sigma2), qr already R q scaled.
+  // Every row group of every wave needs the same values: wave 0's first row group puts them in
+  // LDS (the barrier before the main loop publishes them), where reads are broadcasts.
+  __shared__ __align__(16) float s_qj[QJL ? GMAX : 1][QJL ? D : 4];
+  if constexpr (QJL) {
+    if (wave == 0 && sub == 0) {
+      uint32_t sbits2 = 0;
+#pragma unroll
+      for (int e = 0; e < C; e += 8) sbits2 |= sign_byte(L.signs2, (C * j + e) / 8) << e;
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        float t[C];
+#pragma unroll
+        for (int e = 0; e < C; ++e) t[e] = ((sbits2 >> e) & 1u) ? -qr[g][e] : qr[g][e];
+        wht_row<C, P>(t, j);
+#pragma unroll
+        for (int e = 0; e < C; ++e) s_qj[g][C * j + e] = t[e] * (kQjlKappa / (float)D);
+      }
+    }
+  }
 
   float m[GMAX], l[GMAX], acc[GMAX][C];
   float mv[GMAX];  // mean-removal format: sums of 2^(s - m) mu_V
@@ -402,6 +428,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     st.vn = *reinterpret_cast<const float*>(base + voff + L.vcode_bytes);
     st.km = L.mean ? *reinterpret_cast<const float*>(base + L.kcode_bytes + 4) : 0.0f;
     st.vm = L.mean ? *reinterpret_cast<const float*>(base + voff + L.vcode_bytes + 4) : 0.0f;
+    st.zb = 0;
+    st.kg = 0.0f;
+    if constexpr (QJL) {  // C sketch bits at bit C j of the sketch (C = 8 or 16)
+      if constexpr (C == 16) st.zb = reinterpret_cast<const uint16_t*>(base + L.kqjl)[j];
+      else st.zb = base[L.kqjl + j];
+      st.kg = *reinterpret_cast<const float*>(base + L.kqjl + D / 8);
+    }
     return st;
   };
 
@@ -414,8 +447,24 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < C; ++e) d += qr[g][e] * kf[e];
-      d = group_sum<P>(d);
-      s[g] = st.pos < lim[g] ? st.kn * d + st.km * qsum[g] : -INFINITY;
+      if constexpr (QJL) {  // norm and gamma are the row's: one reduction for both parts
+        float tz = 0.0f;
+        int qoff = g * D + C * j;
+        asm volatile("" : "+v"(qoff));  // keep the reads in the loop: hoisted, they fill registers
+#pragma unroll
+        for (int e = 0; e < C; e += 4) {
+          const float4 w = *reinterpret_cast<const float4*>(&s_qj[0][0] + qoff + e);
+          tz += ((st.zb >> e) & 1u) ? w.x : -w.x;
+          tz += ((st.zb >> (e + 1)) & 1u) ? w.y : -w.y;
+          tz += ((st.zb >> (e + 2)) & 1u) ? w.z : -w.z;
+          tz += ((st.zb >> (e + 3)) & 1u) ? w.w : -w.w;
+        }
+        d = group_sum<P>(st.kn * d + st.kg * tz);
+        s[g] = st.pos < lim[g] ? d + st.km * qsum[g] : -INFINITY;
+      } else {
+        d = group_sum<P>(d);
+        s[g] = st.pos < lim[g] ? st.kn * d + st.km * qsum[g] : -INFINITY;
+      }
     }
     bool grow = false;
 #pragma unroll
@@ -446,18 +495,20 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  // kPrefetch-deep register ring: slot u always holds step it0 + u.
-  Step<NBK, NBV> ring[kPrefetch];
+  // kPF-deep register ring: slot u always holds step it0 + u (two deep for the QJL key format,
+  // whose sketch bits and norms would otherwise push the registers past the file).
+  constexpr int kPF = QJL ? 2 : kPrefetch;
+  Step<NBK, NBV> ring[kPF];
 #pragma unroll
-  for (int u = 0; u < kPrefetch; ++u)
+  for (int u = 0; u < kPF; ++u)
     if (u < n_it) ring[u] = fetch(u);
-  for (int it0 = 0; it0 < n_it; it0 += kPrefetch) {
+  for (int it0 = 0; it0 < n_it; it0 += kPF) {
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
+    for (int u = 0; u < kPF; ++u) {
       const int it = it0 + u;
       if (it < n_it) {
         const Step<NBK, NBV> cur = ring[u];
-        if (it + kPrefetch < n_it) ring[u] = fetch(it + kPrefetch);
+        if (it + kPF < n_it) ring[u] = fetch(it + kPF);
         consume(cur);
       }
     }
@@ -1363,6 +1414,15 @@ void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
 template <int D, int KB, int VB, int GMAX>
 void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
   DecodeArgs a = a0;
+  if constexpr (KB <= 4) {  // QJL key format (keys of 2-4 bits): the vector-ALU split kernel
+    if (a.L.qjl) {
+      dim3 grid = sgrid;
+      grid.x += a.rows_blocks;
+      hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX, true>), grid, dim3(kWG), 0, st, a);
+      launch_merge<D, GMAX>(a, mgrid, st);
+      return;
+    }
+  }
   constexpr bool separate_rows = mfma_format(D, KB, VB) && GMAX > 4;
   dim3 grid = sgrid;
   if (separate_rows) {

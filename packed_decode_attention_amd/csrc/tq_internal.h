@@ -27,8 +27,11 @@ struct TqLayer {
   int vcode_bytes;     // ceil(D * vb / 8)
   int norm_corr;       // 1: the stored norm is n / ||c[idx]|| (norm-correction format)
   int mean;            // 1: each region ends with the row mean (mean-removal format)
-  int kreg;            // K region bytes: codes, norm (and mean); the V region starts here
+  int qjl;             // 1: keys carry a 1-bit residual sketch and its norm (QJL key format)
+  int kqjl;            // offset of the sketch bits in the slot (gamma follows them)
+  int kreg;            // K region bytes: codes, norm (and mean), sketch; the V region starts here
   TqSigns signs;
+  TqSigns signs2;      // sign vector of the residual sketch (QJL key format)
   const float *kc, *kt, *vc, *vt;
 };
 

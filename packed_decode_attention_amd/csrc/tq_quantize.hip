@@ -509,10 +509,15 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
 // =============================================================================================
 // Dequantize slots (bit-exact route: exact fp64 Walsh-Hadamard of the fp32 centroids)
 // =============================================================================================
+// 1-bit QJL key residual (tq-kv, "How It Works", step [5]; the QJL estimator of the TurboQuant
+// paper): sqrt(pi/2) / D times gamma times S^T z, in the rotated frame.
+constexpr double kQjlKappa = 1.2533141373155002512;  // sqrt(pi / 2)
+
 template <int D>
 __device__ __forceinline__ void dequant_region(const uint8_t* __restrict__ region, int bits,
                                                int code_bytes, const float* s_c, uint32_t sbyte,
-                                               int j, float rsqrt_d, int mean, float* __restrict__ out) {
+                                               int j, float rsqrt_d, int mean, float* __restrict__ out,
+                                               int qjl_off = -1, uint32_t sbyte2 = 0) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 8;
   const uint64_t cw = lane_codes(region, bits, j);
@@ -523,11 +528,28 @@ __device__ __forceinline__ void dequant_region(const uint8_t* __restrict__ regio
   wht_rowgroup<LPR>(z, j);  // exact: every partial sum fits in 53 bits
   const float n = *reinterpret_cast<const float*>(region + code_bytes);
   const float g = n * rsqrt_d;
+  // QJL key format: t = H diag(sigma2) H z, exact in fp64 (integers below D^2); its weight
+  // sqrt(pi/2) / D * gamma * D^(-1/2) makes R^T of the sketched residual.
+  double t[8];
+  float gq = 0.0f;
+  if (qjl_off >= 0) {
+    const uint32_t zb = region[qjl_off + j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = ((zb >> e) & 1u) ? 1.0 : -1.0;
+    wht_rowgroup<LPR>(t, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((sbyte2 >> e) & 1u) t[e] = -t[e];
+    wht_rowgroup<LPR>(t, j);
+    const float gamma = *reinterpret_cast<const float*>(region + qjl_off + D / 8);
+    gq = (float)(kQjlKappa / D * (double)gamma * (double)rsqrt_d);
+  }
   float o[8];
   const float mu = mean ? *reinterpret_cast<const float*>(region + code_bytes + 4) : 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float r = (float)z[e] * g;
+    float r = (float)z[e] * g;
+    if (qjl_off >= 0) r = r + (float)t[e] * gq;
     o[e] = ((sbyte >> e) & 1u) ? -r : r;
     if (mean) o[e] = o[e] + mu;  // mean-removal format: fp32(x_hat + mu)
   }
@@ -556,9 +578,65 @@ __global__ __launch_bounds__(kWG) void tq_dequant_kernel(TqLayer L, float rsqrt_
   const int h = (int)(row - i * L.Hkv);
   const uint8_t* src = pages + (slots[i] * L.Hkv + h) * (int64_t)L.stride;
   const uint32_t sb = sign_byte(L.signs, j);
-  dequant_region<D>(src, L.kb, L.kcode_bytes, s_kc, sb, j, rsqrt_d, L.mean, k_out + row * D);
+  dequant_region<D>(src, L.kb, L.kcode_bytes, s_kc, sb, j, rsqrt_d, L.mean, k_out + row * D,
+                    L.qjl ? L.kqjl : -1, sign_byte(L.signs2, j));
   dequant_region<D>(src + L.kreg, L.vb, L.vcode_bytes, s_vc, sb, j, rsqrt_d, L.mean,
                     v_out + row * D);
+}
+
+// QJL key format: the residual sketch of the keys tq_quantize_kernel has just written (same
+// stream, so its codes, norm and mean are in place).  D/8 lanes per row, 8 coordinates each:
+// v = H (s * (x - mu)) / sqrt(D) = R (x - mu 1), r = v - n_s c[idx], gamma = ||r||, then
+// S r = H (sigma2 * r) and one bit per coordinate, b = [(S r)_i >= 0], one byte per lane.
+template <int D>
+__global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, float rsqrt_d,
+                                                     const uint16_t* __restrict__ k,
+                                                     const int64_t* __restrict__ slot_mapping,
+                                                     int64_t n_rows, uint8_t* __restrict__ pages) {
+  constexpr int P = D / 8;
+  constexpr int RPW = kWG / P;
+  __shared__ float s_kc[256];
+  for (int i = threadIdx.x; i < (1 << L.kb); i += kWG) s_kc[i] = L.kc[i];
+  __syncthreads();
+  const int j = threadIdx.x % P;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / P;
+  if (row >= n_rows) return;  // whole row groups leave together: the DPP steps stay in a group
+  const int64_t t = row / L.Hkv;
+  const int h = (int)(row - t * L.Hkv);
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  uint8_t* dst = pages + (slot * L.Hkv + h) * (int64_t)L.stride;
+  float x[8];
+  load8_f16(k + row * D + 8 * j, x);
+  const float mu = L.mean ? *reinterpret_cast<const float*>(dst + L.kcode_bytes + 4) : 0.0f;
+  const uint32_t sb = sign_byte(L.signs, j);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float d = x[e] - mu;
+    x[e] = ((sb >> e) & 1u) ? -d : d;
+  }
+  wht_row8_dpp<P>(x, j);
+  const float ns = *reinterpret_cast<const float*>(dst + L.kcode_bytes);
+  const uint64_t cw = lane_codes(dst, L.kb, j);
+  const uint32_t mask = (1u << L.kb) - 1u;
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float r = x[e] * rsqrt_d - ns * s_kc[(cw >> (e * L.kb)) & mask];
+    x[e] = r;
+    ss += r * r;
+  }
+  const float gamma = sqrtf(group_sum<P>(ss));
+  const uint32_t sb2 = sign_byte(L.signs2, j);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((sb2 >> e) & 1u) x[e] = -x[e];
+  wht_row8_dpp<P>(x, j);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bits |= (x[e] >= 0.0f ? 1u : 0u) << e;
+  dst[L.kqjl + j] = (uint8_t)bits;
+  if (j == 0) *reinterpret_cast<float*>(dst + L.kqjl + D / 8) = gamma;
 }
 
 }  // namespace
@@ -614,6 +692,16 @@ int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int
   const bool ok = L.D == 128 ? dispatch_kb<128>(L, grid, tab_bytes, st, k, v, slot_mapping, rows, pages)
                              : dispatch_kb<64>(L, grid, tab_bytes, st, k, v, slot_mapping, rows, pages);
   if (!ok) return (int)hipErrorInvalidValue;  // bit widths are validated by the API layer
+  if (L.qjl) {
+    const int rpw = kWG / (L.D / 8);
+    const dim3 qgrid((unsigned)((rows + rpw - 1) / rpw));
+    if (L.D == 128)
+      hipLaunchKernelGGL(tq_qjl_kernel<128>, qgrid, dim3(kWG), 0, st, L, rsqrt_of(128),
+                         (const uint16_t*)k, slot_mapping, rows, (uint8_t*)pages);
+    else
+      hipLaunchKernelGGL(tq_qjl_kernel<64>, qgrid, dim3(kWG), 0, st, L, rsqrt_of(64),
+                         (const uint16_t*)k, slot_mapping, rows, (uint8_t*)pages);
+  }
   return (int)hipGetLastError();
 }
 

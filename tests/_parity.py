@@ -8,6 +8,7 @@ import numpy as np
 
 from oracle import attention as oatt
 from oracle import codebook as ocb
+from oracle import qjl as oqjl
 from oracle import quantize as oq
 
 # Attention tolerance (fp32 accumulation on the GPU vs fp64 oracle): max-abs and relative L2.
@@ -32,7 +33,7 @@ def check_attention(got: np.ndarray, want: np.ndarray, seqs=None):
 
 def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D: int, kb: int,
                   vb: int, stride: int, k_tie: np.ndarray, v_tie: np.ndarray,
-                  norm_correction=None, mean: bool = False) -> int:
+                  norm_correction=None, mean: bool = False, qjl_tie=None) -> int:
     """Packed bytes must be identical except for indices at oracle-listed ties (|u - t_j| <= 1e-6),
     where the neighbouring index is accepted.  Returns the number of accepted tie differences.
 
@@ -40,9 +41,16 @@ def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D
     norm_correction: None for the plain format, else ((k_norms, v_norms) [n, H] fp32 plain norms,
     (k_centroids, v_centroids)); a row whose indices differ at a tie must then store the corrected
     norm of its own indices.
+    qjl_tie: None for keys without the residual sketch, else the oracle's sketch tie mask [n, H, D]:
+    on rows whose key codes match, sketch bits may differ only at sketch ties and the residual
+    norm gamma within 1e-5 relative (it is a sum of fp32 squares); rows whose key codes moved at a
+    code tie have a different residual and are not compared there.
     """
     keep = slots >= 0
     slots, k_tie, v_tie = slots[keep], k_tie[keep], v_tie[keep]
+    qjl = qjl_tie is not None
+    if qjl:
+        qjl_tie = qjl_tie[keep]
     if norm_correction is not None:
         (kn, vn), cents = norm_correction
         plain = (np.asarray(kn)[keep].reshape(-1), np.asarray(vn)[keep].reshape(-1))
@@ -50,11 +58,13 @@ def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D
     r = ref.reshape(-1, H, stride)[slots]
     if np.array_equal(g, r):
         return 0
-    sb = oq.slot_bytes(D, kb, vb, mean)
+    sb = oq.slot_bytes(D, kb, vb, mean, qjl)
     kr = oq.region_bytes(D, kb, mean)
+    kq = oq.key_region_bytes(D, kb, mean, qjl)
     assert np.array_equal(g[:, :, sb:], r[:, :, sb:]), "padding bytes differ"
     ties = 0
-    for side, (lo, hi, bits, tie) in enumerate(((0, kr, kb, k_tie), (kr, sb, vb, v_tie))):
+    k_moved = None
+    for side, (lo, hi, bits, tie) in enumerate(((0, kr, kb, k_tie), (kq, sb, vb, v_tie))):
         gb, rb = g[:, :, lo:hi].reshape(-1, hi - lo), r[:, :, lo:hi].reshape(-1, hi - lo)
         gi, gn = oq.unpack_regions(gb, D, bits)
         ri, rn = oq.unpack_regions(rb, D, bits)
@@ -76,6 +86,19 @@ def compare_pages(gpu: np.ndarray, ref: np.ndarray, slots: np.ndarray, H: int, D
         assert np.all(t[bad]), f"{int(np.sum(bad & ~t))} index differences outside the tie band"
         assert np.all(np.abs(gi[bad] - ri[bad]) == 1)
         ties += int(bad.sum())
+        if side == 0:
+            k_moved = bad.any(axis=1)
+    if qjl:
+        gq, rq = g[:, :, kr:kq].reshape(-1, kq - kr), r[:, :, kr:kq].reshape(-1, kq - kr)
+        gbits, ggam = oqjl.unpack(gq, D)
+        rbits, rgam = oqjl.unpack(rq, D)
+        ok = ~k_moved
+        qt = qjl_tie.reshape(-1, D)[ok]
+        flip = gbits[ok] != rbits[ok]
+        assert np.all(qt[flip]), f"{int(np.sum(flip & ~qt))} sketch bits differ outside the tie band"
+        gg, rg = ggam[ok].astype(np.float64), rgam[ok].astype(np.float64)
+        assert np.all(np.abs(gg - rg) <= 1e-5 * rg + 1e-30), "residual norms differ"
+        ties += int(flip.sum())
     return ties
 
 
@@ -90,7 +113,7 @@ class Case:
     block tables, and the oracle's pages."""
 
     def __init__(self, w, layer=0, lens=None, slack=0, family="beta", slot_stride=0,
-                 norm_correction=False, mean_removal=False):
+                 norm_correction=False, mean_removal=False, qjl=False):
         import torch
         from packed_decode_attention_amd import workloads as wl
         self.w = w
@@ -101,7 +124,8 @@ class Case:
         self.bt, self.num_blocks = wl.block_tables(w, np.maximum(self.lens, 1), slack)
         self.family = family
         self.mean = mean_removal
-        self.slot_stride = slot_stride or oq.slot_bytes(self.D, kb, vb, mean_removal)
+        self.qjl = qjl
+        self.slot_stride = slot_stride or oq.slot_bytes(self.D, kb, vb, mean_removal, qjl)
         n_tok = int(self.lens.sum())
         self.k = wl.kv_values(w, layer, n_tok, "k")
         self.v = wl.kv_values(w, layer, n_tok, "v")
@@ -112,13 +136,16 @@ class Case:
         (kc, kt), (vc, vt) = oracle_codebooks(self.D, kb, vb, family)
         self.kcb, self.vcb = (kc, kt), (vc, vt)
         self.layer_dict = dict(D=self.D, H_kv=self.H, block_size=w.block_size, k_bits=kb, v_bits=vb,
-                               seed=0, slot_stride=self.slot_stride, mean=mean_removal)
+                               seed=0, slot_stride=self.slot_stride, mean=mean_removal, qjl=qjl)
         self.norm_correction = norm_correction
         self.pages_ref = np.zeros(self.num_blocks * w.block_size * self.H * self.slot_stride, np.uint8)
-        self.k_tie, self.v_tie = oq.append_rows_fast(
+        ties = oq.append_rows_fast(
             self.pages_ref, self.k.numpy(), self.v.numpy(), self.slots, kt, vt, kb, vb, 0,
             self.slot_stride, k_centroids32=kc if norm_correction else None,
-            v_centroids32=vc if norm_correction else None, mean=mean_removal)
+            v_centroids32=vc if norm_correction else None, mean=mean_removal,
+            qjl_centroids32=kc if qjl else None)
+        self.k_tie, self.v_tie = ties[0], ties[1]
+        self.q_tie = ties[2] if qjl else None
         self._torch = torch
 
     # ---- HIP path -------------------------------------------------------------------------
@@ -126,9 +153,9 @@ class Case:
         from packed_decode_attention_amd import LayerFormat
         return LayerFormat(self.D, self.Hq, self.H, self.kb, self.vb, self.w.block_size, 0,
                            self.family, slot_stride=self.slot_stride if self.slot_stride !=
-                           oq.slot_bytes(self.D, self.kb, self.vb, self.mean) else 0,
+                           oq.slot_bytes(self.D, self.kb, self.vb, self.mean, self.qjl) else 0,
                            k_codebook=self.kcb, v_codebook=self.vcb,
-                           norm_correction=self.norm_correction, mean_removal=self.mean)
+                           norm_correction=self.norm_correction, mean_removal=self.mean, qjl=self.qjl)
 
     def nc_args(self):
         """compare_pages' norm_correction argument: the oracle's plain norms and the centroids."""
@@ -244,8 +271,13 @@ class Case:
                                      self.kcb[0], self.vcb[0], sk, sv, self.w.n_sink, scale=scale, seqs=seqs)
 
     def oracle_dequant(self, slots):
+        """(K, V) rows: the bit-exact fp32 route; for the QJL key format K is the plain fp64
+        definition with the dequantized residual (compared to a tolerance)."""
         r = oq.read_slots(self.pages_ref, slots, self.H, self.D, self.kb, self.vb, self.slot_stride,
-                          self.mean)
+                          self.mean, self.qjl)
         k_mu, v_mu = (r[4], r[5]) if self.mean else (None, None)
-        return (oq.dequantize_spec(r[0], r[1], self.kcb[0], 0, k_mu),
-                oq.dequantize_spec(r[2], r[3], self.vcb[0], 0, v_mu))
+        if self.qjl:
+            k = oq.dequantize_plain(r[0], r[1], self.kcb[0], 0, k_mu) + oqjl.residual_estimate(r[-2], r[-1], 0)
+        else:
+            k = oq.dequantize_spec(r[0], r[1], self.kcb[0], 0, k_mu)
+        return k, oq.dequantize_spec(r[2], r[3], self.vcb[0], 0, v_mu)

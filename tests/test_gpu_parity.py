@@ -45,6 +45,17 @@ CASES = {
     "g5-mean-nc": dict(w=wl.Workload("g5-mean-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                      values="student_t", seed=16),
                        lens=[333, 96, 1], family="gaussian", norm_correction=True, mean_removal=True),
+    # QJL key format (1-bit residual sketch of 2-4-bit keys) on the vector kernel: 4 heads per kv
+    # head at 16 coordinates per lane, 8 heads at 8, D = 64 with 5 heads, 2-bit keys with block
+    # size 7, sinks and a padded stride, and combined with the other two format flags
+    "llama-qjl": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], qjl=True),
+    "ragged-qjl": dict(w=wl.scaled(W["ragged"], num_seqs=3), lens=[700, 65, 1], qjl=True),
+    "edges-qjl-mean": dict(w=wl.Workload("edges-qjl", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
+                                         values="normal", tables="fragmented", seed=17),
+                           lens=[0, 1, 3, 5, 66, 200], slot_stride=160, mean_removal=True, qjl=True),
+    "g5-qjl-nc": dict(w=wl.Workload("g5-qjl-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
+                                    values="student_t", seed=18),
+                      lens=[333, 96, 1], family="gaussian", norm_correction=True, qjl=True),
 }
 
 
@@ -72,7 +83,7 @@ def test_quantize_bytes(cases, name):
     print(f"[parity] quantize {name}: rows={len(c.slots)} H={c.H} D={c.D} K{c.kb}/V{c.vb}", flush=True)
     pages = c.gpu_quantize(fmt).cpu().numpy().reshape(-1)
     ties = compare_pages(pages, c.pages_ref, c.slots, c.H, c.D, c.kb, c.vb, c.slot_stride, c.k_tie, c.v_tie,
-                         c.nc_args(), c.mean)
+                         c.nc_args(), c.mean, c.q_tie)
     assert ties <= max(4, 1e-4 * c.slots.size * c.H * c.D)
     # untouched slots keep their contents
     used = np.zeros(c.num_blocks * c.w.block_size, bool)
@@ -94,7 +105,12 @@ def test_dequantize_rows_bit_exact(cases, name):
     tq.tq_dequantize_rows(fmt.desc, c.ref_pages_on_gpu(), c.num_blocks, torch.from_numpy(slots).cuda(), ko, vo)
     torch.cuda.synchronize()
     kr, vr = c.oracle_dequant(slots)
-    assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
+    if c.qjl:  # fp32 sums of the codes' and the sketch's transforms: a few ulps of the row
+        k = ko.cpu().numpy().astype(np.float64)
+        scale = np.abs(kr).max(axis=-1, keepdims=True) + 1e-30
+        assert np.all(np.abs(k - kr) <= 4e-6 * scale)
+    else:
+        assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
     assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
 
 
@@ -132,7 +148,7 @@ def test_decode_attention(cases, name):
 # (edges: G = 3, 2/3-bit codes, block size 7), sinks, and sequences shorter than T.
 MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
          ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
-         ("llama-mean", 2), ("edges-mean", 3)]
+         ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2)]
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
@@ -163,6 +179,7 @@ WINDOWS = {
     "ragged-small": ([1, 100, 0, 65, 17, 128], 130),
     "edges": ([0, 0, 0, 1, 13, 196], 200),
     "gaussian-g5": ([300, 0, 1], 301),
+    "llama-qjl": ([64, 0], 100),
 }
 
 

@@ -37,12 +37,15 @@ def test_slot_bytes(lib):
         for kb in range(1, 9):
             for vb in range(1, 9):
                 assert lib.tq_slot_bytes(D, kb, vb) == oq.slot_bytes(D, kb, vb)
-                for flags in (0, 1, 2, 3):  # norm correction, mean removal
-                    assert lib.tq_slot_bytes_ex(D, kb, vb, flags) == oq.slot_bytes(D, kb, vb, bool(flags & 2))
+                for flags in range(8):  # norm correction, mean removal, QJL key sketch
+                    assert lib.tq_slot_bytes_ex(D, kb, vb, flags) == oq.slot_bytes(D, kb, vb, bool(flags & 2),
+                                                                                 bool(flags & 4))
     with pytest.raises(lib.TqError):
         lib.tq_slot_bytes(128, 9, 4)
     with pytest.raises(lib.TqError):
-        lib.tq_slot_bytes_ex(128, 4, 4, 4)
+        lib.tq_slot_bytes_ex(128, 4, 4, 8)
+    with pytest.raises(lib.TqError):
+        lib.tq_slot_bytes_ex(100, 4, 4, 4)   # the sketch needs D a multiple of 8
 
 
 def test_rht_signs_match_oracle(lib):
@@ -102,7 +105,9 @@ def test_argument_validation_before_launch(lib):
     assert q(_desc(lib, v_bits=1)) == E.TQ_ERR_UNSUPPORTED
     assert q(_desc(lib, slot_stride=100)) == E.TQ_ERR_INVALID_ARG      # < 136
     assert q(_desc(lib, slot_stride=138)) == E.TQ_ERR_INVALID_ARG      # not a multiple of 4
-    assert q(_desc(lib, flags=4)) == E.TQ_ERR_INVALID_ARG              # unknown format flag
+    assert q(_desc(lib, flags=8)) == E.TQ_ERR_INVALID_ARG              # unknown format flag
+    assert q(_desc(lib, flags=4, k_bits=8)) == E.TQ_ERR_UNSUPPORTED    # the sketch is for 2-4-bit keys
+    assert q(_desc(lib, flags=4, slot_stride=136)) == E.TQ_ERR_INVALID_ARG  # < 156 with the sketch
     assert q(_desc(lib, flags=2, slot_stride=136)) == E.TQ_ERR_INVALID_ARG  # < 144 with the mean
     assert q(_desc(lib, flags=-1)) == E.TQ_ERR_INVALID_ARG
     assert q(_desc(lib, num_kv_heads=0)) == E.TQ_ERR_INVALID_ARG
