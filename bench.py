@@ -92,7 +92,7 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
 
 
 def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, n_queries=1,
-          mean_removal=False):
+          mean_removal=False, qjl=False):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -111,7 +111,7 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, 
         if (kb, vb) not in fmts:
             fmts[(kb, vb)] = tq.LayerFormat(D, w.num_q_heads, H, kb, vb, w.block_size, 0,
                                             norm_correction=norm_correction,
-                                            mean_removal=mean_removal)
+                                            mean_removal=mean_removal, qjl=qjl)
         fmt = fmts[(kb, vb)]
         pages = fmt.new_pages(num_blocks)
         t_layer = fill_layer(w, l, fmt, pages, ctx_slots, num_blocks, torch, tq, wl)
@@ -318,6 +318,9 @@ def main():
                     help="store corrected norms n / ||c[idx]|| (the norm-correction page format)")
     ap.add_argument("--mean-removal", action="store_true",
                     help="centre each row and store its mean (the mean-removal page format)")
+    ap.add_argument("--qjl", action="store_true",
+                    help="keys carry a 1-bit residual sketch and its norm (the QJL key format; keys "
+                         "of 2-4 bits)")
     ap.add_argument("--queries", type=int, default=1, metavar="T",
                     help="decode T causal queries per sequence (its last T positions) per call, "
                          "through tq_paged_decode_attention_multi")
@@ -343,8 +346,10 @@ def main():
     t0 = time.time()
     if args.queries > 1 and args.hot_window:
         sys.exit("--queries and --hot-window do not combine (the multi-query call has no window)")
+    if args.qjl and max(max(w.bits(l)[0] for l in range(w.layers)), w.k_bits) > 4:
+        sys.exit(f"--qjl needs keys of 2-4 bits; workload {w.name} has wider keys")
     S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction, args.queries,
-              args.mean_removal)
+              args.mean_removal, args.qjl)
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -375,7 +380,8 @@ def main():
     kv_tokens_step = int(lens.sum()) * w.layers
     value = kv_tokens_step / (ms_per_step / 1e3)
     fmt_flags = (tq.TQ_FLAG_NORM_CORRECTION if args.norm_correction else 0) | \
-                (tq.TQ_FLAG_MEAN_REMOVAL if args.mean_removal else 0)
+                (tq.TQ_FLAG_MEAN_REMOVAL if args.mean_removal else 0) | \
+                (tq.TQ_FLAG_QJL if args.qjl else 0)
     per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None,
                                         args.queries, fmt_flags)
     layer_ids = np.arange(n) % w.layers
@@ -402,14 +408,16 @@ def main():
                                              if args.hot_window else "")
                                + (", norm-correction format" if args.norm_correction else "")
                                + (", mean-removal format" if args.mean_removal else "")
+                               + (", QJL key format" if args.qjl else "")
                                + (f", {args.queries} causal queries per sequence" if args.queries > 1 else ""),
                    "kv_tokens_per_layer": int(lens.sum()),
                    "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal)
-                                 else recorded_traffic(w)),
-                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits)),
+                     "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal
+                                          or args.qjl) else recorded_traffic(w)),
+                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits,
+                                                                                   args.qjl)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},
         "append": {"step_us_per_layer": float(app_ms.mean() * 1e3),

@@ -719,6 +719,8 @@ struct MfmaTile {
   uint32_t v[2][MfmaCfg<D, KB, VB>::VW];  // V codes of the same tokens and coordinates
   float kn[2], vn[2];
   float km[2], vm[2];  // row means (mean-removal format; else 0)
+  uint32_t zb[2];      // QJL key format: sketch bits of the lane group's coordinates
+  float kg[2];         // QJL key format: residual norms gamma
 };
 
 // Page rows of a 32-position tile for one kv head, as fetched when page blocks hold whole runs of
@@ -771,8 +773,12 @@ __device__ __forceinline__ uint4 k_operand(const typename OpTable<KB>::E* tab, c
   }
 }
 
-template <int D, int KB, int VB, bool G8, bool UBLK>
+// QJL key format on the matrix cores: the residual term (S R q) . z of a 16-token sub-tile is one
+// more product per 32 coordinates, A = the sketched query (two fp16 parts per head, rows as in
+// QK), B = the tokens' sketch bits as fp16 +-1 (exact), four bits per read of a 16-entry table.
+template <int D, int KB, int VB, bool G8, bool UBLK, bool QJL = false>
 __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!(QJL && UBLK), "the staged tile layout is the plain slot format");
   using C = MfmaCfg<D, KB, VB>;
   using KE = typename OpTable<KB>::E;
   using VE = typename OpTable<VB>::E;
@@ -818,8 +824,14 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   __shared__ float s_qmax[8];
   __shared__ float s_qsum[8];  // mean-removal format: scale log2(e) sum(q) per head
   __shared__ float s_r1[D];    // mean-removal format: R 1 = D^(-1/2) H s
+  constexpr int NZ = D / 32;   // QJL products per 16-token sub-tile
+  __shared__ __align__(16) uint4 s_ajq[QJL ? NZ : 1][64];  // QJL: A operands per step and lane
+  __shared__ uint2 s_ztab[16];  // QJL: four sketch bits -> four fp16 +-1
+  __shared__ float s_qjmax[8];  // QJL: largest |sketched query| per head, scaled
   __shared__ __align__(16) uint32_t s_w[kNW][16][C::WROW];
   float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_x);
+  float(*s_qj)[D] = reinterpret_cast<float(*)[D]>(s_x) + 8;  // QJL: sketched queries, after s_q
+  static_assert(!QJL || kXBytes >= 16 * D * 4, "room for the queries and the sketched queries");
   float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_x);  // [wave * H8 + head]
 
   const int tid = threadIdx.x;
@@ -830,6 +842,12 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
 
   build_op_table<KB>(s_ktab, L.kc, tid);
   build_op_table<VB>(s_vtab, L.vc, tid);
+  if (QJL && tid < 16) {  // entry e: fp16 +1 where bit i of e is set, else -1
+    uint32_t hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = ((tid >> i) & 1) ? 0x3C00u : 0xBC00u;
+    s_ztab[tid] = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+  }
 
   const int p0 = split * a.chunk;
   const int p_end = min(p0 + a.chunk, packed_end);
@@ -868,6 +886,21 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     }
     mx = lanes_max<LPH>(mx);
     if (j == 0) s_qmax[g] = mx * a.qscale;
+    if constexpr (QJL) {  // y = H (sigma2 * x); the score term is qscale sqrt(pi/2) / D y . z
+      const uint32_t sb2 = sign_byte(L.signs2, j);
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = ((sb2 >> e) & 1u) ? -x[e] : x[e];
+      wht_row8_dpp<LPH>(y, j);
+      float my = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_qj[g][8 * j + e] = y[e];
+        my = fmaxf(my, fabsf(y[e]));
+      }
+      my = lanes_max<LPH>(my);
+      if (j == 0) s_qjmax[g] = my * a.qscale * (kQjlKappa / (float)D);
+    }
   } else if (!UBLK && L.mean && tid >= 192 && tid < 192 + LPH) {  // R 1, by the last wave (G <= 8 heads
     const int j = tid - 192;                             // use at most 128 threads above)
     const uint32_t sb = sign_byte(L.signs, j);
@@ -905,6 +938,34 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       aq[st] = repeat_operand<C::VK>(pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16));
     }
   }
+  // QJL: A operands of the residual products, step st: coordinates QC q4 + 8 st + 0..7 of row
+  // m = t16 (one fp16 part of qscale sqrt(pi/2) / D y, times the head's power of two).  They
+  // depend on the lane only: wave 0 writes them for all waves.
+  auto qj_exp = [&](int g) {
+    const float qm = s_qjmax[g];
+    return qm > 0.0f ? 13 - ilogbf(qm) : 0;
+  };
+  if constexpr (QJL) {
+    if (wave == 0) {
+      const int g = (t16 >> 2) + 4 * ((t16 >> 1) & 1);
+      const bool lo_part = t16 & 1;
+      const bool live = g < G;
+      const float f = live ? ldexpf(a.qscale * (kQjlKappa / (float)D), qj_exp(g)) : 0.0f;
+#pragma unroll
+      for (int st = 0; st < NZ; ++st) {
+        uint32_t pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = live ? s_qj[g][C::QC * q4 + 8 * st + i] * f : 0.0f;
+          uint32_t hi, lo;
+          split_f16(x, hi, lo);
+          pr[i] = lo_part ? lo : hi;
+        }
+        s_ajq[st][lane] = make_uint4(pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16),
+                                     pr[4] | (pr[5] << 16), pr[6] | (pr[7] << 16));
+      }
+    }
+  }
   const int g0 = q4, g1 = q4 + 4;
   const bool live0 = g0 < G, live1 = G8 && g1 < G;
   // positions visible to heads g0, g1: the split's end, or earlier for causal queries
@@ -912,6 +973,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   // Score factors of the heads this lane holds: 2^-(e + 8).
   const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
   const float f1 = live1 ? ldexpf(1.0f, -(head_exp(g1) + kLutShift)) : 0.0f;
+  // QJL: residual-term factors of the same heads, 2^-e
+  const float fq0 = (QJL && live0) ? ldexpf(1.0f, -qj_exp(g0)) : 0.0f;
+  const float fq1 = (QJL && live1) ? ldexpf(1.0f, -qj_exp(g1)) : 0.0f;
 
   const int voff = L.kreg;  // V region
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
@@ -949,6 +1013,11 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       m.vn[u] = *reinterpret_cast<const float*>(r + voff + L.vcode_bytes);
       m.km[u] = L.mean ? *reinterpret_cast<const float*>(r + L.kcode_bytes + 4) : 0.0f;
       m.vm[u] = L.mean ? *reinterpret_cast<const float*>(r + voff + L.vcode_bytes + 4) : 0.0f;
+      if constexpr (QJL) {  // the lane group's QC sketch bits (4 or 2 bytes) and gamma
+        if constexpr (C::QC == 32) m.zb[u] = *reinterpret_cast<const uint32_t*>(r + L.kqjl + 4 * q4);
+        else m.zb[u] = *reinterpret_cast<const uint16_t*>(r + L.kqjl + 2 * q4);
+        m.kg[u] = *reinterpret_cast<const float*>(r + L.kqjl + D / 8);
+      }
     }
   };
   // Whole runs of 16 positions per block: the tile's slots as consecutive chunks (see MfmaRaw),
@@ -1028,7 +1097,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   // cur: the lane's code runs and norms (blocks of any size); with UBLK they come from the stage.
   auto process = [&](const Tile& cur, int tile) {
     // ---- QK on the matrix cores ----
-    float4_t sc[2];
+    float4_t sc[2], sq[2];
     float kn[2], vn[2], km[2] = {0.0f, 0.0f}, vm[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -1066,6 +1135,16 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         sb = mfma_f16(aq[st + 1], kop[st + 1], sb);
       }
       sc[u] = sa + sb;
+      if constexpr (QJL) {  // residual products: sketch bits as fp16 +-1, four per table read
+        float4_t za = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < NZ; ++st) {
+          const uint32_t byte = (cur.zb[u] >> (8 * st)) & 0xffu;
+          const uint2 lo = s_ztab[byte & 15u], hi = s_ztab[byte >> 4];
+          za = mfma_f16(s_ajq[st][lane], make_uint4(lo.x, lo.y, hi.x, hi.y), za);
+        }
+        sq[u] = za;
+      }
     }
 
     // ---- online softmax, tokens t16 and 16 + t16 ----
@@ -1075,6 +1154,10 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     for (int u = 0; u < 2; ++u) {
       const int p = pbase + 16 * u + t16;
       float t0 = (sc[u][0] + sc[u][1]) * kn[u] * f0, t1 = (sc[u][2] + sc[u][3]) * kn[u] * f1;
+      if constexpr (QJL) {
+        t0 += (sq[u][0] + sq[u][1]) * cur.kg[u] * fq0;
+        t1 += (sq[u][2] + sq[u][3]) * cur.kg[u] * fq1;
+      }
       if constexpr (kMean) {
         t0 += km[u] * qsum0;
         t1 += km[u] * qsum1;
@@ -1414,15 +1497,6 @@ void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
 template <int D, int KB, int VB, int GMAX>
 void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
   DecodeArgs a = a0;
-  if constexpr (KB <= 4) {  // QJL key format (keys of 2-4 bits): the vector-ALU split kernel
-    if (a.L.qjl) {
-      dim3 grid = sgrid;
-      grid.x += a.rows_blocks;
-      hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX, true>), grid, dim3(kWG), 0, st, a);
-      launch_merge<D, GMAX>(a, mgrid, st);
-      return;
-    }
-  }
   constexpr bool separate_rows = mfma_format(D, KB, VB) && GMAX > 4;
   dim3 grid = sgrid;
   if (separate_rows) {
@@ -1432,14 +1506,22 @@ void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
   } else {
     grid.x += a.rows_blocks;
   }
+  // The QJL key format (keys of 2-4 bits) has its own instances: the matrix-core kernel with the
+  // residual products, or the vector kernel with the residual term.
+  constexpr bool kQjlOk = KB <= 4;
   if constexpr (mfma_format(D, KB, VB)) {
     constexpr bool G8 = GMAX > 4;
-    if (a.L.bs % 16 == 0 && !a.L.mean)  // the staged tile layout is the plain slot format
+    if (kQjlOk && a.L.qjl)
+      hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false, kQjlOk>), grid, dim3(kWG), 0, st, a);
+    else if (a.L.bs % 16 == 0 && !a.L.mean)  // the staged tile layout is the plain slot format
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, true>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false>), grid, dim3(kWG), 0, st, a);
   } else {
-    hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX>), grid, dim3(kWG), 0, st, a);
+    if (kQjlOk && a.L.qjl)
+      hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX, kQjlOk>), grid, dim3(kWG), 0, st, a);
+    else
+      hipLaunchKernelGGL((tq_decode_split_kernel<D, KB, VB, GMAX>), grid, dim3(kWG), 0, st, a);
   }
   launch_merge<D, GMAX>(a, mgrid, st);
 }

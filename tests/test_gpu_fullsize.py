@@ -10,7 +10,7 @@ oracle from the same fp16 rows:
     attention tolerance.
 The rest of the batch still runs, so the grid, split geometry and workspace are the benchmark's.
 One case uses the norm-correction page format (bench.py --norm-correction), one the mean-removal
-format (bench.py --mean-removal), one decodes two
+format (bench.py --mean-removal), one the QJL key format (bench.py --qjl), one decodes two
 causal queries per sequence (bench.py --queries 2).  One case adds a hot
 window (bench.py --hot-window): the last W positions of every sequence also
 come from fp16 rows (the sampled sequences' own rows, random rows elsewhere) and the decode runs
@@ -46,7 +46,7 @@ def _pick(w, lens, which):
     return list(which)
 
 
-CASES = [  # workload, layer, sampled sequences, hot window, norm-correction format, queries
+CASES = [  # workload, layer, sampled sequences, hot window, format (True: norm correction), queries
     ("llama3-8b", 1, (0, 13), 0, False, 1),
     ("mistral-7b", 2, (1,), 0, False, 1),
     ("ragged", 5, "extremes", 0, False, 1),
@@ -55,12 +55,14 @@ CASES = [  # workload, layer, sampled sequences, hot window, norm-correction for
     ("llama3-8b", 6, (9,), 0, True, 1),
     ("llama3-8b", 2, (3,), 0, False, 2),
     ("llama3-8b", 5, (7,), 0, "mean", 1),
+    ("llama3-8b", 4, (11,), 0, "qjl", 1),
 ]
 
 
 @pytest.mark.parametrize("name,layer,which,window,nc,nq", CASES,
                          ids=[f"{c[0]}-L{c[1]}" + (f"-W{c[3]}" if c[3] else "")
-                              + ("-MEAN" if c[4] == "mean" else "-NC" if c[4] else "")
+                              + ("-MEAN" if c[4] == "mean" else "-QJL" if c[4] == "qjl" else
+                                 "-NC" if c[4] else "")
                               + (f"-Q{c[5]}" if c[5] > 1 else "") for c in CASES])
 def test_full_size_sampled(name, layer, which, window, nc, nq):
     import torch
@@ -80,9 +82,10 @@ def test_full_size_sampled(name, layer, which, window, nc, nq):
 
     heads = {b: (7 * b + layer) % H for b in seqs}  # one kv head per sampled sequence
     G = Hq // H
-    mean = nc == "mean"  # the format column: norm correction, or mean removal
+    mean = nc == "mean"  # the format column: norm correction, mean removal or the QJL key sketch
+    qjl = nc == "qjl"
     nc = nc is True
-    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0, norm_correction=nc, mean_removal=mean)
+    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0, norm_correction=nc, mean_removal=mean, qjl=qjl)
     pages = fmt.new_pages(num_blocks)
     ctx_off = np.concatenate([[0], np.cumsum(lens - 1)])
     rows = {b: ([], []) for b in seqs}
@@ -118,14 +121,16 @@ def test_full_size_sampled(name, layer, which, window, nc, nq):
         slots1 = wl.token_slots(bt1, 0, np.arange(L), bs)
         ref = np.zeros(nblk1 * bs * stride, np.uint8)
         cents = dict(k_centroids32=kc, v_centroids32=vc) if nc else {}
-        k_tie, v_tie = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride, mean=mean, **cents)
+        ties_ = oq.append_rows_fast(ref, k, v, slots1, kt, vt, kb, vb, 0, stride, mean=mean,
+                                    qjl_centroids32=kc if qjl else None, **cents)
+        k_tie, v_tie, q_tie = ties_ if qjl else ties_ + (None,)
         # the GPU's rows of the same positions and kv head
         slots = torch.from_numpy(wl.token_slots(bt_np, b, np.arange(L), bs)).cuda()
         gpu_rows = flat[slots, hh].cpu().numpy()
         ref_rows = ref.reshape(-1, stride)[slots1]
         nc_args = ((oq.norm_fp32(k), oq.norm_fp32(v)), (kc, vc)) if nc else None
         ties = compare_pages(gpu_rows.reshape(-1), ref_rows.reshape(-1), np.arange(L), 1, D, kb, vb,
-                             stride, k_tie, v_tie, nc_args, mean)
+                             stride, k_tie, v_tie, nc_args, mean, q_tie)
         print(f"[fullsize]   seq {b} kv head {hh} (L={L}): page rows match, {ties} tie indices",
               flush=True)
         # the oracle's bytes into the GPU pages of this sequence and kv head
@@ -164,7 +169,7 @@ def test_full_size_sampled(name, layer, which, window, nc, nq):
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got)), "non-finite output in the batch"
     layer_dict = dict(D=D, H_kv=1, block_size=bs, k_bits=kb, v_bits=vb, seed=0, slot_stride=stride,
-                      mean=mean)
+                      mean=mean, qjl=qjl)
     qn = q.cpu().numpy()
     skn = None if sink_k is None else sink_k.cpu().numpy()
     svn = None if sink_v is None else sink_v.cpu().numpy()

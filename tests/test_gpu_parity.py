@@ -45,10 +45,12 @@ CASES = {
     "g5-mean-nc": dict(w=wl.Workload("g5-mean-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                      values="student_t", seed=16),
                        lens=[333, 96, 1], family="gaussian", norm_correction=True, mean_removal=True),
-    # QJL key format (1-bit residual sketch of 2-4-bit keys) on the vector kernel: 4 heads per kv
-    # head at 16 coordinates per lane, 8 heads at 8, D = 64 with 5 heads, 2-bit keys with block
-    # size 7, sinks and a padded stride, and combined with the other two format flags
+    # QJL key format (1-bit residual sketch of 2-4-bit keys): the matrix-core kernel's residual
+    # products at 4 and 8 heads (D = 128) and 5 heads (D = 64), the vector kernel (3-bit values,
+    # block size 7, sinks, padded stride), and combined with the other two format flags
     "llama-qjl": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], qjl=True),
+    "llama-qjl-mean": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[517, 64], qjl=True,
+                           mean_removal=True),
     "ragged-qjl": dict(w=wl.scaled(W["ragged"], num_seqs=3), lens=[700, 65, 1], qjl=True),
     "edges-qjl-mean": dict(w=wl.Workload("edges-qjl", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
                                          values="normal", tables="fragmented", seed=17),
