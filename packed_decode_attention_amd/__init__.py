@@ -96,6 +96,8 @@ class LayerFormat:
 def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int, qjl: bool = False):
     """Names of the kernels one tq_paged_decode_attention call launches for this format, in
     launch order (as they appear in a kernel trace)."""
-    mfma = not qjl and ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
-                        (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
+    # the QJL key format (keys of 2-4 bits) runs on the same kernels, with its residual products
+    del qjl
+    mfma = ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
+            (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
     return ["tq_decode_mfma_kernel" if mfma else "tq_decode_split_kernel", "tq_decode_merge_kernel"]
