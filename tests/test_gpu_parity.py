@@ -46,8 +46,8 @@ CASES = {
                                      values="student_t", seed=16),
                        lens=[333, 96, 1], family="gaussian", norm_correction=True, mean_removal=True),
     # QJL key format (1-bit residual sketch of 2-4-bit keys): the matrix-core kernel's residual
-    # products at 4 and 8 heads (D = 128) and 5 heads (D = 64), the vector kernel (3-bit values,
-    # block size 7, sinks, padded stride), and combined with the other two format flags
+    # products at 4 and 8 heads (D = 128) and 5 heads (D = 64) and with block size 7, sinks and a
+    # padded stride; the vector kernel (3-bit values); combined with the other two format flags
     "llama-qjl": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], qjl=True),
     "llama-qjl-mean": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[517, 64], qjl=True,
                            mean_removal=True),
@@ -55,6 +55,9 @@ CASES = {
     "edges-qjl-mean": dict(w=wl.Workload("edges-qjl", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
                                          values="normal", tables="fragmented", seed=17),
                            lens=[0, 1, 3, 5, 66, 200], slot_stride=160, mean_removal=True, qjl=True),
+    "edges-qjl": dict(w=wl.Workload("edges-qjl2", 1, 6, 6, 2, 128, 2, 2, 0, block_size=7, n_sink=4,
+                                    values="normal", tables="fragmented", seed=19),
+                      lens=[0, 1, 3, 5, 66, 200], slot_stride=160, qjl=True),
     "g5-qjl-nc": dict(w=wl.Workload("g5-qjl-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                     values="student_t", seed=18),
                       lens=[333, 96, 1], family="gaussian", norm_correction=True, qjl=True),
@@ -150,7 +153,7 @@ def test_decode_attention(cases, name):
 # (edges: G = 3, 2/3-bit codes, block size 7), sinks, and sequences shorter than T.
 MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
          ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
-         ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2)]
+         ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2), ("edges-qjl", 3)]
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
