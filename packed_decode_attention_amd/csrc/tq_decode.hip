@@ -724,16 +724,21 @@ struct MfmaTile {
 };
 
 // Page rows of a 32-position tile for one kv head, as fetched when page blocks hold whole runs of
-// 16 positions and slots are unpadded: a slot is N16 16-byte chunks and an 8-byte tail.  Lane l
-// fetches chunk c = 64 i + l of the tile (row c / N16, chunk c % N16) into c[i] and, for l < 32,
-// the tail of row l: consecutive lanes read consecutive bytes of a row, so a wave's load covers
-// 64 / N16 whole slots instead of a 16-byte piece of 16 slots.
-template <int D, int KB, int VB>
+// 16 positions and slots are unpadded: a slot is N16 16-byte chunks and, in the plain format, an
+// 8-byte tail (mean-removal slots, MEAN, are whole chunks).  Lane l fetches chunk c = 64 i + l of
+// the tile (row c / N16, chunk c % N16) into c[i] and, for l < 32, the tail of row l: consecutive
+// lanes read consecutive bytes of a row, so a wave's load covers 64 / N16 whole slots instead of
+// a 16-byte piece of 16 slots.  In the wave's LDS stage row r starts at r * SS, with SS / 4 = 2
+// mod 4 (a mean-removal slot gets 8 bytes of padding for that).
+template <int D, int KB, int VB, bool MEAN = false>
 struct MfmaRaw {
-  static constexpr int SB = D * KB / 8 + 4 + D * VB / 8 + 4;  // slot bytes
-  static constexpr int N16 = (SB - 8) / 16;
+  static constexpr int SB = D * KB / 8 + D * VB / 8 + (MEAN ? 16 : 8);  // slot bytes
+  static constexpr int TAIL = SB % 16;
+  static constexpr int N16 = (SB - TAIL) / 16;
   static constexpr int NI = (32 * N16 + 63) / 64;
-  static_assert((SB - 8) % 16 == 0, "slot = whole 16-byte chunks + an 8-byte tail");
+  static constexpr int SS = TAIL ? SB : SB + 8;  // stage row stride
+  static_assert(TAIL == 8 || TAIL == 0, "slot = whole 16-byte chunks + an 8-byte tail, or chunks only");
+  static_assert((SS / 4) % 4 == 2, "stage rows 2 mod 4 dwords apart");
   uint4 c[NI];
   uint2 t;
 };
@@ -776,14 +781,17 @@ __device__ __forceinline__ uint4 k_operand(const typename OpTable<KB>::E* tab, c
 // QJL key format on the matrix cores: the residual term (S R q) . z of a 16-token sub-tile is one
 // more product per 32 coordinates, A = the sketched query (two fp16 parts per head, rows as in
 // QK), B = the tokens' sketch bits as fp16 +-1 (exact), four bits per read of a 16-entry table.
-template <int D, int KB, int VB, bool G8, bool UBLK, bool QJL = false>
+template <int D, int KB, int VB, bool G8, bool UBLK, bool QJL = false, bool MEANT = false>
 __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
-  static_assert(!(QJL && UBLK), "the staged tile layout is the plain slot format");
+  static_assert(!(QJL && UBLK), "the staged tile layout has no sketch");
+  static_assert(!MEANT || UBLK, "MEANT: the staged tile layout of the mean-removal format");
+  // Mean terms: on the per-lane path at run time, on the staged path in the MEANT instances only
+  constexpr bool kMean = !UBLK || MEANT;
   using C = MfmaCfg<D, KB, VB>;
   using KE = typename OpTable<KB>::E;
   using VE = typename OpTable<VB>::E;
   using Tile = MfmaTile<D, KB, VB>;
-  using Raw = MfmaRaw<D, KB, VB>;
+  using Raw = MfmaRaw<D, KB, VB, MEANT>;
   constexpr int H8 = G8 ? 8 : 4;  // query heads per kv head this instance handles at most
   const TqLayer& L = a.L;
   const int G = L.G;
@@ -791,7 +799,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   // s_x holds, in turn: the rotated queries (prologue); per wave, the page rows of the current
   // tile (UBLK) or its value codes; the per-wave partial results (epilogue).  The fp16-row chunk
   // workgroups use it for their own sums.
-  constexpr int kTileBytes = UBLK ? kNW * 32 * Raw::SB : kNW * 32 * C::VROW * 4;
+  constexpr int kTileBytes = UBLK ? kNW * 32 * Raw::SS : kNW * 32 * C::VROW * 4;
   constexpr int kQPBytes = kNW * H8 * (D + 2) * 4;
   constexpr int kRowsBytes = G8 ? 0 : 4 * fp16_chunk_lds<D, 4>();
   constexpr int kXBytes = (kTileBytes > kQPBytes ? kTileBytes : kQPBytes) > kRowsBytes
@@ -866,7 +874,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     const int g = tid / LPH, j = tid % LPH;
     float x[8];
     load8_f16(a.q + q_row(a, b, h, g) * D + 8 * j, x);
-    if (!UBLK && L.mean) {
+    if (kMean && L.mean) {
       float qs = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) qs += x[e];
@@ -901,7 +909,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       my = lanes_max<LPH>(my);
       if (j == 0) s_qjmax[g] = my * a.qscale * (kQjlKappa / (float)D);
     }
-  } else if (!UBLK && L.mean && tid >= 192 && tid < 192 + LPH) {  // R 1, by the last wave (G <= 8 heads
+  } else if (kMean && L.mean && tid >= 192 && tid < 192 + LPH) {  // R 1, by the last wave (G <= 8 heads
     const int j = tid - 192;                             // use at most 128 threads above)
     const uint32_t sb = sign_byte(L.signs, j);
     float x[8];
@@ -1030,7 +1038,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     const int c = 64 * i + lane;
     const int row = c / Raw::N16, col = c - row * Raw::N16;
     goff[i] = __umul24((uint32_t)(row & 15), row_bytes32) + 16 * col;
-    loff[i] = row * Raw::SB + 16 * col;
+    loff[i] = row * Raw::SS + 16 * col;
   }
   const uint32_t goff_t = __umul24((uint32_t)(lane & 15), row_bytes32) + 16 * Raw::N16;
   auto fetch_raw = [&](int tile, Raw& m) {
@@ -1047,9 +1055,9 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         m.c[i] = *reinterpret_cast<const uint4*>(base + goff[i]);
       }
     }
-    if (lane < 32) m.t = *reinterpret_cast<const uint2*>((lane < 16 ? r0 : r1) + goff_t);
+    if (Raw::TAIL && lane < 32) m.t = *reinterpret_cast<const uint2*>((lane < 16 ? r0 : r1) + goff_t);
   };
-  uint8_t* stage = s_x + wave * 32 * Raw::SB;
+  uint8_t* stage = s_x + wave * 32 * Raw::SS;
   auto stage_raw = [&](const Raw& m) {
 #pragma unroll
     for (int i = 0; i < Raw::NI; ++i) {
@@ -1059,7 +1067,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         d[1] = make_uint2(m.c[i].z, m.c[i].w);
       }
     }
-    if (lane < 32) *reinterpret_cast<uint2*>(stage + lane * Raw::SB + 16 * Raw::N16) = m.t;
+    if (Raw::TAIL && lane < 32) *reinterpret_cast<uint2*>(stage + lane * Raw::SS + 16 * Raw::N16) = m.t;
   };
 
   // Online-softmax state.  kSent is a finite "minus infinity": masked positions score kSent, so
@@ -1068,8 +1076,6 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   float m_s[2] = {kSent, kSent};   // running max of scores (heads g0, g1)
   float m_w[2] = {kSent, kSent};   // running max of score + log2(n_V)
   float l_s[2] = {0.0f, 0.0f};     // per-lane partial sums of 2^(s - m_s)
-  // Mean-removal format (per-lane fetch only: the staged tile layout is the plain slot format).
-  constexpr bool kMean = !UBLK;
   float mv_s[2] = {0.0f, 0.0f};    // mean-removal format: partial sums of 2^(s - m_s) mu_V
   const float qsum0 = (kMean && L.mean && live0) ? s_qsum[g0] : 0.0f;  // mu_K term of the scores
   const float qsum1 = (kMean && L.mean && live1) ? s_qsum[g1] : 0.0f;
@@ -1103,7 +1109,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     for (int u = 0; u < 2; ++u) {
       uint32_t kw[C::KW];
       if constexpr (UBLK) {
-        const uint8_t* row = stage + (16 * u + t16) * Raw::SB;
+        const uint8_t* row = stage + (16 * u + t16) * Raw::SS;
         if constexpr (C::KW % 2 == 0) {
 #pragma unroll
           for (int i = 0; i < C::KW; i += 2) {
@@ -1117,6 +1123,10 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
         }
         kn[u] = *reinterpret_cast<const float*>(row + L.kcode_bytes);
         vn[u] = *reinterpret_cast<const float*>(row + voff + L.vcode_bytes);
+        if constexpr (MEANT) {  // the row means follow the norms
+          km[u] = *reinterpret_cast<const float*>(row + L.kcode_bytes + 4);
+          vm[u] = *reinterpret_cast<const float*>(row + voff + L.vcode_bytes + 4);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < C::KW; ++i) kw[i] = cur.k[u][i];
@@ -1253,7 +1263,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 8 * q4 + 4 * j + i;
-        const uint32_t* src = UBLK ? reinterpret_cast<const uint32_t*>(stage + tok * Raw::SB + voff)
+        const uint32_t* src = UBLK ? reinterpret_cast<const uint32_t*>(stage + tok * Raw::SS + voff)
                                    : vt + tok * C::VROW;
         if constexpr (VBITS == 64) {  // the stage's value codes are 4-byte aligned only
           cw[i][0] = src[2 * t16];
@@ -1513,8 +1523,10 @@ void launch_t(const DecodeArgs& a0, dim3 sgrid, dim3 mgrid, hipStream_t st) {
     constexpr bool G8 = GMAX > 4;
     if (kQjlOk && a.L.qjl)
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false, kQjlOk>), grid, dim3(kWG), 0, st, a);
-    else if (a.L.bs % 16 == 0 && !a.L.mean)  // the staged tile layout is the plain slot format
+    else if (a.L.bs % 16 == 0 && !a.L.mean)  // staged tiles (whole runs of 16 rows per block)
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, true>), grid, dim3(kWG), 0, st, a);
+    else if (a.L.bs % 16 == 0)  // staged tiles of the mean-removal format
+      hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, true, false, true>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((tq_decode_mfma_kernel<D, KB, VB, G8, false>), grid, dim3(kWG), 0, st, a);
   } else {
