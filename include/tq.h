@@ -86,8 +86,7 @@ typedef enum tq_codebook_family {
  *   sqrt(pi/2) / D * gamma * R^T S^T (2 b - 1), so decode adds
  *   scale * sqrt(pi/2) / D * gamma * (S R q) . (2 b - 1) to each score.  Values are unchanged.
  *   The sign bits and gamma come from fp32 arithmetic: a bit whose |(S r)_i| is within about
- *   1e-4 gamma of 0 may differ from an exact computation.  Decode of this format runs on the
- *   vector-ALU kernel.  Combines with the other flags.
+ *   1e-4 gamma of 0 may differ from an exact computation.  Combines with the other flags.
  * Other bits must be 0. */
 #define TQ_FLAG_NORM_CORRECTION 1
 #define TQ_FLAG_MEAN_REMOVAL 2
