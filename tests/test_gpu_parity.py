@@ -58,6 +58,9 @@ CASES = {
     "edges-qjl": dict(w=wl.Workload("edges-qjl2", 1, 6, 6, 2, 128, 2, 2, 0, block_size=7, n_sink=4,
                                     values="normal", tables="fragmented", seed=19),
                       lens=[0, 1, 3, 5, 66, 200], slot_stride=160, qjl=True),
+    # the largest sink count (128): sequences shorter than, equal to and longer than it
+    "sinks-max": dict(w=wl.Workload("sinks-max", 1, 4, 8, 2, 128, 4, 4, 0, n_sink=128, values="normal",
+                                    seed=20), lens=[100, 128, 129, 700]),
     "g5-qjl-nc": dict(w=wl.Workload("g5-qjl-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                     values="student_t", seed=18),
                       lens=[333, 96, 1], family="gaussian", norm_correction=True, qjl=True),
@@ -153,7 +156,8 @@ def test_decode_attention(cases, name):
 # (edges: G = 3, 2/3-bit codes, block size 7), sinks, and sequences shorter than T.
 MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
          ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
-         ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2), ("edges-qjl", 3)]
+         ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2), ("edges-qjl", 3),
+         ("tiny", 64), ("sinks-max", 64)]  # 64: the largest query count
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
@@ -185,6 +189,7 @@ WINDOWS = {
     "edges": ([0, 0, 0, 1, 13, 196], 200),
     "gaussian-g5": ([300, 0, 1], 301),
     "llama-qjl": ([64, 0], 100),
+    "sinks-max": ([0, 0, 1, 572], 1024),  # the largest sink count and window capacity together
 }
 
 
