@@ -237,7 +237,11 @@ int tq_paged_decode_attention_multi(const tq_layer_desc* layer, const void* q, i
 
 /* Dequantize whole slots (turboquant-serve 0.1.2, "Architecture" _decode(): unpack, Lloyd-Max
  * decode, restore magnitude, rotate back).  Bit-exact definition: c_i = centroid[idx_i] (fp32);
- * z = H c computed exactly (fp64); g = fp32(n * fp32(1/sqrt(D))); x_i = s_i * fp32(fp32(z_i) * g).
+ * z = H c computed exactly (fp64); g = fp32(n * fp32(1/sqrt(D))); x_i = s_i * fp32(fp32(z_i) * g),
+ * then fp32(x_i + mu) with TQ_FLAG_MEAN_REMOVAL.  With TQ_FLAG_QJL a key also gains its sketched
+ * residual: t = H diag(sigma2) H (2b - 1) exactly (fp64), and
+ * x_i = s_i * fp32(fp32(fp32(z_i) * g) + fp32(fp32(t_i) * gq)), gq = fp32(sqrt(pi/2) / D * gamma *
+ * fp32(1/sqrt(D))) (the product in fp64).
  *   slots         device int64 [n]: slot ids (< num_blocks * block_size)
  *   k_out, v_out  device fp32 [n][num_kv_heads][D] (written) */
 int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages, int64_t num_blocks,
