@@ -61,6 +61,8 @@ CASES = {
     # the largest sink count (128): sequences shorter than, equal to and longer than it
     "sinks-max": dict(w=wl.Workload("sinks-max", 1, 4, 8, 2, 128, 4, 4, 0, n_sink=128, values="normal",
                                     seed=20), lens=[100, 128, 129, 700]),
+    "g8-v3-qjl": dict(w=wl.Workload("g8-v3-qjl", 1, 3, 16, 2, 128, 4, 3, 0, values="normal", seed=21),
+                      lens=[777, 64, 2], qjl=True),  # the vector kernel's 8-head instance
     "g5-qjl-nc": dict(w=wl.Workload("g5-qjl-nc", 1, 3, 10, 2, 64, 4, 8, 0, block_size=32,
                                     values="student_t", seed=18),
                       lens=[333, 96, 1], family="gaussian", norm_correction=True, qjl=True),
