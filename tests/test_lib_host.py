@@ -186,3 +186,21 @@ def test_multi_query_workspace_bytes(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert isinstance(lib.tq_status_str(s), str) and lib.tq_status_str(s)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: with the HIP library absent, the first call raises instead of computing."""
+    import subprocess
+    import sys
+    code = ("import packed_decode_attention_amd as tq\n"
+            "try:\n"
+            "    tq.tq_slot_bytes(128, 4, 4)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('computed')\n")
+    env = dict(os.environ, TQ_LIB=str(tmp_path / "absent" / "libtq.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "not built" in r.stdout
