@@ -1,5 +1,6 @@
 // C ABI entry points: argument validation on the host, rotation sign mask, split geometry, and
 // the kernel launches.  Nothing here allocates device memory.
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -109,6 +110,13 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t 
   return tq_decode_ws_bytes(L, num_seqs, tq_decode_split(L, num_seqs, max_seq_len));
 }
 
+// The split grid (packed splits of every sequence and kv head, plus the fp16-row chunks) must fit
+// the kernels' 32-bit workgroup arithmetic.
+static bool grid_fits(const TqLayer& L, int32_t num_seqs, const TqSplit& sp) {
+  const int64_t units = (int64_t)num_seqs * sp.max_split + 8;
+  return units * L.Hkv + (int64_t)num_seqs * L.Hkv * 16 <= INT32_MAX;
+}
+
 static int paged_decode(const tq_layer_desc* layer, const void* q, const void* pages,
                         int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
@@ -135,6 +143,7 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
   if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
   const TqSplit sp = tq_decode_split(L, num_seqs, max_seq_len);
+  if (!grid_fits(L, num_seqs, sp)) return TQ_ERR_UNSUPPORTED;
   if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) return TQ_ERR_WORKSPACE;
   return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
                           sink_k, sink_v, n_sink, win_k, win_v, win_lens, win_cap, scale, out,
@@ -210,6 +219,7 @@ extern "C" int tq_paged_decode_attention_multi(
   TqLayer Lv = L;
   Lv.G = G * (n_queries < per ? n_queries : per);
   const TqSplit sp = tq_decode_split(Lv, num_seqs, max_seq_len);
+  if (!grid_fits(Lv, num_seqs, sp)) return TQ_ERR_UNSUPPORTED;
   if (workspace_bytes < tq_decode_ws_bytes(Lv, num_seqs, sp)) return TQ_ERR_WORKSPACE;
   // each group of queries is one split + merge launch pair; the pair after it reuses the
   // workspace in stream order
@@ -231,6 +241,7 @@ extern "C" int tq_dequantize_rows(const tq_layer_desc* layer, const void* pages,
   if (st != TQ_OK) return st;
   if (n < 0 || num_blocks < 0) return TQ_ERR_INVALID_ARG;
   if (n == 0) return TQ_OK;
+  if (n > ((int64_t)1 << 35) / L.Hkv) return TQ_ERR_UNSUPPORTED;  // one workgroup per 16 or 32 rows
   if (pages == nullptr || slots == nullptr || k_out == nullptr || v_out == nullptr)
     return TQ_ERR_INVALID_ARG;
   return tq_launch_dequant(L, pages, slots, n, k_out, v_out, stream) == 0 ? TQ_OK : TQ_ERR_HIP;

@@ -599,44 +599,47 @@ __global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, float rsqrt_d,
   for (int i = threadIdx.x; i < (1 << L.kb); i += kWG) s_kc[i] = L.kc[i];
   __syncthreads();
   const int j = threadIdx.x % P;
-  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / P;
-  if (row >= n_rows) return;  // whole row groups leave together: the DPP steps stay in a group
-  const int64_t t = row / L.Hkv;
-  const int h = (int)(row - t * L.Hkv);
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
-  uint8_t* dst = pages + (slot * L.Hkv + h) * (int64_t)L.stride;
-  float x[8];
-  load8_f16(k + row * D + 8 * j, x);
-  const float mu = L.mean ? *reinterpret_cast<const float*>(dst + L.kcode_bytes + 4) : 0.0f;
-  const uint32_t sb = sign_byte(L.signs, j);
+  // grid-stride over groups of RPW rows; a row group skips a row as a whole, so the DPP steps
+  // stay inside active groups
+  for (int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / P; row < n_rows;
+       row += (int64_t)gridDim.x * RPW) {
+    const int64_t t = row / L.Hkv;
+    const int h = (int)(row - t * L.Hkv);
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    uint8_t* dst = pages + (slot * L.Hkv + h) * (int64_t)L.stride;
+    float x[8];
+    load8_f16(k + row * D + 8 * j, x);
+    const float mu = L.mean ? *reinterpret_cast<const float*>(dst + L.kcode_bytes + 4) : 0.0f;
+    const uint32_t sb = sign_byte(L.signs, j);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float d = x[e] - mu;
-    x[e] = ((sb >> e) & 1u) ? -d : d;
+    for (int e = 0; e < 8; ++e) {
+      const float d = x[e] - mu;
+      x[e] = ((sb >> e) & 1u) ? -d : d;
+    }
+    wht_row8_dpp<P>(x, j);
+    const float ns = *reinterpret_cast<const float*>(dst + L.kcode_bytes);
+    const uint64_t cw = lane_codes(dst, L.kb, j);
+    const uint32_t mask = (1u << L.kb) - 1u;
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = x[e] * rsqrt_d - ns * s_kc[(cw >> (e * L.kb)) & mask];
+      x[e] = r;
+      ss += r * r;
+    }
+    const float gamma = sqrtf(group_sum<P>(ss));
+    const uint32_t sb2 = sign_byte(L.signs2, j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((sb2 >> e) & 1u) x[e] = -x[e];
+    wht_row8_dpp<P>(x, j);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bits |= (x[e] >= 0.0f ? 1u : 0u) << e;
+    dst[L.kqjl + j] = (uint8_t)bits;
+    if (j == 0) *reinterpret_cast<float*>(dst + L.kqjl + D / 8) = gamma;
   }
-  wht_row8_dpp<P>(x, j);
-  const float ns = *reinterpret_cast<const float*>(dst + L.kcode_bytes);
-  const uint64_t cw = lane_codes(dst, L.kb, j);
-  const uint32_t mask = (1u << L.kb) - 1u;
-  float ss = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float r = x[e] * rsqrt_d - ns * s_kc[(cw >> (e * L.kb)) & mask];
-    x[e] = r;
-    ss += r * r;
-  }
-  const float gamma = sqrtf(group_sum<P>(ss));
-  const uint32_t sb2 = sign_byte(L.signs2, j);
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if ((sb2 >> e) & 1u) x[e] = -x[e];
-  wht_row8_dpp<P>(x, j);
-  uint32_t bits = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) bits |= (x[e] >= 0.0f ? 1u : 0u) << e;
-  dst[L.kqjl + j] = (uint8_t)bits;
-  if (j == 0) *reinterpret_cast<float*>(dst + L.kqjl + D / 8) = gamma;
 }
 
 }  // namespace
@@ -694,7 +697,8 @@ int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int
   if (!ok) return (int)hipErrorInvalidValue;  // bit widths are validated by the API layer
   if (L.qjl) {
     const int rpw = kWG / (L.D / 8);
-    const dim3 qgrid((unsigned)((rows + rpw - 1) / rpw));
+    const int64_t need = (rows + rpw - 1) / rpw;
+    const dim3 qgrid((unsigned)(need < 65536 ? need : 65536));  // the kernel strides past the grid
     if (L.D == 128)
       hipLaunchKernelGGL(tq_qjl_kernel<128>, qgrid, dim3(kWG), 0, st, L, rsqrt_of(128),
                          (const uint16_t*)k, slot_mapping, rows, (uint8_t*)pages);

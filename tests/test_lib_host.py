@@ -130,6 +130,8 @@ def test_argument_validation_before_launch(lib):
     assert dec(_desc(lib), bt=None) == E.TQ_ERR_INVALID_ARG
     assert dec(_desc(lib), B=0) == E.TQ_OK
     assert dec(_desc(lib), B=-1) == E.TQ_ERR_INVALID_ARG
+    # a split grid beyond 32-bit workgroup counts
+    assert dec(_desc(lib), B=65535, max_len=2 ** 31 - 1, mb=2 ** 27) == E.TQ_ERR_UNSUPPORTED
 
     def decw(d, cap=16, wk=P, wl=P, B=4):
         return so.tq_paged_decode_attention_window(ctypes.byref(d), P, P, 100, P, 7, P, B, 100, None,
@@ -150,11 +152,15 @@ def test_argument_validation_before_launch(lib):
     assert decm(_desc(lib), n_sink=2) == E.TQ_ERR_INVALID_ARG             # sinks without arrays
     assert decm(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
     assert decm(_desc(lib), B=0) == E.TQ_OK
+    assert so.tq_paged_decode_attention_multi(ctypes.byref(_desc(lib)), P, 2, P, 100, P, 2 ** 27, P, 65535,
+                                              2 ** 31 - 1, None, None, 0, 0.0, P, P, 1 << 40,
+                                              None) == E.TQ_ERR_UNSUPPORTED
 
     dq = lambda d, n=3: so.tq_dequantize_rows(ctypes.byref(d), P, 10, P, n, P, P, None)
     assert dq(_desc(lib, head_dim=256)) == E.TQ_ERR_UNSUPPORTED
     assert dq(_desc(lib), n=-2) == E.TQ_ERR_INVALID_ARG
     assert dq(_desc(lib), n=0) == E.TQ_OK
+    assert dq(_desc(lib), n=2 ** 35) == E.TQ_ERR_UNSUPPORTED                # grid beyond 2^31 workgroups
     assert so.tq_dequantize_rows(ctypes.byref(_desc(lib)), None, 10, P, 3, P, P, None) == E.TQ_ERR_INVALID_ARG
 
 
