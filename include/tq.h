@@ -49,7 +49,8 @@ typedef struct ihipStream_t* tq_stream_t; /* a hipStream_t; NULL = the default s
 typedef enum tq_status {
   TQ_OK = 0,
   TQ_ERR_INVALID_ARG = -1,    /* a null pointer, a negative size, H_q % H_kv != 0, ...       */
-  TQ_ERR_UNSUPPORTED = -2,    /* head_dim or bit width outside what the kernels implement    */
+  TQ_ERR_UNSUPPORTED = -2,    /* head_dim, bit width or a size outside what the kernels       *
+                               * implement (a launch grid beyond 32-bit workgroup counts)     */
   TQ_ERR_WORKSPACE = -3,      /* decode workspace smaller than tq_decode_workspace_bytes()   */
   TQ_ERR_HIP = -4,            /* the HIP runtime reported an error while enqueueing          */
   TQ_ERR_NO_CONVERGENCE = -5  /* the Lloyd-Max solver did not reach its tolerance            */
