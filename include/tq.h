@@ -86,8 +86,10 @@ typedef enum tq_codebook_family {
  *   vector of rht_seed XOR 0x514A4C5F534B4554.  The dequantized key gains
  *   sqrt(pi/2) / D * gamma * R^T S^T (2 b - 1), so decode adds
  *   scale * sqrt(pi/2) / D * gamma * (S R q) . (2 b - 1) to each score.  Values are unchanged.
- *   The sign bits and gamma come from fp32 arithmetic: a bit whose |(S r)_i| is within about
- *   1e-4 gamma of 0 may differ from an exact computation.  Combines with the other flags.
+ *   r, gamma and S r are formed in fp64 (R (x - mu 1) as an exact Walsh-Hadamard transform of the
+ *   fp16 row times fp64(1/sqrt(D))): a bit whose |(S r)_i| is within about 1e-12 gamma of 0, or a
+ *   gamma within that distance of an fp32 rounding midpoint, may differ from an exact
+ *   computation.  Combines with the other flags.
  * Other bits must be 0. */
 #define TQ_FLAG_NORM_CORRECTION 1
 #define TQ_FLAG_MEAN_REMOVAL 2
@@ -168,6 +170,8 @@ size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs, i
  *   q             device fp16 [num_seqs][num_q_heads][D]
  *   pages         device uint8 page tensor (read only)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *                 (pages and block_tables may be NULL when max_seq_len <= n_sink: every position
+ *                 is then a sink token)
  *   seq_lens      device int32 [num_seqs]: cached tokens of each sequence, sinks included;
  *                 each <= max_seq_len (a host value used to size the grid)
  *   sink_k, sink_v device fp16 [num_seqs][n_sink][num_kv_heads][D], or NULL when n_sink == 0.

@@ -17,8 +17,7 @@ attention  Dense decode attention over dequantized K/V with GQA, block tables an
 qjl        1-bit QJL residual sketch of keys (SRHT signs + residual norm) and its estimator.
 
 Parity pins: every function here is pinned by the CPU tests against closed forms, textbook
-values, printed byte counts on the pages, or brute force.  The one exception is recorded in
-the module that holds it (search for "parity unpinned").
+values, printed byte counts on the pages, or brute force.  None is left unpinned.
 """
 
 from . import codebook, rotation, quantize, qjl, attention  # noqa: F401

@@ -83,12 +83,7 @@ def slot_bytes(D: int, k_bits: int, v_bits: int, mean: bool = False, qjl: bool =
 def norm_fp32(x16: np.ndarray) -> np.ndarray:
     """Stored fp32 norm of each fp16 row: exact squares, stride-halving fp32 tree, fp32 sqrt."""
     x = np.asarray(x16, dtype=np.float16).astype(np.float32)
-    sq = (x * x).astype(np.float32)
-    h = sq.shape[-1] // 2
-    while h >= 1:
-        sq = (sq[..., :h] + sq[..., h:2 * h]).astype(np.float32)
-        h //= 2
-    return np.sqrt(sq[..., 0]).astype(np.float32)
+    return np.sqrt(_tree_sum32((x * x).astype(np.float32))).astype(np.float32)
 
 
 def row_mean(x16: np.ndarray) -> np.ndarray:
@@ -323,7 +318,7 @@ def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, 
                      k_centroids32=None, v_centroids32=None, mean: bool = False, qjl_centroids32=None):
     """append_rows() with the vectorised packer (same bytes; used for larger test cases); mean:
     the mean-removal format; qjl_centroids32 (the K centroids): the QJL key format, and the sketch
-    tie mask [n_tok, H_kv, D] is returned third."""
+    tie masks (bits [n_tok, H_kv, D], gamma [n_tok, H_kv]) are returned third, as a pair."""
     from . import qjl as _qjl
     qjl = qjl_centroids32 is not None
     n_tok, H_kv, D = k16.shape
@@ -340,7 +335,9 @@ def append_rows_fast(pages: np.ndarray, k16, v16, slot_mapping, k_boundaries32, 
     rows[:, :, :kr] = pack_regions(k_idx.reshape(-1, D), k_n.reshape(-1), k_bits, k_mu).reshape(n_tok, H_kv, kr)
     q_tie = None
     if qjl:
-        bits, gamma, q_tie = _qjl.encode(k16, k_idx, k_n, qjl_centroids32, seed, kq[3] if mean else None)
+        bits, gamma, b_tie, g_tie = _qjl.encode(k16, k_idx, k_n, qjl_centroids32, seed,
+                                                kq[3] if mean else None, with_gamma_tie=True)
+        q_tie = (b_tie, g_tie)
         rows[:, :, kr:kq_end] = _qjl.pack(bits.reshape(-1, D), gamma.reshape(-1)).reshape(n_tok, H_kv, kq_end - kr)
     rows[:, :, kq_end:sb] = pack_regions(v_idx.reshape(-1, D), v_n.reshape(-1), v_bits, v_mu).reshape(n_tok, H_kv, sb - kq_end)
     view = pages.reshape(-1, H_kv, stride)

@@ -134,9 +134,11 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
   if (num_seqs == 0) return TQ_OK;
   if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
+  // positions below n_sink come from the sink arrays: a batch of sink tokens only needs no pages
   if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
     return TQ_ERR_INVALID_ARG;
-  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (max_seq_len > n_sink && (int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len)
+    return TQ_ERR_INVALID_ARG;
   if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
   if (win_cap > 0 && (win_k == nullptr || win_v == nullptr || win_lens == nullptr))
     return TQ_ERR_INVALID_ARG;
@@ -208,9 +210,11 @@ extern "C" int tq_paged_decode_attention_multi(
   if (num_seqs == 0) return TQ_OK;
   if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
+  // positions below n_sink come from the sink arrays: a batch of sink tokens only needs no pages
   if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
     return TQ_ERR_INVALID_ARG;
-  if ((int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (max_seq_len > n_sink && (int64_t)max_blocks_per_seq * L.bs < (int64_t)max_seq_len)
+    return TQ_ERR_INVALID_ARG;
   if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
   if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;

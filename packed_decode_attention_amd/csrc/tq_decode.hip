@@ -857,12 +857,17 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     s_ztab[tid] = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
   }
 
-  const int p0 = split * a.chunk;
-  const int p_end = min(p0 + a.chunk, packed_end);
+  // The split's page positions start at the first non-sink one: the sinks' block-table entries
+  // and page slots are never read (they may be absent).  The staged fetch needs 16-aligned runs,
+  // so it starts at the run holding position ns, which lies in the block holding ns; rows below
+  // ns are masked.  A split with no packed position reads nothing at all.
+  const int p0 = max(split * a.chunk, UBLK ? (ns & ~15) : ns);
+  const int p_end = min(split * a.chunk + a.chunk, packed_end);
+  const bool any_rows = p_end > max(p0, ns);
   auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
-  const int blk0 = block_of(p0);
-  const int blk_last = p_end > p0 ? block_of(p_end - 1) : blk0;
-  const int nblk = p_end > p0 ? blk_last - blk0 + 1 : 0;
+  const int blk0 = any_rows ? block_of(p0) : 0;
+  const int blk_last = any_rows ? block_of(p_end - 1) : blk0;
+  const int nblk = any_rows ? blk_last - blk0 + 1 : 0;
   const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
   const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
   for (int i = tid; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
@@ -988,7 +993,7 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const int voff = L.kreg;  // V region
   const uint32_t row_bytes32 = (uint32_t)row_bytes;
   const uint8_t* head_base = a.pages + (int64_t)h * L.stride;
-  const int n_tiles = p_end > p0 ? (p_end - p0 + 31) / 32 : 0;
+  const int n_tiles = any_rows ? (p_end - p0 + 31) / 32 : 0;
 
   // Row base of the 16 positions starting at pu (a multiple of 16).  With a block size that is a
   // multiple of 16 the 16 rows lie in one page block, so the base is the same for the whole wave;
@@ -1005,8 +1010,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
                       ((int64_t)__builtin_amdgcn_readfirstlane((int)(boff >> 32)) << 32);
     return head_base + o + (int64_t)r0 * row_bytes;
   };
-  auto row_ptr = [&](int p) {  // any block size: one lane's row
-    const int pc = min(p, p_end - 1);
+  auto row_ptr = [&](int p) {  // any block size: one lane's row (masked rows re-read a packed one)
+    const int pc = max(min(p, p_end - 1), p0);
     const int bi = block_of(pc);
     return head_base + s_boff[bi - blk0] + __umul24((uint32_t)(pc - bi * L.bs), row_bytes32);
   };
@@ -1174,7 +1179,12 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
       }
       s0[u] = (p >= ns && p < lim0 && live0) ? t0 : kSent;
       if (G8) s1[u] = (p >= ns && p < lim1 && live1) ? t1 : kSent;
-      lv[u] = __builtin_amdgcn_logf(vn[u]);  // log2(n_V); -inf for a zero row
+      // log2(n_V) (-inf for a zero row).  Rows outside [ns, p_end) are not packed tokens of this
+      // split (sink or hot-window slots, slots not yet written): whatever bytes they hold, they
+      // add nothing, neither to the weights' maximum nor to the mean sums.
+      const bool packed = p >= ns && p < p_end;
+      lv[u] = packed ? __builtin_amdgcn_logf(vn[u]) : 0.0f;
+      if constexpr (kMean) vm[u] = packed ? vm[u] : 0.0f;
     }
     const float ms0 = fmaxf(m_s[0], row16_max(fmaxf(s0[0], s0[1])));
     const float mw0 = fmaxf(m_w[0], row16_max(fmaxf(s0[0] + lv[0], s0[1] + lv[1])));
@@ -1601,10 +1611,18 @@ TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
   return sp;
 }
 
-size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
+// Partials per (sequence, kv head): the packed splits, then one per chunk of fp16 rows (sinks and
+// hot-window rows) of this call.
+static int row_chunks_of(int n_sink, int win_cap) { return (n_sink + win_cap + kRowChunk - 1) / kRowChunk; }
+
+size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp, int n_sink, int win_cap) {
   const size_t bh = (size_t)num_seqs * L.Hkv;
-  // packed splits, then room for the fp16-row chunks of the largest sink count and window
-  return bh * (size_t)(sp.max_split + kMaxRowChunks) * L.G * (L.D + 2) * sizeof(float);
+  return bh * (size_t)(sp.max_split + row_chunks_of(n_sink, win_cap)) * L.G * (L.D + 2) * sizeof(float);
+}
+
+size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
+  // room for the fp16-row chunks of the largest sink count and window
+  return tq_decode_ws_bytes_for(L, num_seqs, sp, TQ_MAX_SINKS, TQ_MAX_WINDOW);
 }
 
 int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
@@ -1626,8 +1644,8 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.seq_lens = seq_lens;
   a.chunk = sp.chunk;
   a.max_split = sp.max_split;
-  a.part_stride = sp.max_split + kMaxRowChunks;
-  a.row_chunks = (n_sink + win_cap + kRowChunk - 1) / kRowChunk;
+  a.row_chunks = row_chunks_of(n_sink, win_cap);
+  a.part_stride = sp.max_split + a.row_chunks;
   a.rows_blocks = num_seqs * L.Hkv * a.row_chunks;
   a.n_units = num_seqs * sp.max_split;
   a.bs_shift = ilog2_exact(L.bs);

@@ -585,11 +585,21 @@ __global__ __launch_bounds__(kWG) void tq_dequant_kernel(TqLayer L, float rsqrt_
 }
 
 // QJL key format: the residual sketch of the keys tq_quantize_kernel has just written (same
-// stream, so its codes, norm and mean are in place).  D/8 lanes per row, 8 coordinates each:
-// v = H (s * (x - mu)) / sqrt(D) = R (x - mu 1), r = v - n_s c[idx], gamma = ||r||, then
-// S r = H (sigma2 * r) and one bit per coordinate, b = [(S r)_i >= 0], one byte per lane.
+// stream, so its codes, norm and mean are in place).  D/8 lanes per row, 8 coordinates each, in
+// fp64 so the stored bytes are reproducible: d = x - mu and H (s * d) are exact in fp64 (fp16
+// inputs, an fp32 mean); v = H (s * d) / sqrt(D) = R (x - mu 1), r = v - n_s c[idx] (n_s c is
+// exact), gamma = fp32(||r||), then S r = H (sigma2 * r) and b = [(S r)_i >= 0], one byte per
+// lane.  Only the fp64 roundings of v, r and S r (about 1e-15 of gamma) separate these from an
+// exact computation.
+template <int P>
+__device__ __forceinline__ double group_sum_f64(double x) {
+#pragma unroll
+  for (int m = 1; m < P; m <<= 1) x += __shfl_xor(x, m, P);
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, float rsqrt_d,
+__global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, double rsqrt_d,
                                                      const uint16_t* __restrict__ k,
                                                      const int64_t* __restrict__ slot_mapping,
                                                      int64_t n_rows, uint8_t* __restrict__ pages) {
@@ -599,8 +609,8 @@ __global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, float rsqrt_d,
   for (int i = threadIdx.x; i < (1 << L.kb); i += kWG) s_kc[i] = L.kc[i];
   __syncthreads();
   const int j = threadIdx.x % P;
-  // grid-stride over groups of RPW rows; a row group skips a row as a whole, so the DPP steps
-  // stay inside active groups
+  // grid-stride over groups of RPW rows; a row group skips a row as a whole, so the cross-lane
+  // steps stay inside active groups
   for (int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / P; row < n_rows;
        row += (int64_t)gridDim.x * RPW) {
     const int64_t t = row / L.Hkv;
@@ -608,35 +618,36 @@ __global__ __launch_bounds__(kWG) void tq_qjl_kernel(TqLayer L, float rsqrt_d,
     const int64_t slot = slot_mapping[t];
     if (slot < 0) continue;
     uint8_t* dst = pages + (slot * L.Hkv + h) * (int64_t)L.stride;
-    float x[8];
-    load8_f16(k + row * D + 8 * j, x);
-    const float mu = L.mean ? *reinterpret_cast<const float*>(dst + L.kcode_bytes + 4) : 0.0f;
+    float xf[8];
+    load8_f16(k + row * D + 8 * j, xf);
+    const double mu = L.mean ? (double)*reinterpret_cast<const float*>(dst + L.kcode_bytes + 4) : 0.0;
     const uint32_t sb = sign_byte(L.signs, j);
+    double x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float d = x[e] - mu;
+      const double d = (double)xf[e] - mu;
       x[e] = ((sb >> e) & 1u) ? -d : d;
     }
-    wht_row8_dpp<P>(x, j);
-    const float ns = *reinterpret_cast<const float*>(dst + L.kcode_bytes);
+    wht_rowgroup<P>(x, j);
+    const double ns = (double)*reinterpret_cast<const float*>(dst + L.kcode_bytes);
     const uint64_t cw = lane_codes(dst, L.kb, j);
     const uint32_t mask = (1u << L.kb) - 1u;
-    float ss = 0.0f;
+    double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float r = x[e] * rsqrt_d - ns * s_kc[(cw >> (e * L.kb)) & mask];
+      const double r = x[e] * rsqrt_d - ns * (double)s_kc[(cw >> (e * L.kb)) & mask];
       x[e] = r;
       ss += r * r;
     }
-    const float gamma = sqrtf(group_sum<P>(ss));
+    const float gamma = (float)sqrt(group_sum_f64<P>(ss));
     const uint32_t sb2 = sign_byte(L.signs2, j);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if ((sb2 >> e) & 1u) x[e] = -x[e];
-    wht_row8_dpp<P>(x, j);
+    wht_rowgroup<P>(x, j);
     uint32_t bits = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bits |= (x[e] >= 0.0f ? 1u : 0u) << e;
+    for (int e = 0; e < 8; ++e) bits |= (x[e] >= 0.0 ? 1u : 0u) << e;
     dst[L.kqjl + j] = (uint8_t)bits;
     if (j == 0) *reinterpret_cast<float*>(dst + L.kqjl + D / 8) = gamma;
   }
@@ -700,10 +711,10 @@ int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int
     const int64_t need = (rows + rpw - 1) / rpw;
     const dim3 qgrid((unsigned)(need < 65536 ? need : 65536));  // the kernel strides past the grid
     if (L.D == 128)
-      hipLaunchKernelGGL(tq_qjl_kernel<128>, qgrid, dim3(kWG), 0, st, L, rsqrt_of(128),
+      hipLaunchKernelGGL(tq_qjl_kernel<128>, qgrid, dim3(kWG), 0, st, L, 1.0 / __builtin_sqrt(128.0),
                          (const uint16_t*)k, slot_mapping, rows, (uint8_t*)pages);
     else
-      hipLaunchKernelGGL(tq_qjl_kernel<64>, qgrid, dim3(kWG), 0, st, L, rsqrt_of(64),
+      hipLaunchKernelGGL(tq_qjl_kernel<64>, qgrid, dim3(kWG), 0, st, L, 0.125,
                          (const uint16_t*)k, slot_mapping, rows, (uint8_t*)pages);
   }
   return (int)hipGetLastError();

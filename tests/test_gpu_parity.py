@@ -21,6 +21,9 @@ CASES = {
     "mistral-small": dict(w=wl.scaled(W["mistral-7b"], num_seqs=3), lens=[900, 3, 130]),
     "mistral-protected": dict(w=wl.scaled(W["mistral-7b"], num_seqs=2), layer=31, lens=[640, 70]),
     "ragged-small": dict(w=wl.scaled(W["ragged"], num_seqs=6), lens=[1, 613, 64, 65, 300, 129]),
+    # a power-of-two slot stride (136 -> 256 bytes, the TQ4 page tensor's optional padding) on the
+    # staged matrix-core path
+    "llama-pow2": dict(w=wl.scaled(W["llama3-8b"], num_seqs=2), lens=[1100, 333], slot_stride=256),
     "edges": dict(w=wl.Workload("edges", 1, 6, 6, 2, 128, 2, 3, 0, block_size=7, n_sink=4,
                                 values="normal", tables="fragmented", seed=11),
                   lens=[0, 1, 4, 5, 17, 200], slot_stride=160),
@@ -115,12 +118,7 @@ def test_dequantize_rows_bit_exact(cases, name):
     tq.tq_dequantize_rows(fmt.desc, c.ref_pages_on_gpu(), c.num_blocks, torch.from_numpy(slots).cuda(), ko, vo)
     torch.cuda.synchronize()
     kr, vr = c.oracle_dequant(slots)
-    if c.qjl:  # fp32 sums of the codes' and the sketch's transforms: a few ulps of the row
-        k = ko.cpu().numpy().astype(np.float64)
-        scale = np.abs(kr).max(axis=-1, keepdims=True) + 1e-30
-        assert np.all(np.abs(k - kr) <= 4e-6 * scale)
-    else:
-        assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
+    assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
     assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
 
 

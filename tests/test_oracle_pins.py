@@ -257,6 +257,36 @@ def test_norm_tree():
     assert quantize.norm_fp32(np.zeros((3, 64), np.float16)).tolist() == [0.0, 0.0, 0.0]
 
 
+def test_norm_tree_by_brute_force():
+    # One row's stride-halving fp32 tree written out element by element: pairs (i, i + D/2) first,
+    # then D/4, ..., every sum rounded to fp32, then a correctly rounded fp32 square root.  The row
+    # is drawn so that summing adjacent pairs first, or accumulating in fp64 with one final
+    # rounding, gives a different fp32 value: either mistake in norm_fp32 fails here.
+    D = 32
+    rng = np.random.default_rng(2024)
+    for _ in range(1000):
+        x = (rng.standard_normal(D) * np.exp(2.0 * rng.standard_normal(D))).astype(np.float16)
+        sq = [np.float32(np.float32(v) * np.float32(v)) for v in x]
+        vals = list(sq)
+        h = D // 2
+        while h >= 1:
+            vals = [np.float32(vals[i] + vals[i + h]) for i in range(h)]
+            h //= 2
+        want = np.float32(np.sqrt(vals[0]))
+        adj = list(sq)
+        while len(adj) > 1:
+            adj = [np.float32(adj[2 * i] + adj[2 * i + 1]) for i in range(len(adj) // 2)]
+        adjacent = np.float32(np.sqrt(adj[0]))
+        wide = np.float32(np.sqrt(np.sum(np.asarray(x, np.float64) ** 2)))
+        if adjacent != want and wide != want:
+            break
+    else:
+        pytest.fail("no row separates the tree order from its alternatives")
+    got = quantize.norm_fp32(x[None])[0]
+    assert got.view(np.uint32) == want.view(np.uint32)
+    assert got != adjacent and got != wide
+
+
 def test_decision_rule_ties_go_up():
     t = np.array([-0.5, 0.0, 0.5], np.float32)
     u = np.array([-1.0, -0.5, -0.25, 0.0, 0.25, 0.5, 0.75, 0.5 - 2e-7])

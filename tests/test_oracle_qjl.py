@@ -161,3 +161,32 @@ def test_attention_routes_agree_with_qjl(D, H_kv, G, kb, vb, L, ns, mean, rng):
     args = (q, pages, bt[None], np.array([L]), layer, ck.centroids32, cv.centroids32, sk, sk, ns)
     np.testing.assert_allclose(attention.decode_attention(*args), attention.decode_attention_rotated(*args),
                                atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("D, bits_, mean", [(64, 2, False), (128, 4, True), (128, 3, False)])
+def test_dequantize_key_spec_matches_plain_route(D, bits_, mean, rng):
+    """The library's bit-exact fp32 chain for QJL keys against the fp64 plain route n R^T c[idx] +
+    sqrt(pi/2)/D gamma R^T S^T (2b - 1) (+ mu): within 3 roundings of the codes' and the residual's
+    parts (plus one of the mean).  Planted slips (the sketch transform used for its transpose, a
+    dropped sign vector, gamma left out) are far outside the bound."""
+    seed = 6
+    cb = codebook.codebook(D, bits_)
+    x = (rng.standard_normal((40, D)) * 3.0 + (2.0 if mean else 0.0)).astype(np.float16)
+    out = quantize.quantize_rows(x, cb.boundaries32, seed, None, mean)
+    idx, n = out[0], out[1]
+    mu = out[3] if mean else None
+    b, g, _ = qjl.encode(x, idx, n, cb.centroids32, seed, mu)
+    spec = qjl.dequantize_key_spec(idx, n, cb.centroids32, b, g, seed, mu).astype(np.float64)
+    code = quantize.dequantize_plain(idx, n, cb.centroids32, seed)
+    resid = qjl.residual_estimate(b, g, seed)
+    plain = code + resid + (0.0 if mu is None else mu.astype(np.float64)[:, None])
+    u = 2.0 ** -24
+    bound = 3 * u * (np.abs(code) + np.abs(resid)) + (2 * u * np.abs(plain) if mean else 0.0)
+    assert np.all(np.abs(spec - plain) <= bound)
+    # the chain reads its own gamma and bits: a slip in either moves the result by far more
+    R = rotation.rotation_matrix(seed, D)
+    S = qjl.sketch_matrix(seed, D)
+    z = 2.0 * b - 1.0
+    wrong_t = (qjl.KAPPA_NUM / D) * g.astype(np.float64)[:, None] * ((z @ S.T) @ R)  # S for S^T
+    assert np.max(np.abs(code + wrong_t + (plain - code - resid) - spec) - bound) > 0
+    assert np.max(np.abs(code + (plain - code - resid) - spec) - bound) > 0      # gamma dropped
