@@ -97,7 +97,6 @@ __device__ __forceinline__ int window_len(const DecodeArgs& a, int b, int seq_le
 
 // fp16 rows (sinks, then hot-window rows) of a sequence, kRowChunk at a time.
 constexpr int kRowChunk = 128;
-constexpr int kMaxRowChunks = (TQ_MAX_SINKS + TQ_MAX_WINDOW + kRowChunk - 1) / kRowChunk;
 
 __device__ __forceinline__ int fp16_rows(const DecodeArgs& a, int b, int seq_len) {
   const int ns = min(a.n_sink, seq_len);
