@@ -25,7 +25,9 @@
  * Conventions for every call below:
  *   - Pointers marked "device" are device memory of the current HIP device; the caller owns
  *     them and keeps them alive until the stream has finished the work.  The library never
- *     allocates or frees device memory and keeps no pointer after a call returns.
+ *     allocates or frees device memory and keeps no pointer after a call returns.  (Its one
+ *     device array, the static workspace of tq_paged_decode_attention_noalloc, is part of the
+ *     loaded code object.)
  *   - Calls that take a stream only enqueue work on it and return without waiting.
  *   - Every argument is validated on the host before anything is enqueued.  A call returns
  *     TQ_OK (0) or a negative tq_status; on error nothing was enqueued.  No exception crosses
@@ -53,7 +55,9 @@ typedef enum tq_status {
                                * implement (a launch grid beyond 32-bit workgroup counts)     */
   TQ_ERR_WORKSPACE = -3,      /* decode workspace smaller than tq_decode_workspace_bytes()   */
   TQ_ERR_HIP = -4,            /* the HIP runtime reported an error while enqueueing          */
-  TQ_ERR_NO_CONVERGENCE = -5  /* the Lloyd-Max solver did not reach its tolerance            */
+  TQ_ERR_NO_CONVERGENCE = -5, /* the Lloyd-Max solver did not reach its tolerance            */
+  TQ_ERR_NOALLOC_LIMIT = -6   /* the sizes need more workspace than the library's static     *
+                               * array holds (tq_paged_decode_attention_noalloc)              */
 } tq_status;
 
 typedef enum tq_codebook_family {
@@ -190,6 +194,26 @@ int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q, const v
                               int32_t max_seq_len, const void* sink_k, const void* sink_v,
                               int32_t n_sink, float scale, float* out, void* workspace,
                               size_t workspace_bytes, tq_stream_t stream);
+
+/* The same decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc): the split-K partials go to a static device
+ * array that the library holds per GPU, TQ_NOALLOC_WORKSPACE_BYTES bytes, loaded with the library
+ * and kept until the process ends.  The call allocates nothing; the caller still passes every
+ * input and output.  Arguments are those of tq_paged_decode_attention without the workspace.
+ * Returns TQ_ERR_NOALLOC_LIMIT when the sizes need more than the array holds (the partials of
+ * num_seqs * num_kv_heads * num_q_heads/num_kv_heads * (D + 2) fp32 per split, with about three
+ * splits per compute unit of the batch; e.g. 256 sequences x 8 kv heads x 8 query heads per kv
+ * head at D = 128 take 17 MB), TQ_ERR_HIP when the array's address cannot be obtained.
+ * Every call on one GPU shares its array: calls that may overlap on one GPU (on different
+ * streams, or from several threads) race and must be ordered by the caller; calls on one stream
+ * are ordered by it.  The array needs no clearing: each call writes what it reads. */
+#define TQ_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int tq_paged_decode_attention_noalloc(const tq_layer_desc* layer, const void* q, const void* pages,
+                                      int64_t num_blocks, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      int32_t num_seqs, int32_t max_seq_len, const void* sink_k,
+                                      const void* sink_v, int32_t n_sink, float scale, float* out,
+                                      tq_stream_t stream);
 
 /* The same decode with an fp16 hot window: the most recent tokens of each sequence kept
  * uncompressed and merged with the packed tokens by online softmax.

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     tq_layer_desc,
     tq_paged_decode_attention,
     tq_paged_decode_attention_multi,
+    tq_paged_decode_attention_noalloc,
     tq_paged_decode_attention_window,
     tq_quantize_append,
     tq_rht_signs,

@@ -22,11 +22,13 @@ TQ_ERR_UNSUPPORTED = -2
 TQ_ERR_WORKSPACE = -3
 TQ_ERR_HIP = -4
 TQ_ERR_NO_CONVERGENCE = -5
+TQ_ERR_NOALLOC_LIMIT = -6
+TQ_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 FAMILIES = {"beta": 0, "gaussian": 1}
 
 EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_slot_bytes_ex", "tq_quantize_append",
-           "tq_decode_workspace_bytes", "tq_paged_decode_attention",
+           "tq_decode_workspace_bytes", "tq_paged_decode_attention", "tq_paged_decode_attention_noalloc",
            "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
            "tq_paged_decode_attention_multi", "tq_dequantize_rows", "tq_status_str")
 TQ_MAX_QUERIES = 64
@@ -83,6 +85,9 @@ def _lib():
         lib.tq_paged_decode_attention.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P, I32,
                                                   ctypes.c_float, P, P, SZ, P]
         lib.tq_paged_decode_attention.restype = ctypes.c_int
+        lib.tq_paged_decode_attention_noalloc.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P,
+                                                          I32, ctypes.c_float, P, P]
+        lib.tq_paged_decode_attention_noalloc.restype = ctypes.c_int
         lib.tq_paged_decode_attention_window.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P,
                                                          I32, P, P, P, I32, ctypes.c_float, P, P,
                                                          SZ, P]
@@ -177,6 +182,19 @@ def tq_paged_decode_attention(desc, q, pages, num_blocks: int, block_tables, seq
         _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, scale,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("tq_paged_decode_attention", st)
+
+
+def tq_paged_decode_attention_noalloc(desc, q, pages, num_blocks: int, block_tables, seq_lens,
+                                      max_seq_len: int, out, sink_k=None, sink_v=None, n_sink: int = 0,
+                                      scale: float = 0.0, stream=None) -> None:
+    """tq_paged_decode_attention with the library's static workspace (no workspace argument)."""
+    num_seqs = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    st = _lib().tq_paged_decode_attention_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(pages), num_blocks, _ptr(block_tables), max_blocks,
+        _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, scale,
+        _ptr(out), _stream(stream))
+    _check("tq_paged_decode_attention_noalloc", st)
 
 
 def tq_paged_decode_attention_window(desc, q, pages, num_blocks: int, block_tables, seq_lens,

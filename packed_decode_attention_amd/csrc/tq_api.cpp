@@ -117,12 +117,14 @@ static bool grid_fits(const TqLayer& L, int32_t num_seqs, const TqSplit& sp) {
   return units * L.Hkv + (int64_t)num_seqs * L.Hkv * 16 <= INT32_MAX;
 }
 
+// workspace == NULL with noalloc: the library's static array of the current device.
 static int paged_decode(const tq_layer_desc* layer, const void* q, const void* pages,
                         int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                         const void* sink_k, const void* sink_v, int32_t n_sink, const void* win_k,
                         const void* win_v, const int32_t* win_lens, int32_t win_cap, float scale,
-                        float* out, void* workspace, size_t workspace_bytes, tq_stream_t stream) {
+                        float* out, void* workspace, size_t workspace_bytes, tq_stream_t stream,
+                        bool noalloc = false) {
   TqLayer L;
   const int st = make_layer(layer, true, &L);
   if (st != TQ_OK) return st;
@@ -132,7 +134,7 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
   if (num_seqs > 65535) return TQ_ERR_UNSUPPORTED;
   if (n_sink > TQ_MAX_SINKS || win_cap > TQ_MAX_WINDOW) return TQ_ERR_UNSUPPORTED;
   if (num_seqs == 0) return TQ_OK;
-  if (q == nullptr || out == nullptr || seq_lens == nullptr || workspace == nullptr)
+  if (q == nullptr || out == nullptr || seq_lens == nullptr || (workspace == nullptr && !noalloc))
     return TQ_ERR_INVALID_ARG;
   // positions below n_sink come from the sink arrays: a batch of sink tokens only needs no pages
   if (max_seq_len > n_sink && (pages == nullptr || block_tables == nullptr))
@@ -146,7 +148,13 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
   if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
   const TqSplit sp = tq_decode_split(L, num_seqs, max_seq_len);
   if (!grid_fits(L, num_seqs, sp)) return TQ_ERR_UNSUPPORTED;
-  if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) return TQ_ERR_WORKSPACE;
+  if (noalloc) {
+    if (tq_decode_ws_bytes_for(L, num_seqs, sp, n_sink, win_cap) > TQ_NOALLOC_WORKSPACE_BYTES)
+      return TQ_ERR_NOALLOC_LIMIT;
+    if (tq_noalloc_workspace(&workspace) != 0) return TQ_ERR_HIP;
+  } else if (workspace_bytes < tq_decode_ws_bytes(L, num_seqs, sp)) {
+    return TQ_ERR_WORKSPACE;
+  }
   return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
                           sink_k, sink_v, n_sink, win_k, win_v, win_lens, win_cap, scale, out,
                           workspace, stream) == 0
@@ -165,6 +173,19 @@ extern "C" int tq_paged_decode_attention(const tq_layer_desc* layer, const void*
   return paged_decode(layer, q, pages, num_blocks, block_tables, max_blocks_per_seq, seq_lens,
                       num_seqs, max_seq_len, sink_k, sink_v, n_sink, nullptr, nullptr, nullptr, 0,
                       scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int tq_paged_decode_attention_noalloc(const tq_layer_desc* layer, const void* q,
+                                                 const void* pages, int64_t num_blocks,
+                                                 const int32_t* block_tables,
+                                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                 int32_t num_seqs, int32_t max_seq_len,
+                                                 const void* sink_k, const void* sink_v,
+                                                 int32_t n_sink, float scale, float* out,
+                                                 tq_stream_t stream) {
+  return paged_decode(layer, q, pages, num_blocks, block_tables, max_blocks_per_seq, seq_lens,
+                      num_seqs, max_seq_len, sink_k, sink_v, n_sink, nullptr, nullptr, nullptr, 0,
+                      scale, out, nullptr, 0, stream, true);
 }
 
 extern "C" int tq_paged_decode_attention_window(
@@ -259,6 +280,7 @@ extern "C" const char* tq_status_str(int status) {
     case TQ_ERR_WORKSPACE: return "decode workspace too small";
     case TQ_ERR_HIP: return "HIP runtime error while enqueueing";
     case TQ_ERR_NO_CONVERGENCE: return "Lloyd-Max solver did not converge";
+    case TQ_ERR_NOALLOC_LIMIT: return "sizes need more than the library's static decode workspace";
     default: return "unknown status";
   }
 }

@@ -26,7 +26,9 @@
 // workgroup i on XCD i % 8) and share its L2.
 
 #include <climits>
+#include <mutex>
 
+#include "../../include/tq.h"
 #include "tq_device.h"
 
 namespace {
@@ -1622,6 +1624,31 @@ size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp,
 size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
   // room for the fp16-row chunks of the largest sink count and window
   return tq_decode_ws_bytes_for(L, num_seqs, sp, TQ_MAX_SINKS, TQ_MAX_WINDOW);
+}
+
+// The split-K partials of tq_paged_decode_attention_noalloc, for callers that cannot allocate:
+// one array per GPU, loaded with the library and held until the process ends.  Host code reaches
+// it only through the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_WORKSPACE_BYTES];
+
+int tq_noalloc_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *ptr = ptrs[dev];
+  return 0;
 }
 
 int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,

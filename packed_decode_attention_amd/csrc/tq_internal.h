@@ -45,6 +45,9 @@ TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len);
 // Workspace bytes for the largest sink count and window (the public size), and for a given call.
 size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp);
 size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp, int n_sink, int win_cap);
+// Device address of the library's static decode workspace on the current device (a hipError_t
+// value, 0 on success).
+int tq_noalloc_workspace(void** ptr);
 
 // Launchers: return a hipError_t value (0 on success).
 int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,
