@@ -416,8 +416,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal
                                           or args.qjl) else recorded_traffic(w)),
-                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(w.head_dim, w.k_bits, w.v_bits,
-                                                                                   args.qjl)),
+                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(
+                         w.head_dim, w.k_bits, w.v_bits, args.qjl, w.num_kv_heads, w.group, fmt_flags)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},
         "append": {"step_us_per_layer": float(app_ms.mean() * 1e3),

@@ -70,7 +70,12 @@ class LayerFormat:
         vc, vt = v_codebook if v_codebook is not None else host_codebook(head_dim, v_bits, family)
         as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
         self.k_centroids, self.k_boundaries = as_dev(kc), as_dev(kt)
-        self.v_centroids, self.v_boundaries = as_dev(vc), as_dev(vt)
+        if np.array_equal(np.asarray(kc, np.float32), np.asarray(vc, np.float32)) and \
+                np.array_equal(np.asarray(kt, np.float32), np.asarray(vt, np.float32)):
+            # one codebook for K and V: one device array, which lets decode keep one LDS table
+            self.v_centroids, self.v_boundaries = self.k_centroids, self.k_boundaries
+        else:
+            self.v_centroids, self.v_boundaries = as_dev(vc), as_dev(vt)
         self.desc = tq_layer_desc(
             head_dim=head_dim, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
             block_size=block_size, k_bits=k_bits, v_bits=v_bits, slot_stride=slot_stride,
@@ -94,11 +99,13 @@ class LayerFormat:
         return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int, qjl: bool = False):
+def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int, qjl: bool = False,
+                        num_kv_heads: int = 0, group: int = 0, flags: int = 0):
     """Names of the kernels one tq_paged_decode_attention call launches for this format, in
     launch order (as they appear in a kernel trace)."""
-    # the QJL key format (keys of 2-4 bits) runs on the same kernels, with its residual products
-    del qjl
+    if (head_dim == 128 and k_bits == 4 and v_bits == 4 and num_kv_heads == 8 and 0 < group <= 4
+            and flags & ~1 == 0 and not qjl):  # unpadded slots, page blocks of whole 16-position runs
+        return ["tq_decode_block_kernel", "tq_decode_merge_kernel"]
     mfma = ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
             (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))
     return ["tq_decode_mfma_kernel" if mfma else "tq_decode_split_kernel", "tq_decode_merge_kernel"]

@@ -32,6 +32,7 @@ SOURCES = [
     # products are one-shot, never accumulated across instructions)
     ("tq_quantize.hip", "device", ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("tq_decode.hip", "device", ["-fno-honor-nans"]),
+    ("tq_decode_block.hip", "device", ["-fno-honor-nans"]),
     ("tq_api.cpp", "host", []),
     ("tq_codebook.cpp", "host", []),
 ]

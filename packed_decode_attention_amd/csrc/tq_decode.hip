@@ -1596,6 +1596,7 @@ int ilog2_exact(int v) {
 // pays a fixed prologue (rotated query, lookup tables, block offsets) and writes one partial, so
 // fewer, longer splits win as long as every CU still holds a few of them.
 TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
+  if (tq_decode_block_format(L)) return tq_decode_block_split(num_seqs, max_seq_len);
   const long bh = (long)num_seqs * L.Hkv;
   const long tokens = (long)(max_seq_len > 0 ? max_seq_len : 1);
   const long target_wgs = 768;
@@ -1687,6 +1688,17 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real > 0 ? g_real : L.G;
+  const dim3 mgrid0((unsigned)(num_seqs * L.Hkv));
+  if (tq_decode_block_format(L)) {  // whole-block streaming kernel (tq_decode_block.hip)
+    if (a.rows_blocks > 0)
+      hipLaunchKernelGGL((tq_decode_rows_kernel<128, 4>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
+    const int e = tq_launch_decode_block(L, q, pages, block_tables, max_blocks, seq_lens, num_seqs, sp,
+                                         n_sink, a.win_lens, win_cap, a.qscale, a.partials,
+                                         a.part_stride, nq, q0, a.g_real, stream);
+    if (e != 0) return e;
+    launch_merge<128, 4>(a, mgrid0, st);
+    return (int)hipGetLastError();
+  }
   const long groups = (a.n_units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * L.Hkv));  // packed splits; launch_t adds the row chunks
   const dim3 mgrid((unsigned)(num_seqs * L.Hkv));

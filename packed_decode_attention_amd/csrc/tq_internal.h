@@ -49,6 +49,15 @@ size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp,
 // value, 0 on success).
 int tq_noalloc_workspace(void** ptr);
 
+// The whole-block streaming decode kernel (tq_decode_block.hip): the formats it serves, its split
+// geometry and its launch (the split kernel only; the caller launches fp16-row chunks and merge).
+bool tq_decode_block_format(const TqLayer& L);
+TqSplit tq_decode_block_split(int num_seqs, int max_seq_len);
+int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
+                           int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
+                           int n_sink, const int32_t* win_lens, int win_cap, float qscale, float* partials,
+                           int part_stride, int nq, int q0, int g_real, void* stream);
+
 // Launchers: return a hipError_t value (0 on success).
 int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,
                        int64_t n_tok, void* pages, void* stream);

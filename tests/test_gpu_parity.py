@@ -61,6 +61,17 @@ CASES = {
     "edges-qjl": dict(w=wl.Workload("edges-qjl2", 1, 6, 6, 2, 128, 2, 2, 0, block_size=7, n_sink=4,
                                     values="normal", tables="fragmented", seed=19),
                       lens=[0, 1, 3, 5, 66, 200], slot_stride=160, qjl=True),
+    # the whole-block streaming kernel (K4/V4, D = 128, eight kv heads): lengths around run and
+    # stage edges, G = 2 with 32-position blocks, G = 3 with more units than workgroups (each
+    # workgroup takes several), G = 1 with sinks ending mid-run
+    "blk-edges": dict(w=wl.Workload("blk-edges", 1, 10, 32, 8, 128, 4, 4, 0, values="outliers", seed=51),
+                      lens=[1, 15, 16, 17, 31, 32, 33, 48, 500, 2047]),
+    "blk-g2-bs32": dict(w=wl.Workload("blk-g2", 1, 3, 16, 8, 128, 4, 4, 0, block_size=32, seed=52),
+                        lens=[1000, 333, 77]),
+    "blk-g3-many": dict(w=wl.Workload("blk-g3", 1, 300, 24, 8, 128, 4, 4, 0, seed=53),
+                        lens=list(np.random.default_rng(53).integers(1, 121, 300))),
+    "blk-g1-sinks": dict(w=wl.Workload("blk-g1", 1, 4, 8, 8, 128, 4, 4, 0, n_sink=20, seed=54),
+                         lens=[700, 33, 21, 5]),
     # the largest sink count (128): sequences shorter than, equal to and longer than it
     "sinks-max": dict(w=wl.Workload("sinks-max", 1, 4, 8, 2, 128, 4, 4, 0, n_sink=128, values="normal",
                                     seed=20), lens=[100, 128, 129, 700]),
@@ -157,7 +168,8 @@ def test_decode_attention(cases, name):
 MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-small", 5),
          ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
          ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2), ("edges-qjl", 3),
-         ("tiny", 64), ("sinks-max", 64)]  # 64: the largest query count
+         ("tiny", 64), ("sinks-max", 64),  # 64: the largest query count
+         ("blk-g2-bs32", 2), ("blk-g1-sinks", 4)]  # two or four queries on the whole-block kernel
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
@@ -190,6 +202,8 @@ WINDOWS = {
     "gaussian-g5": ([300, 0, 1], 301),
     "llama-qjl": ([64, 0], 100),
     "sinks-max": ([0, 0, 1, 572], 1024),  # the largest sink count and window capacity together
+    "blk-edges": ([0, 1, 16, 0, 31, 1, 17, 48, 100, 1000], 1024),
+    "blk-g1-sinks": ([680, 0, 1, 0], 700),
 }
 
 
