@@ -1417,77 +1417,74 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (sequence, kv head): merge the packed splits and the fp16-row chunks, rotate
-// back, normalise.
+// One workgroup per (sequence, kv head, query head), one thread per coordinate: merge the packed
+// splits and the fp16-row chunks, rotate back, normalise.
 template <int D, int GMAX>
-__global__ __launch_bounds__(kWG) void tq_decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void tq_decode_merge_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
   const int G = L.G;
-  const int h = blockIdx.x % L.Hkv;
-  const int b = blockIdx.x / L.Hkv;
+  const int g = blockIdx.x % G;
+  const int bh = blockIdx.x / G;
+  const int h = bh % L.Hkv;
+  const int b = bh / L.Hkv;
+  const int d = threadIdx.x;
   const int seq_len = a.seq_lens[b];
+  if (seq_len == 0) {
+    a.out[q_row(a, b, h, g) * D + d] = 0.0f;
+    return;
+  }
   const int nf = fp16_rows(a, b, seq_len);
   const int nsplit = num_splits(seq_len - (nf - min(a.n_sink, seq_len)), a.chunk);
   const int nrc = (nf + kRowChunk - 1) / kRowChunk;
   const int nparts = nsplit + nrc;
-  if (seq_len == 0) {
-    for (int i = threadIdx.x; i < G * D; i += kWG) a.out[q_row(a, b, h, i / D) * D + i % D] = 0.0f;
-    return;
-  }
-  __shared__ float s_acc[GMAX * D];  // merged rotated accumulators
-  __shared__ float s_ml[2 * GMAX];   // max, sum
+  __shared__ float s_acc[D];  // merged rotated accumulator
 
-  // Online log-sum-exp merge of the partials (packed splits, then fp16-row chunks), one (head,
-  // coordinate) per thread.  Partials are loaded eight at a time so their loads are in flight
-  // together.  Empty partials carry a maximum of -inf or kSent and contribute exp2(. - M) = 0
-  // once a real score is in M.
-  const int64_t bh = (int64_t)b * L.Hkv + h;
-  const float* pb = a.partials + bh * a.part_stride * (int64_t)G * (D + 2);
-  for (int i = threadIdx.x; i < G * D; i += kWG) {
-    const int g = i / D, d = i % D;
-    float M = kSent;
-    float l = 0.0f, acc = 0.0f;
-    for (int s0 = 0; s0 < nparts; s0 += 8) {
-      float ms[8], ls[8], as[8];
+  // Log-sum-exp merge of the partials (packed splits, then fp16-row chunks), sixteen at a time so
+  // their loads are in flight together.  Empty partials carry a maximum of -inf or kSent and
+  // contribute exp2(. - M) = 0 once a real score is in M.
+  const float* pb = a.partials + (int64_t)bh * a.part_stride * G * (D + 2) + g * (D + 2);
+  float M = kSent, l = 0.0f, acc = 0.0f;
+  for (int s0 = 0; s0 < nparts; s0 += 16) {
+    float ms[16], ls[16], as[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int pi = s0 + k;
-        const bool in = pi < nparts;
-        const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
-        const float* e = pb + ((int64_t)idx * G + g) * (D + 2);
-        ms[k] = in ? e[0] : -INFINITY;
-        ls[k] = in ? e[1] : 0.0f;
-        as[k] = in ? e[2 + d] : 0.0f;
-      }
+    for (int k = 0; k < 16; ++k) {
+      const int pi = s0 + k;
+      const bool in = pi < nparts;
+      const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
+      const float* e = pb + (int64_t)idx * G * (D + 2);
+      ms[k] = in ? e[0] : -INFINITY;
+      ls[k] = in ? e[1] : 0.0f;
+      as[k] = in ? e[2 + d] : 0.0f;
+    }
+    float mc = ms[0];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float Mn = fmaxf(M, ms[k]);
-        const float fo = __builtin_amdgcn_exp2f(M - Mn), fn = __builtin_amdgcn_exp2f(ms[k] - Mn);
-        l = l * fo + ls[k] * fn;
-        acc = acc * fo + as[k] * fn;
-        M = Mn;
-      }
+    for (int k = 1; k < 16; ++k) mc = fmaxf(mc, ms[k]);
+    const float Mn = fmaxf(M, mc);
+    const float fo = __builtin_amdgcn_exp2f(M - Mn);
+    l *= fo;
+    acc *= fo;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float fn = __builtin_amdgcn_exp2f(ms[k] - Mn);
+      l += ls[k] * fn;
+      acc += as[k] * fn;
     }
-    s_acc[g * D + d] = acc;
-    if (d == 0) {
-      s_ml[g] = M;
-      s_ml[GMAX + g] = l;
-    }
+    M = Mn;
   }
+  s_acc[d] = acc;
   __syncthreads();
 
-  // R^T a = D^(-1/2) diag(s) H a, divided by the sum: D/8 lanes of one DPP row per head, 8
-  // coordinates per lane.
+  // R^T a = D^(-1/2) diag(s) H a, divided by the sum: D/8 lanes of one DPP row, 8 coordinates each.
   constexpr int LPH = D / 8;
-  if (threadIdx.x < LPH * G) {
-    const int g = threadIdx.x / LPH, j = threadIdx.x % LPH;
+  if (d < LPH) {
+    const int j = d;
     float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = s_acc[g * D + 8 * j + e];
+    for (int e = 0; e < 8; ++e) x[e] = s_acc[8 * j + e];
     wht_row8_dpp<LPH>(x, j);
     const uint32_t sb = sign_byte(L.signs, j);
     // a query before the first position (several queries per sequence) sees nothing: zero
-    const float inv_l = q_limit(a, seq_len, g) > 0 ? 1.0f / s_ml[GMAX + g] : 0.0f;
+    const float inv_l = q_limit(a, seq_len, g) > 0 ? 1.0f / l : 0.0f;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1509,7 +1506,7 @@ __global__ __launch_bounds__(kWG) void tq_decode_rows_kernel(DecodeArgs a) {
 
 template <int D, int GMAX>
 void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
-  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(kWG), 0, st, a);
+  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(D), 0, st, a);
 }
 
 // Split kernel for one format and query-group bound (the fp16-row chunks at the front of its grid,
@@ -1688,7 +1685,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real > 0 ? g_real : L.G;
-  const dim3 mgrid0((unsigned)(num_seqs * L.Hkv));
+  const dim3 mgrid0((unsigned)(num_seqs * L.Hkv * L.G));  // merge: one workgroup per query head
   if (tq_decode_block_format(L)) {  // whole-block streaming kernel (tq_decode_block.hip)
     if (a.rows_blocks > 0)
       hipLaunchKernelGGL((tq_decode_rows_kernel<128, 4>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
@@ -1701,7 +1698,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   }
   const long groups = (a.n_units + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * L.Hkv));  // packed splits; launch_t adds the row chunks
-  const dim3 mgrid((unsigned)(num_seqs * L.Hkv));
+  const dim3 mgrid((unsigned)(num_seqs * L.Hkv * L.G));
   if (L.D == 128) launch_k<128>(a, grid, mgrid, st);
   else launch_k<64>(a, grid, mgrid, st);
   return (int)hipGetLastError();

@@ -9,7 +9,7 @@
 //  * One persistent workgroup of 8 waves per compute unit takes (sequence, split) units in turn;
 //    wave h computes kv head h.  The workgroup reads whole page runs (16 positions x 8 heads =
 //    17 KB contiguous): each load instruction moves 1 KB of page bytes straight into LDS
-//    (buffer_load ... lds), in a ring of five run buffers (three in flight while two are read).
+//    (buffer_load ... lds), in a ring of five run buffers (four in flight while one is read).
 //    Fetching one kv head's 136-byte rows instead (1088 bytes apart) streams about a quarter
 //    slower on this chip.
 //  * LDS reads are free of bank conflicts.  The loads place the 16-byte chunks of a run rotated
@@ -52,10 +52,12 @@ constexpr int kWaveChunks = kRunBytes / 16 / kW;  // 16-byte chunks of a run eac
 constexpr int kRing = 5;                       // run buffers
 constexpr int kCP = 32;                        // table copies
 constexpr int kLutShift = 8;                   // table entries hold c * 2^8
-constexpr int kWShift = 14;                    // weights enter PV as w * 2^14 (below 2^15)
-constexpr float kThr = 1.0f;                   // lazy rescale threshold, log2 units
+constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (below 2^15)
+constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
 constexpr int kMaxRuns = 192;                  // runs per unit (three lanes' worth of run rows)
+constexpr int kBuf0 = 256 * kCP * 8;           // first run buffer, after the 64 KB table
+constexpr int kLdsBytes = kBuf0 + kRing * kRunBytes;
 
 __device__ __forceinline__ float4_t mfma16(const uint4& a, const uint4& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
@@ -86,6 +88,11 @@ __device__ __forceinline__ float lane_value(float x, int l) {  // x of lane l, w
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Workgroup barrier that leaves this wave's LDS reads in flight (table lookups that read no run
+// buffer).  Used where every read of the run buffer released by the barrier has already been
+// consumed, so its data is in registers.
+__device__ __forceinline__ void step_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // s_waitcnt immediate leaving n vector memory operations outstanding (gfx9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
@@ -183,24 +190,28 @@ __device__ __forceinline__ TqUnit unit_of(const TqBlockArgs& a, int unit) {
   return u;
 }
 
-__global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a) {
-  __shared__ __align__(16) uint2 s_tab[256 * kCP];
-  __shared__ __align__(16) uint8_t s_r0[kRunBytes];
-  __shared__ __align__(16) uint8_t s_r1[kRunBytes];
-  __shared__ __align__(16) uint8_t s_r2[kRunBytes];
-  __shared__ __align__(16) uint8_t s_r3[kRunBytes];
-  __shared__ __align__(16) uint8_t s_r4[kRunBytes];
+__global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a) {
+  // One LDS array placed by hand: the table at byte 0, run buffer k at kBuf0 + 17408 k.  Only the
+  // producer wave has loads in flight, and it reads no LDS, so the compute waves' reads need no
+  // alias information to stay clear of pending loads.
+  __shared__ __align__(16) uint8_t s_lds[kLdsBytes];
+  uint2* const s_tab = reinterpret_cast<uint2*>(s_lds);
+  uint8_t* const s_r0 = s_lds + kBuf0;
+  uint8_t* const s_r1 = s_r0 + kRunBytes;
+  uint8_t* const s_r2 = s_r1 + kRunBytes;
+  uint8_t* const s_r3 = s_r2 + kRunBytes;
+  uint8_t* const s_r4 = s_r3 + kRunBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7: kv head; 8: run loads
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7: kv head; 8..11: run loads
   const int t16 = lane & 15, q4 = lane >> 4;
   const int G = a.G;
 
   // Centroid operand table: entry e (a code byte: coordinates 2j, 2j + 1 in its low and high
   // nibble) holds the fp16 high parts of c[e & 15], c[e >> 4], then their low parts, scaled by
   // 2^8; copy k of entry e at byte 256 e + 8 k.
-  for (int i = tid; i < 256 * kCP; i += kT + 64) {
+  for (int i = tid; i < 256 * kCP; i += kT + 256) {
     const int e = i / kCP;
     uint32_t h0, l0, h1, l1;
     split_half(ldexpf(a.c[e & 15], kLutShift), h0, l0);
@@ -208,23 +219,22 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
     s_tab[i] = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
   }
   // The run buffers are written by the loads (which the compiler does not see as stores): one
-  // ordinary store each keeps it from treating them as never written.
-  if (tid == 0) {
-    s_r0[0] = 0;
-    s_r1[0] = 0;
-    s_r2[0] = 0;
-    s_r3[0] = 0;
-    s_r4[0] = 0;
-  }
+  // ordinary store keeps it from treating the array as never written there.
+  if (tid == 0) s_r0[0] = 0;
 
-  if (wave == kW) {
-    // ======== producer wave: every page load of the workgroup ========
-    // Run r goes to buffer r mod 5 in 17 loads of 1 KB (LDS chunks 64 k + lane), r + 1 .. r + 3
-    // in flight while the compute waves read r and r + 1.  The compute waves never issue a vector
-    // memory instruction in the loop, so a busy load path stalls this wave only.
-    int src_off[17];
+  if (wave >= kW) {
+    // ======== producer waves: every page load of the workgroup ========
+    // Run r goes to buffer r mod 5 in 17 loads of 1 KB (LDS chunks 64 k + lane); producer p issues
+    // loads k = p, p + 4, ... of every run.  One wave issues such loads at about a fifth of the
+    // rate the memory system serves a compute unit, so a run's loads are spread over four waves.
+    // While the compute waves read run s + 1, runs s + 2 .. s + 5 are in flight.  The compute
+    // waves never issue a vector memory instruction in the loop, so a busy load path stalls these
+    // waves only.
+    const int pw = wave - kW;           // producer 0..3
+    const int nk = pw == 0 ? 5 : 4;     // loads per run of this producer
+    int src_off[5];
 #pragma unroll
-    for (int k = 0; k < 17; ++k) src_off[k] = 16 * run_chunk_at(64 * k + lane);
+    for (int i = 0; i < 5; ++i) src_off[i] = 16 * run_chunk_at(64 * min(pw + 4 * i, 16) + lane);
     for (int unit = blockIdx.x; unit < a.n_units; unit += gridDim.x) {
       const TqUnit u = unit_of(a, unit);
       if (!u.live) continue;
@@ -237,40 +247,69 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
         rows1 = run_row(a, u.b, u.run0 + min(lane + 64, n_run - 1));
         rows2 = run_row(a, u.b, u.run0 + min(lane + 128, n_run - 1));
       }
-      auto issue = [&](int s, lds_u8* buf) {
-        const int row = s < 64 ? __builtin_amdgcn_readlane(rows0, s)
-                               : s < 128 ? __builtin_amdgcn_readlane(rows1, s - 64)
-                                         : __builtin_amdgcn_readlane(rows2, s - 128);
+      auto issue = [&](int r, lds_u8* buf) {
+        const int row = r < 64 ? __builtin_amdgcn_readlane(rows0, r)
+                               : r < 128 ? __builtin_amdgcn_readlane(rows1, r - 64)
+                                         : __builtin_amdgcn_readlane(rows2, r - 128);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.pages + (int64_t)row * kRowBytes, kRunBytes);
 #pragma unroll
-        for (int k = 0; k < 17; ++k) lds_dma16(rs, buf + 1024 * k, src_off[k]);
+        for (int i = 0; i < 4; ++i) lds_dma16(rs, buf + 1024 * (pw + 4 * i), src_off[i]);
+        if (pw == 0) lds_dma16(rs, buf + 1024 * 16, src_off[4]);
       };
-      // runs 0..3, then wait for run 0 (the others stay in flight)
+      // wait for this wave's loads of run r, with those of the later runs (up to three) in flight
+      auto wait_run = [&](int r) {
+        const int later = min(n_run - 1, r + 3) - r;
+        if (later >= 3) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+        } else if (later == 2) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        } else if (later == 1) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+      };
+      (void)nk;
+      // runs 0..3 (buffer 4 holds the compute waves' queries until the first barrier)
       if (n_run > 0) issue(0, lds_ptr(s_r0));
       if (n_run > 1) issue(1, lds_ptr(s_r1));
       if (n_run > 2) issue(2, lds_ptr(s_r2));
       if (n_run > 3) issue(3, lds_ptr(s_r3));
       if (n_run <= 0) continue;
-      if (n_run >= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(51));
-      else if (n_run == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(34));
-      else if (n_run == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(17));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      lds_barrier();  // run 0 is in
-      // step s: run s + 1 in, barrier, then fetch s + 4 into the buffer of run s - 1
+      // run 0 is in (runs 1..3 may be in flight; run 4 is not issued yet)
+      {
+        const int later = min(n_run - 1, 3);
+        if (later >= 3) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+        } else if (later == 2) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        } else if (later == 1) {
+          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+      }
+      lds_barrier();
+      if (n_run > 4) issue(4, lds_ptr(s_r4));
+      // step s: every producer waits for its loads of run s + 1, barrier (every wave is done with
+      // run s), then they fetch run s + 5 into run s's buffer
       auto step = [&](int s, lds_u8* fill) {
-        const int ahead = min(n_run, s + 4) - (s + 2);  // runs issued beyond s + 1
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(34));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(17));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (s + 1 < n_run) wait_run(s + 1);
         lds_barrier();
-        if (s + 4 < n_run) issue(s + 4, fill);
+        if (s + 5 < n_run) issue(s + 5, fill);
       };
       for (int s = 0; s < n_run; s += kRing) {
-        step(s, lds_ptr(s_r4));
-        if (s + 1 < n_run) step(s + 1, lds_ptr(s_r0));
-        if (s + 2 < n_run) step(s + 2, lds_ptr(s_r1));
-        if (s + 3 < n_run) step(s + 3, lds_ptr(s_r2));
-        if (s + 4 < n_run) step(s + 4, lds_ptr(s_r3));
+        step(s, lds_ptr(s_r0));
+        if (s + 1 < n_run) step(s + 1, lds_ptr(s_r1));
+        if (s + 2 < n_run) step(s + 2, lds_ptr(s_r2));
+        if (s + 3 < n_run) step(s + 3, lds_ptr(s_r3));
+        if (s + 4 < n_run) step(s + 4, lds_ptr(s_r4));
       }
     }
     return;
@@ -285,16 +324,27 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
   // K codes of token t16, bytes 16 q4 .. 16 q4 + 15 of the K region, as two 8-byte reads; lanes
   // with odd q4 read the upper half first (the two halves of a 32-lane pass then use distinct
   // banks).  Word order: w[0..1] = first read, w[2..3] = second.
+  // Each offset is held as an LDS address less 64 KB (opaque to the compiler), so a read adds the
+  // buffer's base minus 64 KB as the DS instruction's immediate offset: no address arithmetic
+  // per read for the four buffers whose base is below 128 KB.
+  auto lane_addr = [](int off) {
+    int x = off + kBuf0;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   const int sw = q4 & 1;
   const int kbase = kRowBytes * t16 + kSB * h + 16 * q4;
-  const int off_k0 = run_lds_offset(kbase + 8 * sw);
-  const int off_k1 = run_lds_offset(kbase + 8 * (1 - sw));
-  const int off_kn = run_lds_offset(kRowBytes * t16 + kSB * h + 64);
-  const int off_vn = run_lds_offset(kRowBytes * t16 + kSB * h + kVOff + 64);
+  const int off_k0 = lane_addr(run_lds_offset(kbase + 8 * sw));
+  const int off_k1 = lane_addr(run_lds_offset(kbase + 8 * (1 - sw)));
+  const int off_kn = lane_addr(run_lds_offset(kRowBytes * t16 + kSB * h + 64));
+  const int off_vn = lane_addr(run_lds_offset(kRowBytes * t16 + kSB * h + kVOff + 64));
   // V codes: dword t16 (coordinates 8 t16 .. 8 t16 + 7) of tokens q4 + 4 m, m = 0..3
   int off_v[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) off_v[m] = run_lds_offset(kRowBytes * (q4 + 4 * m) + kSB * h + kVOff + 4 * t16);
+  for (int m = 0; m < 4; ++m)
+    off_v[m] = lane_addr(run_lds_offset(kRowBytes * (q4 + 4 * m) + kSB * h + kVOff + 4 * t16));
+  // read of buffer `buf` at lane address x
+  auto at = [&](const uint8_t* buf, int x) { return buf - kBuf0 + x; };
   // PV weight gather: row t16 of the A operand is (head t16 >> 2, nibble (t16 >> 1) & 1, weight
   // part t16 & 1); it takes the weights of tokens q4 + 4 m from softmax lane 16 (t16 >> 2) + token.
   const int bp_base = 4 * (16 * (t16 >> 2) + q4);
@@ -398,16 +448,17 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
     const int hi_l = live0 ? lim0 - t16 : INT_MIN;                            // p < lim0
 
     float m_s = kSent, m_w = kSent, l_s = 0.0f;
+    float t_s = kSent + kThr, t_w = kSent + kThr, m_b = kSent - (float)kWShift;  // thresholds, weight base
     float4_t acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // ---- key half of one run: table entries of this lane's 16 code bytes, and the norms ----
     auto key_codes = [&](const uint8_t* buf, uint32_t (&w)[4], float& kn, float& vn) {
-      const u32x2 r0 = *reinterpret_cast<const u32x2*>(buf + off_k0);
-      const u32x2 r1 = *reinterpret_cast<const u32x2*>(buf + off_k1);
-      kn = *reinterpret_cast<const float*>(buf + off_kn);
-      vn = *reinterpret_cast<const float*>(buf + off_vn);
+      const u32x2 r0 = *reinterpret_cast<const u32x2*>(at(buf, off_k0));
+      const u32x2 r1 = *reinterpret_cast<const u32x2*>(at(buf, off_k1));
+      kn = *reinterpret_cast<const float*>(at(buf, off_kn));
+      vn = *reinterpret_cast<const float*>(at(buf, off_vn));
       w[0] = r0.x;
       w[1] = r0.y;
       w[2] = r1.x;
@@ -426,32 +477,15 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
     };
     // QK: this lane's score (token t16, head g0) before the norm and scales
     auto key_mfma = [&](const uint2 (&ke)[16]) {
-      float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, sb = sa;
+      float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int mi = 0; mi < 8; mi += 2) {
+      for (int mi = 0; mi < 8; ++mi)
         sa = mfma16(aq[mi], make_uint4(ke[2 * mi].x, ke[2 * mi].y, ke[2 * mi + 1].x, ke[2 * mi + 1].y), sa);
-        sb = mfma16(aq[mi + 1], make_uint4(ke[2 * mi + 2].x, ke[2 * mi + 2].y, ke[2 * mi + 3].x, ke[2 * mi + 3].y),
-                    sb);
-      }
-      return (sa[0] + sa[1]) + (sb[0] + sb[1]);
+      return sa[0] + sa[1];
     };
 
-    float sc = 0.0f, kn = 0.0f, vn = 0.0f;  // run s: raw score and norms of token t16
-    // One pipelined step: run s from buffer cur (softmax, PV), run s + 1 from buffer nxt (key
-    // lookups, QK; after the last run nxt holds no run and the result is unused).
-    auto body = [&](int s, const uint8_t* cur, const uint8_t* nxt) {
-      // all LDS reads of the step first (they stay in flight through the softmax): run s + 1's key
-      // entries and norms, run s's value codes and their entries
-      uint32_t kw[4], cw[4];
-      float kn1, vn1;
-      key_codes(nxt, kw, kn1, vn1);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) cw[m] = *reinterpret_cast<const uint32_t*>(cur + off_v[m]);
-      __builtin_amdgcn_sched_barrier(0);  // the code reads go out first
-      uint2 ke[16];
-      key_lookup(kw, ke);
-      // value entries: tokens (q4, q4 + 4) then (q4 + 8, q4 + 12), code byte mi of dword t16
-      uint2 ve[16];
+    // value entries of one run: tokens (q4, q4 + 4) then (q4 + 8, q4 + 12), code byte mi of dword t16
+    auto value_lookup = [&](const uint32_t (&cw)[4], uint2 (&ve)[16]) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -462,15 +496,36 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
               *reinterpret_cast<const uint2*>(tab + __builtin_amdgcn_perm(cw[2 * hf + 1], kcopy, sel));
         }
       }
+    };
+    auto value_codes = [&](const uint8_t* buf, uint32_t (&cw)[4]) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) cw[m] = *reinterpret_cast<const uint32_t*>(at(buf, off_v[m]));
+    };
+
+    // Pipeline state carried from step s - 1: run s's raw scores and norms (token t16) and its value
+    // entries.  Step s issues run s + 1's key lookups, then does run s's softmax and PV, then
+    // issues run s + 1's value lookups (after PV has consumed run s's) and does run s + 1's QK.
+    // Table lookups stay in flight across the step barrier; every read of a run buffer is
+    // consumed within its step, before the barrier that can release the buffer.
+    float sc = 0.0f, knf = 0.0f, lv = 0.0f;  // run s: raw score, n_K * f0, log2 n_V (token t16)
+    uint2 ve[16];
+    auto body = [&](int s, const uint8_t* nxt) {
+      uint32_t kw[4], cw[4];
+      float kn1, vn1;
+      key_codes(nxt, kw, kn1, vn1);
+      value_codes(nxt, cw);
+      __builtin_amdgcn_sched_barrier(0);  // the code reads go out first
+      uint2 ke[16];
+      key_lookup(kw, ke);
 
       // softmax of run s, lane (token t16, head g0); masked rows never touch their garbage norms.
       // The references m_s (scores) and m_w (scores + log2 n_V) move only when some score passes
       // them by more than kThr: terms stay below 2^kThr, weights below 2^(kWShift + kThr).
       const int pb = (run0 + s) * 16;
       const bool valid = pb >= lo_l && pb < hi_l;
-      const float s0 = valid ? sc * kn * f0 : -INFINITY;
-      const float sw0 = valid ? s0 + __builtin_amdgcn_logf(vn) : -INFINITY;  // + log2(n_V)
-      if (__builtin_amdgcn_ballot_w64(s0 > m_s + kThr || sw0 > m_w + kThr) != 0) {
+      const float s0 = valid ? sc * knf : -INFINITY;
+      const float sw0 = valid ? s0 + lv : -INFINITY;  // + log2(n_V)
+      if (__builtin_amdgcn_ballot_w64(s0 > t_s || sw0 > t_w) != 0) {
         const float ns2 = fmaxf(m_s, max16(s0)), nw2 = fmaxf(m_w, max16(sw0));
         l_s *= __builtin_amdgcn_exp2f(m_s - ns2);
         const float r = __builtin_amdgcn_exp2f(m_w - nw2);
@@ -478,9 +533,12 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
         for (int c = 0; c < 4; ++c) acc[c] *= r;
         m_s = ns2;
         m_w = nw2;
+        t_s = m_s + kThr;
+        t_w = m_w + kThr;
+        m_b = m_w - (float)kWShift;
       }
       l_s += __builtin_amdgcn_exp2f(s0 - m_s);
-      const float wt = __builtin_amdgcn_exp2f(sw0 - (m_w - (float)kWShift));
+      const float wt = __builtin_amdgcn_exp2f(sw0 - m_b);
       const auto h2 = __builtin_amdgcn_cvt_pkrtz(wt, 0.0f);
       const auto p2 = __builtin_amdgcn_cvt_pkrtz(wt, wt - (float)h2[0]);
       const uint32_t wpk = __builtin_bit_cast(uint32_t, p2);  // both fp16 parts of the weight
@@ -501,39 +559,48 @@ __global__ __launch_bounds__(kT + 64) void tq_decode_block_kernel(TqBlockArgs a)
           acc[mi] = mfma16(aw, make_uint4(e0.x, e0.y, e1.x, e1.y), acc[mi]);
         }
       }
+      value_lookup(cw, ve);  // run s + 1
       sc = key_mfma(ke);
-      kn = kn1;
-      vn = vn1;
+      // the norms of run s + 1 are used here, so no read of its buffer outlives the step
+      knf = kn1 * f0;
+      lv = __builtin_amdgcn_logf(vn1);
     };
 
     if (n_run > 0) {
       lds_barrier();  // run 0 is in
       {
-        uint32_t kw[4];
+        uint32_t kw[4], cw[4];
         uint2 ke[16];
-        key_codes(s_r0, kw, kn, vn);
+        float kn0, vn0;
+        key_codes(s_r0, kw, kn0, vn0);
+        value_codes(s_r0, cw);
         key_lookup(kw, ke);
+        value_lookup(cw, ve);
         sc = key_mfma(ke);
+        knf = kn0 * f0;
+        lv = __builtin_amdgcn_logf(vn0);
       }
-      // step s: barrier (run s + 1 is in, every wave is done with run s - 1), then the body
+      // step s: barrier (run s + 1 is in; run s's buffer, read and used up by step s - 1, may be
+      // refilled), then the body.  After the last run the body reads a buffer that holds no run;
+      // its results are unused.
       for (int s = 0; s < n_run; s += kRing) {
-        lds_barrier();
-        body(s, s_r0, s_r1);
+        step_barrier();
+        body(s, s_r1);
         if (s + 1 < n_run) {
-          lds_barrier();
-          body(s + 1, s_r1, s_r2);
+          step_barrier();
+          body(s + 1, s_r2);
         }
         if (s + 2 < n_run) {
-          lds_barrier();
-          body(s + 2, s_r2, s_r3);
+          step_barrier();
+          body(s + 2, s_r3);
         }
         if (s + 3 < n_run) {
-          lds_barrier();
-          body(s + 3, s_r3, s_r4);
+          step_barrier();
+          body(s + 3, s_r4);
         }
         if (s + 4 < n_run) {
-          lds_barrier();
-          body(s + 4, s_r4, s_r0);
+          step_barrier();
+          body(s + 4, s_r0);
         }
       }
     }
@@ -612,6 +679,6 @@ int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, c
   a.q0 = q0;
   a.g_real = g_real;
   const int grid = a.n_units < 256 ? a.n_units : 256;
-  hipLaunchKernelGGL(tq_decode_block_kernel, dim3(grid), dim3(kT + 64), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(tq_decode_block_kernel, dim3(grid), dim3(kT + 256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
