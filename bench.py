@@ -214,7 +214,7 @@ def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1, flags=0):
     return per_layer
 
 
-DECODE_SOURCES = ("tq_decode.hip", "tq_device.h", "tq_internal.h")
+DECODE_SOURCES = ("tq_decode.hip", "tq_decode_block.hip", "tq_device.h", "tq_internal.h")
 
 
 def decode_source_digest():
@@ -255,11 +255,59 @@ def copy_probe(torch, mib):
     print(json.dumps({"copy_probe_bytes": n, "dispatches": 4}), flush=True)
 
 
-def cpu_baseline(w, budget_s=15.0):
+def stream_probe(torch, tq, w, reps=10):
+    """Streaming ceilings from the diagnostic kernel of include/tq_probe.h, no compute: the page
+    tensor of workload w read in a random block order in units of the block decode kernel's split
+    size, the same tensor in place order, and a 4:1 read:write stream the size of the bulk
+    quantize-append's traffic.  One JSON line."""
+    from packed_decode_attention_amd import workloads as wl
+    lens = wl.seq_lens(w)
+    kb, vb = w.bits(w.layers // 2)  # the format of most layers
+    slot = tq.tq_slot_bytes(w.head_dim, kb, vb)
+    block_bytes = w.block_size * w.num_kv_heads * slot
+    usable = (block_bytes // 1024) * 1024
+    n_blocks = int(sum((int(L) + w.block_size - 1) // w.block_size for L in lens))
+    chunk = -(-int(lens.sum()) // 256)
+    chunk = -(-chunk // 16) * 16
+    per_unit = max(1, chunk // w.block_size)
+    gen = torch.Generator().manual_seed(7)
+    order = torch.randperm(n_blocks, generator=gen).to(torch.int32).cuda()
+    src = torch.full((n_blocks * usable,), 0x11, dtype=torch.uint8, device="cuda")
+
+    def timeit(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return min(ts), float(np.mean(ts))
+
+    out = {"probe": "stream", "workload": w.name, "block_bytes_read": usable, "blocks": n_blocks,
+           "blocks_per_unit": per_unit}
+    for name, od in (("random_block_order", order), ("in_place_order", None)):
+        best, mean = timeit(lambda: tq.tq_probe_stream(src, n_blocks, usable, od, per_unit))
+        out[name] = {"bytes": n_blocks * usable, "best_us": best, "mean_us": mean,
+                     "best_GBps": n_blocks * usable / best / 1e3, "frac": n_blocks * usable / best / 1e3 / HBM_PEAK_GBS}
+    del src
+    # 4:1 read:write, 16 KB read blocks, about the bulk fill's bytes (fp16 K and V rows in, slots out)
+    n4 = (int(lens.sum()) * w.num_kv_heads * 4 * w.head_dim) // 16384
+    src4 = torch.full((n4 * 16384,), 0x22, dtype=torch.uint8, device="cuda")
+    dst4 = torch.empty((n4 * 4096,), dtype=torch.uint8, device="cuda")
+    best, mean = timeit(lambda: tq.tq_probe_stream(src4, n4, 16384, None, max(1, n4 // 256), dst4, 4))
+    moved = n4 * (16384 + 4096)
+    out["read4_write1"] = {"bytes": moved, "best_us": best, "mean_us": mean, "best_GBps": moved / best / 1e3,
+                           "frac": moved / best / 1e3 / HBM_PEAK_GBS}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_run(w, budget_s):
     """The oracle as it stands, on a bounded sample: one layer, the first sequences in turn until
     about `budget_s` seconds of decode work have been timed; pages built by the oracle itself."""
-    import threadpoolctl
-    import torch
     from oracle import attention as oatt
     from oracle import codebook as ocb
     from oracle import quantize as oq
@@ -296,21 +344,40 @@ def cpu_baseline(w, budget_s=15.0):
         seqs.append(b)
         if t_dec + t_q > budget_s:
             break
+    return tokens / t_dec, tokens, seqs, rows_q / t_q
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle timed twice on the host: with its BLAS pool at one thread, then at the pool's
+    full size.  Its per-sequence and per-head loops and its unpacking are Python on one thread in
+    both runs; only the BLAS calls use the pool."""
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(limits=1):
+        v1, tok1, seqs1, rq1 = cpu_baseline_run(w, budget_s)
+    vn, tokn, seqsn, rqn = cpu_baseline_run(w, budget_s)
     threads = max([p["num_threads"] for p in threadpoolctl.threadpool_info()] + [1])
-    return {"value": tokens / t_dec, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"layer 0 decode of sequences {seqs} ({tokens} KV tokens, {w.num_kv_heads} kv heads, "
-                       f"{w.num_q_heads} q heads) with fp64 NumPy oracle on {os.cpu_count()} host cores; "
-                       f"oracle quantize of the same {rows_q} rows took {t_q:.1f}s ({rows_q / t_q:.0f} rows/s)")}
+    def sample(tokens, seqs, rows_rate):
+        return (f"layer 0 decode of sequences {seqs} ({tokens} KV tokens, {w.num_kv_heads} kv heads, "
+                f"{w.num_q_heads} q heads) with the fp64 NumPy oracle; its quantize of the same rows ran at "
+                f"{rows_rate:.0f} rows/s")
+    return {"value": vn, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample(tokn, seqsn, rqn) + f"; BLAS pool of {threads} threads on a host with "
+                      f"{os.cpu_count()} logical CPUs (the Python loops run on one thread)",
+            "one_thread": {"value": v1, "unit": "KV tokens/s", "cores": 1,
+                           "sample": sample(tok1, seqs1, rq1) + "; BLAS pool limited to 1 thread"}}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (the GPU clock settles within the first few hundred "
+                         "milliseconds of load)")
     ap.add_argument("--workload", default="llama3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work per CPU baseline run (two runs: 1 thread, all threads)")
     ap.add_argument("--hot-window", type=int, default=0, metavar="W",
                     help="keep the last W tokens of each sequence as fp16 rows (decode through "
                          "tq_paged_decode_attention_window)")
@@ -326,6 +393,9 @@ def main():
                          "through tq_paged_decode_attention_multi")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only measure the streaming ceilings of the workload's access patterns "
+                         "(the diagnostic kernel of include/tq_probe.h)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -341,6 +411,9 @@ def main():
         copy_probe(torch, args.copy_probe)
         return
     w = wl.WORKLOADS[args.workload]
+    if args.stream_probe:
+        stream_probe(torch, tq, w)
+        return
     log(f"workload {describe(w)}")
     total = args.warmup + args.steps
     t0 = time.time()
@@ -402,7 +475,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 hi+lo MFMA operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": describe(w) + (f", fp16 hot window of {args.hot_window} tokens"
                                              if args.hot_window else "")

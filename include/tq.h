@@ -46,7 +46,10 @@
 extern "C" {
 #endif
 
+#ifndef TQ_STREAM_T_DEFINED
+#define TQ_STREAM_T_DEFINED
 typedef struct ihipStream_t* tq_stream_t; /* a hipStream_t; NULL = the default stream */
+#endif
 
 typedef enum tq_status {
   TQ_OK = 0,

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     tq_paged_decode_attention_multi,
     tq_paged_decode_attention_noalloc,
     tq_paged_decode_attention_window,
+    tq_probe_stream,
     tq_quantize_append,
     tq_rht_signs,
     tq_slot_bytes,

@@ -32,6 +32,7 @@ EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_slot_bytes_
            "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
            "tq_paged_decode_attention_multi", "tq_dequantize_rows", "tq_status_str")
 TQ_MAX_QUERIES = 64
+PROBE_EXPORTS = ("tq_probe_stream",)  # include/tq_probe.h (diagnostics)
 
 
 class TqError(RuntimeError):
@@ -101,6 +102,8 @@ def _lib():
         lib.tq_dequantize_rows.restype = ctypes.c_int
         lib.tq_status_str.argtypes = [ctypes.c_int]
         lib.tq_status_str.restype = ctypes.c_char_p
+        lib.tq_probe_stream.argtypes = [P, I64, I32, P, I32, P, I32, P]
+        lib.tq_probe_stream.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -238,3 +241,14 @@ def tq_dequantize_rows(desc, pages, num_blocks: int, slots, k_out, v_out, stream
     st = _lib().tq_dequantize_rows(ctypes.byref(desc), _ptr(pages), num_blocks, _ptr(slots),
                                    slots.numel(), _ptr(k_out), _ptr(v_out), _stream(stream))
     _check("tq_dequantize_rows", st)
+
+
+def tq_probe_stream(src, n_blocks: int, block_bytes: int, order=None, blocks_per_unit: int = 1, dst=None,
+                    write_div: int = 0, stream=None) -> None:
+    """include/tq_probe.h: the streaming-rate diagnostic (reads n_blocks blocks of src in the given
+    order; with dst, writes block_bytes / write_div bytes per block beside the reads)."""
+    st = _lib().tq_probe_stream(_ptr(src), n_blocks, block_bytes, _ptr(order) if order is not None else None,
+                                blocks_per_unit, _ptr(dst) if dst is not None else None, write_div,
+                                _stream(stream))
+    if st != TQ_OK:
+        raise TqError("tq_probe_stream", st)

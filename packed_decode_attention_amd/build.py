@@ -33,6 +33,7 @@ SOURCES = [
     ("tq_quantize.hip", "device", ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("tq_decode.hip", "device", ["-fno-honor-nans"]),
     ("tq_decode_block.hip", "device", ["-fno-honor-nans"]),
+    ("tq_probe.hip", "device", []),  # diagnostics (include/tq_probe.h)
     ("tq_api.cpp", "host", []),
     ("tq_codebook.cpp", "host", []),
 ]

@@ -30,6 +30,11 @@ def test_library_exports_every_declared_symbol(lib):
     so = ctypes.CDLL(lib.LIB_PATH)
     for name in declared:
         assert hasattr(so, name), name
+    with open(os.path.join(ROOT, "include", "tq_probe.h")) as f:
+        probe = set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", f.read()))
+    assert probe == set(lib.PROBE_EXPORTS)
+    for name in probe:
+        assert hasattr(so, name), name
 
 
 def test_slot_bytes(lib):
