@@ -104,8 +104,9 @@ def decode_kernel_names(head_dim: int, k_bits: int, v_bits: int, qjl: bool = Fal
                         num_kv_heads: int = 0, group: int = 0, flags: int = 0):
     """Names of the kernels one tq_paged_decode_attention call launches for this format, in
     launch order (as they appear in a kernel trace)."""
-    if (head_dim == 128 and k_bits == 4 and v_bits == 4 and num_kv_heads == 8 and 0 < group <= 4
-            and flags & ~1 == 0 and not qjl):  # unpadded slots, page blocks of whole 16-position runs
+    if (head_dim == 128 and num_kv_heads == 8 and flags & ~1 == 0 and not qjl and  # unpadded slots,
+            ((k_bits, v_bits) == (4, 4) and 0 < group <= 4 or  # page blocks of whole 16-position runs
+             (k_bits, v_bits) == (3, 2) and 0 < group <= 8)):
         return ["tq_decode_block_kernel", "tq_decode_merge_kernel"]
     mfma = ((head_dim == 128 and k_bits in (2, 3, 4, 8) and v_bits in (2, 4, 8)) or
             (head_dim == 64 and k_bits in (4, 8) and v_bits in (4, 8)))

@@ -114,6 +114,8 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t 
 // the kernels' 32-bit workgroup arithmetic.
 static bool grid_fits(const TqLayer& L, int32_t num_seqs, const TqSplit& sp) {
   const int64_t units = (int64_t)num_seqs * sp.max_split + 8;
+  // the block kernel counts the batch's runs in 32 bits
+  if (sp.max_runs > 0 && (int64_t)num_seqs * sp.max_runs > INT32_MAX) return false;
   return units * L.Hkv + (int64_t)num_seqs * L.Hkv * 16 <= INT32_MAX;
 }
 
@@ -202,15 +204,34 @@ extern "C" int tq_paged_decode_attention_window(
 // Queries per launch of the multi-query decode: up to 8 kernel heads per kv head.
 static int queries_per_launch(const TqLayer& L) { return L.G >= 8 ? 1 : 8 / L.G; }
 
+// The layer as one launch of the multi-query decode sees it: the queries q0 .. q0 + count - 1 as
+// count * G heads per kv head.
+static TqLayer multi_group(const TqLayer& L, int32_t n_queries, int q0) {
+  const int per = queries_per_launch(L);
+  TqLayer Lg = L;
+  Lg.G = L.G * (n_queries - q0 < per ? n_queries - q0 : per);
+  return Lg;
+}
+
+// Workspace of the multi-query decode: the largest of its launches' (each launch chooses its own
+// kernel and split for its head count; they reuse the workspace in stream order).
+static size_t multi_ws_bytes(const TqLayer& L, int32_t num_seqs, int32_t max_seq_len, int32_t n_queries) {
+  size_t need = 0;
+  for (int q0 = 0; q0 < n_queries; q0 += queries_per_launch(L)) {
+    const TqLayer Lg = multi_group(L, n_queries, q0);
+    const size_t b = tq_decode_ws_bytes(Lg, num_seqs, tq_decode_split(Lg, num_seqs, max_seq_len));
+    if (b > need) need = b;
+  }
+  return need;
+}
+
 extern "C" size_t tq_decode_multi_workspace_bytes(const tq_layer_desc* layer, int32_t num_seqs,
                                                   int32_t max_seq_len, int32_t n_queries) {
   TqLayer L;
   if (make_layer(layer, true, &L) != TQ_OK || num_seqs < 0 || max_seq_len < 0 || n_queries < 1 ||
       n_queries > TQ_MAX_QUERIES)
     return 0;
-  const int per = queries_per_launch(L);
-  L.G *= n_queries < per ? n_queries : per;
-  return tq_decode_ws_bytes(L, num_seqs, tq_decode_split(L, num_seqs, max_seq_len));
+  return multi_ws_bytes(L, num_seqs, max_seq_len, n_queries);
 }
 
 extern "C" int tq_paged_decode_attention_multi(
@@ -239,20 +260,20 @@ extern "C" int tq_paged_decode_attention_multi(
   if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr)) return TQ_ERR_INVALID_ARG;
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L.D));
   if (!std::isfinite(scale)) return TQ_ERR_INVALID_ARG;
-  const int G = L.G;
   const int per = queries_per_launch(L);
-  TqLayer Lv = L;
-  Lv.G = G * (n_queries < per ? n_queries : per);
-  const TqSplit sp = tq_decode_split(Lv, num_seqs, max_seq_len);
-  if (!grid_fits(Lv, num_seqs, sp)) return TQ_ERR_UNSUPPORTED;
-  if (workspace_bytes < tq_decode_ws_bytes(Lv, num_seqs, sp)) return TQ_ERR_WORKSPACE;
+  for (int q0 = 0; q0 < n_queries; q0 += per) {
+    const TqLayer Lg = multi_group(L, n_queries, q0);
+    if (!grid_fits(Lg, num_seqs, tq_decode_split(Lg, num_seqs, max_seq_len))) return TQ_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < multi_ws_bytes(L, num_seqs, max_seq_len, n_queries)) return TQ_ERR_WORKSPACE;
   // each group of queries is one split + merge launch pair; the pair after it reuses the
   // workspace in stream order
   for (int q0 = 0; q0 < n_queries; q0 += per) {
-    Lv.G = G * (n_queries - q0 < per ? n_queries - q0 : per);
-    if (tq_launch_decode(Lv, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
+    const TqLayer Lg = multi_group(L, n_queries, q0);
+    const TqSplit sp = tq_decode_split(Lg, num_seqs, max_seq_len);
+    if (tq_launch_decode(Lg, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
                          sink_k, sink_v, n_sink, nullptr, nullptr, nullptr, 0, scale, out,
-                         workspace, stream, n_queries, q0, G) != 0)
+                         workspace, stream, n_queries, q0, L.G) != 0)
       return TQ_ERR_HIP;
   }
   return TQ_OK;

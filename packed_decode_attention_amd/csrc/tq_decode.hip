@@ -65,6 +65,7 @@ struct DecodeArgs {
   int win_cap;
   float* out;
   float* partials;   // [B][Hkv][part_stride][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
+  const int32_t* nsplit_of;  // packed partials per sequence as the block kernel wrote them, or NULL
   // Several queries per sequence: the kernels' G heads of a kv head are G_real query heads for
   // each of this launch's queries q0 .. q0 + G / G_real - 1 out of nq (one query: nq = 1, q0 = 0,
   // g_real = G).
@@ -1417,6 +1418,37 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// NB partials from index s0 into the running (M, l, acc) of coordinate d.
+template <int NB, int D>
+__device__ __forceinline__ void merge_batch(const DecodeArgs& a, const float* pb, int s0, int nparts, int nsplit,
+                                            int G, int d, float& M, float& l, float& acc) {
+  float ms[NB], ls[NB], as[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int pi = s0 + k;
+    const bool in = pi < nparts;
+    const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
+    const float* e = pb + (int64_t)idx * G * (D + 2);
+    ms[k] = in ? e[0] : -INFINITY;
+    ls[k] = in ? e[1] : 0.0f;
+    as[k] = in ? e[2 + d] : 0.0f;
+  }
+  float mc = ms[0];
+#pragma unroll
+  for (int k = 1; k < NB; ++k) mc = fmaxf(mc, ms[k]);
+  const float Mn = fmaxf(M, mc);
+  const float fo = __builtin_amdgcn_exp2f(M - Mn);
+  l *= fo;
+  acc *= fo;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const float fn = __builtin_amdgcn_exp2f(ms[k] - Mn);
+    l += ls[k] * fn;
+    acc += as[k] * fn;
+  }
+  M = Mn;
+}
+
 // One workgroup per (sequence, kv head, query head), one thread per coordinate: merge the packed
 // splits and the fp16-row chunks, rotate back, normalise.
 template <int D, int GMAX>
@@ -1434,43 +1466,20 @@ __global__ __launch_bounds__(D) void tq_decode_merge_kernel(DecodeArgs a) {
     return;
   }
   const int nf = fp16_rows(a, b, seq_len);
-  const int nsplit = num_splits(seq_len - (nf - min(a.n_sink, seq_len)), a.chunk);
+  const int nsplit = a.nsplit_of != nullptr ? a.nsplit_of[b]
+                                             : num_splits(seq_len - (nf - min(a.n_sink, seq_len)), a.chunk);
   const int nrc = (nf + kRowChunk - 1) / kRowChunk;
   const int nparts = nsplit + nrc;
   __shared__ float s_acc[D];  // merged rotated accumulator
 
   // Log-sum-exp merge of the partials (packed splits, then fp16-row chunks), sixteen at a time so
-  // their loads are in flight together.  Empty partials carry a maximum of -inf or kSent and
-  // contribute exp2(. - M) = 0 once a real score is in M.
+  // their loads are in flight together, the rest four at a time.  Empty partials carry a maximum
+  // of -inf or kSent and contribute exp2(. - M) = 0 once a real score is in M.
   const float* pb = a.partials + (int64_t)bh * a.part_stride * G * (D + 2) + g * (D + 2);
   float M = kSent, l = 0.0f, acc = 0.0f;
-  for (int s0 = 0; s0 < nparts; s0 += 16) {
-    float ms[16], ls[16], as[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int pi = s0 + k;
-      const bool in = pi < nparts;
-      const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
-      const float* e = pb + (int64_t)idx * G * (D + 2);
-      ms[k] = in ? e[0] : -INFINITY;
-      ls[k] = in ? e[1] : 0.0f;
-      as[k] = in ? e[2 + d] : 0.0f;
-    }
-    float mc = ms[0];
-#pragma unroll
-    for (int k = 1; k < 16; ++k) mc = fmaxf(mc, ms[k]);
-    const float Mn = fmaxf(M, mc);
-    const float fo = __builtin_amdgcn_exp2f(M - Mn);
-    l *= fo;
-    acc *= fo;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float fn = __builtin_amdgcn_exp2f(ms[k] - Mn);
-      l += ls[k] * fn;
-      acc += as[k] * fn;
-    }
-    M = Mn;
-  }
+  int s0 = 0;
+  for (; s0 + 16 <= nparts; s0 += 16) merge_batch<16, D>(a, pb, s0, nparts, nsplit, G, d, M, l, acc);
+  for (; s0 < nparts; s0 += 4) merge_batch<4, D>(a, pb, s0, nparts, nsplit, G, d, M, l, acc);
   s_acc[d] = acc;
   __syncthreads();
 
@@ -1614,9 +1623,16 @@ TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len) {
 // hot-window rows) of this call.
 static int row_chunks_of(int n_sink, int win_cap) { return (n_sink + win_cap + kRowChunk - 1) / kRowChunk; }
 
-size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp, int n_sink, int win_cap) {
+// Partials, then (block kernel) the piece count of each sequence.
+static size_t partials_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp, int n_sink, int win_cap) {
   const size_t bh = (size_t)num_seqs * L.Hkv;
-  return bh * (size_t)(sp.max_split + row_chunks_of(n_sink, win_cap)) * L.G * (L.D + 2) * sizeof(float);
+  const size_t b = bh * (size_t)(sp.max_split + row_chunks_of(n_sink, win_cap)) * L.G * (L.D + 2) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp, int n_sink, int win_cap) {
+  const size_t meta = tq_decode_block_format(L) ? (size_t)num_seqs * sizeof(int32_t) : 0;
+  return partials_bytes(L, num_seqs, sp, n_sink, win_cap) + meta;
 }
 
 size_t tq_decode_ws_bytes(const TqLayer& L, int num_seqs, const TqSplit& sp) {
@@ -1682,18 +1698,24 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.win_cap = win_cap;
   a.out = out;
   a.partials = (float*)workspace;
+  a.nsplit_of = nullptr;
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real > 0 ? g_real : L.G;
   const dim3 mgrid0((unsigned)(num_seqs * L.Hkv * L.G));  // merge: one workgroup per query head
   if (tq_decode_block_format(L)) {  // whole-block streaming kernel (tq_decode_block.hip)
-    if (a.rows_blocks > 0)
-      hipLaunchKernelGGL((tq_decode_rows_kernel<128, 4>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
+    if (a.rows_blocks > 0) {
+      if (L.G <= 4) hipLaunchKernelGGL((tq_decode_rows_kernel<128, 4>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
+      else hipLaunchKernelGGL((tq_decode_rows_kernel<128, 8>), dim3(a.rows_blocks), dim3(kWG), 0, st, a);
+    }
+    int32_t* nsplit = (int32_t*)((uint8_t*)workspace + partials_bytes(L, num_seqs, sp, n_sink, win_cap));
     const int e = tq_launch_decode_block(L, q, pages, block_tables, max_blocks, seq_lens, num_seqs, sp,
-                                         n_sink, a.win_lens, win_cap, a.qscale, a.partials,
+                                         n_sink, a.win_lens, win_cap, a.qscale, a.partials, nsplit,
                                          a.part_stride, nq, q0, a.g_real, stream);
     if (e != 0) return e;
-    launch_merge<128, 4>(a, mgrid0, st);
+    a.nsplit_of = nsplit;
+    if (L.G <= 4) launch_merge<128, 4>(a, mgrid0, st);
+    else launch_merge<128, 8>(a, mgrid0, st);
     return (int)hipGetLastError();
   }
   const long groups = (a.n_units + 7) / 8;

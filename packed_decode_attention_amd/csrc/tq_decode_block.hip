@@ -1,32 +1,39 @@
 // Fused paged decode attention over packed TQ pages, whole-block streaming kernel (gfx950), for
-// the K4/V4 page format at D = 128 with eight kv heads of unpadded 136-byte slots, one codebook
-// for keys and values, and up to four query heads per kv head (the Llama-3-8B-shaped workload).
+// page formats at D = 128 with eight kv heads of unpadded slots: K4/V4 with one codebook for keys
+// and values and up to four query heads per kv head (the Llama-3-8B-shaped workload), and K3/V2
+// with up to eight (the ragged serving batch).
 //
 // Method as in tq_decode.hip: scores on the codes with a rotated query, online softmax, values
 // summed in the rotated frame, split-K partials merged by tq_decode_merge_kernel (tq-kv, "Custom
 // CUDA Kernel Stack": split-KV flash decode on compressed KV; turboquant-pro 1.4.2, "Fused CUDA
 // decode": split-K decode on the codes).  What differs is how page bytes reach the matrix cores:
-//  * One persistent workgroup of 8 waves per compute unit takes (sequence, split) units in turn;
-//    wave h computes kv head h.  The workgroup reads whole page runs (16 positions x 8 heads =
-//    17 KB contiguous): each load instruction moves 1 KB of page bytes straight into LDS
-//    (buffer_load ... lds), in a ring of five run buffers (four in flight while one is read).
-//    Fetching one kv head's 136-byte rows instead (1088 bytes apart) streams about a quarter
-//    slower on this chip.
+//  * One persistent workgroup of 12 waves per compute unit: compute wave h (0..7) computes kv
+//    head h, and four producer waves issue every page load.  The workgroup reads whole page runs
+//    (16 positions x 8 heads, contiguous: 17 KB at K4/V4, 11 KB at K3/V2): each load instruction
+//    moves 1 KB of page bytes straight into LDS (buffer_load ... lds), in a ring of five run
+//    buffers (four in flight while one is read).  The compute waves issue no vector memory
+//    instruction inside the run loop.  Fetching one kv head's rows instead (136 bytes every 1088
+//    at K4/V4) streams about a quarter slower on this chip.
+//  * Balanced work: the runs of all sequences form one sequence, and workgroup k takes the k-th
+//    contiguous range of it, so a ragged batch gives every compute unit the same number of runs.
+//    A range splits into pieces at sequence boundaries; each piece writes one partial, and
+//    workgroup 0 records each sequence's piece count for the merge.
 //  * LDS reads are free of bank conflicts.  The loads place the 16-byte chunks of a run rotated
-//    by (token / 4) within each aligned group of 16 chunks (the loads choose their source chunks,
-//    the LDS side stays contiguous), so the 16 tokens of a run, 1088 bytes apart, no longer fall
-//    on 4 banks.  The centroid operand table (one code byte -> fp16 high and low parts of its two
-//    centroids, 8 bytes) is held in 32 interleaved copies, lane l reading copy l mod 32: the 32
-//    lanes of each LDS pass read distinct bank pairs.  Its byte address (code << 8 | 8 copy) is
-//    one v_perm of the code word.
+//    by (position / 4) within each aligned group of 16 chunks (the loads choose their source
+//    chunks, the LDS side stays contiguous), so the 16 positions of a run, a page row apart, no
+//    longer fall on 4 banks.  The centroid operand tables (one code group -> fp16 high and low
+//    parts of its two centroids, 8 bytes: a byte of 4-bit codes, six bits of 3-bit codes, a
+//    nibble of 2-bit codes) are held in 32 interleaved copies, lane l reading copy l mod 32: the
+//    32 lanes of each LDS pass read distinct bank pairs.
 //  * QK on v_mfma_f32_16x16x32_f16: rows are (query head, fp16 part of the query), columns the 16
-//    tokens, K the coordinates with both fp16 parts of each centroid.  PV: rows are (query head,
-//    fp16 part of the weight, nibble of the code byte), columns the code bytes of a dword (two
-//    coordinates each), K the tokens with both centroid parts; every row is live, and the code
-//    byte of one token indexes the table directly.
+//    positions, K the coordinates with both fp16 parts of each centroid.  PV: rows are (query
+//    head, fp16 part of the weight, which coordinate of the code group), columns the code groups
+//    a lane holds (two coordinates each), K the positions with both centroid parts; every row is
+//    live, and the code group of one position indexes the table directly.  With eight query
+//    heads per kv head the QK rows are all live and PV takes two row sets.
 //  * Software pipeline: each step issues the next run's key lookups, then does the current run's
 //    softmax and PV, then the next run's QK.  The running maxima are rescaled lazily (only when a
-//    run's maximum exceeds the reference by more than one, in log2 units), which keeps the step
+//    run's maximum exceeds the reference by more than two, in log2 units), which keeps the step
 //    one basic block in the common case.
 
 #include <climits>
@@ -40,15 +47,13 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // one 8-byte LDS read
 
-constexpr int kW = 8;                          // waves per workgroup: one per kv head
-constexpr int kT = kW * 64;                    // threads per workgroup
+constexpr int kW = 8;                          // compute waves per workgroup: one per kv head
+constexpr int kT = kW * 64;                    // compute threads
+constexpr int kNP = 4;                         // producer waves
+constexpr int kThreads = kT + 64 * kNP;        // threads per workgroup
+constexpr int kWaves = kThreads / 64;
 constexpr int kH = 8;                          // kv heads
 constexpr int kD = 128;
-constexpr int kSB = 136;                       // slot bytes: K codes, K norm, V codes, V norm
-constexpr int kVOff = 68;                      // V region offset in a slot
-constexpr int kRowBytes = kH * kSB;            // one position, every kv head: 1088
-constexpr int kRunBytes = 16 * kRowBytes;      // one run of 16 positions: 17408
-constexpr int kWaveChunks = kRunBytes / 16 / kW;  // 16-byte chunks of a run each wave loads: 136
 constexpr int kRing = 5;                       // run buffers
 constexpr int kCP = 32;                        // table copies
 constexpr int kLutShift = 8;                   // table entries hold c * 2^8
@@ -56,8 +61,41 @@ constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (
 constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
 constexpr int kMaxRuns = 192;                  // runs per unit (three lanes' worth of run rows)
-constexpr int kBuf0 = 256 * kCP * 8;           // first run buffer, after the 64 KB table
-constexpr int kLdsBytes = kBuf0 + kRing * kRunBytes;
+constexpr int kPlanInts = 40;                  // LDS words of the work plan
+constexpr int kGrid = 256;                     // workgroups: one per compute unit of the MI355X
+
+// Geometry of one page format: KB-bit keys, VB-bit values, up to GM query heads per kv head.
+template <int KB, int VB, int GM>
+struct Fmt {
+  static constexpr int kKCode = kD * KB / 8;         // K code bytes (the K norm follows)
+  static constexpr int kVOff = kKCode + 4;           // V region offset in a slot
+  static constexpr int kVCode = kD * VB / 8;
+  static constexpr int kSB = kVOff + kVCode + 4;     // slot bytes: 136 at K4/V4, 88 at K3/V2
+  static constexpr int kRowBytes = kH * kSB;         // one position, every kv head
+  static constexpr int kRunBytes = 16 * kRowBytes;   // one run of 16 positions
+  static constexpr int kLoads = kRunBytes / 1024;    // 1 KB loads per run
+  static constexpr int kLoadsHi = (kLoads + kNP - 1) / kNP;  // loads per run of producer p <
+  static constexpr int kLoadsLo = kLoads / kNP;              // kLoads % kNP, and of the others
+  static constexpr int kGroupChunks = kRowBytes / 4;  // 16-byte chunks of four positions
+  static constexpr bool kOneTable = KB == VB;        // K and V share the table (one codebook)
+  static constexpr int kKEnt = KB == 4 ? 256 : 64;   // K table entries: a byte, or six bits
+  static constexpr int kVEnt = kOneTable ? 0 : (VB == 4 ? 256 : 16);
+  static constexpr int kVTab = kOneTable ? 0 : kKEnt * 256;  // V table byte offset
+  static constexpr int kBuf0 = (kKEnt + kVEnt) * 256;        // first run buffer, after the tables
+  static constexpr int kNZ = GM / 4;                 // query heads per softmax lane
+  // The queries of a piece's first unit are staged in the last run buffer when a wave's share of
+  // it holds GM fp32 rows (the buffer takes a run only after the first step); else in a region of
+  // their own after the ring.
+  static constexpr int kQBytes = GM * 512;           // per wave: GM rotated fp32 rows
+  static constexpr bool kQInRing = kRunBytes / kW >= kQBytes;
+  static constexpr int kQBase = kBuf0 + kRing * kRunBytes;
+  static constexpr int kPlanOff = kQBase + (kQInRing ? 0 : kW * kQBytes);
+  static constexpr int kLdsBytes = kPlanOff + 4 * kPlanInts;
+  static_assert(kRunBytes % 1024 == 0, "runs are whole 1 KB loads");
+  static_assert(kRowBytes % 64 == 0, "four positions are whole groups of 16 chunks");
+  static_assert(kLoadsHi <= 5 && kLoadsHi * 3 <= 63, "source offsets and wait counts");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
 
 __device__ __forceinline__ float4_t mfma16(const uint4& a, const uint4& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
@@ -76,6 +114,13 @@ __device__ __forceinline__ float max16(float x) {  // maximum over a 16-lane row
   x = fmaxf(x, dpp<kDppQuadXor2>(x));
   x = fmaxf(x, dpp<kDppHalfRowMirror>(x));
   return fmaxf(x, dpp<kDppRowMirror>(x));
+}
+
+__device__ __forceinline__ float sum16(float x) {  // sum over a 16-lane row, in every lane
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppHalfRowMirror>(x);
+  return x + dpp<kDppRowMirror>(x);
 }
 
 __device__ __forceinline__ float lane_value(float x, int l) {  // x of lane l, wave-uniform
@@ -117,17 +162,29 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lds_u8* dst
 }
 __device__ __forceinline__ lds_u8* lds_ptr(uint8_t* p) { return (lds_u8*)p; }
 
-// LDS placement of a run: byte g of the run (position g / 1088, slot byte g mod 1088) sits in
-// chunk slot ((g / 16 + q) mod 16) of its aligned group of 16 chunks, q = g / 4352 (the token's
-// index divided by four).  A group never straddles two values of q (4352 bytes = 17 groups).
+// LDS placement of a run: byte g of the run (position g / row bytes) sits in chunk slot
+// ((g / 16 + q) mod 16) of its aligned group of 16 chunks, q = the position divided by four
+// (QC = chunks of four positions).  A group never straddles two values of q.
+template <int QC>
 __device__ __forceinline__ int run_lds_offset(int g) {
-  const int c = g >> 4, q = c / 272;
+  const int c = g >> 4, q = c / QC;
   return (((c & ~15) | ((c + q) & 15)) << 4) | (g & 15);
 }
 // The run chunk that LDS chunk p holds (the inverse of the placement above).
+template <int QC>
 __device__ __forceinline__ int run_chunk_at(int p) {
-  const int q = p / 272;
+  const int q = p / QC;
   return (p & ~15) | ((p - q) & 15);
+}
+
+// Inclusive prefix sum across a wave (the work plan only).
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
 }
 
 }  // namespace
@@ -139,11 +196,13 @@ struct TqBlockArgs {
   const int32_t* seq_lens;
   const int32_t* win_lens;  // NULL: no hot window
   float* partials;          // [B][8][part_stride][G][D + 2]
-  const float* c;           // the codebook of keys and values (16 centroids)
+  int32_t* nsplit;          // [B]: pieces (partials) of each sequence, written by workgroup 0
+  const float* kc;          // key codebook (2^KB centroids)
+  const float* vc;          // value codebook (2^VB centroids)
   TqSigns signs;
   float qscale;             // scale * log2(e) / sqrt(D)
   int max_blocks, bs, bs_shift, G, Hq, n_sink, win_cap;
-  int chunk, max_split, part_stride, n_units;
+  int num_seqs, part_stride, max_pieces, max_parts, max_runs;
   int nq, q0, g_real;       // several queries per sequence (one: 1, 0, G)
 };
 
@@ -161,46 +220,237 @@ __device__ __forceinline__ int run_row(const TqBlockArgs& a, int b, int r) {
   return a.bt[(int64_t)b * a.max_blocks + blk] * a.bs + (pos - blk * a.bs);
 }
 
-// Unit bookkeeping shared by the producer and the compute waves (every wave takes the same
-// branches, so the workgroup barriers match).
-struct TqUnit {
-  int b, split, seq_len, ns, end, run0, n_run;
-  bool live;  // false: no partial is read for this split
+// The packed positions of a sequence, [ns, end), read as runs run0 .. run0 + n_run - 1 (the run
+// holding ns first; rows below ns and from end on are masked).  Sinks and hot-window rows come
+// from the fp16-row chunks.
+struct TqSeq {
+  int seq_len, ns, end, run0, n_run;
 };
 
-__device__ __forceinline__ TqUnit unit_of(const TqBlockArgs& a, int unit) {
-  TqUnit u;
-  u.b = unit / a.max_split;
-  u.split = unit - u.b * a.max_split;
-  u.seq_len = load_uniform(a.seq_lens + u.b);
-  u.ns = min(a.n_sink, u.seq_len);
+template <bool UNIFORM>
+__device__ __forceinline__ TqSeq seq_of(const TqBlockArgs& a, int b) {
+  TqSeq s;
+  s.seq_len = UNIFORM ? load_uniform(a.seq_lens + b) : a.seq_lens[b];
+  s.ns = min(a.n_sink, s.seq_len);
   int win = 0;
-  if (a.win_lens != nullptr) win = max(0, min(load_uniform(a.win_lens + u.b), min(a.win_cap, u.seq_len - u.ns)));
-  const int packed_end = u.seq_len - win;
-  const int nsplit = packed_end > 0 ? (packed_end + a.chunk - 1) / a.chunk : 1;
-  u.live = u.split < nsplit;  // the merge reads the partials of splits below nsplit only
-  const int start = u.split * a.chunk;
-  u.end = min(start + a.chunk, packed_end);
-  // Positions from the run holding the first non-sink position; rows below ns are masked, runs of
-  // sinks only are never read.
-  const int p0 = max(start, u.ns & ~15);
-  const bool any = u.end > max(p0, u.ns);
-  u.run0 = p0 >> 4;
-  u.n_run = any ? ((u.end - 1) >> 4) - u.run0 + 1 : 0;
-  return u;
+  if (a.win_lens != nullptr) {
+    const int wl = UNIFORM ? load_uniform(a.win_lens + b) : a.win_lens[b];
+    win = max(0, min(wl, min(a.win_cap, s.seq_len - s.ns)));
+  }
+  s.end = s.seq_len - win;
+  s.run0 = s.ns >> 4;
+  s.n_run = s.end > s.ns ? ((s.end - 1) >> 4) - s.run0 + 1 : 0;
+  return s;
 }
 
-__global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a) {
-  // One LDS array placed by hand: the table at byte 0, run buffer k at kBuf0 + 17408 k.  Only the
-  // producer wave has loads in flight, and it reads no LDS, so the compute waves' reads need no
+// This workgroup's share of the batch, in one of two forms.
+//  * Aligned: when the sequences with packed runs split evenly over the workgroups (c of them per
+//    sequence, no piece longer than an even share of all runs), workgroup k takes piece k mod c of
+//    the (k / c)-th such sequence, and no workgroup switches sequences.
+//  * Ranges: otherwise the runs of all sequences form one sequence and workgroup k takes runs
+//    [S, E) of it, rpw runs per workgroup, cut into pieces at sequence boundaries; b is the first
+//    sequence with a run in the share and R the index of its first run.
+// A piece is cut into units of at most kMaxRuns runs, and every unit writes a partial of its own:
+// a sequence's partials are numbered in run order, part0 being that of the share's first unit.
+// Workgroup 0 writes each sequence's partial count.  Every thread of the workgroup calls it.  An
+// aligned piece is walked as a share of one sequence whose runs count from its first run (R = 0).
+// The host bounds the batch's runs by INT32_MAX, so 32-bit counts suffice.
+struct TqPlan {
+  int S, E, R, rpw, b, part0;
+};
+
+constexpr int kAlignSlack = 2;  // runs an aligned piece may exceed the even share by
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d);
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x = max(x, __shfl_xor(x, d));
+  return x;
+}
+__device__ __forceinline__ int units_of(int runs) { return (runs + kMaxRuns - 1) / kMaxRuns; }
+
+// Units of share k (runs [k rpw, (k + 1) rpw)) inside a sequence's runs [R, R + n).
+__device__ __forceinline__ int units_in_share(int k, int rpw, int R, int n) {
+  const int64_t lo = max((int64_t)k * rpw, (int64_t)R), hi = min((int64_t)(k + 1) * rpw, (int64_t)R + n);
+  return hi > lo ? units_of((int)(hi - lo)) : 0;
+}
+
+// n_own: the run count of sequence tid (0 past the batch), loaded by the caller at kernel entry so
+// the load overlaps the table fill.  A batch of at most kThreads sequences takes one pass over
+// the run counts; a larger one takes a second, kThreads sequences at a time.
+__device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave, int lane, int n_own) {
+  const int B = a.num_seqs;
+  const bool one_pass = B <= kThreads;
+  // total runs, sequences with runs, longest sequence (and, in one pass, the prefixes)
+  int t = 0, nz = 0, mx = 0, incl = 0, incl_nz = 0;
+  if (one_pass) {
+    incl = wave_incl_scan(n_own, lane);
+    incl_nz = wave_incl_scan(n_own > 0, lane);
+    t = __shfl(incl, 63);
+    nz = __shfl(incl_nz, 63);
+    mx = n_own;
+  } else {
+    for (int b = tid; b < B; b += kThreads) {
+      const int n = seq_of<false>(a, b).n_run;
+      t += n;
+      nz += n > 0;
+      mx = max(mx, n);
+    }
+    t = wave_sum(t);
+    nz = wave_sum(nz);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) {
+    s_plan[wave] = t;
+    s_plan[kWaves + wave] = nz;
+    s_plan[2 * kWaves + wave] = mx;
+  }
+  if (tid == 0) {
+    s_plan[3 * kWaves] = -1;
+    s_plan[3 * kWaves + 1] = 0;
+    s_plan[3 * kWaves + 2] = 0;
+  }
+  __syncthreads();
+  // the waves' totals, lane w holding wave w's, reduced across the wave
+  const int wt = lane < kWaves ? s_plan[lane] : 0;
+  const int wz = lane < kWaves ? s_plan[kWaves + lane] : 0;
+  const int T = wave_sum(wt), NZS = wave_sum(wz);
+  const int MX = wave_max(lane < kWaves ? s_plan[2 * kWaves + lane] : 0);
+  const int base = wave_sum(lane < wave ? wt : 0), base_nz = wave_sum(lane < wave ? wz : 0);
+  // runs per workgroup: an even share, and enough that no sequence (at most max_runs runs) spans
+  // more than max_pieces - 1 workgroups ((n - 1) / rpw + 2 at most)
+  int rpw = (int)(((int64_t)T + gridDim.x - 1) / gridDim.x);
+  const int floor_rpw = (int)(((int64_t)a.max_runs + a.max_pieces - 3) / (a.max_pieces - 2));
+  if (rpw < floor_rpw) rpw = floor_rpw;
+  if (rpw < 1) rpw = 1;
+  const int c = NZS > 0 ? min((int)gridDim.x / NZS, a.max_pieces - 1) : 0;  // aligned pieces per sequence
+  const bool aligned = c >= 1 && (MX + c - 1) / c <= rpw + kAlignSlack;
+  const int k = blockIdx.x;
+  TqPlan p;
+  p.rpw = rpw;
+  p.S = (int)min((int64_t)k * rpw, (int64_t)T);
+  p.E = min(p.S + rpw, T);
+  p.b = B;
+  p.R = p.E;
+  p.part0 = 0;
+  const int target = c > 0 ? k / c : 0;  // aligned: the target-th sequence with runs
+  // sequence b with n runs, its first run R and its rank among the sequences with runs: the partial
+  // count for the merge, and whether this workgroup's share starts in it
+  auto place = [&](int b, int n, int R, int rank) {
+    int parts = 0;
+    if (n > 0) {
+      if (aligned) {
+        const int ps = (n + c - 1) / c;  // runs per aligned piece of this sequence
+        const int pieces = (n + ps - 1) / ps;
+        parts = (pieces - 1) * units_of(ps) + units_of(n - (pieces - 1) * ps);
+        if (rank == target) {
+          s_plan[3 * kWaves] = b;
+          s_plan[3 * kWaves + 1] = ps;
+          s_plan[3 * kWaves + 2] = n;
+        }
+      } else {
+        for (int kk = R / rpw; kk <= (R + n - 1) / rpw; ++kk) parts += units_in_share(kk, rpw, R, n);
+        if (R <= p.S && p.S < R + n) {
+          s_plan[3 * kWaves] = b;
+          s_plan[3 * kWaves + 1] = R;
+          s_plan[3 * kWaves + 2] = n;
+        }
+      }
+    }
+    // (a sequence longer than the host's bound would have more partials than slots: those past
+    // the bound are neither computed nor merged)
+    if (k == 0) a.nsplit[b] = min(parts, a.max_parts);
+  };
+  if (one_pass) {
+    if (tid < B) place(tid, n_own, base + incl - n_own, base_nz + incl_nz - 1);
+  } else {
+    __syncthreads();
+    // exclusive prefixes of the run counts and of the sequences with runs, kThreads at a time
+    int carry = 0, carry_nz = 0;
+    for (int c0 = 0; c0 < B; c0 += kThreads) {
+      const int b = c0 + tid;
+      const int n = b < B ? seq_of<false>(a, b).n_run : 0;
+      const int in = wave_incl_scan(n, lane);
+      const int in_nz = wave_incl_scan(n > 0, lane);
+      if (lane == 63) {
+        s_plan[wave] = in;
+        s_plan[kWaves + wave] = in_nz;
+      }
+      __syncthreads();
+      const int ct = lane < kWaves ? s_plan[lane] : 0;
+      const int cz = lane < kWaves ? s_plan[kWaves + lane] : 0;
+      const int total = wave_sum(ct), total_nz = wave_sum(cz);
+      const int bs = carry + wave_sum(lane < wave ? ct : 0), bs_nz = carry_nz + wave_sum(lane < wave ? cz : 0);
+      if (b < B) place(b, n, bs + in - n, bs_nz + in_nz - 1);
+      carry += total;
+      carry_nz += total_nz;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const int found = s_plan[3 * kWaves];
+  if (found >= 0) {
+    const int f1 = s_plan[3 * kWaves + 1], n = s_plan[3 * kWaves + 2];
+    p.b = found;
+    if (aligned) {  // piece j of the sequence, runs [j ps, (j + 1) ps)
+      const int j = k - target * c, ps = f1;
+      p.R = 0;
+      p.S = min(n, j * ps);
+      p.E = min(n, j * ps + ps);
+      p.rpw = INT_MAX;
+      p.part0 = j * units_of(ps);
+    } else {  // units of the earlier shares in the first sequence
+      p.R = f1;
+      for (int kk = f1 / rpw; kk < k; ++kk) p.part0 += units_in_share(kk, rpw, f1, n);
+    }
+  }
+  // The values are the same in every lane (LDS reads and cross-lane sums the compiler cannot
+  // prove uniform): in scalar registers the unit loops branch on scalars.
+  p.S = __builtin_amdgcn_readfirstlane(p.S);
+  p.E = __builtin_amdgcn_readfirstlane(p.E);
+  p.R = __builtin_amdgcn_readfirstlane(p.R);
+  p.rpw = __builtin_amdgcn_readfirstlane(p.rpw);
+  p.b = __builtin_amdgcn_readfirstlane(p.b);
+  p.part0 = __builtin_amdgcn_readfirstlane(p.part0);
+  return p;
+}
+
+// The units of a plan in order: f(seq, b, run_first, n_run, part) is called in the same order,
+// with the same wave-uniform values, in every wave.
+template <typename Fn>
+__device__ __forceinline__ void for_each_unit(const TqBlockArgs& a, const TqPlan& p, Fn&& f) {
+  int R = p.R, part = p.part0;
+  for (int b = p.b; R < p.E && b < a.num_seqs; ++b) {
+    const TqSeq sq = seq_of<true>(a, b);
+    const int hi = min(p.E, R + sq.n_run);
+    for (int u0 = max(p.S, R); u0 < hi && part < a.max_parts; u0 += kMaxRuns, ++part)
+      f(sq, b, sq.run0 + (u0 - R), min(kMaxRuns, hi - u0), part);
+    R += sq.n_run;
+    part = 0;  // a later sequence starts in this share
+  }
+}
+
+template <int KB, int VB, int GM>
+__global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a) {
+  using F = Fmt<KB, VB, GM>;
+  constexpr int kSB = F::kSB, kVOff = F::kVOff, kRowBytes = F::kRowBytes, kRunBytes = F::kRunBytes;
+  constexpr int kBuf0 = F::kBuf0, QC = F::kGroupChunks, NZ = F::kNZ;
+  // One LDS array placed by hand: the tables at byte 0, run buffer k at kBuf0 + k run bytes, then
+  // the query region (unless the last buffer holds the queries) and the plan words.  Only the
+  // producer waves have loads in flight, and they read no LDS, so the compute waves' reads need no
   // alias information to stay clear of pending loads.
-  __shared__ __align__(16) uint8_t s_lds[kLdsBytes];
+  __shared__ __align__(16) uint8_t s_lds[F::kLdsBytes];
   uint2* const s_tab = reinterpret_cast<uint2*>(s_lds);
   uint8_t* const s_r0 = s_lds + kBuf0;
   uint8_t* const s_r1 = s_r0 + kRunBytes;
   uint8_t* const s_r2 = s_r1 + kRunBytes;
   uint8_t* const s_r3 = s_r2 + kRunBytes;
   uint8_t* const s_r4 = s_r3 + kRunBytes;
+  int* const s_plan = reinterpret_cast<int*>(s_lds + F::kPlanOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -208,99 +458,91 @@ __global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a
   const int t16 = lane & 15, q4 = lane >> 4;
   const int G = a.G;
 
-  // Centroid operand table: entry e (a code byte: coordinates 2j, 2j + 1 in its low and high
-  // nibble) holds the fp16 high parts of c[e & 15], c[e >> 4], then their low parts, scaled by
-  // 2^8; copy k of entry e at byte 256 e + 8 k.
-  for (int i = tid; i < 256 * kCP; i += kT + 256) {
+  // this thread's sequence's run count for the work plan, loaded first so that it overlaps the
+  // table fill
+  const int n_own = tid < a.num_seqs ? seq_of<false>(a, tid).n_run : 0;
+
+  // Centroid operand tables: entry e (a code group: coordinates 2j, 2j + 1 in its low and high
+  // half) holds the fp16 high parts of both centroids, then their low parts, scaled by 2^8; copy
+  // k of entry e at byte 256 e + 8 k.  The V table (if any) follows the K table.
+  for (int i = tid; i < (F::kKEnt + F::kVEnt) * kCP; i += kThreads) {
     const int e = i / kCP;
+    float c0, c1;
+    if (e < F::kKEnt) {
+      c0 = a.kc[e & ((1 << KB) - 1)];
+      c1 = a.kc[e >> KB];
+    } else {
+      const int ev = e - F::kKEnt;
+      c0 = a.vc[ev & ((1 << VB) - 1)];
+      c1 = a.vc[ev >> VB];
+    }
     uint32_t h0, l0, h1, l1;
-    split_half(ldexpf(a.c[e & 15], kLutShift), h0, l0);
-    split_half(ldexpf(a.c[e >> 4], kLutShift), h1, l1);
+    split_half(ldexpf(c0, kLutShift), h0, l0);
+    split_half(ldexpf(c1, kLutShift), h1, l1);
     s_tab[i] = make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
   }
   // The run buffers are written by the loads (which the compiler does not see as stores): one
   // ordinary store keeps it from treating the array as never written there.
   if (tid == 0) s_r0[0] = 0;
 
+  const TqPlan plan = make_plan(a, s_plan, tid, wave, lane, n_own);  // its barriers also cover the tables
+
   if (wave >= kW) {
     // ======== producer waves: every page load of the workgroup ========
-    // Run r goes to buffer r mod 5 in 17 loads of 1 KB (LDS chunks 64 k + lane); producer p issues
-    // loads k = p, p + 4, ... of every run.  One wave issues such loads at about a fifth of the
-    // rate the memory system serves a compute unit, so a run's loads are spread over four waves.
-    // While the compute waves read run s + 1, runs s + 2 .. s + 5 are in flight.  The compute
-    // waves never issue a vector memory instruction in the loop, so a busy load path stalls these
-    // waves only.
-    const int pw = wave - kW;           // producer 0..3
-    const int nk = pw == 0 ? 5 : 4;     // loads per run of this producer
-    int src_off[5];
+    // Run r goes to buffer r mod 5 in kLoads loads of 1 KB (LDS chunks 64 k + lane); producer p
+    // issues loads k = p, p + 4, ... of every run.  One wave issues such loads at about a fifth
+    // of the rate the memory system serves a compute unit, so a run's loads are spread over four
+    // waves.  While the compute waves read run s + 1, runs s + 2 .. s + 5 are in flight.  The
+    // compute waves never issue a vector memory instruction in the loop, so a busy load path
+    // stalls these waves only.
+    const int pw = wave - kW;                        // producer 0..3
+    const bool more = pw < F::kLoads % kNP;          // this producer issues kLoadsHi loads a run
+    int src_off[F::kLoadsHi];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) src_off[i] = 16 * run_chunk_at(64 * min(pw + 4 * i, 16) + lane);
-    for (int unit = blockIdx.x; unit < a.n_units; unit += gridDim.x) {
-      const TqUnit u = unit_of(a, unit);
-      if (!u.live) continue;
-      const int n_run = u.n_run;
-      lds_barrier();  // every wave is done with the previous unit's buffers
-      // page rows of runs run0 + lane, + 64, + 128 (clamped to the last run)
-      int rows0 = 0, rows1 = 0, rows2 = 0;
-      if (n_run > 0) {
-        rows0 = run_row(a, u.b, u.run0 + min(lane, n_run - 1));
-        rows1 = run_row(a, u.b, u.run0 + min(lane + 64, n_run - 1));
-        rows2 = run_row(a, u.b, u.run0 + min(lane + 128, n_run - 1));
+    for (int i = 0; i < F::kLoadsHi; ++i)
+      src_off[i] = 16 * run_chunk_at<QC>(64 * min(pw + 4 * i, F::kLoads - 1) + lane);
+    // wait for this wave's loads of the oldest run in flight, `later` runs being issued after it
+    auto wait_later = [&](int later) {
+      if (later >= 3) {
+        if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * F::kLoadsHi));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * F::kLoadsLo));
+      } else if (later == 2) {
+        if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * F::kLoadsHi));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * F::kLoadsLo));
+      } else if (later == 1) {
+        if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(F::kLoadsHi));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(F::kLoadsLo));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
+    };
+    for_each_unit(a, plan, [&](const TqSeq&, int b, int run_first, int n_run, int) {
+      lds_barrier();  // every wave is done with the previous unit's buffers
+      // page rows of runs run_first + lane, + 64, + 128 (clamped to the last run)
+      const int rows0 = run_row(a, b, run_first + min(lane, n_run - 1));
+      const int rows1 = run_row(a, b, run_first + min(lane + 64, n_run - 1));
+      const int rows2 = run_row(a, b, run_first + min(lane + 128, n_run - 1));
       auto issue = [&](int r, lds_u8* buf) {
         const int row = r < 64 ? __builtin_amdgcn_readlane(rows0, r)
                                : r < 128 ? __builtin_amdgcn_readlane(rows1, r - 64)
                                          : __builtin_amdgcn_readlane(rows2, r - 128);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.pages + (int64_t)row * kRowBytes, kRunBytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(rs, buf + 1024 * (pw + 4 * i), src_off[i]);
-        if (pw == 0) lds_dma16(rs, buf + 1024 * 16, src_off[4]);
+        for (int i = 0; i < F::kLoadsHi; ++i)
+          if (i < F::kLoadsLo || more) lds_dma16(rs, buf + 1024 * (pw + 4 * i), src_off[i]);
       };
-      // wait for this wave's loads of run r, with those of the later runs (up to three) in flight
-      auto wait_run = [&](int r) {
-        const int later = min(n_run - 1, r + 3) - r;
-        if (later >= 3) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
-        } else if (later == 2) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-        } else if (later == 1) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        } else {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-      };
-      (void)nk;
-      // runs 0..3 (buffer 4 holds the compute waves' queries until the first barrier)
-      if (n_run > 0) issue(0, lds_ptr(s_r0));
+      // runs 0..3 (the last buffer may hold the compute waves' queries until the first barrier)
+      issue(0, lds_ptr(s_r0));
       if (n_run > 1) issue(1, lds_ptr(s_r1));
       if (n_run > 2) issue(2, lds_ptr(s_r2));
       if (n_run > 3) issue(3, lds_ptr(s_r3));
-      if (n_run <= 0) continue;
-      // run 0 is in (runs 1..3 may be in flight; run 4 is not issued yet)
-      {
-        const int later = min(n_run - 1, 3);
-        if (later >= 3) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
-        } else if (later == 2) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-        } else if (later == 1) {
-          if (pw == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-        } else {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-      }
+      wait_later(min(n_run - 1, 3));  // run 0 is in
       lds_barrier();
       if (n_run > 4) issue(4, lds_ptr(s_r4));
       // step s: every producer waits for its loads of run s + 1, barrier (every wave is done with
       // run s), then they fetch run s + 5 into run s's buffer
       auto step = [&](int s, lds_u8* fill) {
-        if (s + 1 < n_run) wait_run(s + 1);
+        if (s + 1 < n_run) wait_later(min(n_run - 1, s + 4) - (s + 1));
         lds_barrier();
         if (s + 5 < n_run) issue(s + 5, fill);
       };
@@ -311,7 +553,7 @@ __global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a
         if (s + 3 < n_run) step(s + 3, lds_ptr(s_r3));
         if (s + 4 < n_run) step(s + 4, lds_ptr(s_r4));
       }
-    }
+    });
     return;
   }
 
@@ -321,193 +563,262 @@ __global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a
   const uint32_t kcopy = 8u * (uint32_t)(lane & 31);
 
   // ---- per-lane LDS offsets within a run buffer (the same for every run) ----
-  // K codes of token t16, bytes 16 q4 .. 16 q4 + 15 of the K region, as two 8-byte reads; lanes
-  // with odd q4 read the upper half first (the two halves of a 32-lane pass then use distinct
-  // banks).  Word order: w[0..1] = first read, w[2..3] = second.
-  // Each offset is held as an LDS address less 64 KB (opaque to the compiler), so a read adds the
-  // buffer's base minus 64 KB as the DS instruction's immediate offset: no address arithmetic
-  // per read for the four buffers whose base is below 128 KB.
+  // Each offset is held as an LDS address less kBuf0 (opaque to the compiler), so a read adds the
+  // buffer's base minus kBuf0 as the DS instruction's immediate offset: no address arithmetic per
+  // read for the four buffers whose base is within 64 KB of the first.
   auto lane_addr = [](int off) {
     int x = off + kBuf0;
     asm volatile("" : "+v"(x));
     return x;
   };
-  const int sw = q4 & 1;
-  const int kbase = kRowBytes * t16 + kSB * h + 16 * q4;
-  const int off_k0 = lane_addr(run_lds_offset(kbase + 8 * sw));
-  const int off_k1 = lane_addr(run_lds_offset(kbase + 8 * (1 - sw)));
-  const int off_kn = lane_addr(run_lds_offset(kRowBytes * t16 + kSB * h + 64));
-  const int off_vn = lane_addr(run_lds_offset(kRowBytes * t16 + kSB * h + kVOff + 64));
-  // V codes: dword t16 (coordinates 8 t16 .. 8 t16 + 7) of tokens q4 + 4 m, m = 0..3
+  // K codes of position t16, the lane's coordinates 32 q4 .. 32 q4 + 31.  4-bit codes: bytes
+  // 16 q4 .. 16 q4 + 15 as two 8-byte reads, lanes with odd q4 reading the upper half first (the
+  // two halves of a 32-lane pass then use distinct banks); word order w[0..1] = first read,
+  // w[2..3] = second.  3-bit codes: bytes 12 q4 .. 12 q4 + 11 as three dword reads.
+  const int sw = KB == 4 ? (q4 & 1) : 0;
+  const int kbase = kRowBytes * t16 + kSB * h + (kD * KB / 32) * q4;
+  int off_k[3];
+  if constexpr (KB == 4) {
+    off_k[0] = lane_addr(run_lds_offset<QC>(kbase + 8 * sw));
+    off_k[1] = lane_addr(run_lds_offset<QC>(kbase + 8 * (1 - sw)));
+    off_k[2] = 0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) off_k[i] = lane_addr(run_lds_offset<QC>(kbase + 4 * i));
+  }
+  const int off_kn = lane_addr(run_lds_offset<QC>(kRowBytes * t16 + kSB * h + F::kKCode));
+  const int off_vn = lane_addr(run_lds_offset<QC>(kRowBytes * t16 + kSB * h + kVOff + F::kVCode));
+  // V codes of positions q4 + 4 m, m = 0..3: coordinates 8 t16 .. 8 t16 + 7 (a dword of 4-bit
+  // codes, 16 bits of 2-bit codes)
   int off_v[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    off_v[m] = lane_addr(run_lds_offset(kRowBytes * (q4 + 4 * m) + kSB * h + kVOff + 4 * t16));
+    off_v[m] = lane_addr(run_lds_offset<QC>(kRowBytes * (q4 + 4 * m) + kSB * h + kVOff + VB * t16));
   // read of buffer `buf` at lane address x
   auto at = [&](const uint8_t* buf, int x) { return buf - kBuf0 + x; };
-  // PV weight gather: row t16 of the A operand is (head t16 >> 2, nibble (t16 >> 1) & 1, weight
-  // part t16 & 1); it takes the weights of tokens q4 + 4 m from softmax lane 16 (t16 >> 2) + token.
+  // PV weight gather: row t16 of row set z is (query head NZ (t16 >> 2) + z, coordinate (t16 >> 1)
+  // & 1 of the code group, weight part t16 & 1); it takes the weights of positions q4 + 4 m from
+  // softmax lane 16 (t16 >> 2) + position.
   const int bp_base = 4 * (16 * (t16 >> 2) + q4);
   const uint32_t bp_sel = ((t16 >> 1) & 1) ? ((t16 & 1) ? 0x03020c0cu : 0x01000c0cu)
                                            : ((t16 & 1) ? 0x0c0c0302u : 0x0c0c0100u);
+  uint8_t* const qreg = F::kQInRing ? s_r4 + h * (kRunBytes / kW) : s_lds + F::kQBase + h * F::kQBytes;
 
-  for (int unit = blockIdx.x; unit < a.n_units; unit += gridDim.x) {
-    const TqUnit u = unit_of(a, unit);
-    if (!u.live) continue;
-    const int b = u.b, n_run = u.n_run, run0 = u.run0;
-
-    lds_barrier();  // every wave is done with the previous unit's buffers
-
-    // This wave's fp16 queries (4 rows of 256 bytes) into its 2176-byte region of buffer 4, which
-    // takes a run only after the first step's barrier.
-    uint8_t* const qreg = s_r4 + h * (kWaveChunks * 16);
-    {
-      const int g = q4 < G ? q4 : 0;  // query heads past G read a live row, unused
-      const int64_t r0q = q_row(a, b, h, 0);
-      const int dq = (int)(q_row(a, b, h, g) - r0q) * (2 * kD) + 16 * t16;  // bytes from head row 0
-      lds_dma16(buffer_rsrc(a.q + r0q * kD, INT_MAX), lds_ptr(s_r4) + h * (kWaveChunks * 16), dq);  // rows of later queries lie Hq rows on
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-
-    // ---- rotated queries H (s * q): lane (g = q4, j = t16) holds coordinates 8 j .. 8 j + 7 ----
-    float qmax_l;
-    {
-      float x[8];
-      const uint4 raw = *reinterpret_cast<const uint4*>(qreg + 16 * lane);
-      const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = half_bits_to_float(qw[i] & 0xffffu);
-        x[2 * i + 1] = half_bits_to_float(qw[i] >> 16);
-      }
-      const int j = t16;
-      const uint32_t swd = j < 4 ? a.signs.w[0] : j < 8 ? a.signs.w[1] : j < 12 ? a.signs.w[2] : a.signs.w[3];
-      const uint32_t sb = (swd >> (8 * (j & 3))) & 0xffu;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((sb >> e) & 1u) x[e] = -x[e];
-      wht_row8_dpp<16>(x, j);
-      float mx = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
-      qmax_l = max16(mx) * a.qscale;
-      // rotated rows as fp32 [4][128] over the raw rows (this wave's region; LDS keeps its order)
-      float4* d = reinterpret_cast<float4*>(qreg + 512 * q4 + 32 * j);
-      d[0] = make_float4(x[0], x[1], x[2], x[3]);
-      d[1] = make_float4(x[4], x[5], x[6], x[7]);
-    }
-    // scale exponent of head g: its largest |q| * qscale lands near 2^13
-    const float qm0 = lane_value(qmax_l, 0), qm1 = lane_value(qmax_l, 16);
-    const float qm2 = lane_value(qmax_l, 32), qm3 = lane_value(qmax_l, 48);
-    auto head_exp = [&](int g) {
-      const float qm = g == 0 ? qm0 : g == 1 ? qm1 : g == 2 ? qm2 : qm3;
-      return qm > 0.0f ? 13 - ilogbf(qm) : 0;
-    };
-
-    // QK A operand, step mi: row t16 = (query head t16 >> 2, fp16 part t16 & 1; rows with
-    // (t16 >> 1) & 1 are zero); K holds the coordinates of code bytes 2 mi, 2 mi + 1 of this
-    // lane's word order, [x_a, x_b, x_a, x_b, x_c, x_d, x_c, x_d] against the centroid parts
-    // [hi, hi, lo, lo, hi, hi, lo, lo].
-    uint4 aq[8];
-    {
-      const int g = t16 >> 2;
-      const bool live = ((t16 >> 1) & 1) == 0 && g < G;
-      const bool lo_part = t16 & 1;
-      const float f = live ? ldexpf(a.qscale, head_exp(g)) : 0.0f;
-      // this lane's 32 coordinates 32 q4 .. 32 q4 + 31 in word order (upper 16 first if sw)
-      const uint8_t* src = qreg + 512 * (live ? g : 0);
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c4 = (i + 4 * sw) & 7;  // 4-coordinate group at word-order position i
-        const float4 v = *reinterpret_cast<const float4*>(src + 128 * q4 + 16 * c4);
-        x[4 * i] = v.x;
-        x[4 * i + 1] = v.y;
-        x[4 * i + 2] = v.z;
-        x[4 * i + 3] = v.w;
-      }
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi) {
-        uint32_t p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t hi, lo;
-          split_half(live ? x[4 * mi + i] * f : 0.0f, hi, lo);
-          p[i] = lo_part ? lo : hi;
-        }
-        const uint32_t ab = p[0] | (p[1] << 16), cd = p[2] | (p[3] << 16);
-        aq[mi] = make_uint4(ab, ab, cd, cd);
-      }
-    }
-    // softmax lane: token t16, query head g0 = q4
-    const int g0 = q4;
-    const bool live0 = g0 < G;
-    const float f0 = live0 ? ldexpf(1.0f, -(head_exp(g0) + kLutShift)) : 0.0f;
-    const int lim0 = min(u.end, u.seq_len - a.nq + a.q0 + g0 / a.g_real + 1);  // causal limit of head g0
-    const int lo_l = u.ns - t16;                                              // p >= ns
-    const int hi_l = live0 ? lim0 - t16 : INT_MIN;                            // p < lim0
-
-    float m_s = kSent, m_w = kSent, l_s = 0.0f;
-    float t_s = kSent + kThr, t_w = kSent + kThr, m_b = kSent - (float)kWShift;  // thresholds, weight base
-    float4_t acc[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // ---- key half of one run: table entries of this lane's 16 code bytes, and the norms ----
-    auto key_codes = [&](const uint8_t* buf, uint32_t (&w)[4], float& kn, float& vn) {
-      const u32x2 r0 = *reinterpret_cast<const u32x2*>(at(buf, off_k0));
-      const u32x2 r1 = *reinterpret_cast<const u32x2*>(at(buf, off_k1));
-      kn = *reinterpret_cast<const float*>(at(buf, off_kn));
-      vn = *reinterpret_cast<const float*>(at(buf, off_vn));
+  // ---- key half of one run: table entries of this lane's 16 code groups, and the norms ----
+  auto key_codes = [&](const uint8_t* buf, uint32_t (&w)[4], float& kn, float& vn) {
+    if constexpr (KB == 4) {
+      const u32x2 r0 = *reinterpret_cast<const u32x2*>(at(buf, off_k[0]));
+      const u32x2 r1 = *reinterpret_cast<const u32x2*>(at(buf, off_k[1]));
       w[0] = r0.x;
       w[1] = r0.y;
       w[2] = r1.x;
       w[3] = r1.y;
-    };
-    auto key_lookup = [&](const uint32_t (&w)[4], uint2 (&ke)[16]) {
+    } else {
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi) {
+      for (int i = 0; i < 3; ++i) w[i] = *reinterpret_cast<const uint32_t*>(at(buf, off_k[i]));
+      w[3] = 0;
+    }
+    kn = *reinterpret_cast<const float*>(at(buf, off_kn));
+    vn = *reinterpret_cast<const float*>(at(buf, off_vn));
+  };
+  auto key_lookup = [&](const uint32_t (&w)[4], uint2 (&ke)[16], int e0 = 0, int e1 = 16) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t byte = 2 * (mi & 1) + j;
-          const uint32_t off = __builtin_amdgcn_perm(w[mi >> 1], kcopy, 0x0c0c0000u | ((4u + byte) << 8));
-          ke[2 * mi + j] = *reinterpret_cast<const uint2*>(tab + off);
+    for (int e = e0; e < e1; ++e) {
+      uint32_t off;
+      if constexpr (KB == 4) {  // byte e of the word order
+        off = __builtin_amdgcn_perm(w[e >> 2], kcopy, 0x0c0c0000u | ((4u + (e & 3)) << 8));
+      } else {  // bits 6 e .. 6 e + 5 of the lane's 96 code bits, moved to bits 8 .. 13
+        const int P = 6 * e;
+        uint32_t x;
+        if (P < 8) {
+          x = w[0] << (8 - P);
+        } else {
+          const int s = P - 8, j = s >> 5, sh = s & 31;
+          x = j + 1 < 3 ? __builtin_amdgcn_alignbit(w[j + 1], w[j], sh) : (w[j] >> sh);
+        }
+        off = (x & 0x3f00u) | kcopy;
+      }
+      ke[e] = *reinterpret_cast<const uint2*>(tab + off);
+    }
+  };
+
+  // value entries of one run: positions (q4, q4 + 4) then (q4 + 8, q4 + 12), code group mi of the
+  // lane's 8 coordinates
+  auto value_codes = [&](const uint8_t* buf, uint32_t (&cw)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if constexpr (VB == 4) cw[m] = *reinterpret_cast<const uint32_t*>(at(buf, off_v[m]));
+      else cw[m] = *reinterpret_cast<const uint16_t*>(at(buf, off_v[m]));
+    }
+  };
+  auto value_entry = [&](uint32_t x, int mi) {
+    uint32_t off;
+    if constexpr (VB == 4) {
+      off = __builtin_amdgcn_perm(x, kcopy, 0x0c0c0000u | ((4u + mi) << 8));
+    } else {  // nibble mi moved to bits 8 .. 11
+      const uint32_t y = mi == 0 ? x << 8 : mi == 1 ? x << 4 : mi == 2 ? x : x >> 4;
+      off = (y & 0xf00u) | kcopy;
+    }
+    return *reinterpret_cast<const uint2*>(tab + F::kVTab + off);
+  };
+  auto value_lookup = [&](const uint32_t (&cw)[4], uint2 (&ve)[16]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        ve[8 * hf + 2 * mi] = value_entry(cw[2 * hf], mi);
+        ve[8 * hf + 2 * mi + 1] = value_entry(cw[2 * hf + 1], mi);
+      }
+    }
+  };
+
+  for_each_unit(a, plan, [&](const TqSeq& sq, int b, int run_first, int n_run, int part) {
+    lds_barrier();  // every wave is done with the previous unit's buffers
+
+    // Unit state: QK operands of the rotated queries, the softmax references and sums of the
+    // lane's NZ query heads, and the PV accumulators.
+    uint4 aq[8];
+    float f_z[NZ], m_s[NZ], m_w[NZ], l_s[NZ], t_s[NZ], t_w[NZ], m_b[NZ];
+    float4_t acc[NZ][4];
+    {
+      // This wave's fp16 queries (rows of 256 bytes, four per pass) into its query region, whose
+      // ring buffer (if any) takes a run only after the first step's barrier.
+      {
+        const int64_t r0q = q_row(a, b, h, 0);
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + r0q * kD, INT_MAX);
+#pragma unroll
+        for (int zz = 0; zz < NZ; ++zz) {
+          const int g = 4 * zz + q4 < G ? 4 * zz + q4 : 0;  // query heads past G read a live row, unused
+          const int dq = (int)(q_row(a, b, h, g) - r0q) * (2 * kD) + 16 * t16;  // bytes from head row 0
+          lds_dma16(rq, lds_ptr(qreg) + 1024 * zz, dq);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      // rotated queries H (s * q): pass zz, lane (g = 4 zz + q4, j = t16) holds coordinates 8 j ..
+      // 8 j + 7; rotated rows as fp32 [GM][128] over the raw rows (LDS keeps this wave's order)
+      float qmax_l[NZ];
+      {
+        float x[NZ][8];
+#pragma unroll
+        for (int zz = 0; zz < NZ; ++zz) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(qreg + 1024 * zz + 16 * lane);
+          const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[zz][2 * i] = half_bits_to_float(qw[i] & 0xffffu);
+            x[zz][2 * i + 1] = half_bits_to_float(qw[i] >> 16);
+          }
+        }
+        const int j = t16;
+        const uint32_t swd = j < 4 ? a.signs.w[0] : j < 8 ? a.signs.w[1] : j < 12 ? a.signs.w[2] : a.signs.w[3];
+        const uint32_t sb = (swd >> (8 * (j & 3))) & 0xffu;
+#pragma unroll
+        for (int zz = 0; zz < NZ; ++zz) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if ((sb >> e) & 1u) x[zz][e] = -x[zz][e];
+          wht_row8_dpp<16>(x[zz], j);
+          float mx = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[zz][e]));
+          qmax_l[zz] = max16(mx) * a.qscale;
+        }
+#pragma unroll
+        for (int zz = 0; zz < NZ; ++zz) {
+          float4* d = reinterpret_cast<float4*>(qreg + 512 * (4 * zz + q4) + 32 * j);
+          d[0] = make_float4(x[zz][0], x[zz][1], x[zz][2], x[zz][3]);
+          d[1] = make_float4(x[zz][4], x[zz][5], x[zz][6], x[zz][7]);
         }
       }
-    };
-    // QK: this lane's score (token t16, head g0) before the norm and scales
-    auto key_mfma = [&](const uint2 (&ke)[16]) {
+      // scale exponent of head g: its largest |q| * qscale lands near 2^13
+      float qm[GM];
+#pragma unroll
+      for (int g = 0; g < GM; ++g) qm[g] = lane_value(qmax_l[g >> 2], 16 * (g & 3));
+      auto head_exp = [&](int g) {  // g may vary by lane
+        float v = qm[0];
+#pragma unroll
+        for (int k = 1; k < GM; ++k) v = g == k ? qm[k] : v;
+        return v > 0.0f ? 13 - ilogbf(v) : 0;
+      };
+
+      // QK A operand, step mi: row t16 = (query head, fp16 part t16 & 1) -- the head t16 >> 2,
+      // rows with (t16 >> 1) & 1 zero, when GM is 4, else t16 >> 1; K holds the coordinates of
+      // code groups 2 mi, 2 mi + 1 of this lane's word order, [x_a, x_b, x_a, x_b, x_c, x_d, x_c,
+      // x_d] against the centroid parts [hi, hi, lo, lo, hi, hi, lo, lo].
+      {
+        const int hd = GM == 4 ? t16 >> 2 : t16 >> 1;
+        const bool live = (GM == 8 || ((t16 >> 1) & 1) == 0) && hd < G;
+        const bool lo_part = t16 & 1;
+        const float f = live ? ldexpf(a.qscale, head_exp(hd)) : 0.0f;
+        // this lane's 32 coordinates 32 q4 .. 32 q4 + 31 in word order (upper 16 first if sw)
+        const uint8_t* src = qreg + 512 * (live ? hd : 0);
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c4 = (i + 4 * sw) & 7;  // 4-coordinate group at word-order position i
+          const float4 v = *reinterpret_cast<const float4*>(src + 128 * q4 + 16 * c4);
+          x[4 * i] = v.x;
+          x[4 * i + 1] = v.y;
+          x[4 * i + 2] = v.z;
+          x[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+          uint32_t pp[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t hi, lo;
+            split_half(live ? x[4 * mi + i] * f : 0.0f, hi, lo);
+            pp[i] = lo_part ? lo : hi;
+          }
+          const uint32_t ab = pp[0] | (pp[1] << 16), cd = pp[2] | (pp[3] << 16);
+          aq[mi] = make_uint4(ab, ab, cd, cd);
+        }
+      }
+      // softmax lane: position t16, query heads NZ q4 + z
+#pragma unroll
+      for (int z = 0; z < NZ; ++z) {
+        const int g = NZ * q4 + z;
+        f_z[z] = g < G ? ldexpf(1.0f, -(head_exp(g) + kLutShift)) : 0.0f;
+        m_s[z] = kSent;
+        m_w[z] = kSent;
+        l_s[z] = 0.0f;
+        t_s[z] = kSent + kThr;  // thresholds and weight base of the references
+        t_w[z] = kSent + kThr;
+        m_b[z] = kSent - (float)kWShift;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[z][c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+
+    // position masks of the softmax lane (position t16, query heads NZ q4 + z): p >= ns, and p
+    // below the packed end and the head's causal limit
+    // (as one unsigned compare: p - ns < span, span = 0 for dead heads)
+    const int lo_l = sq.ns - t16;
+    uint32_t span[NZ];
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) {
+      const int g = NZ * q4 + z;
+      const int lim = min(sq.end, sq.seq_len - a.nq + a.q0 + g / a.g_real + 1);
+      span[z] = g < G ? (uint32_t)max(lim - sq.ns, 0) : 0u;
+    }
+
+    // QK: this lane's scores (position t16, heads NZ q4 + z) before the norm and scales
+    auto key_mfma = [&](const uint2 (&ke)[16], float (&sc)[NZ]) {
       float4_t sa = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
         sa = mfma16(aq[mi], make_uint4(ke[2 * mi].x, ke[2 * mi].y, ke[2 * mi + 1].x, ke[2 * mi + 1].y), sa);
-      return sa[0] + sa[1];
+#pragma unroll
+      for (int z = 0; z < NZ; ++z) sc[z] = sa[2 * z] + sa[2 * z + 1];
     };
 
-    // value entries of one run: tokens (q4, q4 + 4) then (q4 + 8, q4 + 12), code byte mi of dword t16
-    auto value_lookup = [&](const uint32_t (&cw)[4], uint2 (&ve)[16]) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const uint32_t sel = 0x0c0c0000u | ((4u + mi) << 8);
-          ve[8 * hf + 2 * mi] = *reinterpret_cast<const uint2*>(tab + __builtin_amdgcn_perm(cw[2 * hf], kcopy, sel));
-          ve[8 * hf + 2 * mi + 1] =
-              *reinterpret_cast<const uint2*>(tab + __builtin_amdgcn_perm(cw[2 * hf + 1], kcopy, sel));
-        }
-      }
-    };
-    auto value_codes = [&](const uint8_t* buf, uint32_t (&cw)[4]) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) cw[m] = *reinterpret_cast<const uint32_t*>(at(buf, off_v[m]));
-    };
-
-    // Pipeline state carried from step s - 1: run s's raw scores and norms (token t16) and its value
-    // entries.  Step s issues run s + 1's key lookups, then does run s's softmax and PV, then
-    // issues run s + 1's value lookups (after PV has consumed run s's) and does run s + 1's QK.
-    // Table lookups stay in flight across the step barrier; every read of a run buffer is
+    // Pipeline state carried from step s - 1: run s's raw scores and norms (position t16) and its
+    // value entries.  Step s issues run s + 1's key lookups, then does run s's softmax and PV,
+    // then issues run s + 1's value lookups (after PV has consumed run s's) and does run s + 1's
+    // QK.  Table lookups stay in flight across the step barrier; every read of a run buffer is
     // consumed within its step, before the barrier that can release the buffer.
-    float sc = 0.0f, knf = 0.0f, lv = 0.0f;  // run s: raw score, n_K * f0, log2 n_V (token t16)
+    float sc[NZ], knf[NZ], lv = 0.0f;  // run s: raw scores, n_K * f_z, log2 n_V (position t16)
     uint2 ve[16];
     auto body = [&](int s, const uint8_t* nxt) {
       uint32_t kw[4], cw[4];
@@ -516,142 +827,183 @@ __global__ __launch_bounds__(kT + 256) void tq_decode_block_kernel(TqBlockArgs a
       value_codes(nxt, cw);
       __builtin_amdgcn_sched_barrier(0);  // the code reads go out first
       uint2 ke[16];
-      key_lookup(kw, ke);
+      // With eight query heads the second half of the key lookups waits until PV has used this
+      // run's value entries (registers)
+      key_lookup(kw, ke, 0, NZ == 1 ? 16 : 8);
 
-      // softmax of run s, lane (token t16, head g0); masked rows never touch their garbage norms.
-      // The references m_s (scores) and m_w (scores + log2 n_V) move only when some score passes
-      // them by more than kThr: terms stay below 2^kThr, weights below 2^(kWShift + kThr).
-      const int pb = (run0 + s) * 16;
-      const bool valid = pb >= lo_l && pb < hi_l;
-      const float s0 = valid ? sc * knf : -INFINITY;
-      const float sw0 = valid ? s0 + lv : -INFINITY;  // + log2(n_V)
-      if (__builtin_amdgcn_ballot_w64(s0 > t_s || sw0 > t_w) != 0) {
-        const float ns2 = fmaxf(m_s, max16(s0)), nw2 = fmaxf(m_w, max16(sw0));
-        l_s *= __builtin_amdgcn_exp2f(m_s - ns2);
-        const float r = __builtin_amdgcn_exp2f(m_w - nw2);
+      // softmax of run s, lane (position t16, heads NZ q4 + z); masked rows never touch their
+      // garbage norms.  The references m_s (scores) and m_w (scores + log2 n_V) move only when
+      // some score passes them by more than kThr: terms stay below 2^kThr, weights below
+      // 2^(kWShift + kThr).
+      const int pb = (run_first + s) * 16;
+      float s0[NZ], sw0[NZ];
+      bool over = false;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] *= r;
-        m_s = ns2;
-        m_w = nw2;
-        t_s = m_s + kThr;
-        t_w = m_w + kThr;
-        m_b = m_w - (float)kWShift;
+      for (int z = 0; z < NZ; ++z) {
+        const bool valid = (uint32_t)(pb - lo_l) < span[z];
+        s0[z] = valid ? sc[z] * knf[z] : -INFINITY;
+        sw0[z] = valid ? s0[z] + lv : -INFINITY;  // + log2(n_V)
+        // (eight heads: the thresholds are recomputed, which saves their registers)
+        if constexpr (NZ == 1) over = over || s0[z] > t_s[z] || sw0[z] > t_w[z];
+        else over = over || s0[z] > m_s[z] + kThr || sw0[z] > m_w[z] + kThr;
       }
-      l_s += __builtin_amdgcn_exp2f(s0 - m_s);
-      const float wt = __builtin_amdgcn_exp2f(sw0 - m_b);
-      const auto h2 = __builtin_amdgcn_cvt_pkrtz(wt, 0.0f);
-      const auto p2 = __builtin_amdgcn_cvt_pkrtz(wt, wt - (float)h2[0]);
-      const uint32_t wpk = __builtin_bit_cast(uint32_t, p2);  // both fp16 parts of the weight
-
-      // PV A operands: tokens q4 + 4 m of head t16 >> 2, one weight part, at the row's nibble
-      uint32_t wg[4];
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) wg[m] = __builtin_amdgcn_ds_bpermute(bp_base + 16 * m, wpk);
-      uint32_t d[4];
+        for (int z = 0; z < NZ; ++z) {
+          const float ns2 = fmaxf(m_s[z], max16(s0[z])), nw2 = fmaxf(m_w[z], max16(sw0[z]));
+          l_s[z] *= __builtin_amdgcn_exp2f(m_s[z] - ns2);
+          const float r = __builtin_amdgcn_exp2f(m_w[z] - nw2);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) d[m] = __builtin_amdgcn_perm(wg[m], wg[m], bp_sel);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint4 aw = make_uint4(d[2 * hf], d[2 * hf], d[2 * hf + 1], d[2 * hf + 1]);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const uint2 e0 = ve[8 * hf + 2 * mi], e1 = ve[8 * hf + 2 * mi + 1];
-          acc[mi] = mfma16(aw, make_uint4(e0.x, e0.y, e1.x, e1.y), acc[mi]);
+          for (int c = 0; c < 4; ++c) acc[z][c] *= r;
+          m_s[z] = ns2;
+          m_w[z] = nw2;
+          t_s[z] = ns2 + kThr;
+          t_w[z] = nw2 + kThr;
+          m_b[z] = nw2 - (float)kWShift;
         }
       }
-      value_lookup(cw, ve);  // run s + 1
-      sc = key_mfma(ke);
+#pragma unroll
+      for (int z = 0; z < NZ; ++z) {
+        l_s[z] += __builtin_amdgcn_exp2f(s0[z] - m_s[z]);
+        const float wt = __builtin_amdgcn_exp2f(sw0[z] - (NZ == 1 ? m_b[z] : m_w[z] - (float)kWShift));
+        const auto h2 = __builtin_amdgcn_cvt_pkrtz(wt, 0.0f);
+        const auto p2 = __builtin_amdgcn_cvt_pkrtz(wt, wt - (float)h2[0]);
+        const uint32_t wpk = __builtin_bit_cast(uint32_t, p2);  // both fp16 parts of the weight
+
+        // PV A operands: positions q4 + 4 m of head NZ (t16 >> 2) + z, one weight part, at the
+        // row's coordinate of the code group
+        uint32_t wg[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) wg[m] = __builtin_amdgcn_ds_bpermute(bp_base + 16 * m, wpk);
+        uint32_t d[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d[m] = __builtin_amdgcn_perm(wg[m], wg[m], bp_sel);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint4 aw = make_uint4(d[2 * hf], d[2 * hf], d[2 * hf + 1], d[2 * hf + 1]);
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const uint2 e0 = ve[8 * hf + 2 * mi], e1 = ve[8 * hf + 2 * mi + 1];
+            acc[z][mi] = mfma16(aw, make_uint4(e0.x, e0.y, e1.x, e1.y), acc[z][mi]);
+          }
+        }
+      }
+      if constexpr (NZ == 1) {
+        value_lookup(cw, ve);  // run s + 1
+        key_mfma(ke, sc);
+      } else {  // the value lookups follow QK and stay in flight across the barrier
+        key_lookup(kw, ke, 8, 16);
+        key_mfma(ke, sc);
+        value_lookup(cw, ve);
+      }
       // the norms of run s + 1 are used here, so no read of its buffer outlives the step
-      knf = kn1 * f0;
+#pragma unroll
+      for (int z = 0; z < NZ; ++z) knf[z] = kn1 * f_z[z];
       lv = __builtin_amdgcn_logf(vn1);
     };
 
-    if (n_run > 0) {
-      lds_barrier();  // run 0 is in
-      {
-        uint32_t kw[4], cw[4];
-        uint2 ke[16];
-        float kn0, vn0;
-        key_codes(s_r0, kw, kn0, vn0);
-        value_codes(s_r0, cw);
-        key_lookup(kw, ke);
-        value_lookup(cw, ve);
-        sc = key_mfma(ke);
-        knf = kn0 * f0;
-        lv = __builtin_amdgcn_logf(vn0);
-      }
-      // step s: barrier (run s + 1 is in; run s's buffer, read and used up by step s - 1, may be
-      // refilled), then the body.  After the last run the body reads a buffer that holds no run;
-      // its results are unused.
-      for (int s = 0; s < n_run; s += kRing) {
+    lds_barrier();  // run 0 is in
+    {
+      uint32_t kw[4], cw[4];
+      uint2 ke[16];
+      float kn0, vn0;
+      key_codes(s_r0, kw, kn0, vn0);
+      value_codes(s_r0, cw);
+      key_lookup(kw, ke);
+      value_lookup(cw, ve);
+      key_mfma(ke, sc);
+#pragma unroll
+      for (int z = 0; z < NZ; ++z) knf[z] = kn0 * f_z[z];
+      lv = __builtin_amdgcn_logf(vn0);
+    }
+    // step s: barrier (run s + 1 is in; run s's buffer, read and used up by step s - 1, may be
+    // refilled), then the body.  After the last run the body reads a buffer that holds no run;
+    // its results are unused.
+    for (int s = 0; s < n_run; s += kRing) {
+      step_barrier();
+      body(s, s_r1);
+      if (s + 1 < n_run) {
         step_barrier();
-        body(s, s_r1);
-        if (s + 1 < n_run) {
-          step_barrier();
-          body(s + 1, s_r2);
-        }
-        if (s + 2 < n_run) {
-          step_barrier();
-          body(s + 2, s_r3);
-        }
-        if (s + 3 < n_run) {
-          step_barrier();
-          body(s + 3, s_r4);
-        }
-        if (s + 4 < n_run) {
-          step_barrier();
-          body(s + 4, s_r0);
-        }
+        body(s + 1, s_r2);
+      }
+      if (s + 2 < n_run) {
+        step_barrier();
+        body(s + 2, s_r3);
+      }
+      if (s + 3 < n_run) {
+        step_barrier();
+        body(s + 3, s_r4);
+      }
+      if (s + 4 < n_run) {
+        step_barrier();
+        body(s + 4, s_r0);
       }
     }
 
-    // ---- this wave's partial for head g0: coordinates 8 t16 + 2 mi + nibble ----
-    l_s += dpp<kDppQuadXor1>(l_s);
-    l_s += dpp<kDppQuadXor2>(l_s);
-    l_s += dpp<kDppHalfRowMirror>(l_s);
-    l_s += dpp<kDppRowMirror>(l_s);
-    if (live0) {
-      const float c0 = __builtin_amdgcn_exp2f(m_w - m_s) * ldexpf(1.0f, -(kWShift + kLutShift));
-      float* part = a.partials + ((((int64_t)b * kH + h) * a.part_stride + u.split) * G + g0) * (kD + 2);
-      float2* o = reinterpret_cast<float2*>(part + 2 + 8 * t16);
+    {
+      // ---- this wave's partials for heads NZ q4 + z: coordinates 8 t16 + 2 mi + (0, 1) ----
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        o[mi] = make_float2((acc[mi][0] + acc[mi][1]) * c0, (acc[mi][2] + acc[mi][3]) * c0);
-      if (t16 == 0) *reinterpret_cast<float2*>(part) = make_float2(m_s, l_s);
+      for (int z = 0; z < NZ; ++z) {
+        const int g = NZ * q4 + z;
+        const float ls = sum16(l_s[z]);
+        if (g < G) {
+          const float c0 = __builtin_amdgcn_exp2f(m_w[z] - m_s[z]) * ldexpf(1.0f, -(kWShift + kLutShift));
+          float* pt = a.partials + ((((int64_t)b * kH + h) * a.part_stride + part) * G + g) * (kD + 2);
+          float2* o = reinterpret_cast<float2*>(pt + 2 + 8 * t16);
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+            o[mi] = make_float2((acc[z][mi][0] + acc[z][mi][1]) * c0, (acc[z][mi][2] + acc[z][mi][3]) * c0);
+          if (t16 == 0) *reinterpret_cast<float2*>(pt) = make_float2(m_s[z], ls);
+        }
+      }
     }
-  }
+  });
+}
+
+template <int KB, int VB, int GM>
+void launch_block(const TqBlockArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((tq_decode_block_kernel<KB, VB, GM>), dim3(kGrid), dim3(kThreads), 0, st, a);
 }
 
 }  // namespace
 
-// Whether the block-streaming kernel serves a format: K4/V4 at D = 128, eight kv heads, unpadded
-// plain slots (norm correction changes the stored norm only), one codebook array for keys and
-// values, page blocks of whole 16-position runs, at most four query heads per kv head.
+// Whether the block-streaming kernel serves a format: D = 128, eight kv heads, unpadded plain
+// slots (norm correction changes the stored norm only), page blocks of whole 16-position runs;
+// K4/V4 with one codebook array for keys and values and at most four query heads per kv head, or
+// K3/V2 with at most eight.
 bool tq_decode_block_format(const TqLayer& L) {
-  return L.D == 128 && L.kb == 4 && L.vb == 4 && L.Hkv == kH && L.stride == kSB && L.slot_bytes == kSB &&
-         !L.mean && !L.qjl && L.bs % 16 == 0 && L.G <= 4 && L.kc == L.vc;
+  if (!(L.D == 128 && L.Hkv == kH && L.stride == L.slot_bytes && !L.mean && !L.qjl && L.bs % 16 == 0))
+    return false;
+  if (L.kb == 4 && L.vb == 4) return L.G <= 4 && L.kc == L.vc;
+  if (L.kb == 3 && L.vb == 2) return L.G <= 8;
+  return false;
 }
 
-// Split geometry of the block kernel: about one (sequence, split) unit per compute unit, splits of
-// whole runs, at most kMaxRuns runs each.
+// Work geometry of the block kernel.  max_runs bounds a sequence's runs; max_pieces bounds the
+// workgroups one sequence spans: enough that the workgroups can share a few long sequences evenly,
+// few enough that a large batch keeps a small workspace.  max_split bounds its partials (per
+// sequence and kv head).
 TqSplit tq_decode_block_split(int num_seqs, int max_seq_len) {
-  constexpr long kUnits = 256;  // compute units of the MI355X
-  const long tokens = max_seq_len > 0 ? max_seq_len : 1;
-  long chunk = (tokens * num_seqs + kUnits - 1) / kUnits;
-  chunk = ((chunk + 15) / 16) * 16;
-  if (chunk < 64) chunk = 64;
-  if (chunk > 16L * kMaxRuns) chunk = 16L * kMaxRuns;
+  const long runs = max_seq_len > 0 ? ((long)max_seq_len + 15) / 16 : 1;
+  const long ns = num_seqs > 0 ? num_seqs : 1;
+  long pieces = (2L * kGrid + ns - 1) / ns + 2;
+  if (pieces > runs + 2) pieces = runs + 2;
+  if (pieces < 3) pieces = 3;
   TqSplit sp;
-  sp.chunk = (int)chunk;
-  sp.max_split = (int)((tokens + chunk - 1) / chunk);
+  sp.chunk = 16;
+  sp.max_pieces = (int)pieces;
+  // partials: a unit of at most kMaxRuns runs each, pieces - 1 pieces at most
+  sp.max_split = (int)(pieces + (runs + kMaxRuns - 1) / kMaxRuns);
+  sp.max_runs = (int)runs;
   return sp;
 }
 
 int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                            int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                            int n_sink, const int32_t* win_lens, int win_cap, float qscale, float* partials,
-                           int part_stride, int nq, int q0, int g_real, void* stream) {
-  if (sp.chunk % 16 != 0 || sp.chunk > 16 * kMaxRuns) return (int)hipErrorInvalidValue;
+                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream) {
+  if (sp.max_pieces < 3 || sp.max_runs < 1 || sp.max_split < sp.max_pieces || part_stride < sp.max_split)
+    return (int)hipErrorInvalidValue;
   TqBlockArgs a;
   a.q = (const uint16_t*)q;
   a.pages = (const uint8_t*)pages;
@@ -659,7 +1011,9 @@ int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, c
   a.seq_lens = seq_lens;
   a.win_lens = win_cap > 0 ? win_lens : nullptr;
   a.partials = partials;
-  a.c = L.kc;
+  a.nsplit = nsplit;
+  a.kc = L.kc;
+  a.vc = L.vc;
   a.signs = L.signs;
   a.qscale = qscale;
   a.max_blocks = max_blocks;
@@ -671,14 +1025,17 @@ int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, c
   a.Hq = L.Hq;
   a.n_sink = n_sink;
   a.win_cap = win_cap;
-  a.chunk = sp.chunk;
-  a.max_split = sp.max_split;
+  a.num_seqs = num_seqs;
   a.part_stride = part_stride;
-  a.n_units = num_seqs * sp.max_split;
+  a.max_pieces = sp.max_pieces;
+  a.max_parts = sp.max_split;
+  a.max_runs = sp.max_runs;
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real;
-  const int grid = a.n_units < 256 ? a.n_units : 256;
-  hipLaunchKernelGGL(tq_decode_block_kernel, dim3(grid), dim3(kT + 256), 0, (hipStream_t)stream, a);
+  const hipStream_t st = (hipStream_t)stream;
+  if (L.kb == 4) launch_block<4, 4, 4>(a, st);
+  else if (L.G <= 4) launch_block<3, 2, 4>(a, st);
+  else launch_block<3, 2, 8>(a, st);
   return (int)hipGetLastError();
 }

@@ -37,8 +37,10 @@ struct TqLayer {
 
 // Decode split geometry chosen on the host.
 struct TqSplit {
-  int chunk;      // page tokens per split
-  int max_split;  // splits per (sequence, kv head) at max_seq_len
+  int chunk;          // page tokens per split
+  int max_split;      // splits per (sequence, kv head) at max_seq_len (block kernel: pieces)
+  int max_runs = 0;   // block kernel: 16-position runs of a sequence at max_seq_len
+  int max_pieces = 0; // block kernel: workgroups one sequence may span, plus two
 };
 
 TqSplit tq_decode_split(const TqLayer& L, int num_seqs, int max_seq_len);
@@ -56,7 +58,7 @@ TqSplit tq_decode_block_split(int num_seqs, int max_seq_len);
 int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                            int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                            int n_sink, const int32_t* win_lens, int win_cap, float qscale, float* partials,
-                           int part_stride, int nq, int q0, int g_real, void* stream);
+                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream);
 
 // Launchers: return a hipError_t value (0 on success).
 int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,

@@ -1,13 +1,13 @@
 """CPU check of the block decode kernel's gfx950 assembly (csrc/tq_decode_block.hip, compiled
-with the flags the build uses, about 5 s).
+with the flags the build uses, about 5 s), for each format instance of the kernel.
 
-The kernel's speed rests on three properties of the code the compiler emits, which a compiler
-change could silently break:
+The kernel's speed rests on properties of the code the compiler emits, which a compiler change
+could silently break:
   * the compute waves' step loop issues no vector memory instruction and waits on no vector
     memory counter (every page byte reaches them through LDS, loaded by the producer waves);
-  * nothing in either loop spills to scratch;
-  * the producer waves' loop loads with buffer_load ... lds and waits only with the counted
-    waits the source writes (a compiler-inserted vmcnt(0) would drain the runs in flight).
+  * the producer waves' loop loads with buffer_load ... lds, touches no scratch and waits only
+    with the counted waits the source writes (a compiler-inserted vmcnt(0) would drain the runs
+    in flight).
 """
 
 import os
@@ -20,7 +20,15 @@ import pytest
 from packed_decode_attention_amd import build as B
 
 SRC = os.path.join(B.CSRC, "tq_decode_block.hip")
-PRODUCER_WAITS = {0, 4, 5, 8, 10, 12, 15}  # one producer's loads of 0..3 runs (4 or 5 per run)
+INSTANCES = {(4, 4, 4), (3, 2, 4), (3, 2, 8)}  # (K bits, V bits, query heads per kv head)
+
+
+def producer_waits(kb, vb):
+    """The counted waits of one producer: its loads of 0..3 runs in flight (run bytes / 1 KB
+    loads, split over four producers)."""
+    loads = 16 * 8 * ((128 * kb // 8 + 4) + (128 * vb // 8 + 4)) // 1024
+    per = {(loads + 3) // 4, loads // 4}
+    return {0} | {n * p for n in (1, 2, 3) for p in per}
 
 
 @pytest.fixture(scope="module")
@@ -36,62 +44,74 @@ def asm(tmp_path_factory):
         return f.read()
 
 
-def _kernel_body(text):
-    name = re.search(r"^(_Z\S*tq_decode_block_kernel\S*):", text, re.M).group(1)
-    i = text.index(name + ":")
-    return text[i:text.index(".Lfunc_end", i)].split("\n")
+def _kernels(text):
+    """{(KB, VB, GM): body lines} of every instance of the kernel."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*tq_decode_block_kernelILi(\d)ELi(\d)ELi(\d)E\S*):", text, re.M):
+        i = m.start()
+        out[(int(m.group(2)), int(m.group(3)), int(m.group(4)))] = text[i:text.index(".Lfunc_end", i)].split("\n")
+    return out
 
 
-def _inner_loops(body):
-    """Instructions of each depth-2 loop, keyed by its header block, from the compiler's
-    block comments."""
-    loops, cur = {}, None
-    for k, line in enumerate(body):
-        label = re.match(r"^(\.LBB\w+|; %bb\.\d+):(.*)$", line)
+def _innermost_loops(body):
+    """Instructions of each innermost loop, keyed by its header block, from the compiler's block
+    comments (a header says 'This Inner Loop Header'; its other blocks 'in Loop: Header=...')."""
+    loops, cur, k = {}, None, 0
+    while k < len(body):
+        line = body[k]
+        label = re.match(r"^(\.LBB(\w+)|; %bb\.\d+):(.*)$", line)
         if label:
-            comment = label.group(2)
-            nxt = body[k + 1] if k + 1 < len(body) else ""
-            m = re.search(r"Header=(BB\w+) Depth=2", comment)
-            if "Inner Loop Header: Depth=2" in comment or "Inner Loop Header: Depth=2" in nxt:
-                cur = "BB" + label.group(1)[4:] if label.group(1).startswith(".LBB") else None
-            elif m:
+            comment = label.group(3)
+            while k + 1 < len(body) and re.match(r"^\s+;", body[k + 1]):
+                k += 1
+                comment += body[k]
+            m = re.search(r"in Loop: Header=(BB\w+) Depth", comment)
+            if "This Inner Loop Header" in comment and label.group(2):
+                cur = "BB" + label.group(2)
+                loops.setdefault(cur, [])
+            elif m and m.group(1) in loops:
                 cur = m.group(1)
             else:
                 cur = None
-            if cur is not None:
-                loops.setdefault(cur, [])
-            continue
-        ins = line.strip()
-        if cur is not None and ins and not ins.startswith(";") and not ins.startswith("."):
-            loops[cur].append(ins)
+        else:
+            ins = line.strip()
+            if cur is not None and ins and not ins.startswith(";") and not ins.startswith("."):
+                loops[cur].append(ins)
+        k += 1
     return loops
 
 
-def _classify(asm):
-    loops = _inner_loops(_kernel_body(asm))
+def _classify(body):
+    loops = _innermost_loops(body)
     compute = [v for v in loops.values() if any(i.startswith("v_mfma") for i in v)]
     producer = [v for v in loops.values() if any(i.startswith("buffer_load") for i in v)]
     return compute, producer
 
 
-def test_one_compute_loop_and_one_producer_loop(asm):
-    compute, producer = _classify(asm)
-    assert len(compute) == 1 and len(producer) == 1
+def test_every_instance_has_one_compute_loop_and_one_producer_loop(asm):
+    kernels = _kernels(asm)
+    assert set(kernels) == INSTANCES
+    for key, body in kernels.items():
+        compute, producer = _classify(body)
+        assert len(compute) == 1 and len(producer) == 1, key
 
 
 def test_compute_loop_has_no_vector_memory_work(asm):
-    (loop,), _ = _classify(asm)
-    vmem = [i for i in loop if re.match(r"(global|buffer|scratch|flat)_", i)]
-    assert not vmem, vmem[:5]
-    assert not [i for i in loop if i.startswith("s_waitcnt") and "vmcnt" in i]
-    assert sum(1 for i in loop if i.startswith("v_mfma")) % 16 == 0  # 8 QK + 8 PV per step
-    assert sum(1 for i in loop if i.startswith("s_barrier")) >= 1
+    for (kb, vb, gm), body in _kernels(asm).items():
+        (loop,), _ = _classify(body)
+        vmem = [i for i in loop if re.match(r"(global|buffer|scratch|flat)_", i)]
+        assert not vmem, ((kb, vb, gm), vmem[:5])
+        assert not [i for i in loop if i.startswith("s_waitcnt") and "vmcnt" in i], (kb, vb, gm)
+        per_step = 8 + 8 * (gm // 4)  # QK, then PV for each set of four query heads
+        assert sum(1 for i in loop if i.startswith("v_mfma")) % per_step == 0, (kb, vb, gm)
+        assert sum(1 for i in loop if i.startswith("s_barrier")) >= 1
 
 
 def test_producer_loop_waits_only_counted(asm):
-    _, (loop,) = _classify(asm)
-    loads = [i for i in loop if i.startswith("buffer_load_dwordx4") and i.endswith(" lds")]
-    assert loads
-    assert not [i for i in loop if re.match(r"(global|scratch|flat)_", i)]
-    waits = [int(m.group(1)) for i in loop for m in [re.search(r"vmcnt\((\d+)\)", i)] if m]
-    assert waits and set(waits) <= PRODUCER_WAITS, sorted(set(waits))
+    for (kb, vb, gm), body in _kernels(asm).items():
+        _, (loop,) = _classify(body)
+        loads = [i for i in loop if i.startswith("buffer_load_dwordx4") and i.endswith(" lds")]
+        assert loads, (kb, vb, gm)
+        assert not [i for i in loop if re.match(r"(global|scratch|flat)_", i)], (kb, vb, gm)
+        waits = [int(m.group(1)) for i in loop for m in [re.search(r"vmcnt\((\d+)\)", i)] if m]
+        assert waits and set(waits) <= producer_waits(kb, vb), ((kb, vb, gm), sorted(set(waits)))

@@ -72,6 +72,24 @@ CASES = {
                         lens=list(np.random.default_rng(53).integers(1, 121, 300))),
     "blk-g1-sinks": dict(w=wl.Workload("blk-g1", 1, 4, 8, 8, 128, 4, 4, 0, n_sink=20, seed=54),
                          lens=[700, 33, 21, 5]),
+    # the whole-block kernel's K3/V2 instances (the ragged batch's format): G = 8 around run
+    # edges with a sequence spread over many workgroups, G = 4 with sinks ending mid-run and
+    # fragmented tables, many short sequences (several pieces per workgroup), and one long
+    # sequence cut into hundreds of pieces
+    "blk32-edges": dict(w=wl.Workload("blk32-edges", 1, 9, 64, 8, 128, 3, 2, 0, values="outliers", seed=61),
+                        lens=[1, 15, 16, 17, 33, 48, 500, 2047, 6000]),
+    "blk32-g4-sinks": dict(w=wl.Workload("blk32-g4", 1, 4, 32, 8, 128, 3, 2, 0, n_sink=20,
+                                         tables="fragmented", seed=62), lens=[700, 33, 21, 5]),
+    "blk32-many": dict(w=wl.Workload("blk32-many", 1, 400, 64, 8, 128, 3, 2, 0, seed=63),
+                       lens=list(np.random.default_rng(63).integers(1, 200, 400))),
+    "blk32-long": dict(w=wl.Workload("blk32-long", 1, 1, 64, 8, 128, 3, 2, 0, values="student_t", seed=64),
+                       lens=[20000]),
+    # balanced ranges whose pieces exceed one unit of 192 runs (a 500-run sequence among 255
+    # one-run ones: 250 runs per workgroup), and workgroups with over a hundred pieces
+    "blk32-units": dict(w=wl.Workload("blk32-units", 1, 256, 64, 8, 128, 3, 2, 0, seed=65),
+                        lens=[16] * 100 + [8000] + [16] * 155),
+    "blk-units": dict(w=wl.Workload("blk-units", 1, 256, 32, 8, 128, 4, 4, 0, seed=66),
+                      lens=[16] * 40 + [7999] + [16] * 215),
     # the largest sink count (128): sequences shorter than, equal to and longer than it
     "sinks-max": dict(w=wl.Workload("sinks-max", 1, 4, 8, 2, 128, 4, 4, 0, n_sink=128, values="normal",
                                     seed=20), lens=[100, 128, 129, 700]),
@@ -169,7 +187,8 @@ MULTI = [("llama-small", 1), ("llama-small", 2), ("llama-small", 3), ("llama-sma
          ("mistral-small", 2), ("ragged-small", 3), ("edges", 2), ("gaussian-g5", 2), ("tiny", 4),
          ("llama-mean", 2), ("edges-mean", 3), ("llama-qjl", 2), ("ragged-qjl", 2), ("edges-qjl", 3),
          ("tiny", 64), ("sinks-max", 64),  # 64: the largest query count
-         ("blk-g2-bs32", 2), ("blk-g1-sinks", 4)]  # two or four queries on the whole-block kernel
+         ("blk-g2-bs32", 2), ("blk-g1-sinks", 4),  # two or four queries on the whole-block kernel
+         ("blk32-g4-sinks", 2), ("blk32-edges", 2)]  # K3/V2: one launch of eight heads, two of eight
 
 
 @pytest.mark.parametrize("name,T", MULTI, ids=[f"{n}-T{t}" for n, t in MULTI])
@@ -204,6 +223,7 @@ WINDOWS = {
     "sinks-max": ([0, 0, 1, 572], 1024),  # the largest sink count and window capacity together
     "blk-edges": ([0, 1, 16, 0, 31, 1, 17, 48, 100, 1000], 1024),
     "blk-g1-sinks": ([680, 0, 1, 0], 700),
+    "blk32-edges": ([1, 0, 16, 1, 0, 47, 300, 1024, 1024], 1024),
 }
 
 

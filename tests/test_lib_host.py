@@ -175,8 +175,12 @@ def test_workspace_bytes(lib):
     a = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 32769)
     b = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 100)
     assert a >= b > 0
-    # split partials: (m, l, acc[D]) per sequence, query head and split
-    assert a >= 16 * 8 * 4 * 130 * 4 and a % (32 * 130 * 4) == 0
+    # block kernel: partials (m, l, acc[D]) per sequence, kv head, piece (2 * 256 / 16 + 2 = 34
+    # for 16 sequences) and query head, rounded up to 256 bytes, then a piece count per sequence
+    assert a >= 16 * 8 * 34 * 4 * 130 * 4 + 16 * 4 and (a - 16 * 4) % 256 == 0
+    # the split kernel (another format): partials only, per sequence, query head and split
+    c = so.tq_decode_workspace_bytes(ctypes.byref(_desc(lib, k_bits=8)), 16, 32769)
+    assert c >= 16 * 8 * 4 * 130 * 4 and c % (32 * 130 * 4) == 0
     assert so.tq_decode_workspace_bytes(ctypes.byref(_desc(lib, head_dim=80)), 16, 100) == 0
 
 
@@ -185,11 +189,12 @@ def test_multi_query_workspace_bytes(lib):
     d = _desc(lib)                                       # G = 4: two queries per launch
     one = so.tq_decode_workspace_bytes(ctypes.byref(d), 16, 32769)
     assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 1) == one
-    # a launch of two queries is a launch of eight query heads per kv head (its own split geometry)
+    # a launch of two queries is a launch of eight query heads per kv head (its own kernel and
+    # split geometry); the launches reuse one workspace, sized for the largest of them
     two = so.tq_decode_workspace_bytes(ctypes.byref(_desc(lib, num_q_heads=64)), 16, 32769)
-    assert two >= one
     assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 2) == two
-    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 7) == two  # launches reuse it
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 8) == two
+    assert so.tq_decode_multi_workspace_bytes(ctypes.byref(d), 16, 32769, 7) == max(one, two)  # 2+2+2+1
     g8 = _desc(lib, num_q_heads=64)                      # G = 8: one query per launch
     assert (so.tq_decode_multi_workspace_bytes(ctypes.byref(g8), 4, 1000, 5) ==
             so.tq_decode_workspace_bytes(ctypes.byref(g8), 4, 1000))
