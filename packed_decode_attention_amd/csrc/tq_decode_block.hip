@@ -61,7 +61,7 @@ constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (
 constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
 constexpr int kMaxRuns = 192;                  // runs per unit (three lanes' worth of run rows)
-constexpr int kPlanInts = 40;                  // LDS words of the work plan
+constexpr int kPlanInts = 48;                  // LDS words of the work plan (3 per wave, 7 more)
 constexpr int kGrid = 256;                     // workgroups: one per compute unit of the MI355X
 
 // Geometry of one page format: KB-bit keys, VB-bit values, up to GM query heads per kv head.
@@ -177,15 +177,34 @@ __device__ __forceinline__ int run_chunk_at(int p) {
   return (p & ~15) | ((p - q) & 15);
 }
 
-// Inclusive prefix sum across a wave (the work plan only).
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+// Inclusive prefix sum and maximum across a wave (the work plan only), by DPP: row shifts within
+// each 16-lane row, then row broadcasts of lanes 15 and 31 into the later rows.  Lanes a step has
+// no source for add 0 (counts are non-negative, so 0 also serves the maximum).
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_int(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_int<0x111>(x);        // row_shr:1
+  x += dpp_int<0x112>(x);        // row_shr:2
+  x += dpp_int<0x114>(x);        // row_shr:4
+  x += dpp_int<0x118>(x);        // row_shr:8
+  x += dpp_int<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_int<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
   return x;
 }
+__device__ __forceinline__ int wave_incl_max(int x) {
+  x = max(x, dpp_int<0x111>(x));
+  x = max(x, dpp_int<0x112>(x));
+  x = max(x, dpp_int<0x114>(x));
+  x = max(x, dpp_int<0x118>(x));
+  x = max(x, dpp_int<0x142, 0xa>(x));
+  x = max(x, dpp_int<0x143, 0xc>(x));
+  return x;
+}
+// Sum and maximum over the wave (lane 63 of the inclusive forms), wave-uniform.
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
+__device__ __forceinline__ int wave_max(int x) { return __builtin_amdgcn_readlane(wave_incl_max(x), 63); }
 
 }  // namespace
 
@@ -243,6 +262,16 @@ __device__ __forceinline__ TqSeq seq_of(const TqBlockArgs& a, int b) {
   return s;
 }
 
+// A sequence record in five LDS words.
+__device__ __forceinline__ void put_seq(int* w, const TqSeq& s) {
+  w[0] = s.seq_len;
+  w[1] = s.ns;
+  w[2] = s.end;
+  w[3] = s.run0;
+  w[4] = s.n_run;
+}
+__device__ __forceinline__ TqSeq get_seq(const int* w) { return TqSeq{w[0], w[1], w[2], w[3], w[4]}; }
+
 // This workgroup's share of the batch, in one of two forms.
 //  * Aligned: when the sequences with packed runs split evenly over the workgroups (c of them per
 //    sequence, no piece longer than an even share of all runs), workgroup k takes piece k mod c of
@@ -257,20 +286,11 @@ __device__ __forceinline__ TqSeq seq_of(const TqBlockArgs& a, int b) {
 // The host bounds the batch's runs by INT32_MAX, so 32-bit counts suffice.
 struct TqPlan {
   int S, E, R, rpw, b, part0;
+  TqSeq sq0;  // sequence b
 };
 
 constexpr int kAlignSlack = 2;  // runs an aligned piece may exceed the even share by
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d);
-  return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x = max(x, __shfl_xor(x, d));
-  return x;
-}
 __device__ __forceinline__ int units_of(int runs) { return (runs + kMaxRuns - 1) / kMaxRuns; }
 
 // Units of share k (runs [k rpw, (k + 1) rpw)) inside a sequence's runs [R, R + n).
@@ -282,16 +302,17 @@ __device__ __forceinline__ int units_in_share(int k, int rpw, int R, int n) {
 // n_own: the run count of sequence tid (0 past the batch), loaded by the caller at kernel entry so
 // the load overlaps the table fill.  A batch of at most kThreads sequences takes one pass over
 // the run counts; a larger one takes a second, kThreads sequences at a time.
-__device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave, int lane, int n_own) {
+__device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave, int lane, const TqSeq& own) {
+  const int n_own = own.n_run;
   const int B = a.num_seqs;
   const bool one_pass = B <= kThreads;
   // total runs, sequences with runs, longest sequence (and, in one pass, the prefixes)
   int t = 0, nz = 0, mx = 0, incl = 0, incl_nz = 0;
   if (one_pass) {
-    incl = wave_incl_scan(n_own, lane);
-    incl_nz = wave_incl_scan(n_own > 0, lane);
-    t = __shfl(incl, 63);
-    nz = __shfl(incl_nz, 63);
+    incl = wave_incl_scan(n_own);
+    incl_nz = wave_incl_scan(n_own > 0);
+    t = __builtin_amdgcn_readlane(incl, 63);
+    nz = __builtin_amdgcn_readlane(incl_nz, 63);
     mx = n_own;
   } else {
     for (int b = tid; b < B; b += kThreads) {
@@ -309,18 +330,15 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
     s_plan[kWaves + wave] = nz;
     s_plan[2 * kWaves + wave] = mx;
   }
-  if (tid == 0) {
-    s_plan[3 * kWaves] = -1;
-    s_plan[3 * kWaves + 1] = 0;
-    s_plan[3 * kWaves + 2] = 0;
-  }
+  if (tid == 0) s_plan[3 * kWaves] = -1;
   __syncthreads();
   // the waves' totals, lane w holding wave w's, reduced across the wave
-  const int wt = lane < kWaves ? s_plan[lane] : 0;
-  const int wz = lane < kWaves ? s_plan[kWaves + lane] : 0;
-  const int T = wave_sum(wt), NZS = wave_sum(wz);
+  const int st = wave_incl_scan(lane < kWaves ? s_plan[lane] : 0);
+  const int sz = wave_incl_scan(lane < kWaves ? s_plan[kWaves + lane] : 0);
+  const int T = __builtin_amdgcn_readlane(st, 63), NZS = __builtin_amdgcn_readlane(sz, 63);
   const int MX = wave_max(lane < kWaves ? s_plan[2 * kWaves + lane] : 0);
-  const int base = wave_sum(lane < wave ? wt : 0), base_nz = wave_sum(lane < wave ? wz : 0);
+  const int base = wave > 0 ? __builtin_amdgcn_readlane(st, wave - 1) : 0;
+  const int base_nz = wave > 0 ? __builtin_amdgcn_readlane(sz, wave - 1) : 0;
   // runs per workgroup: an even share, and enough that no sequence (at most max_runs runs) spans
   // more than max_pieces - 1 workgroups ((n - 1) / rpw + 2 at most)
   int rpw = (int)(((int64_t)T + gridDim.x - 1) / gridDim.x);
@@ -340,7 +358,8 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
   const int target = c > 0 ? k / c : 0;  // aligned: the target-th sequence with runs
   // sequence b with n runs, its first run R and its rank among the sequences with runs: the partial
   // count for the merge, and whether this workgroup's share starts in it
-  auto place = [&](int b, int n, int R, int rank) {
+  auto place = [&](int b, const TqSeq& sq, int R, int rank) {
+    const int n = sq.n_run;
     int parts = 0;
     if (n > 0) {
       if (aligned) {
@@ -350,14 +369,14 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
         if (rank == target) {
           s_plan[3 * kWaves] = b;
           s_plan[3 * kWaves + 1] = ps;
-          s_plan[3 * kWaves + 2] = n;
+          put_seq(s_plan + 3 * kWaves + 2, sq);
         }
       } else {
         for (int kk = R / rpw; kk <= (R + n - 1) / rpw; ++kk) parts += units_in_share(kk, rpw, R, n);
         if (R <= p.S && p.S < R + n) {
           s_plan[3 * kWaves] = b;
           s_plan[3 * kWaves + 1] = R;
-          s_plan[3 * kWaves + 2] = n;
+          put_seq(s_plan + 3 * kWaves + 2, sq);
         }
       }
     }
@@ -366,26 +385,29 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
     if (k == 0) a.nsplit[b] = min(parts, a.max_parts);
   };
   if (one_pass) {
-    if (tid < B) place(tid, n_own, base + incl - n_own, base_nz + incl_nz - 1);
+    if (tid < B) place(tid, own, base + incl - n_own, base_nz + incl_nz - 1);
   } else {
     __syncthreads();
     // exclusive prefixes of the run counts and of the sequences with runs, kThreads at a time
     int carry = 0, carry_nz = 0;
     for (int c0 = 0; c0 < B; c0 += kThreads) {
       const int b = c0 + tid;
-      const int n = b < B ? seq_of<false>(a, b).n_run : 0;
-      const int in = wave_incl_scan(n, lane);
-      const int in_nz = wave_incl_scan(n > 0, lane);
+      TqSeq sq{};
+      if (b < B) sq = seq_of<false>(a, b);
+      const int n = sq.n_run;
+      const int in = wave_incl_scan(n);
+      const int in_nz = wave_incl_scan(n > 0);
       if (lane == 63) {
         s_plan[wave] = in;
         s_plan[kWaves + wave] = in_nz;
       }
       __syncthreads();
-      const int ct = lane < kWaves ? s_plan[lane] : 0;
-      const int cz = lane < kWaves ? s_plan[kWaves + lane] : 0;
-      const int total = wave_sum(ct), total_nz = wave_sum(cz);
-      const int bs = carry + wave_sum(lane < wave ? ct : 0), bs_nz = carry_nz + wave_sum(lane < wave ? cz : 0);
-      if (b < B) place(b, n, bs + in - n, bs_nz + in_nz - 1);
+      const int ct = wave_incl_scan(lane < kWaves ? s_plan[lane] : 0);
+      const int cz = wave_incl_scan(lane < kWaves ? s_plan[kWaves + lane] : 0);
+      const int total = __builtin_amdgcn_readlane(ct, 63), total_nz = __builtin_amdgcn_readlane(cz, 63);
+      const int bs = carry + (wave > 0 ? __builtin_amdgcn_readlane(ct, wave - 1) : 0);
+      const int bs_nz = carry_nz + (wave > 0 ? __builtin_amdgcn_readlane(cz, wave - 1) : 0);
+      if (b < B) place(b, sq, bs + in - n, bs_nz + in_nz - 1);
       carry += total;
       carry_nz += total_nz;
       __syncthreads();
@@ -393,8 +415,11 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
   }
   __syncthreads();
   const int found = s_plan[3 * kWaves];
+  p.sq0 = TqSeq{};
   if (found >= 0) {
-    const int f1 = s_plan[3 * kWaves + 1], n = s_plan[3 * kWaves + 2];
+    const int f1 = s_plan[3 * kWaves + 1];
+    p.sq0 = get_seq(s_plan + 3 * kWaves + 2);
+    const int n = p.sq0.n_run;
     p.b = found;
     if (aligned) {  // piece j of the sequence, runs [j ps, (j + 1) ps)
       const int j = k - target * c, ps = f1;
@@ -416,6 +441,11 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
   p.rpw = __builtin_amdgcn_readfirstlane(p.rpw);
   p.b = __builtin_amdgcn_readfirstlane(p.b);
   p.part0 = __builtin_amdgcn_readfirstlane(p.part0);
+  p.sq0.seq_len = __builtin_amdgcn_readfirstlane(p.sq0.seq_len);
+  p.sq0.ns = __builtin_amdgcn_readfirstlane(p.sq0.ns);
+  p.sq0.end = __builtin_amdgcn_readfirstlane(p.sq0.end);
+  p.sq0.run0 = __builtin_amdgcn_readfirstlane(p.sq0.run0);
+  p.sq0.n_run = __builtin_amdgcn_readfirstlane(p.sq0.n_run);
   return p;
 }
 
@@ -425,7 +455,7 @@ template <typename Fn>
 __device__ __forceinline__ void for_each_unit(const TqBlockArgs& a, const TqPlan& p, Fn&& f) {
   int R = p.R, part = p.part0;
   for (int b = p.b; R < p.E && b < a.num_seqs; ++b) {
-    const TqSeq sq = seq_of<true>(a, b);
+    const TqSeq sq = b == p.b ? p.sq0 : seq_of<true>(a, b);
     const int hi = min(p.E, R + sq.n_run);
     for (int u0 = max(p.S, R); u0 < hi && part < a.max_parts; u0 += kMaxRuns, ++part)
       f(sq, b, sq.run0 + (u0 - R), min(kMaxRuns, hi - u0), part);
@@ -460,7 +490,8 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
 
   // this thread's sequence's run count for the work plan, loaded first so that it overlaps the
   // table fill
-  const int n_own = tid < a.num_seqs ? seq_of<false>(a, tid).n_run : 0;
+  TqSeq own{};
+  if (tid < a.num_seqs) own = seq_of<false>(a, tid);
 
   // Centroid operand tables: entry e (a code group: coordinates 2j, 2j + 1 in its low and high
   // half) holds the fp16 high parts of both centroids, then their low parts, scaled by 2^8; copy
@@ -485,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
   // ordinary store keeps it from treating the array as never written there.
   if (tid == 0) s_r0[0] = 0;
 
-  const TqPlan plan = make_plan(a, s_plan, tid, wave, lane, n_own);  // its barriers also cover the tables
+  const TqPlan plan = make_plan(a, s_plan, tid, wave, lane, own);  // its barriers also cover the tables
 
   if (wave >= kW) {
     // ======== producer waves: every page load of the workgroup ========
