@@ -66,6 +66,7 @@ struct DecodeArgs {
   float* out;
   float* partials;   // [B][Hkv][part_stride][G][D + 2]: (m, l, acc[D]), log2 domain, rotated frame
   const int32_t* nsplit_of;  // packed partials per sequence as the block kernel wrote them, or NULL
+  int merge_pre;             // packed partials expected per sequence (the merge's first batch)
   // Several queries per sequence: the kernels' G heads of a kv head are G_real query heads for
   // each of this launch's queries q0 .. q0 + G / G_real - 1 out of nq (one query: nq = 1, q0 = 0,
   // g_real = G).
@@ -1418,21 +1419,10 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// NB partials from index s0 into the running (M, l, acc) of coordinate d.
-template <int NB, int D>
-__device__ __forceinline__ void merge_batch(const DecodeArgs& a, const float* pb, int s0, int nparts, int nsplit,
-                                            int G, int d, float& M, float& l, float& acc) {
-  float ms[NB], ls[NB], as[NB];
-#pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    const int pi = s0 + k;
-    const bool in = pi < nparts;
-    const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
-    const float* e = pb + (int64_t)idx * G * (D + 2);
-    ms[k] = in ? e[0] : -INFINITY;
-    ls[k] = in ? e[1] : 0.0f;
-    as[k] = in ? e[2 + d] : 0.0f;
-  }
+// Fold NB loaded partials (ms, ls, as: maximum, sum, coordinate d) into the running (M, l, acc).
+template <int NB>
+__device__ __forceinline__ void merge_fold(const float (&ms)[NB], const float (&ls)[NB], const float (&as)[NB],
+                                           float& M, float& l, float& acc) {
   float mc = ms[0];
 #pragma unroll
   for (int k = 1; k < NB; ++k) mc = fmaxf(mc, ms[k]);
@@ -1449,9 +1439,29 @@ __device__ __forceinline__ void merge_batch(const DecodeArgs& a, const float* pb
   M = Mn;
 }
 
+// NB partials from index s0 into the running (M, l, acc) of coordinate d.
+template <int NB, int D>
+__device__ __forceinline__ void merge_batch(const DecodeArgs& a, const float* pb, int s0, int nparts, int nsplit,
+                                            int G, int d, float& M, float& l, float& acc) {
+  float ms[NB], ls[NB], as[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int pi = s0 + k;
+    const bool in = pi < nparts;
+    const int idx = !in ? 0 : pi < nsplit ? pi : a.max_split + (pi - nsplit);
+    const float* e = pb + (int64_t)idx * G * (D + 2);
+    ms[k] = in ? e[0] : -INFINITY;
+    ls[k] = in ? e[1] : 0.0f;
+    as[k] = in ? e[2 + d] : 0.0f;
+  }
+  merge_fold<NB>(ms, ls, as, M, l, acc);
+}
+
 // One workgroup per (sequence, kv head, query head), one thread per coordinate: merge the packed
 // splits and the fp16-row chunks, rotate back, normalise.
-template <int D, int GMAX>
+// PRE: partials whose loads are issued before the sequence's partial count is known (16 when the
+// launch expects about sixteen per sequence, else 4).
+template <int D, int GMAX, int PRE>
 __global__ __launch_bounds__(D) void tq_decode_merge_kernel(DecodeArgs a) {
   const TqLayer& L = a.L;
   const int G = L.G;
@@ -1460,6 +1470,22 @@ __global__ __launch_bounds__(D) void tq_decode_merge_kernel(DecodeArgs a) {
   const int h = bh % L.Hkv;
   const int b = bh / L.Hkv;
   const int d = threadIdx.x;
+  const float* pb = a.partials + (int64_t)bh * a.part_stride * G * (D + 2) + g * (D + 2);
+  // Without fp16 rows in the call the first partials are packed splits at indices 0..PRE-1: their
+  // loads go out with those of the sequence's length and partial count instead of after them
+  // (indices past the stride are clamped into this row of partials and masked below).
+  constexpr int kPre = PRE;
+  float pm[kPre], pl[kPre], pa[kPre];
+  const bool pre = a.row_chunks == 0;
+  if (pre) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const float* e = pb + (int64_t)min(k, a.part_stride - 1) * G * (D + 2);
+      pm[k] = e[0];
+      pl[k] = e[1];
+      pa[k] = e[2 + d];
+    }
+  }
   const int seq_len = a.seq_lens[b];
   if (seq_len == 0) {
     a.out[q_row(a, b, h, g) * D + d] = 0.0f;
@@ -1475,9 +1501,19 @@ __global__ __launch_bounds__(D) void tq_decode_merge_kernel(DecodeArgs a) {
   // Log-sum-exp merge of the partials (packed splits, then fp16-row chunks), sixteen at a time so
   // their loads are in flight together, the rest four at a time.  Empty partials carry a maximum
   // of -inf or kSent and contribute exp2(. - M) = 0 once a real score is in M.
-  const float* pb = a.partials + (int64_t)bh * a.part_stride * G * (D + 2) + g * (D + 2);
   float M = kSent, l = 0.0f, acc = 0.0f;
   int s0 = 0;
+  if (pre) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const bool in = k < nparts;
+      pm[k] = in ? pm[k] : -INFINITY;
+      pl[k] = in ? pl[k] : 0.0f;
+      pa[k] = in ? pa[k] : 0.0f;
+    }
+    merge_fold<kPre>(pm, pl, pa, M, l, acc);
+    s0 = kPre;
+  }
   for (; s0 + 16 <= nparts; s0 += 16) merge_batch<16, D>(a, pb, s0, nparts, nsplit, G, d, M, l, acc);
   for (; s0 < nparts; s0 += 4) merge_batch<4, D>(a, pb, s0, nparts, nsplit, G, d, M, l, acc);
   s_acc[d] = acc;
@@ -1515,7 +1551,8 @@ __global__ __launch_bounds__(kWG) void tq_decode_rows_kernel(DecodeArgs a) {
 
 template <int D, int GMAX>
 void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t st) {
-  hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX>), mgrid, dim3(D), 0, st, a);
+  if (a.merge_pre >= 12) hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX, 16>), mgrid, dim3(D), 0, st, a);
+  else hipLaunchKernelGGL((tq_decode_merge_kernel<D, GMAX, 4>), mgrid, dim3(D), 0, st, a);
 }
 
 // Split kernel for one format and query-group bound (the fp16-row chunks at the front of its grid,
@@ -1699,6 +1736,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.out = out;
   a.partials = (float*)workspace;
   a.nsplit_of = nullptr;
+  a.merge_pre = sp.max_split;
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real > 0 ? g_real : L.G;
@@ -1714,6 +1752,8 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
                                          a.part_stride, nq, q0, a.g_real, stream);
     if (e != 0) return e;
     a.nsplit_of = nsplit;
+    // the block kernel's aligned pieces: about 256 / num_seqs per sequence
+    a.merge_pre = num_seqs > 0 ? (256 / num_seqs < sp.max_split ? 256 / num_seqs : sp.max_split) : 1;
     if (L.G <= 4) launch_merge<128, 4>(a, mgrid0, st);
     else launch_merge<128, 8>(a, mgrid0, st);
     return (int)hipGetLastError();
