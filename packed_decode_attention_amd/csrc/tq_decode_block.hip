@@ -60,7 +60,7 @@ constexpr int kLutShift = 8;                   // table entries hold c * 2^8
 constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (below 2^15)
 constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
-constexpr int kMaxRuns = 192;                  // runs per unit (three lanes' worth of run rows)
+constexpr int kMaxRuns = 384;                  // runs per unit (six lanes' worth of run rows)
 constexpr int kPlanInts = 48;                  // LDS words of the work plan (3 per wave, 7 more)
 constexpr int kGrid = 256;                     // workgroups: one per compute unit of the MI355X
 
@@ -549,14 +549,15 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
     };
     for_each_unit(a, plan, [&](const TqSeq&, int b, int run_first, int n_run, int) {
       lds_barrier();  // every wave is done with the previous unit's buffers
-      // page rows of runs run_first + lane, + 64, + 128 (clamped to the last run)
-      const int rows0 = run_row(a, b, run_first + min(lane, n_run - 1));
-      const int rows1 = run_row(a, b, run_first + min(lane + 64, n_run - 1));
-      const int rows2 = run_row(a, b, run_first + min(lane + 128, n_run - 1));
+      // page rows of runs run_first + lane + 64 i (clamped to the last run)
+      int rows[kMaxRuns / 64];
+#pragma unroll
+      for (int i = 0; i < kMaxRuns / 64; ++i) rows[i] = run_row(a, b, run_first + min(lane + 64 * i, n_run - 1));
       auto issue = [&](int r, lds_u8* buf) {
-        const int row = r < 64 ? __builtin_amdgcn_readlane(rows0, r)
-                               : r < 128 ? __builtin_amdgcn_readlane(rows1, r - 64)
-                                         : __builtin_amdgcn_readlane(rows2, r - 128);
+        int row = __builtin_amdgcn_readlane(rows[0], r & 63);
+#pragma unroll
+        for (int i = 1; i < kMaxRuns / 64; ++i)
+          if ((r >> 6) == i) row = __builtin_amdgcn_readlane(rows[i], r & 63);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.pages + (int64_t)row * kRowBytes, kRunBytes);
 #pragma unroll
         for (int i = 0; i < F::kLoadsHi; ++i)

@@ -83,3 +83,22 @@ def test_noalloc_rejects_sizes_beyond_its_array():
     with pytest.raises(tq.TqError) as e:
         tq.tq_paged_decode_attention_noalloc(fmt.desc, q, pages, 1, bt, sl, L, out)
     assert e.value.status == _lib.TQ_ERR_NOALLOC_LIMIT
+
+
+def test_noalloc_accepts_the_full_ragged_batch():
+    """The largest benchmark batch (256 sequences of up to 16 385 + 256 tokens, K3/V2, eight query
+    heads per kv head) fits the static array; with every length 0 nothing is read and the output
+    is zero."""
+    import torch
+    import packed_decode_attention_amd as tq
+    fmt = tq.LayerFormat(128, 64, 8, 3, 2)
+    B, L = 256, 16385 + 256
+    print(f"[noalloc] full ragged batch sizes: B={B} L={L}", flush=True)
+    q = torch.zeros((B, 64, 128), dtype=torch.float16, device="cuda")
+    out = torch.full((B, 64, 128), 7.0, dtype=torch.float32, device="cuda")
+    pages = torch.zeros((1, 16, 8, fmt.slot_stride), dtype=torch.uint8, device="cuda")
+    bt = torch.zeros((B, (L + 15) // 16), dtype=torch.int32, device="cuda")
+    sl = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    tq.tq_paged_decode_attention_noalloc(fmt.desc, q, pages, 1, bt, sl, L, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
