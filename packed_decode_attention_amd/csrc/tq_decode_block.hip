@@ -762,14 +762,16 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
           d[1] = make_float4(x[zz][4], x[zz][5], x[zz][6], x[zz][7]);
         }
       }
-      // scale exponent of head g: its largest |q| * qscale lands near 2^13
-      float qm[GM];
+      // scale exponent of head g: its largest |q| * qscale lands near 2^13.  (g may vary by lane:
+      // each head's maximum is read from its lane as a scalar, not kept in an array the compiler
+      // could turn into an indexed scratch load.)
+      auto head_exp = [&](int g) {
+        float v = 0.0f;
 #pragma unroll
-      for (int g = 0; g < GM; ++g) qm[g] = lane_value(qmax_l[g >> 2], 16 * (g & 3));
-      auto head_exp = [&](int g) {  // g may vary by lane
-        float v = qm[0];
-#pragma unroll
-        for (int k = 1; k < GM; ++k) v = g == k ? qm[k] : v;
+        for (int k = 0; k < GM; ++k) {
+          const float qk = lane_value(qmax_l[k >> 2], 16 * (k & 3));
+          v = g == k ? qk : v;
+        }
         return v > 0.0f ? 13 - ilogbf(v) : 0;
       };
 

@@ -115,3 +115,11 @@ def test_producer_loop_waits_only_counted(asm):
         assert not [i for i in loop if re.match(r"(global|scratch|flat)_", i)], (kb, vb, gm)
         waits = [int(m.group(1)) for i in loop for m in [re.search(r"vmcnt\((\d+)\)", i)] if m]
         assert waits and set(waits) <= producer_waits(kb, vb), ((kb, vb, gm), sorted(set(waits)))
+
+
+def test_no_indexed_private_arrays(asm):
+    # a scratch access through a VGPR address is a private array indexed at run time (a select
+    # over an array the compiler turned into a load): a memory round trip on the path it sits on
+    for key, body in _kernels(asm).items():
+        idx = [l.strip() for l in body if re.match(r"\s*scratch_\w+ v\S+, v\d+, off", l)]
+        assert not idx, (key, idx[:3])
