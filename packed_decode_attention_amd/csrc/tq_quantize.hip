@@ -378,6 +378,38 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
   extern __shared__ uint2 s_tab[];  // K table (qtab_entries(kb)), then V table
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+
+  // Each wave stages its next tile in its own LDS buffer (global_load_lds: lane l's 16 bytes of
+  // block b land at b * 1024 + 16 l, the same lane reads them back; the slot id of lane l's row
+  // lands as two dwords) while it works on the current one from registers.  All vector memory
+  // operations share one in-order counter: the next tile's loads are issued before the current
+  // tile's stores, and the wait at the top of an iteration lets exactly those stores stay in
+  // flight.  The first tile's loads go out before the codebook is read, so that their latency
+  // overlaps the table build (a small append is that one tile).
+  uint8_t* stage = s_stage[wave];
+  const int64_t n_tiles = (n_rows + 15) / 16;
+  const int64_t tstep = (int64_t)gridDim.x * kNWQ;
+  constexpr int kStores = region_stores(KB) + region_stores(VB);
+  auto issue = [&](int64_t T) {
+    const int64_t row = T * 16 + c;
+    const int64_t rr = row < n_rows ? row : n_rows - 1;  // rows past the end load the last row
+    const uint16_t* sk = k + rr * D + 8 * g;
+    const uint16_t* sv = v + rr * D + 8 * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      __builtin_amdgcn_global_load_lds(sk + 32 * b, stage + b * 1024, 16, 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      __builtin_amdgcn_global_load_lds(sv + 32 * b, stage + (NB + b) * 1024, 16, 0, 0);
+    const uint32_t* sl = reinterpret_cast<const uint32_t*>(slot_mapping + rr / L.Hkv);
+    __builtin_amdgcn_global_load_lds(sl, stage + 2 * NB * 1024, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sl + 1, stage + 2 * NB * 1024 + 256, 4, 0, 0);
+  };
+  const int64_t T0 = (int64_t)blockIdx.x * kNWQ + wave;
+  if (T0 < n_tiles) issue(T0);
+
   constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
   static_assert(nbk < kWG && nbv < kWG, "one boundary gap per thread");
   for (int i = tid; i < nbk; i += kWG) s_t[0][i] = L.kt[i];
@@ -417,8 +449,6 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
   __syncthreads();
   const int shk = s_sh[0], shv = s_sh[1];
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
   // A operands: lane (row m = lane % 16, k = 8 (lane / 16) + j) of tile t holds
   // H_32[8 (m / 4) + 4 t + m % 4][k] * s_{32 b + k} as fp16 +-1.
   uint4 A[NB][2];
@@ -445,37 +475,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
   float zero;  // an addend of 0 the compiler cannot fold, so a lone square stays one v_fma_mix
   asm("v_mov_b32 %0, 0" : "=v"(zero));
 
-  // Each wave stages its next tile in its own LDS buffer (global_load_lds: lane l's 16 bytes of
-  // block b land at b * 1024 + 16 l, the same lane reads them back; the slot id of lane l's row
-  // lands as two dwords) while it works on the current one from registers.  All vector memory
-  // operations share one in-order counter: the next tile's loads are issued before the current
-  // tile's stores, and the wait at the top of an iteration lets exactly those stores stay in
-  // flight.
-  uint8_t* stage = s_stage[wave];
-  const int64_t n_tiles = (n_rows + 15) / 16;
-  const int64_t tstep = (int64_t)gridDim.x * kNWQ;
-  constexpr int kStores = region_stores(KB) + region_stores(VB);
-  auto issue = [&](int64_t T) {
-    const int64_t row = T * 16 + c;
-    const int64_t rr = row < n_rows ? row : n_rows - 1;  // rows past the end load the last row
-    const uint16_t* sk = k + rr * D + 8 * g;
-    const uint16_t* sv = v + rr * D + 8 * g;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      __builtin_amdgcn_global_load_lds(sk + 32 * b, stage + b * 1024, 16, 0, 0);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      __builtin_amdgcn_global_load_lds(sv + 32 * b, stage + (NB + b) * 1024, 16, 0, 0);
-    const uint32_t* sl = reinterpret_cast<const uint32_t*>(slot_mapping + rr / L.Hkv);
-    __builtin_amdgcn_global_load_lds(sl, stage + 2 * NB * 1024, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(sl + 1, stage + 2 * NB * 1024 + 256, 4, 0, 0);
-  };
   // Two complete tile loops, one per decision method (a codebook too fine for its table sends
   // both regions to the binary search), so neither loop carries the other's registers.
   auto tile_loop = [&](auto use_table) {
     constexpr bool kTable = decltype(use_table)::value;
-    int64_t T = (int64_t)blockIdx.x * kNWQ + wave;
-    if (T < n_tiles) issue(T);
+    int64_t T = T0;  // its loads are in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     for (; T < n_tiles; T += tstep) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStores));  // all but the previous tile's stores
