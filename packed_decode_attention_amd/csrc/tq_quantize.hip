@@ -328,24 +328,82 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
   }
 }
 
-// Bucket table of one codebook (see above): entries for buckets k = -(S + 1) .. S, entry
-// {S t_base as bits, base} with base = #{t < k / S}.
-__device__ __forceinline__ void build_qtab(const float* s_t, int nb, int sh, uint2* tab, int tid) {
-  const int S = 1 << sh;
-  constexpr int kPer = (kQTabLarge + kWG - 1) / kWG;  // entries per thread at most
+// Bucket table of one codebook (see above), entries i0 .. i0 + kPer - 1 of this thread: entry
+// {S t_base as bits, base} with base = #{t < k / S} for bucket k = i - (S + 1).  base0 is the
+// entry i0's count.  Boundary base0 + m lies in bucket k0 + d_m (k0 = i0 - (S + 1), d_m >= m, the
+// d_m distinct: one boundary per bucket at most), and it is below the edge of entry i0 + r exactly
+// when d_m < r.  So with M the bit set of the d_m, entry i0 + r counts base0 + popcount(M below
+// bit r).
+template <int BITS, int kPer>
+__device__ __forceinline__ void fill_qtab(const float* s_t, int sh, int i0, int base0, uint2* tab) {
+  constexpr int nb = (1 << BITS) - 1;
+  constexpr int kW = kPer > 1 ? kPer - 1 : 1;
+  const bool valid = sh != kQNoTable;
+  const int S = valid ? 1 << sh : 0;
+  const int k0 = i0 - (S + 1);
+  // (the empty asm statements keep each group of LDS reads unconditional and in flight together)
+  float tb[kW];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {  // unrolled: the threads' searches overlap
-    const int i = tid + r * kWG;
-    if (i < 2 * S + 2) {
-      const float edge = ldexpf((float)(i - (S + 1)), -sh);
-      int lo = 0;  // #{t < edge}: branchless lower bound over the (at most 255) sorted boundaries
+  for (int m = 0; m + 1 < kPer; ++m) tb[m] = s_t[min(base0 + m, nb - 1)];
 #pragma unroll
-      for (int st = 128; st >= 1; st >>= 1)
-        if (lo + st <= nb && s_t[lo + st - 1] < edge) lo += st;
-      const float next = lo < nb ? ldexpf(s_t[lo], sh) : 3.0e38f;
-      tab[i] = make_uint2(__float_as_uint(next), (uint32_t)lo);
+  for (int m = 0; m + 1 < kPer; ++m) asm volatile("" : "+v"(tb[m]));
+  uint32_t M = 0;
+#pragma unroll
+  for (int m = 0; m + 1 < kPer; ++m) {
+    const int d = base0 + m < nb ? min((int)floorf(ldexpf(tb[m], sh)) - k0, 31) : 31;
+    M |= 1u << d;
+  }
+  int cnt[kPer];
+  float nx[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    cnt[r] = base0 + __builtin_popcount(M & ((1u << r) - 1u));
+    nx[r] = s_t[min(cnt[r], nb - 1)];
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) asm volatile("" : "+v"(nx[r]));
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    if (valid && i0 + r < 2 * S + 2) {
+      const float next = cnt[r] < nb ? ldexpf(nx[r], sh) : 3.0e38f;
+      tab[i0 + r] = make_uint2(__float_as_uint(next), (uint32_t)cnt[r]);
     }
   }
+}
+
+// Bucket tables of the K and V codebooks: each thread takes consecutive entries (up to nine per
+// table), finds the count of its first entry by a branchless lower-bound search over the sorted
+// boundaries (both tables' searches advance together), and derives the rest from the next few
+// boundaries, so the build takes a few LDS round trips rather than one search per entry.
+template <int KB, int VB>
+__device__ __forceinline__ void build_qtabs(const float (*s_t)[256], int shk, int shv, uint2* tabk,
+                                            uint2* tabv, int tid) {
+  constexpr int kPK = (qtab_entries(KB) + kWG - 1) / kWG;  // entries per thread at most
+  constexpr int kPV = (qtab_entries(VB) + kWG - 1) / kWG;
+  constexpr int kStK = 1 << (KB - 1), kStV = 1 << (VB - 1);  // first step: nb = 2 st - 1
+  constexpr int kSt0 = kStK > kStV ? kStK : kStV;
+  const int i0k = tid * kPK, i0v = tid * kPV;
+  auto edge0 = [](int i0, int sh) {
+    return sh == kQNoTable ? 0.0f : ldexpf((float)(i0 - ((1 << sh) + 1)), -sh);
+  };
+  const float ek = edge0(i0k, shk), ev = edge0(i0v, shv);
+  int bk = 0, bv = 0;
+  // after the steps above st, a count is <= 2 st0 - 2 st, so count + st <= nb: every read is a
+  // boundary
+#pragma unroll
+  for (int st = kSt0; st >= 1; st >>= 1) {
+    if (st <= kStK) {
+      const int j = bk + st;
+      bk = s_t[0][j - 1] < ek ? j : bk;
+    }
+    if (st <= kStV) {
+      const int j = bv + st;
+      bv = s_t[1][j - 1] < ev ? j : bv;
+    }
+  }
+  asm volatile("" : "+v"(bk), "+v"(bv));  // both searches above, interleaved
+  fill_qtab<KB, kPK>(s_t[0], shk, i0k, bk, tabk);
+  fill_qtab<VB, kPV>(s_t[1], shv, i0v, bv, tabv);
 }
 
 // Destination of the stores of rows that have no slot (past the end of the input, or a negative
@@ -410,13 +468,45 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
   const int64_t T0 = (int64_t)blockIdx.x * kNWQ + wave;
   if (T0 < n_tiles) issue(T0);
 
+  // The codebooks (at most one boundary and one centroid per thread), then, while they load, the
+  // Hadamard operands, which depend on no load.
   constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
   static_assert(nbk < kWG && nbv < kWG, "one boundary gap per thread");
-  for (int i = tid; i < nbk; i += kWG) s_t[0][i] = L.kt[i];
-  for (int i = tid; i < nbv; i += kWG) s_t[1][i] = L.vt[i];
+  const float tk = L.kt[min(tid, nbk - 1)];
+  const float tv = L.vt[min(tid, nbv - 1)];
+  float ck = 0.0f, cv = 0.0f;
   if constexpr (NC) {
-    for (int i = tid; i <= nbk; i += kWG) s_c[0][i] = L.kc[i];
-    for (int i = tid; i <= nbv; i += kWG) s_c[1][i] = L.vc[i];
+    ck = L.kc[min(tid, nbk)];
+    cv = L.vc[min(tid, nbv)];
+  }
+  // A operands: lane (row m = lane % 16, k = 8 (lane / 16) + j) of tile t holds
+  // H_32[r][k] * s_{32 b + k} as fp16 +-1, r = 8 (m / 4) + 4 t + m % 4.  The sign of H_32[r][8 g + j]
+  // is parity(r & 8 g) (one bit per lane) xor parity((r & 7) & j) (bit j of the 8-point Walsh row
+  // r & 7, a byte of a 64-bit constant), and the sign flips of s are bits 8 g .. 8 g + 7 of the
+  // block's sign word.
+  constexpr uint64_t kWalsh8 = 0x963C5AF066CCAA00ull;  // byte x: bit j = parity(x & j)
+  const uint32_t hpar = (__builtin_popcount((c >> 2) & g) & 1) ? 0xffu : 0u;
+  uint4 A[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t x = ((uint32_t)(kWalsh8 >> (8 * (4 * t + (c & 3)))) & 0xffu) ^ hpar ^
+                         ((L.signs.w[b] >> (8 * g)) & 0xffu);
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)  // fp16 +-1 pair: sign bits 2 q and 2 q + 1 of x
+        w[q] = 0x3C003C00u | ((x << (15 - 2 * q)) & 0x8000u) | ((x << (30 - 2 * q)) & 0x80000000u);
+      A[b][t] = make_uint4(w[0], w[1], w[2], w[3]);
+      // computed here, while the codebook loads are in flight, not sunk past the table build
+      asm volatile("" : "+v"(A[b][t].x), "+v"(A[b][t].y), "+v"(A[b][t].z), "+v"(A[b][t].w));
+    }
+  }
+  if (tid < nbk) s_t[0][tid] = tk;
+  if (tid < nbv) s_t[1][tid] = tv;
+  if constexpr (NC) {
+    if (tid <= nbk) s_c[0][tid] = ck;
+    if (tid <= nbv) s_c[1][tid] = cv;
   }
   __syncthreads();
   {  // smallest gap between consecutive boundaries, one gap per thread (at most 254 of them)
@@ -442,36 +532,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
     s_sh[tid] = sh;
   }
   __syncthreads();
+  const int shk = s_sh[0], shv = s_sh[1];
   uint2* tabk = s_tab;
   uint2* tabv = s_tab + qtab_entries(KB);
-  if (s_sh[0] != kQNoTable) build_qtab(s_t[0], nbk, s_sh[0], tabk, tid);
-  if (s_sh[1] != kQNoTable) build_qtab(s_t[1], nbv, s_sh[1], tabv, tid);
+  build_qtabs<KB, VB>(s_t, shk, shv, tabk, tabv, tid);
   __syncthreads();
-  const int shk = s_sh[0], shv = s_sh[1];
-
-  // A operands: lane (row m = lane % 16, k = 8 (lane / 16) + j) of tile t holds
-  // H_32[8 (m / 4) + 4 t + m % 4][k] * s_{32 b + k} as fp16 +-1.
-  uint4 A[NB][2];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 8 * (c >> 2) + 4 * t + (c & 3);
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t hv[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kk = 8 * g + 2 * q + h;
-          const uint32_t neg = (__builtin_popcount(r & kk) + (L.signs.w[b] >> kk)) & 1u;
-          hv[h] = neg ? 0xBC00u : 0x3C00u;
-        }
-        w[q] = hv[0] | (hv[1] << 16);
-      }
-      A[b][t] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
   float zero;  // an addend of 0 the compiler cannot fold, so a lone square stays one v_fma_mix
   asm("v_mov_b32 %0, 0" : "=v"(zero));
 
