@@ -114,8 +114,8 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_layer_desc* layer, int32_t 
 // the kernels' 32-bit workgroup arithmetic.
 static bool grid_fits(const TqLayer& L, int32_t num_seqs, const TqSplit& sp) {
   const int64_t units = (int64_t)num_seqs * sp.max_split + 8;
-  // the block kernel counts the batch's runs in 32 bits
-  if (sp.max_runs > 0 && (int64_t)num_seqs * sp.max_runs > INT32_MAX) return false;
+  // the block kernel counts the batch's runs, plus a fixed cost per sequence, in 32 bits
+  if (sp.max_runs > 0 && (int64_t)num_seqs * (sp.max_runs + kTqUnitCostRuns) > INT32_MAX) return false;
   return units * L.Hkv + (int64_t)num_seqs * L.Hkv * 16 <= INT32_MAX;
 }
 

@@ -276,9 +276,12 @@ __device__ __forceinline__ TqSeq get_seq(const int* w) { return TqSeq{w[0], w[1]
 //  * Aligned: when the sequences with packed runs split evenly over the workgroups (c of them per
 //    sequence, no piece longer than an even share of all runs), workgroup k takes piece k mod c of
 //    the (k / c)-th such sequence, and no workgroup switches sequences.
-//  * Ranges: otherwise the runs of all sequences form one sequence and workgroup k takes runs
-//    [S, E) of it, rpw runs per workgroup, cut into pieces at sequence boundaries; b is the first
-//    sequence with a run in the share and R the index of its first run.
+//  * Ranges: otherwise the sequences with runs are laid end to end on one cost axis, each as
+//    kTqUnitCostRuns of fixed cost followed by its runs, and workgroup k takes the runs in cost
+//    [S, E), rpw per workgroup, cut into pieces at sequence boundaries; b is the first sequence
+//    in the share and R the cost position of its run 0.  A workgroup pays the fixed cost of every
+//    unit it starts (its queries, block-table rows and first runs arrive before it can compute),
+//    so one that touches many short sequences takes fewer runs.
 // A piece is cut into units of at most kMaxRuns runs, and every unit writes a partial of its own:
 // a sequence's partials are numbered in run order, part0 being that of the share's first unit.
 // Workgroup 0 writes each sequence's partial count.  Every thread of the workgroup calls it.  An
@@ -340,26 +343,33 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
   const int base = wave > 0 ? __builtin_amdgcn_readlane(st, wave - 1) : 0;
   const int base_nz = wave > 0 ? __builtin_amdgcn_readlane(sz, wave - 1) : 0;
   // runs per workgroup: an even share, and enough that no sequence (at most max_runs runs) spans
-  // more than max_pieces - 1 workgroups ((n - 1) / rpw + 2 at most)
-  int rpw = (int)(((int64_t)T + gridDim.x - 1) / gridDim.x);
+  // more than max_pieces - 1 workgroups ((n - 1) / rpw + 2 at most); the ranges take an even share
+  // of the cost axis (runs plus kTqUnitCostRuns per sequence with runs; the host bounds it by
+  // INT32_MAX), with the same floor
   const int floor_rpw = (int)(((int64_t)a.max_runs + a.max_pieces - 3) / (a.max_pieces - 2));
+  int rpw = (int)(((int64_t)T + gridDim.x - 1) / gridDim.x);
   if (rpw < floor_rpw) rpw = floor_rpw;
   if (rpw < 1) rpw = 1;
+  const int TC = T + kTqUnitCostRuns * NZS;  // length of the cost axis
+  int cpw = (int)(((int64_t)TC + gridDim.x - 1) / gridDim.x);
+  if (cpw < floor_rpw) cpw = floor_rpw;
+  if (cpw < 1) cpw = 1;
   const int c = NZS > 0 ? min((int)gridDim.x / NZS, a.max_pieces - 1) : 0;  // aligned pieces per sequence
   const bool aligned = c >= 1 && (MX + c - 1) / c <= rpw + kAlignSlack;
   const int k = blockIdx.x;
   TqPlan p;
-  p.rpw = rpw;
-  p.S = (int)min((int64_t)k * rpw, (int64_t)T);
-  p.E = min(p.S + rpw, T);
+  p.rpw = cpw;
+  p.S = (int)min((int64_t)k * cpw, (int64_t)TC);
+  p.E = min(p.S + cpw, TC);
   p.b = B;
   p.R = p.E;
   p.part0 = 0;
   const int target = c > 0 ? k / c : 0;  // aligned: the target-th sequence with runs
-  // sequence b with n runs, its first run R and its rank among the sequences with runs: the partial
-  // count for the merge, and whether this workgroup's share starts in it
-  auto place = [&](int b, const TqSeq& sq, int R, int rank) {
+  // sequence b with n runs, the runs before it and its rank among the sequences with runs: the
+  // partial count for the merge, and whether this workgroup's share starts in it
+  auto place = [&](int b, const TqSeq& sq, int before, int rank) {
     const int n = sq.n_run;
+    const int R = before + kTqUnitCostRuns * (rank + 1);  // cost position of its run 0
     int parts = 0;
     if (n > 0) {
       if (aligned) {
@@ -372,8 +382,8 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
           put_seq(s_plan + 3 * kWaves + 2, sq);
         }
       } else {
-        for (int kk = R / rpw; kk <= (R + n - 1) / rpw; ++kk) parts += units_in_share(kk, rpw, R, n);
-        if (R <= p.S && p.S < R + n) {
+        for (int kk = R / cpw; kk <= (R + n - 1) / cpw; ++kk) parts += units_in_share(kk, cpw, R, n);
+        if (R - kTqUnitCostRuns <= p.S && p.S < R + n) {  // from its fixed cost to its last run
           s_plan[3 * kWaves] = b;
           s_plan[3 * kWaves + 1] = R;
           put_seq(s_plan + 3 * kWaves + 2, sq);
@@ -430,7 +440,7 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
       p.part0 = j * units_of(ps);
     } else {  // units of the earlier shares in the first sequence
       p.R = f1;
-      for (int kk = f1 / rpw; kk < k; ++kk) p.part0 += units_in_share(kk, rpw, f1, n);
+      for (int kk = f1 / cpw; kk < k; ++kk) p.part0 += units_in_share(kk, cpw, f1, n);
     }
   }
   // The values are the same in every lane (LDS reads and cross-lane sums the compiler cannot
@@ -459,7 +469,7 @@ __device__ __forceinline__ void for_each_unit(const TqBlockArgs& a, const TqPlan
     const int hi = min(p.E, R + sq.n_run);
     for (int u0 = max(p.S, R); u0 < hi && part < a.max_parts; u0 += kMaxRuns, ++part)
       f(sq, b, sq.run0 + (u0 - R), min(kMaxRuns, hi - u0), part);
-    R += sq.n_run;
+    R += sq.n_run + (sq.n_run > 0 ? kTqUnitCostRuns : 0);  // run 0 of the next sequence
     part = 0;  // a later sequence starts in this share
   }
 }
