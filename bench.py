@@ -2,7 +2,9 @@
 
 A step is one pass of the whole hot path over one batch: for every layer, quantize-on-append of
 one new token per sequence into the packed pages, then fused paged decode attention over all
-cached tokens.  Inputs (pages filled by a bulk quantize of the context, queries, new tokens) are
+cached tokens.  Where the format allows it (the whole-block decode formats, no sinks, window or
+extra queries) both run in one call, tq_paged_decode_attention_append; --separate-append times
+the two calls instead.  Inputs (pages filled by a bulk quantize of the context, queries, new tokens) are
 resident in HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload llama3-8b] [--no-cpu-baseline]
@@ -46,6 +48,7 @@ class LayerState:
     def __init__(self, fmt, pages, num_blocks):
         self.fmt, self.pages, self.num_blocks = fmt, pages, num_blocks
         self.win_k = self.win_v = None  # fp16 hot window [B, W, H_kv, D] (with --hot-window)
+        self.fused = False              # append and decode in one call
 
 
 def context_slots(w, bt_np, lens, wl):
@@ -92,7 +95,7 @@ def new_tokens(w, n_steps_total, wl, dev="cuda"):
 
 
 def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, n_queries=1,
-          mean_removal=False, qjl=False):
+          mean_removal=False, qjl=False, fused=True):
     lens = wl.seq_lens(w)                       # includes the token appended each step
     bt_np, num_blocks = wl.block_tables(w, lens)
     dev = "cuda"
@@ -119,6 +122,9 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, 
             bulk_ms.append(t_layer)
         bulk_rows = n_ctx * H
         st = LayerState(fmt, pages, num_blocks)
+        st.fused = (fused and fmt.flags == 0 and not hot_window and n_queries == 1 and w.n_sink == 0
+                    and B <= tq.TQ_APPEND_MAX_SEQS and tq.decode_kernel_names(
+                        D, kb, vb, False, H, w.group, 0)[0] == "tq_decode_block_kernel")
         if hot_window:  # the last hot_window positions as fp16 rows (their page slots are ignored)
             g = wl.generator(w.seed * 7919 + l, dev)
             shape = (B, hot_window, H, D)
@@ -162,6 +168,15 @@ def run_step(w, S, tq, step, ev=None):
     for l, L in enumerate(S["layers"]):
         if ev is not None:
             ev["a0"][l].record()
+        if L.fused:  # the new token's append inside the decode call
+            if ev is not None:
+                ev["a1"][l].record()
+            tq.tq_paged_decode_attention_append(L.fmt.desc, S["qs"][l], S["new_k"][step, l],
+                                                S["new_v"][step, l], L.pages, L.num_blocks, S["bt"],
+                                                S["seq_lens"], S["max_len"], S["out"], S["ws"])
+            if ev is not None:
+                ev["d1"][l].record()
+            continue
         # with a hot window the quantized token is the one leaving the window, and the new token
         # takes its row in the window (a ring: row step % W)
         if S["n_queries"] > 1:  # T new rows per sequence (the step's rows, repeated)
@@ -214,7 +229,8 @@ def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1, flags=0):
     return per_layer
 
 
-DECODE_SOURCES = ("tq_decode.hip", "tq_decode_block.hip", "tq_device.h", "tq_internal.h")
+DECODE_SOURCES = ("tq_decode.hip", "tq_decode_block.hip", "tq_device.h", "tq_internal.h",
+                  "tq_quant_device.h")
 
 
 def decode_source_digest():
@@ -393,6 +409,9 @@ def main():
                          "through tq_paged_decode_attention_multi")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time tq_quantize_append and tq_paged_decode_attention as two calls even "
+                         "where the fused call serves the format")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure the streaming ceilings of the workload's access patterns "
                          "(the diagnostic kernel of include/tq_probe.h)")
@@ -422,7 +441,8 @@ def main():
     if args.qjl and max(max(w.bits(l)[0] for l in range(w.layers)), w.k_bits) > 4:
         sys.exit(f"--qjl needs keys of 2-4 bits; workload {w.name} has wider keys")
     S = setup(w, torch, tq, wl, total, args.hot_window, args.norm_correction, args.queries,
-              args.mean_removal, args.qjl)
+              args.mean_removal, args.qjl, not args.separate_append)
+    fused = [L.fused for L in S["layers"]]
     log(f"setup done in {time.time() - t0:.1f}s (bulk fill of {w.layers} layers)")
 
     for s in range(args.warmup):
@@ -445,9 +465,10 @@ def main():
     n = w.layers * args.steps
     dec_ms = np.array([ev["a1"][i].elapsed_time(ev["d1"][i]) for i in range(n)])
     app_ms = np.array([ev["a0"][i].elapsed_time(ev["a1"][i]) for i in range(n)])
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; decode {dec_ms.mean() * 1e3:.1f} us/layer "
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; "
+        f"{'append + decode' if all(fused) else 'decode'} {dec_ms.mean() * 1e3:.1f} us/layer "
         f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
-        f"append {app_ms.mean() * 1e3:.1f} us/layer")
+        + ("append fused into the decode call" if all(fused) else f"append {app_ms.mean() * 1e3:.1f} us/layer"))
 
     lens = S["lens"]
     kv_tokens_step = int(lens.sum()) * w.layers
@@ -457,8 +478,11 @@ def main():
                 (tq.TQ_FLAG_QJL if args.qjl else 0)
     per_layer_bytes = algorithmic_bytes(w, lens, tq, S["win_lens_np"] if args.hot_window else None,
                                         args.queries, fmt_flags)
+    # a fused call also reads the new rows and writes their slots
+    app_bytes = [w.num_seqs * w.num_kv_heads * (4 * w.head_dim + tq.tq_slot_bytes_ex(w.head_dim, *w.bits(l), fmt_flags))
+                 if fused[l] else 0 for l in range(w.layers)]
     layer_ids = np.arange(n) % w.layers
-    dec_bytes = np.array([per_layer_bytes[i] for i in layer_ids], np.float64)
+    dec_bytes = np.array([per_layer_bytes[i] + app_bytes[i] for i in layer_ids], np.float64)
     achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
     bulk_ms = float(np.mean(S["bulk_ms"])) if S["bulk_ms"] else float("nan")
     kb, vb = w.bits(1 % w.layers)
@@ -489,11 +513,13 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal
                                           or args.qjl) else recorded_traffic(w)),
-                     "kernel": "decode call: " + " + ".join(tq.decode_kernel_names(
+                     "kernel": ("append + decode call (tq_paged_decode_attention_append): " if all(fused)
+                                else "decode call: ") + " + ".join(tq.decode_kernel_names(
                          w.head_dim, w.k_bits, w.v_bits, args.qjl, w.num_kv_heads, w.group, fmt_flags)),
                      "bytes_per_launch": float(np.mean(dec_bytes)),
                      "avg_launch_us": float(dec_ms.mean() * 1e3)},
-        "append": {"step_us_per_layer": float(app_ms.mean() * 1e3),
+        "append": {"fused_into_decode": bool(all(fused)),
+                   "step_us_per_layer": None if all(fused) else float(app_ms.mean() * 1e3),
                    "bulk_fill_us_per_layer": bulk_ms * 1e3,
                    "bulk_fill_GBps": bulk_bytes / (bulk_ms / 1e3) / 1e9,
                    "bulk_fill_frac": bulk_bytes / (bulk_ms / 1e3) / 1e9 / HBM_PEAK_GBS,

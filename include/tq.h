@@ -218,6 +218,32 @@ int tq_paged_decode_attention_noalloc(const tq_layer_desc* layer, const void* q,
                                       const void* sink_v, int32_t n_sink, float scale, float* out,
                                       tq_stream_t stream);
 
+/* One decode step's append and attention in one call: for every sequence b with seq_lens[b] >= 1,
+ * the new token's K and V rows are quantized into the page slot of position seq_lens[b] - 1 (the
+ * slot the block table gives that position), then decode attention runs as
+ * tq_paged_decode_attention with no sink tokens.  Pages and output are identical, byte for byte,
+ * to tq_quantize_append of those rows at those slots followed by tq_paged_decode_attention.
+ * (turboquant-serve 0.1.2, "Architecture": each new row is rotated, normalised, encoded and packed
+ *  as it is stored; tq-kv, "Custom CUDA Kernel Stack": split-KV flash decode on the compressed
+ *  pages.)  The quantization is done by the decode kernel itself, by the workgroup that reads the
+ *  new token's run, before it loads any run, so the step costs no separate launch.
+ *   k_new, v_new  device fp16 [num_seqs][num_kv_heads][D]: the new token's rows; seq_lens counts
+ *                 the new token
+ *   pages         device, written (the new slots) and read
+ * Other arguments as for tq_paged_decode_attention.  TQ_ERR_UNSUPPORTED unless the layer is one
+ * the whole-block decode kernel serves (D = 128, eight kv heads, unpadded slots, block size a
+ * multiple of 16, K4/V4 with one codebook for K and V and up to four query heads per kv head, or
+ * K3/V2 with up to eight; no format flag) and num_seqs <= TQ_APPEND_MAX_SEQS; such callers use
+ * tq_quantize_append and tq_paged_decode_attention.  The workspace is that of
+ * tq_decode_workspace_bytes. */
+#define TQ_APPEND_MAX_SEQS 512
+int tq_paged_decode_attention_append(const tq_layer_desc* layer, const void* q, const void* k_new,
+                                     const void* v_new, void* pages, int64_t num_blocks,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                     float scale, float* out, void* workspace, size_t workspace_bytes,
+                                     tq_stream_t stream);
+
 /* The same decode with an fp16 hot window: the most recent tokens of each sequence kept
  * uncompressed and merged with the packed tokens by online softmax.
  * (turboquant-pro 1.4.2, "Streaming cache": an uncompressed hot window of recent tokens in front of

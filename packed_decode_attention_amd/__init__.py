@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     TqError,
     tq_build_codebook,
+    TQ_APPEND_MAX_SEQS,
     TQ_MAX_QUERIES,
     tq_decode_multi_workspace_bytes,
     tq_decode_workspace_bytes,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     tq_paged_decode_attention,
     tq_paged_decode_attention_multi,
     tq_paged_decode_attention_noalloc,
+    tq_paged_decode_attention_append,
     tq_paged_decode_attention_window,
     tq_probe_stream,
     tq_quantize_append,

@@ -24,12 +24,13 @@ TQ_ERR_HIP = -4
 TQ_ERR_NO_CONVERGENCE = -5
 TQ_ERR_NOALLOC_LIMIT = -6
 TQ_NOALLOC_WORKSPACE_BYTES = 64 << 20
+TQ_APPEND_MAX_SEQS = 512
 
 FAMILIES = {"beta": 0, "gaussian": 1}
 
 EXPORTS = ("tq_build_codebook", "tq_rht_signs", "tq_slot_bytes", "tq_slot_bytes_ex", "tq_quantize_append",
            "tq_decode_workspace_bytes", "tq_paged_decode_attention", "tq_paged_decode_attention_noalloc",
-           "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
+           "tq_paged_decode_attention_append", "tq_paged_decode_attention_window", "tq_decode_multi_workspace_bytes",
            "tq_paged_decode_attention_multi", "tq_dequantize_rows", "tq_status_str")
 TQ_MAX_QUERIES = 64
 PROBE_EXPORTS = ("tq_probe_stream",)  # include/tq_probe.h (diagnostics)
@@ -89,6 +90,9 @@ def _lib():
         lib.tq_paged_decode_attention_noalloc.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P,
                                                           I32, ctypes.c_float, P, P]
         lib.tq_paged_decode_attention_noalloc.restype = ctypes.c_int
+        lib.tq_paged_decode_attention_append.argtypes = [D, P, P, P, P, I64, P, I32, P, I32, I32,
+                                                         ctypes.c_float, P, P, SZ, P]
+        lib.tq_paged_decode_attention_append.restype = ctypes.c_int
         lib.tq_paged_decode_attention_window.argtypes = [D, P, P, I64, P, I32, P, I32, I32, P, P,
                                                          I32, P, P, P, I32, ctypes.c_float, P, P,
                                                          SZ, P]
@@ -198,6 +202,20 @@ def tq_paged_decode_attention_noalloc(desc, q, pages, num_blocks: int, block_tab
         _ptr(seq_lens), num_seqs, max_seq_len, _ptr(sink_k), _ptr(sink_v), n_sink, scale,
         _ptr(out), _stream(stream))
     _check("tq_paged_decode_attention_noalloc", st)
+
+
+def tq_paged_decode_attention_append(desc, q, k_new, v_new, pages, num_blocks: int, block_tables,
+                                     seq_lens, max_seq_len: int, out, workspace, scale: float = 0.0,
+                                     stream=None) -> None:
+    """Append the new token of every sequence (k_new, v_new [num_seqs][H_kv][D] fp16) at
+    position seq_lens[b] - 1, then decode: one call, one launch of the decode kernels."""
+    num_seqs = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables is not None else 0
+    st = _lib().tq_paged_decode_attention_append(
+        ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pages), num_blocks,
+        _ptr(block_tables), max_blocks, _ptr(seq_lens), num_seqs, max_seq_len, scale, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("tq_paged_decode_attention_append", st)
 
 
 def tq_paged_decode_attention_window(desc, q, pages, num_blocks: int, block_tables, seq_lens,

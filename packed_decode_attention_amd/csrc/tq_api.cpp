@@ -126,7 +126,7 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
                         const void* sink_k, const void* sink_v, int32_t n_sink, const void* win_k,
                         const void* win_v, const int32_t* win_lens, int32_t win_cap, float scale,
                         float* out, void* workspace, size_t workspace_bytes, tq_stream_t stream,
-                        bool noalloc = false) {
+                        bool noalloc = false, const TqAppend* app = nullptr) {
   TqLayer L;
   const int st = make_layer(layer, true, &L);
   if (st != TQ_OK) return st;
@@ -159,9 +159,29 @@ static int paged_decode(const tq_layer_desc* layer, const void* q, const void* p
   }
   return tq_launch_decode(L, q, pages, block_tables, max_blocks_per_seq, seq_lens, num_seqs, sp,
                           sink_k, sink_v, n_sink, win_k, win_v, win_lens, win_cap, scale, out,
-                          workspace, stream) == 0
+                          workspace, stream, 1, 0, 0, app) == 0
              ? TQ_OK
              : TQ_ERR_HIP;
+}
+
+extern "C" int tq_paged_decode_attention_append(const tq_layer_desc* layer, const void* q,
+                                                const void* k_new, const void* v_new, void* pages,
+                                                int64_t num_blocks, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                int32_t num_seqs, int32_t max_seq_len, float scale,
+                                                float* out, void* workspace, size_t workspace_bytes,
+                                                tq_stream_t stream) {
+  TqLayer L;
+  const int st = make_layer(layer, true, &L);
+  if (st != TQ_OK) return st;
+  if (!tq_decode_block_format(L) || L.norm_corr) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs > TQ_APPEND_MAX_SEQS) return TQ_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr || pages == nullptr || block_tables == nullptr))
+    return TQ_ERR_INVALID_ARG;
+  const TqAppend app{k_new, v_new, pages};
+  return paged_decode(layer, q, pages, num_blocks, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                      max_seq_len, nullptr, nullptr, 0, nullptr, nullptr, nullptr, 0, scale, out,
+                      workspace, workspace_bytes, stream, false, &app);
 }
 
 extern "C" int tq_paged_decode_attention(const tq_layer_desc* layer, const void* q,

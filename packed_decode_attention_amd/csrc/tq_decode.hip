@@ -1706,7 +1706,8 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
                      int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                      const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
                      const void* win_v, const int32_t* win_lens, int win_cap, float scale,
-                     float* out, void* workspace, void* stream, int nq, int q0, int g_real) {
+                     float* out, void* workspace, void* stream, int nq, int q0, int g_real,
+                     const TqAppend* app) {
   if (num_seqs == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
   DecodeArgs a;
@@ -1749,7 +1750,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
     int32_t* nsplit = (int32_t*)((uint8_t*)workspace + partials_bytes(L, num_seqs, sp, n_sink, win_cap));
     const int e = tq_launch_decode_block(L, q, pages, block_tables, max_blocks, seq_lens, num_seqs, sp,
                                          n_sink, a.win_lens, win_cap, a.qscale, a.partials, nsplit,
-                                         a.part_stride, nq, q0, a.g_real, stream);
+                                         a.part_stride, nq, q0, a.g_real, stream, app);
     if (e != 0) return e;
     a.nsplit_of = nsplit;
     // the block kernel's aligned pieces: about 256 / num_seqs per sequence

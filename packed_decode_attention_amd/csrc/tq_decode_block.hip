@@ -38,7 +38,8 @@
 
 #include <climits>
 
-#include "tq_device.h"
+#include "../../include/tq.h"
+#include "tq_quant_device.h"
 
 namespace {
 using namespace tqd;
@@ -61,7 +62,7 @@ constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (
 constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
 constexpr int kMaxRuns = 384;                  // runs per unit (six lanes' worth of run rows)
-constexpr int kPlanInts = 48;                  // LDS words of the work plan (3 per wave, 7 more)
+constexpr int kPlanInts = 48;                  // LDS words of the work plan (3 per wave, 8 more)
 constexpr int kGrid = 256;                     // workgroups: one per compute unit of the MI355X
 
 // Geometry of one page format: KB-bit keys, VB-bit values, up to GM query heads per kv head.
@@ -223,7 +224,24 @@ struct TqBlockArgs {
   int max_blocks, bs, bs_shift, G, Hq, n_sink, win_cap;
   int num_seqs, part_stride, max_pieces, max_parts, max_runs;
   int nq, q0, g_real;       // several queries per sequence (one: 1, 0, G)
+  // Fused append (k_new NULL: none).  The new token of each sequence, K and V rows [B][8][128]
+  // fp16, is quantized into the page slot of position seq_len - 1 by the workgroup whose share
+  // holds that position's run, before that workgroup loads any run.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* pages_w;         // the pages, written
+  const float* kt;          // key boundaries (2^KB - 1)
+  const float* vt;          // value boundaries
+  float rsqrt_d;            // 1 / sqrt(D)
 };
+
+// Sequences whose new token one workgroup quantizes at most (the host bounds the batch by it),
+// and the fused append's scratch in the last run buffer: boundaries [2][256] floats, the K and V
+// bucket tables, their shifts, the list of sequences.
+constexpr int kAppendMax = TQ_APPEND_MAX_SEQS;
+constexpr int kAppTabOff = 2048;
+constexpr int kAppShOff = kAppTabOff + 2 * 130 * 8;
+constexpr int kAppListOff = kAppShOff + 64;
 
 namespace {
 
@@ -305,7 +323,8 @@ __device__ __forceinline__ int units_in_share(int k, int rpw, int R, int n) {
 // n_own: the run count of sequence tid (0 past the batch), loaded by the caller at kernel entry so
 // the load overlaps the table fill.  A batch of at most kThreads sequences takes one pass over
 // the run counts; a larger one takes a second, kThreads sequences at a time.
-__device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave, int lane, const TqSeq& own) {
+__device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int* s_list, int tid, int wave, int lane,
+                           const TqSeq& own) {
   const int n_own = own.n_run;
   const int B = a.num_seqs;
   const bool one_pass = B <= kThreads;
@@ -333,7 +352,10 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
     s_plan[kWaves + wave] = nz;
     s_plan[2 * kWaves + wave] = mx;
   }
-  if (tid == 0) s_plan[3 * kWaves] = -1;
+  if (tid == 0) {
+    s_plan[3 * kWaves] = -1;
+    s_plan[3 * kWaves + 7] = 0;  // fused append: sequences in s_list
+  }
   __syncthreads();
   // the waves' totals, lane w holding wave w's, reduced across the wave
   const int st = wave_incl_scan(lane < kWaves ? s_plan[lane] : 0);
@@ -393,6 +415,14 @@ __device__ TqPlan make_plan(const TqBlockArgs& a, int* s_plan, int tid, int wave
     // (a sequence longer than the host's bound would have more partials than slots: those past
     // the bound are neither computed nor merged)
     if (k == 0) a.nsplit[b] = min(parts, a.max_parts);
+    // fused append: the workgroup holding the last run (the new token's) lists the sequence
+    if (a.k_new != nullptr && n > 0) {
+      const int owner = aligned ? rank * c + (n - 1) / ((n + c - 1) / c) : (R + n - 1) / cpw;
+      if (owner == k) {
+        const int i = atomicAdd(&s_plan[3 * kWaves + 7], 1);
+        if (i < kAppendMax) s_list[i] = b;
+      }
+    }
   };
   if (one_pass) {
     if (tid < B) place(tid, own, base + incl - n_own, base_nz + incl_nz - 1);
@@ -474,9 +504,90 @@ __device__ __forceinline__ void for_each_unit(const TqBlockArgs& a, const TqPlan
   }
 }
 
+// Destination of the fused append's stores for rows past the listed tokens (a tile's lanes all
+// store).
+__device__ __align__(16) uint8_t tq_block_append_discard[256];
+
+// Fused append: the new tokens of the n_list sequences in s_list (their last runs are this
+// workgroup's), quantized exactly as tq_quantize_kernel does (the same region code, Hadamard
+// operands and bucket tables) into the slots of their positions seq_len - 1, before the workgroup
+// loads any run.  Scratch in `region` (a run buffer no load has touched yet): boundaries, tables,
+// table shifts.  tk, tv: boundary j of K and V in lane j of wave 0.  Every thread calls it.
+template <int KB, int VB>
+__device__ __forceinline__ void append_tokens(const TqBlockArgs& a, uint8_t* region, const int* s_list,
+                                              int n_list, int tid, int wave, int lane, float tk, float tv) {
+  using F = Fmt<KB, VB, 4>;  // slot geometry
+  constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
+  float(*s_t)[256] = reinterpret_cast<float(*)[256]>(region);
+  uint2* const tabk = reinterpret_cast<uint2*>(region + kAppTabOff);
+  uint2* const tabv = tabk + tqq::qtab_entries(KB);
+  int* const s_sh = reinterpret_cast<int*>(region + kAppShOff);
+  if (wave == 0) {
+    if (lane < nbk) s_t[0][lane] = tk;
+    if (lane < nbv) s_t[1][lane] = tv;
+    // smallest gap between consecutive boundaries, which sit one per lane
+    const float tk1 = __shfl_down(tk, 1), tv1 = __shfl_down(tv, 1);
+    float gk = lane + 1 < nbk ? tk1 - tk : 2.0f;
+    float gv = lane + 1 < nbv ? tv1 - tv : 2.0f;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      gk = fminf(gk, __shfl_xor(gk, m));
+      gv = fminf(gv, __shfl_xor(gv, m));
+    }
+    if (lane == 0) {
+      s_sh[0] = tqq::qtab_shift(gk, KB);
+      s_sh[1] = tqq::qtab_shift(gv, VB);
+    }
+  }
+  __syncthreads();
+  const int shk = __builtin_amdgcn_readfirstlane(s_sh[0]), shv = __builtin_amdgcn_readfirstlane(s_sh[1]);
+  if (tid < kWG) tqq::build_qtabs<KB, VB>(s_t, shk, shv, tabk, tabv, tid);
+  __syncthreads();
+  if (wave < kW) {
+    uint4 A[kD / 32][2];
+    tqq::hadamard_operands<kD / 32>(a.signs, lane, A);
+    float zero;  // an addend of 0 the compiler cannot fold, as in tq_quantize_kernel
+    asm("v_mov_b32 %0, 0" : "=v"(zero));
+    const int c = lane & 15, g = lane >> 4;
+    const int n_rows = kH * n_list;  // (token, kv head) rows, 16 a tile
+    for (int T = wave; 16 * T < n_rows; T += kW) {
+      const int row = 16 * T + c;
+      const bool live = row < n_rows;
+      const int tok = (live ? row : n_rows - 1) / kH, h = row % kH;
+      const int b = s_list[tok];
+      const uint16_t* sk = a.k_new + ((int64_t)b * kH + h) * kD + 8 * g;
+      const uint16_t* sv = a.v_new + ((int64_t)b * kH + h) * kD + 8 * g;
+      uint4 xk[kD / 32], xv[kD / 32];
+#pragma unroll
+      for (int bb = 0; bb < kD / 32; ++bb) {
+        xk[bb] = *reinterpret_cast<const uint4*>(sk + 32 * bb);
+        xv[bb] = *reinterpret_cast<const uint4*>(sv + 32 * bb);
+      }
+      const int pos = a.seq_lens[b] - 1;
+      const int blk = a.bs_shift >= 0 ? (pos >> a.bs_shift) : (pos / a.bs);
+      const int64_t prow = (int64_t)a.bt[(int64_t)b * a.max_blocks + blk] * a.bs + (pos - blk * a.bs);
+      uint8_t* const dst = live ? a.pages_w + (prow * kH + h) * F::kSB : tq_block_append_discard;
+      if (shk != tqq::kQNoTable && shv != tqq::kQNoTable) {
+        tqq::quantize_region<kD, KB, true, false, false>(xk, A, zero, g, F::kKCode, s_t[0], tabk, shk,
+                                                          nullptr, a.rsqrt_d, dst);
+        tqq::quantize_region<kD, VB, true, false, false>(xv, A, zero, g, F::kVCode, s_t[1], tabv, shv,
+                                                          nullptr, a.rsqrt_d, dst + F::kVOff);
+      } else {  // a codebook too fine for its table: both regions by binary search
+        tqq::quantize_region<kD, KB, false, false, false>(xk, A, zero, g, F::kKCode, s_t[0], tabk, shk,
+                                                           nullptr, a.rsqrt_d, dst);
+        tqq::quantize_region<kD, VB, false, false, false>(xv, A, zero, g, F::kVCode, s_t[1], tabv, shv,
+                                                           nullptr, a.rsqrt_d, dst + F::kVOff);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the slots are written before any run is loaded
+  }
+  __syncthreads();
+}
+
 template <int KB, int VB, int GM>
 __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a) {
   using F = Fmt<KB, VB, GM>;
+  static_assert(kAppListOff + 4 * kAppendMax <= F::kRunBytes, "fused append scratch in one run buffer");
   constexpr int kSB = F::kSB, kVOff = F::kVOff, kRowBytes = F::kRowBytes, kRunBytes = F::kRunBytes;
   constexpr int kBuf0 = F::kBuf0, QC = F::kGroupChunks, NZ = F::kNZ;
   // One LDS array placed by hand: the tables at byte 0, run buffer k at kBuf0 + k run bytes, then
@@ -525,8 +636,20 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
   // The run buffers are written by the loads (which the compiler does not see as stores): one
   // ordinary store keeps it from treating the array as never written there.
   if (tid == 0) s_r0[0] = 0;
+  // fused append: the codebook boundaries, boundary j in lane j of wave 0 (they load with the
+  // sequence lengths)
+  float tk = 0.0f, tv = 0.0f;
+  if (a.k_new != nullptr && wave == 0) {
+    tk = a.kt[min(lane, (1 << KB) - 2)];
+    tv = a.vt[min(lane, (1 << VB) - 2)];
+  }
+  int* const s_list = reinterpret_cast<int*>(s_r4 + kAppListOff);
 
-  const TqPlan plan = make_plan(a, s_plan, tid, wave, lane, own);  // its barriers also cover the tables
+  const TqPlan plan = make_plan(a, s_plan, s_list, tid, wave, lane, own);  // its barriers also cover the tables
+  if (a.k_new != nullptr) {  // (the list length is the same in every wave)
+    const int n_list = __builtin_amdgcn_readfirstlane(min(s_plan[3 * kWaves + 7], kAppendMax));
+    if (n_list > 0) append_tokens<KB, VB>(a, s_r4, s_list, n_list, tid, wave, lane, tk, tv);
+  }
 
   if (wave >= kW) {
     // ======== producer waves: every page load of the workgroup ========
@@ -1045,7 +1168,8 @@ TqSplit tq_decode_block_split(int num_seqs, int max_seq_len) {
 int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                            int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                            int n_sink, const int32_t* win_lens, int win_cap, float qscale, float* partials,
-                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream) {
+                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream,
+                           const TqAppend* app) {
   if (sp.max_pieces < 3 || sp.max_runs < 1 || sp.max_split < sp.max_pieces || part_stride < sp.max_split)
     return (int)hipErrorInvalidValue;
   TqBlockArgs a;
@@ -1077,6 +1201,12 @@ int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, c
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real;
+  a.k_new = app != nullptr ? (const uint16_t*)app->k : nullptr;
+  a.v_new = app != nullptr ? (const uint16_t*)app->v : nullptr;
+  a.pages_w = app != nullptr ? (uint8_t*)app->pages : nullptr;
+  a.kt = L.kt;
+  a.vt = L.vt;
+  a.rsqrt_d = (float)(1.0 / __builtin_sqrt((double)kD));  // as tq_quantize_kernel takes it
   const hipStream_t st = (hipStream_t)stream;
   if (L.kb == 4) launch_block<4, 4, 4>(a, st);
   else if (L.G <= 4) launch_block<3, 2, 4>(a, st);

@@ -56,6 +56,14 @@ size_t tq_decode_ws_bytes_for(const TqLayer& L, int num_seqs, const TqSplit& sp,
 // value, 0 on success).
 int tq_noalloc_workspace(void** ptr);
 
+// Fused append of tq_paged_decode_attention_append: the new token of each sequence (K and V rows
+// [num_seqs][Hkv][D] fp16), quantized into the page slot of its position seq_len - 1.
+struct TqAppend {
+  const void* k;
+  const void* v;
+  void* pages;
+};
+
 // The whole-block streaming decode kernel (tq_decode_block.hip): the formats it serves, its split
 // geometry and its launch (the split kernel only; the caller launches fp16-row chunks and merge).
 bool tq_decode_block_format(const TqLayer& L);
@@ -63,7 +71,8 @@ TqSplit tq_decode_block_split(int num_seqs, int max_seq_len);
 int tq_launch_decode_block(const TqLayer& L, const void* q, const void* pages, const int32_t* block_tables,
                            int max_blocks, const int32_t* seq_lens, int num_seqs, const TqSplit& sp,
                            int n_sink, const int32_t* win_lens, int win_cap, float qscale, float* partials,
-                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream);
+                           int32_t* nsplit, int part_stride, int nq, int q0, int g_real, void* stream,
+                           const TqAppend* app = nullptr);
 
 // Launchers: return a hipError_t value (0 on success).
 int tq_launch_quantize(const TqLayer& L, const void* k, const void* v, const int64_t* slot_mapping,
@@ -73,7 +82,7 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
                      const void* sink_k, const void* sink_v, int n_sink, const void* win_k,
                      const void* win_v, const int32_t* win_lens, int win_cap, float scale,
                      float* out, void* workspace, void* stream, int nq = 1, int q0 = 0,
-                     int g_real = 0);
+                     int g_real = 0, const TqAppend* app = nullptr);
 int tq_launch_dequant(const TqLayer& L, const void* pages, const int64_t* slots, int64_t n,
                       float* k_out, float* v_out, void* stream);
 

@@ -7,7 +7,10 @@ could silently break:
     memory counter (every page byte reaches them through LDS, loaded by the producer waves);
   * the producer waves' loop loads with buffer_load ... lds, touches no scratch and waits only
     with the counted waits the source writes (a compiler-inserted vmcnt(0) would drain the runs
-    in flight).
+    in flight);
+  * the fused append's tile loop (the only other loop with matrix-core work) holds no barrier, so
+    every wave passes the workgroup's barriers the same number of times whatever its share of
+    the new tokens.
 """
 
 import os
@@ -82,10 +85,19 @@ def _innermost_loops(body):
 
 
 def _classify(body):
+    """Innermost loops: the compute waves' step loop (matrix-core work and the step barrier) and
+    the producers' loop (LDS loads); _append_loops gives the rest with matrix-core work."""
     loops = _innermost_loops(body)
-    compute = [v for v in loops.values() if any(i.startswith("v_mfma") for i in v)]
+    compute = [v for v in loops.values()
+               if any(i.startswith("v_mfma") for i in v) and any(i.startswith("s_barrier") for i in v)]
     producer = [v for v in loops.values() if any(i.startswith("buffer_load") for i in v)]
     return compute, producer
+
+
+def _append_loops(body):
+    loops = _innermost_loops(body)
+    return [v for v in loops.values()
+            if any(i.startswith("v_mfma") for i in v) and not any(i.startswith("s_barrier") for i in v)]
 
 
 def test_every_instance_has_one_compute_loop_and_one_producer_loop(asm):
@@ -115,6 +127,15 @@ def test_producer_loop_waits_only_counted(asm):
         assert not [i for i in loop if re.match(r"(global|scratch|flat)_", i)], (kb, vb, gm)
         waits = [int(m.group(1)) for i in loop for m in [re.search(r"vmcnt\((\d+)\)", i)] if m]
         assert waits and set(waits) <= producer_waits(kb, vb), ((kb, vb, gm), sorted(set(waits)))
+
+
+def test_append_loop_has_no_barrier(asm):
+    for key, body in _kernels(asm).items():
+        loops = _append_loops(body)
+        assert len(loops) == 1, (key, len(loops))
+        (loop,) = loops
+        assert any(i.startswith("global_load") for i in loop), key  # the new rows, straight to registers
+        assert sum(1 for i in loop if i.startswith("v_mfma")) >= 2 * 2 * 4, key  # K and V, two tiles of 4 blocks
 
 
 def test_no_indexed_private_arrays(asm):

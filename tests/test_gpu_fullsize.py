@@ -191,3 +191,49 @@ def test_full_size_sampled(name, layer, which, window, nc, nq):
             max_abs, rel = check_attention(got[b:b + 1, qh], want)
         print(f"[fullsize]   seq {b} kv head {hh}: decode max-abs {max_abs:.2e}, rel L2 {rel:.2e}",
               flush=True)
+
+
+FUSED = [("llama3-8b", 1), ("ragged", 5)]
+
+
+@pytest.mark.parametrize("name,layer", FUSED, ids=[f"{n}-L{l}" for n, l in FUSED])
+def test_full_size_fused_append(name, layer):
+    """The benchmark's step at full size: tq_paged_decode_attention_append against
+    tq_quantize_append + tq_paged_decode_attention on the same filled layer.  Pages (all of them)
+    and outputs must be identical bit for bit; the two-call path is held to the oracle above."""
+    import torch
+    import packed_decode_attention_amd as tq
+    from packed_decode_attention_amd import workloads as wl
+    bench = _bench()
+
+    w = wl.WORKLOADS[name]
+    kb, vb = w.bits(layer)
+    B, H, D, Hq, bs = w.num_seqs, w.num_kv_heads, w.head_dim, w.num_q_heads, w.block_size
+    lens = wl.seq_lens(w)
+    bt_np, num_blocks = wl.block_tables(w, lens)
+    ctx_np, new_np = bench.context_slots(w, bt_np, lens, wl)
+    print(f"[fullsize] fused append {name} layer {layer} K{kb}/V{vb}: B={B} max_len={int(lens.max())}",
+          flush=True)
+    fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0)
+    assert tq.decode_kernel_names(D, kb, vb, False, H, Hq // H)[0] == "tq_decode_block_kernel"
+    ctx_pages = fmt.new_pages(num_blocks)
+    bench.fill_layer(w, layer, fmt, ctx_pages, torch.from_numpy(ctx_np).cuda(), num_blocks, torch, tq, wl)
+    new_k, new_v = bench.new_tokens(w, 1, wl)
+    q = wl.queries(w, layer, 0, "cuda")
+    bt, sl = torch.from_numpy(bt_np).cuda(), torch.from_numpy(lens).cuda()
+    max_len = int(lens.max())
+
+    pages_two = ctx_pages.clone()
+    out_two = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_quantize_append(fmt.desc, new_k[0, layer], new_v[0, layer], torch.from_numpy(new_np).cuda(),
+                          pages_two, num_blocks)
+    tq.tq_paged_decode_attention(fmt.desc, q, pages_two, num_blocks, bt, sl, max_len, out_two,
+                                 fmt.new_workspace(B, max_len))
+    pages_one = ctx_pages
+    out_one = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_paged_decode_attention_append(fmt.desc, q, new_k[0, layer], new_v[0, layer], pages_one,
+                                        num_blocks, bt, sl, max_len, out_one, fmt.new_workspace(B, max_len))
+    torch.cuda.synchronize()
+    assert torch.equal(pages_one, pages_two)
+    assert torch.equal(out_one.view(torch.int32), out_two.view(torch.int32))
+    print(f"[fullsize]   pages ({pages_one.numel() / 1e6:.0f} MB) and outputs identical", flush=True)

@@ -138,6 +138,21 @@ def test_argument_validation_before_launch(lib):
     # a split grid beyond 32-bit workgroup counts
     assert dec(_desc(lib), B=65535, max_len=2 ** 31 - 1, mb=2 ** 27) == E.TQ_ERR_UNSUPPORTED
 
+    def deca(d, B=4, kn=P, ws_bytes=1 << 40, mb=7, pages=P):
+        return so.tq_paged_decode_attention_append(ctypes.byref(d), P, kn, kn, pages, 100, P, mb, P, B,
+                                                   100, 0.0, P, P, ws_bytes, None)
+    assert deca(_desc(lib, k_bits=8)) == E.TQ_ERR_UNSUPPORTED             # not a whole-block format
+    assert deca(_desc(lib, v_centroids=0x30000)) == E.TQ_ERR_UNSUPPORTED  # K4/V4 with two codebooks
+    assert deca(_desc(lib, flags=1)) == E.TQ_ERR_UNSUPPORTED              # norm correction
+    assert deca(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
+    assert deca(_desc(lib), B=513) == E.TQ_ERR_UNSUPPORTED                # above TQ_APPEND_MAX_SEQS
+    assert deca(_desc(lib), kn=None) == E.TQ_ERR_INVALID_ARG
+    assert deca(_desc(lib), pages=None) == E.TQ_ERR_INVALID_ARG
+    assert deca(_desc(lib), ws_bytes=16) == E.TQ_ERR_WORKSPACE
+    assert deca(_desc(lib), mb=6) == E.TQ_ERR_INVALID_ARG                 # 6 * 16 < 100 tokens
+    assert deca(_desc(lib), B=0, kn=None) == E.TQ_OK                      # nothing to do
+    assert deca(_desc(lib), B=-1) == E.TQ_ERR_INVALID_ARG
+
     def decw(d, cap=16, wk=P, wl=P, B=4):
         return so.tq_paged_decode_attention_window(ctypes.byref(d), P, P, 100, P, 7, P, B, 100, None,
                                                    None, 0, wk, wk, wl, cap, 0.0, P, P, 1 << 40, None)
