@@ -165,17 +165,17 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, 
 
 
 def run_step(w, S, tq, step, ev=None):
+    """One step over all layers; ev maps layer -> (a0, a1, d1) events for the calls to time."""
     for l, L in enumerate(S["layers"]):
-        if ev is not None:
-            ev["a0"][l].record()
-        if L.fused:  # the new token's append inside the decode call
-            if ev is not None:
-                ev["a1"][l].record()
+        e = None if ev is None else ev.get(l)
+        if e is not None:
+            e[0].record()
+        if L.fused:  # the new token's append inside the decode call (a0 starts the call)
             tq.tq_paged_decode_attention_append(L.fmt.desc, S["qs"][l], S["new_k"][step, l],
                                                 S["new_v"][step, l], L.pages, L.num_blocks, S["bt"],
                                                 S["seq_lens"], S["max_len"], S["out"], S["ws"])
-            if ev is not None:
-                ev["d1"][l].record()
+            if e is not None:
+                e[2].record()
             continue
         # with a hot window the quantized token is the one leaving the window, and the new token
         # takes its row in the window (a ring: row step % W)
@@ -191,8 +191,8 @@ def run_step(w, S, tq, step, ev=None):
             r = step % S["hot_window"]
             L.win_k[:, r].copy_(S["new_k"][step, l])
             L.win_v[:, r].copy_(S["new_v"][step, l])
-        if ev is not None:
-            ev["a1"][l].record()
+        if e is not None:
+            e[1].record()
         if S["n_queries"] > 1:
             tq.tq_paged_decode_attention_multi(L.fmt.desc, S["qs"][l], L.pages, L.num_blocks, S["bt"],
                                                S["seq_lens"], S["max_len"], S["out"], S["ws"],
@@ -206,8 +206,8 @@ def run_step(w, S, tq, step, ev=None):
                                                 S["seq_lens"], S["max_len"], S["out"], S["ws"],
                                                 L.win_k, L.win_v, S["win_lens"], S["sink_k"],
                                                 S["sink_v"], w.n_sink)
-        if ev is not None:
-            ev["d1"][l].record()
+        if e is not None:
+            e[2].record()
 
 
 def algorithmic_bytes(w, lens, tq, win_lens=None, n_queries=1, flags=0):
@@ -450,21 +450,26 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(w.layers * args.steps)]
-          for k in ("a0", "a1", "d1")}
+    # HIP events around the calls of one layer in eight per timed step (step s times layers
+    # s mod 8, s mod 8 + 8, ...): an event between two launches costs the stream a few
+    # microseconds, which events around every call would add to the step time
+    sampled = []  # (layer, (a0, a1, d1))
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for s in range(args.steps):
-        sub = {k: v[s * w.layers:(s + 1) * w.layers] for k, v in ev.items()}
-        run_step(w, S, tq, args.warmup + s, sub)
+        ev = {l: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+              for l in range(s % 8, w.layers, 8)}
+        sampled += list(ev.items())
+        run_step(w, S, tq, args.warmup + s, ev)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    n = w.layers * args.steps
-    dec_ms = np.array([ev["a1"][i].elapsed_time(ev["d1"][i]) for i in range(n)])
-    app_ms = np.array([ev["a0"][i].elapsed_time(ev["a1"][i]) for i in range(n)])
+    fused_l = [S["layers"][l].fused for l, _ in sampled]
+    dec_ms = np.array([(e[0] if f else e[1]).elapsed_time(e[2]) for f, (_, e) in zip(fused_l, sampled)])
+    app_ms = np.array([0.0 if f else e[0].elapsed_time(e[1]) for f, (_, e) in zip(fused_l, sampled)])
+    n = len(sampled)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; "
         f"{'append + decode' if all(fused) else 'decode'} {dec_ms.mean() * 1e3:.1f} us/layer "
         f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
@@ -481,7 +486,7 @@ def main():
     # a fused call also reads the new rows and writes their slots
     app_bytes = [w.num_seqs * w.num_kv_heads * (4 * w.head_dim + tq.tq_slot_bytes_ex(w.head_dim, *w.bits(l), fmt_flags))
                  if fused[l] else 0 for l in range(w.layers)]
-    layer_ids = np.arange(n) % w.layers
+    layer_ids = [l for l, _ in sampled]
     dec_bytes = np.array([per_layer_bytes[i] + app_bytes[i] for i in layer_ids], np.float64)
     achieved = float(dec_bytes.sum() / (dec_ms.sum() / 1e3) / 1e9)
     bulk_ms = float(np.mean(S["bulk_ms"])) if S["bulk_ms"] else float("nan")
