@@ -511,8 +511,11 @@ __device__ __align__(16) uint8_t tq_block_append_discard[256];
 // Fused append: the new tokens of the n_list sequences in s_list (their last runs are this
 // workgroup's), quantized exactly as tq_quantize_kernel does (the same region code, Hadamard
 // operands and bucket tables) into the slots of their positions seq_len - 1, before the workgroup
-// loads any run.  Scratch in `region` (a run buffer no load has touched yet): boundaries, tables,
-// table shifts.  tk, tv: boundary j of K and V in lane j of wave 0.  Every thread calls it.
+// loads any run that holds one.  Scratch in `region` (the last run buffer, which takes a run only
+// after the first unit's first step): boundaries, tables, table shifts.  tk, tv: boundary j of K
+// and V in lane j of wave 0.  Every thread calls it, at the same point of the first unit; its
+// barriers leave the producers' run loads in flight, and the compute waves' stores are complete
+// at the last one.
 template <int KB, int VB>
 __device__ __forceinline__ void append_tokens(const TqBlockArgs& a, uint8_t* region, const int* s_list,
                                               int n_list, int tid, int wave, int lane, float tk, float tv) {
@@ -539,10 +542,10 @@ __device__ __forceinline__ void append_tokens(const TqBlockArgs& a, uint8_t* reg
       s_sh[1] = tqq::qtab_shift(gv, VB);
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int shk = __builtin_amdgcn_readfirstlane(s_sh[0]), shv = __builtin_amdgcn_readfirstlane(s_sh[1]);
   if (tid < kWG) tqq::build_qtabs<KB, VB>(s_t, shk, shv, tabk, tabv, tid);
-  __syncthreads();
+  lds_barrier();
   if (wave < kW) {
     uint4 A[kD / 32][2];
     tqq::hadamard_operands<kD / 32>(a.signs, lane, A);
@@ -581,7 +584,14 @@ __device__ __forceinline__ void append_tokens(const TqBlockArgs& a, uint8_t* reg
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the slots are written before any run is loaded
   }
-  __syncthreads();
+  lds_barrier();
+}
+
+// The producer waves' part of append_tokens: its three barriers (they do none of its work).
+__device__ __forceinline__ void append_barriers() {
+  lds_barrier();
+  lds_barrier();
+  lds_barrier();
 }
 
 template <int KB, int VB, int GM>
@@ -646,10 +656,12 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
   int* const s_list = reinterpret_cast<int*>(s_r4 + kAppListOff);
 
   const TqPlan plan = make_plan(a, s_plan, s_list, tid, wave, lane, own);  // its barriers also cover the tables
-  if (a.k_new != nullptr) {  // (the list length is the same in every wave)
-    const int n_list = __builtin_amdgcn_readfirstlane(min(s_plan[3 * kWaves + 7], kAppendMax));
-    if (n_list > 0) append_tokens<KB, VB>(a, s_r4, s_list, n_list, tid, wave, lane, tk, tv);
-  }
+  // fused append: the sequences whose new token this workgroup writes (the same count in every
+  // wave); the compute waves quantize them before their first unit, the producers pass the same
+  // barriers in theirs
+  const int n_list = a.k_new != nullptr
+                         ? __builtin_amdgcn_readfirstlane(min(s_plan[3 * kWaves + 7], kAppendMax)) : 0;
+  bool first_unit = true;
 
   if (wave >= kW) {
     // ======== producer waves: every page load of the workgroup ========
@@ -680,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
     };
-    for_each_unit(a, plan, [&](const TqSeq&, int b, int run_first, int n_run, int) {
+    for_each_unit(a, plan, [&](const TqSeq& sq, int b, int run_first, int n_run, int) {
       lds_barrier();  // every wave is done with the previous unit's buffers
       // page rows of runs run_first + lane + 64 i (clamped to the last run)
       int rows[kMaxRuns / 64];
@@ -696,11 +708,22 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
         for (int i = 0; i < F::kLoadsHi; ++i)
           if (i < F::kLoadsLo || more) lds_dma16(rs, buf + 1024 * (pw + 4 * i), src_off[i]);
       };
+      // fused append (first unit): runs 0..3 go out while the compute waves quantize the new
+      // tokens, unless one of them holds a new token (a unit of at most four runs ending its
+      // sequence), which must wait for the slot's store.  The compute waves pass their three
+      // append barriers, then this unit's start barrier: counted together with this one, the
+      // stores complete at the third, before the fourth that precedes an early issue; a later
+      // run holding a token is issued after the first step's barrier, the fifth.
+      const bool append = first_unit && n_list > 0;
+      const bool token_early = n_run <= 4 && run_first + n_run == sq.run0 + sq.n_run;
+      first_unit = false;
+      if (append && token_early) append_barriers();
       // runs 0..3 (the last buffer may hold the compute waves' queries until the first barrier)
       issue(0, lds_ptr(s_r0));
       if (n_run > 1) issue(1, lds_ptr(s_r1));
       if (n_run > 2) issue(2, lds_ptr(s_r2));
       if (n_run > 3) issue(3, lds_ptr(s_r3));
+      if (append && !token_early) append_barriers();
       wait_later(min(n_run - 1, 3));  // run 0 is in
       lds_barrier();
       if (n_run > 4) issue(4, lds_ptr(s_r4));
@@ -723,6 +746,10 @@ __global__ __launch_bounds__(kThreads) void tq_decode_block_kernel(TqBlockArgs a
   }
 
   // ======== compute waves: wave h computes kv head h ========
+  // fused append first: its three barriers precede the first unit's start barrier here, and meet
+  // the producers' first unit start, then their two or three append barriers (barriers are counted,
+  // not named: either way the slots are stored before the producers load a run that holds one)
+  if (n_list > 0) append_tokens<KB, VB>(a, s_r4, s_list, n_list, tid, wave, lane, tk, tv);
   const int h = wave;
   const uint8_t* const tab = reinterpret_cast<const uint8_t*>(s_tab);
   const uint32_t kcopy = 8u * (uint32_t)(lane & 31);
