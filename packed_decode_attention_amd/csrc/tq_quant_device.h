@@ -200,16 +200,55 @@ __device__ __forceinline__ void centre_row(const uint4 (&x)[NB], float& mu, floa
   }
 }
 
-// One region (K or V, BITS-bit codes) of the wave's 16 rows: norm, rotation, decisions, packing,
-// store.  TABLE: decisions by the bucket table (resolution 2^sh), else by binary search.
+// What one lane stores for one region of its row: the packed run it owns (4 BITS bytes: two
+// 16-byte pieces at 8 bits, 16, 12 or 8 bytes below), the stored norm and, in the mean-removal
+// format, the mean.
+template <int BITS>
+struct RegionBits {
+  uint32_t w[BITS == 8 ? 8 : BITS == 4 ? 4 : BITS == 3 ? 3 : 2];
+  float n_store, mu;
+};
+
+// Stores of one region: lane g < NB its run, lane 0 of the row the norm (and mean).  Every lane
+// stores (rows with no slot write to the discard buffer), so a region issues a fixed number of
+// stores: region_stores(BITS).
+template <int D, int BITS, bool MEAN>
+__device__ __forceinline__ void store_region(const RegionBits<BITS>& r, int g, int code_bytes,
+                                             uint8_t* __restrict__ dst) {
+  constexpr int NB = D / 32;
+  if (NB == 4 || g < NB) {
+    uint8_t* run = dst + 4 * BITS * g;
+    if constexpr (BITS == 8) {
+      uint4* o = reinterpret_cast<uint4*>(run);
+      o[0] = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+      o[1] = make_uint4(r.w[4], r.w[5], r.w[6], r.w[7]);
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint4*>(run) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    } else if constexpr (BITS == 3) {
+      *reinterpret_cast<uint3*>(run) = make_uint3(r.w[0], r.w[1], r.w[2]);
+    } else {
+      *reinterpret_cast<uint2*>(run) = make_uint2(r.w[0], r.w[1]);
+    }
+  }
+  if (g == 0) {
+    if constexpr (MEAN)
+      *reinterpret_cast<uint2*>(dst + code_bytes) = make_uint2(__float_as_uint(r.n_store), __float_as_uint(r.mu));
+    else
+      *reinterpret_cast<float*>(dst + code_bytes) = r.n_store;
+  }
+}
+
+// One region (K or V, BITS-bit codes) of the wave's 16 rows: norm, rotation, decisions, packing;
+// the lane's share of the stores is returned (store_region writes it).  TABLE: decisions by the
+// bucket table (resolution 2^sh), else by binary search.
 // NC: norm-correction format (the stored norm is n / ||c[idx]||; s_c holds the centroids).
 // MEAN: mean-removal format (the centred row is rotated; the mean is stored after the norm).
 template <int D, int BITS, bool TABLE, bool NC, bool MEAN>
-__device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const uint4 (&A)[D / 32][2],
-                                                float zero, int g, int code_bytes,
-                                                const float* s_t, const uint2* tab, int sh,
-                                                const float* s_c, float rsqrt_d,
-                                                uint8_t* __restrict__ dst) {
+__device__ __forceinline__ RegionBits<BITS> quantize_region_bits(const uint4 (&x)[D / 32],
+                                                                 const uint4 (&A)[D / 32][2], float zero,
+                                                                 const float* __restrict__ s_t,
+                                                                 const uint2* __restrict__ tab, int sh,
+                                                                 const float* __restrict__ s_c, float rsqrt_d) {
   constexpr int NB = D / 32;
   float n, mu = 0.0f;
   uint4 xh[NB], xl[NB];
@@ -279,9 +318,7 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
 
   // Pack: run a (the lane's 8 codes at rotated coordinates 32 a + 8 g ..) is bytes BITS (4 a + g)
   // .. BITS (4 a + g + 1) - 1 of the region.  The four lanes of a row transpose their runs, so lane
-  // g < NB then holds the whole 4 BITS-byte run g (its pieces from lanes 0..3 in order) and stores
-  // it in one or two instructions; then the norm.  Every lane stores (rows with no slot write to
-  // the discard buffer), so a region issues a fixed number of stores.
+  // g < NB then holds the whole 4 BITS-byte run g (its pieces from lanes 0..3 in order).
   uint32_t lo[4], hi[4];  // per run: the piece's bits (lo) and, for 8-bit codes, its upper dword
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -299,27 +336,38 @@ __device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const 
   }
   transpose_groups(lo);
   if constexpr (BITS == 8) transpose_groups(hi);
-  if (NB == 4 || g < NB) {
-    uint8_t* run = dst + 4 * BITS * g;
-    if constexpr (BITS == 8) {
-      uint4* o = reinterpret_cast<uint4*>(run);
-      o[0] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
-      o[1] = make_uint4(lo[2], hi[2], lo[3], hi[3]);
-    } else if constexpr (BITS == 4) {
-      *reinterpret_cast<uint4*>(run) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    } else if constexpr (BITS == 3) {  // four 24-bit pieces: 12 bytes
-      *reinterpret_cast<uint3*>(run) = make_uint3(lo[0] | (lo[1] << 24), (lo[1] >> 8) | (lo[2] << 16),
-                                                  (lo[2] >> 16) | (lo[3] << 8));
-    } else {  // four 16-bit pieces: 8 bytes
-      *reinterpret_cast<uint2*>(run) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+  RegionBits<BITS> r;
+  r.n_store = n_store;
+  r.mu = mu;
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      r.w[2 * a] = lo[a];
+      r.w[2 * a + 1] = hi[a];
     }
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) r.w[a] = lo[a];
+  } else if constexpr (BITS == 3) {  // four 24-bit pieces: 12 bytes
+    r.w[0] = lo[0] | (lo[1] << 24);
+    r.w[1] = (lo[1] >> 8) | (lo[2] << 16);
+    r.w[2] = (lo[2] >> 16) | (lo[3] << 8);
+  } else {  // four 16-bit pieces: 8 bytes
+    r.w[0] = lo[0] | (lo[1] << 16);
+    r.w[1] = lo[2] | (lo[3] << 16);
   }
-  if (g == 0) {
-    if constexpr (MEAN)
-      *reinterpret_cast<uint2*>(dst + code_bytes) = make_uint2(__float_as_uint(n_store), __float_as_uint(mu));
-    else
-      *reinterpret_cast<float*>(dst + code_bytes) = n_store;
-  }
+  return r;
+}
+
+// One region quantized and stored at once.
+template <int D, int BITS, bool TABLE, bool NC, bool MEAN>
+__device__ __forceinline__ void quantize_region(const uint4 (&x)[D / 32], const uint4 (&A)[D / 32][2],
+                                                float zero, int g, int code_bytes,
+                                                const float* s_t, const uint2* tab, int sh,
+                                                const float* s_c, float rsqrt_d,
+                                                uint8_t* __restrict__ dst) {
+  const RegionBits<BITS> r = quantize_region_bits<D, BITS, TABLE, NC, MEAN>(x, A, zero, s_t, tab, sh, s_c, rsqrt_d);
+  store_region<D, BITS, MEAN>(r, g, code_bytes, dst);
 }
 
 // Bucket table of one codebook (see above), entries i0 .. i0 + kPer - 1 of this thread: entry

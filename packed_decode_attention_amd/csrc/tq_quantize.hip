@@ -158,10 +158,22 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MEAN ? 3 : 
       for (int i = L.slot_bytes + g; i < L.stride; i += 4) dst[i] = 0;  // padding, before the loads
       if (T + tstep < n_tiles) issue(T + tstep);
 
-      quantize_region<D, KB, kTable, NC, MEAN>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk,
-                                               s_c[0], rsqrt_d, dst);
-      quantize_region<D, VB, kTable, NC, MEAN>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv,
-                                               s_c[1], rsqrt_d, dst + L.kreg);
+      if constexpr (NC || MEAN) {  // each region stored as it is done
+        quantize_region<D, KB, kTable, NC, MEAN>(xk, A, zero, g, L.kcode_bytes, s_t[0], tabk, shk,
+                                                 s_c[0], rsqrt_d, dst);
+        quantize_region<D, VB, kTable, NC, MEAN>(xv, A, zero, g, L.vcode_bytes, s_t[1], tabv, shv,
+                                                 s_c[1], rsqrt_d, dst + L.kreg);
+      } else {
+        // Both regions first, then all of the tile's stores back to back: a row's K and V bytes
+        // share cache lines, which then fill completely before the L2 can write them back (K
+        // stored while V was still being computed left lines to be written back in two parts).
+        const RegionBits<KB> rk = quantize_region_bits<D, KB, kTable, NC, MEAN>(xk, A, zero, s_t[0], tabk,
+                                                                               shk, s_c[0], rsqrt_d);
+        const RegionBits<VB> rv = quantize_region_bits<D, VB, kTable, NC, MEAN>(xv, A, zero, s_t[1], tabv,
+                                                                               shv, s_c[1], rsqrt_d);
+        store_region<D, KB, MEAN>(rk, g, L.kcode_bytes, dst);
+        store_region<D, VB, MEAN>(rv, g, L.vcode_bytes, dst + L.kreg);
+      }
     }
   };
   if (shk != kQNoTable && shv != kQNoTable) tile_loop(std::true_type{});
