@@ -412,6 +412,10 @@ def main():
     ap.add_argument("--separate-append", action="store_true",
                     help="time tq_quantize_append and tq_paged_decode_attention as two calls even "
                          "where the fused call serves the format")
+    ap.add_argument("--graph", action="store_true",
+                    help="also replay each timed step as one captured HIP graph (the host launches "
+                         "one graph per step instead of every kernel); value and ms_per_step are "
+                         "then the replayed steps'")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure the streaming ceilings of the workload's access patterns "
                          "(the diagnostic kernel of include/tq_probe.h)")
@@ -475,6 +479,29 @@ def main():
         f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); "
         + ("append fused into the decode call" if all(fused) else f"append {app_ms.mean() * 1e3:.1f} us/layer"))
 
+    eager_ms_per_step = ms_per_step
+    if args.graph:
+        # the same steps (same inputs, same slots) captured one graph each, replayed once untimed,
+        # then timed; every kernel of the eager step runs in the replay
+        graphs = []
+        for s in range(args.steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(w, S, tq, args.warmup + s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for g in graphs:
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(stop) / args.steps
+        log(f"graph replay of the {args.steps} steps: {ms_per_step:.3f} ms/step "
+            f"(eager {eager_ms_per_step:.3f})")
+
     lens = S["lens"]
     kv_tokens_step = int(lens.sum()) * w.layers
     value = kv_tokens_step / (ms_per_step / 1e3)
@@ -513,7 +540,8 @@ def main():
                                + (", QJL key format" if args.qjl else "")
                                + (f", {args.queries} causal queries per sequence" if args.queries > 1 else ""),
                    "kv_tokens_per_layer": int(lens.sum()),
-                   "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"},
+                   "layers": w.layers, "step": "per layer: quantize-append 1 token/seq + paged decode attention"
+                   + (", each step replayed as one captured HIP graph" if args.graph else "")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (None if (args.hot_window or args.queries > 1 or args.mean_removal
@@ -530,6 +558,8 @@ def main():
                    "bulk_fill_frac": bulk_bytes / (bulk_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                    "bulk_rows": S["bulk_rows"]},
     }
+    if args.graph:
+        result["eager_ms_per_step"] = eager_ms_per_step
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
