@@ -123,8 +123,8 @@ def setup(w, torch, tq, wl, n_steps_total, hot_window=0, norm_correction=False, 
         bulk_rows = n_ctx * H
         st = LayerState(fmt, pages, num_blocks)
         st.fused = (fused and fmt.flags == 0 and not hot_window and n_queries == 1 and w.n_sink == 0
-                    and B <= tq.TQ_APPEND_MAX_SEQS and tq.decode_kernel_names(
-                        D, kb, vb, False, H, w.group, 0)[0] == "tq_decode_block_kernel")
+                    and B <= tq.TQ_APPEND_MAX_SEQS and w.block_size % 16 == 0 and tq.decode_kernel_names(
+                        D, kb, vb, False, H, w.group, 0)[0] in ("tq_decode_block_kernel", "tq_decode_mfma_kernel"))
         if hot_window:  # the last hot_window positions as fp16 rows (their page slots are ignored)
             g = wl.generator(w.seed * 7919 + l, dev)
             shape = (B, hot_window, H, D)

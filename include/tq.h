@@ -226,16 +226,18 @@ int tq_paged_decode_attention_noalloc(const tq_layer_desc* layer, const void* q,
  * (turboquant-serve 0.1.2, "Architecture": each new row is rotated, normalised, encoded and packed
  *  as it is stored; tq-kv, "Custom CUDA Kernel Stack": split-KV flash decode on the compressed
  *  pages.)  The quantization is done by the decode kernel itself, by the workgroup that reads the
- *  new token's run, before it loads any run, so the step costs no separate launch.
+ *  new token's run (of that kv head, in the split-kernel formats), before it loads any run, so the
+ *  step costs no separate launch.
  *   k_new, v_new  device fp16 [num_seqs][num_kv_heads][D]: the new token's rows; seq_lens counts
  *                 the new token
  *   pages         device, written (the new slots) and read
- * Other arguments as for tq_paged_decode_attention.  TQ_ERR_UNSUPPORTED unless the layer is one
- * the whole-block decode kernel serves (D = 128, eight kv heads, unpadded slots, block size a
- * multiple of 16, K4/V4 with one codebook for K and V and up to four query heads per kv head, or
- * K3/V2 with up to eight; no format flag) and num_seqs <= TQ_APPEND_MAX_SEQS; such callers use
- * tq_quantize_append and tq_paged_decode_attention.  The workspace is that of
- * tq_decode_workspace_bytes. */
+ * Other arguments as for tq_paged_decode_attention.  TQ_ERR_UNSUPPORTED unless no format flag is
+ * set, the block size is a multiple of 16, num_seqs <= TQ_APPEND_MAX_SEQS, and the layer is one the
+ * whole-block decode kernel serves (D = 128, eight kv heads, unpadded slots, K4/V4 with one
+ * codebook for K and V and up to four query heads per kv head, or K3/V2 with up to eight) or one
+ * the matrix-core split kernel serves (D = 128 with K codes of 2, 3, 4 or 8 bits and V codes of 2,
+ * 4 or 8 bits; D = 64 with K and V codes of 4 or 8 bits); other callers use tq_quantize_append
+ * and tq_paged_decode_attention.  The workspace is that of tq_decode_workspace_bytes. */
 #define TQ_APPEND_MAX_SEQS 512
 int tq_paged_decode_attention_append(const tq_layer_desc* layer, const void* q, const void* k_new,
                                      const void* v_new, void* pages, int64_t num_blocks,

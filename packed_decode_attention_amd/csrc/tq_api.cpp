@@ -174,7 +174,7 @@ extern "C" int tq_paged_decode_attention_append(const tq_layer_desc* layer, cons
   TqLayer L;
   const int st = make_layer(layer, true, &L);
   if (st != TQ_OK) return st;
-  if (!tq_decode_block_format(L) || L.norm_corr) return TQ_ERR_UNSUPPORTED;
+  if (!tq_decode_append_format(L)) return TQ_ERR_UNSUPPORTED;
   if (num_seqs > TQ_APPEND_MAX_SEQS) return TQ_ERR_UNSUPPORTED;
   if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr || pages == nullptr || block_tables == nullptr))
     return TQ_ERR_INVALID_ARG;

@@ -30,6 +30,7 @@
 
 #include "../../include/tq.h"
 #include "tq_device.h"
+#include "tq_quant_device.h"
 
 namespace {
 using namespace tqd;
@@ -71,6 +72,11 @@ struct DecodeArgs {
   // each of this launch's queries q0 .. q0 + G / G_real - 1 out of nq (one query: nq = 1, q0 = 0,
   // g_real = G).
   int nq, q0, g_real;
+  // Fused append (k_new NULL: none): the new token of each sequence, K and V rows [B][Hkv][D]
+  // fp16, quantized into the page slot of position seq_len - 1 by the last split's workgroup.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* pages_w;  // the pages, written
 };
 
 // Row (in units of D) of q and out for head v of kv head h: query q0 + v / g_real, query head
@@ -781,6 +787,57 @@ __device__ __forceinline__ uint4 k_operand(const typename OpTable<KB>::E* tab, c
   }
 }
 
+// Destination of the fused append's stores from the lanes of rows other than the new token's (a
+// tile's lanes all store).
+__device__ __align__(16) uint8_t tq_decode_append_discard[512];  // >= the largest plain slot (264 B)
+
+// Fused append, one wave: the new token's K and V rows of kv head h of sequence b, quantized
+// exactly as tq_quantize_kernel does (the same region code and Hadamard operands; decisions by
+// binary search over the fp32 boundaries, which select the codes the quantizer's bucket table
+// selects) into the slot of position seq_len - 1.  The wave's 16 tile rows all hold that row;
+// lanes of row 0 store to the page, the others to the discard buffer.  s_t: [2][256] LDS floats
+// of this wave.  The stores are complete on return.
+template <int D, int KB, int VB>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int b, int h, int seq_len, int lane,
+                                           float (*s_t)[256]) {
+  const TqLayer& L = a.L;
+  constexpr int NB = D / 32;
+  constexpr int nbk = (1 << KB) - 1, nbv = (1 << VB) - 1;
+  const int c = lane & 15, g = lane >> 4;
+  const uint16_t* sk = a.k_new + ((int64_t)b * L.Hkv + h) * D + 8 * g;
+  const uint16_t* sv = a.v_new + ((int64_t)b * L.Hkv + h) * D + 8 * g;
+  uint4 xk[NB], xv[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    xk[bb] = *reinterpret_cast<const uint4*>(sk + 32 * bb);
+    xv[bb] = *reinterpret_cast<const uint4*>(sv + 32 * bb);
+  }
+  const int pos = seq_len - 1;
+  const int blk = a.bs_shift >= 0 ? (pos >> a.bs_shift) : (pos / L.bs);
+  const int64_t prow = (int64_t)a.bt[(int64_t)b * a.max_blocks + blk] * L.bs + (pos - blk * L.bs);
+#pragma unroll
+  for (int i = lane; i < 256; i += 64) {
+    if (i < nbk) s_t[0][i] = L.kt[i];
+    if (i < nbv) s_t[1][i] = L.vt[i];
+  }
+  uint4 A[NB][2];
+  tqq::hadamard_operands<NB>(L.signs, lane, A);
+  float zero;  // an addend of 0 the compiler cannot fold, as in tq_quantize_kernel
+  asm("v_mov_b32 %0, 0" : "=v"(zero));
+  // the boundaries were written by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint8_t* const dst = c == 0 ? a.pages_w + (prow * L.Hkv + h) * (int64_t)L.stride : tq_decode_append_discard;
+  if (c == 0)  // padding, as the quantizer writes it (the discard buffer holds a plain slot only)
+    for (int i = L.slot_bytes + g; i < L.stride; i += 4) dst[i] = 0;
+  tqq::quantize_region<D, KB, false, false, false>(xk, A, zero, g, L.kcode_bytes, s_t[0], nullptr, 0,
+                                                   nullptr, a.rsqrt_d, dst);
+  tqq::quantize_region<D, VB, false, false, false>(xv, A, zero, g, L.vcode_bytes, s_t[1], nullptr, 0,
+                                                   nullptr, a.rsqrt_d, dst + L.kreg);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the slot is stored
+}
+
 // QJL key format on the matrix cores: the residual term (S R q) . z of a 16-token sub-tile is one
 // more product per 32 coordinates, A = the sketched query (two fp16 parts per head, rows as in
 // QK), B = the tokens' sketch bits as fp16 +-1 (exact), four bits per read of a 16-entry table.
@@ -840,6 +897,8 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   __shared__ uint2 s_ztab[16];  // QJL: four sketch bits -> four fp16 +-1
   __shared__ float s_qjmax[8];  // QJL: largest |sketched query| per head, scaled
   __shared__ __align__(16) uint32_t s_w[kNW][16][C::WROW];
+  constexpr bool kAppend = UBLK && !QJL && !MEANT;  // the fused append's instances
+  __shared__ float s_app[kAppend ? 2 : 1][256];      // fused append: the boundaries
   float(*s_q)[D] = reinterpret_cast<float(*)[D]>(s_x);
   float(*s_qj)[D] = reinterpret_cast<float(*)[D]>(s_x) + 8;  // QJL: sketched queries, after s_q
   static_assert(!QJL || kXBytes >= 16 * D * 4, "room for the queries and the sketched queries");
@@ -926,6 +985,15 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
     wht_row8_dpp<LPH>(x, j);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_r1[8 * j + e] = x[e] * a.rsqrt_d;
+  }
+  // Fused append: the last split of a sequence holds its new token's position.  Its last wave,
+  // which the query rotation leaves idle (at most 8 heads of D / 8 lanes: the first two waves),
+  // writes the token's slot of this kv head while the others rotate the queries; the stores are
+  // complete before this barrier, which precedes every page load of the workgroup, so the
+  // split's runs read the new slot (the same compute unit, the same L2).
+  if constexpr (kAppend) {
+    if (a.k_new != nullptr && seq_len > 0 && split == nsplit - 1 && wave == kNW - 1)
+      append_row<D, KB, VB>(a, b, h, seq_len, lane, s_app);
   }
   __syncthreads();
 
@@ -1634,6 +1702,15 @@ int ilog2_exact(int v) {
 
 }  // namespace
 
+// Formats whose decode call also takes the step's append (tq_paged_decode_attention_append):
+// plain slots (no norm correction, mean or sketch) of the block kernel's formats, or of the
+// matrix-core split kernel's formats with page blocks of whole 16-position runs (its staged
+// instances).
+bool tq_decode_append_format(const TqLayer& L) {
+  if (L.norm_corr || L.mean || L.qjl) return false;
+  return tq_decode_block_format(L) || (mfma_format(L.D, L.kb, L.vb) && L.bs % 16 == 0);
+}
+
 // Split geometry: page tokens per split are a multiple of 32 (the tokens a workgroup covers per
 // step) and span at most kMaxBtLds page blocks.  About three workgroups per CU: each workgroup
 // pays a fixed prologue (rotated query, lookup tables, block offsets) and writes one partial, so
@@ -1741,6 +1818,9 @@ int tq_launch_decode(const TqLayer& L, const void* q, const void* pages, const i
   a.nq = nq;
   a.q0 = q0;
   a.g_real = g_real > 0 ? g_real : L.G;
+  a.k_new = app != nullptr ? (const uint16_t*)app->k : nullptr;
+  a.v_new = app != nullptr ? (const uint16_t*)app->v : nullptr;
+  a.pages_w = app != nullptr ? (uint8_t*)app->pages : nullptr;
   const dim3 mgrid0((unsigned)(num_seqs * L.Hkv * L.G));  // merge: one workgroup per query head
   if (tq_decode_block_format(L)) {  // whole-block streaming kernel (tq_decode_block.hip)
     if (a.rows_blocks > 0) {

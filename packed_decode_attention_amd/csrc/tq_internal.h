@@ -64,6 +64,9 @@ struct TqAppend {
   void* pages;
 };
 
+// Formats whose decode call also takes the step's append (tq_paged_decode_attention_append).
+bool tq_decode_append_format(const TqLayer& L);
+
 // The whole-block streaming decode kernel (tq_decode_block.hip): the formats it serves, its split
 // geometry and its launch (the split kernel only; the caller launches fp16-row chunks and merge).
 bool tq_decode_block_format(const TqLayer& L);

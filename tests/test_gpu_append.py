@@ -46,19 +46,32 @@ CASES = [
     # page blocks of 32 positions
     ("k4v4-bs32", wl.Workload("append-e", 1, 5, 32, 8, 128, 4, 4, 0, block_size=32, seed=45),
      [100, 33, 64, 1, 257]),
+    # formats of the matrix-core split kernel, whose last split per (sequence, kv head) appends:
+    # the Qwen2.5-0.5B shape (D = 64, K8/V8, 7 query heads per kv head), a new token alone in its
+    # split (lengths one past a multiple of the split) and at the first and last rows of a run
+    ("split-d64-k8v8", wl.scaled(wl.WORKLOADS["qwen2.5-0.5b"], num_seqs=6), [4097, 1, 16, 17, 300, 0]),
+    # K8/V4 at D = 128 with four query heads per kv head (the Mistral-7B layers' format)
+    ("split-k8v4", wl.Workload("append-f", 1, 4, 32, 8, 128, 8, 4, 0, values="student_t", seed=47),
+     [1000, 2, 513, 32]),
+    # K2/V2, four kv heads, page blocks of 32 positions
+    ("split-k2v2-bs32", wl.Workload("append-g", 1, 5, 16, 4, 128, 2, 2, 0, block_size=32,
+                                    tables="fragmented", seed=48), [64, 65, 1, 900, 31]),
 ]
+# padded slots (a stride of 160 bytes): the append zeroes the padding as the quantizer does
+PADDED = [("split-k4v4-pad160", wl.Workload("append-h", 1, 3, 8, 2, 128, 4, 4, 0, seed=49), [300, 45, 1], 160)]
 
 
-@pytest.mark.parametrize("name,w,lens", CASES, ids=[c[0] for c in CASES])
-def test_fused_append_matches_two_calls_and_oracle(name, w, lens):
+@pytest.mark.parametrize("name,w,lens,stride", [c + (0,) for c in CASES] + PADDED,
+                         ids=[c[0] for c in CASES + PADDED])
+def test_fused_append_matches_two_calls_and_oracle(name, w, lens, stride):
     import torch
     import packed_decode_attention_amd as tq
 
     print(f"[append] case {name}: {len(lens)} sequences, lengths {min(lens)}..{max(lens)}", flush=True)
-    c = Case(w, lens=lens)
+    c = Case(w, lens=lens, slot_stride=stride)
     fmt = c.fmt()
-    assert tq.decode_kernel_names(c.D, c.kb, c.vb, num_kv_heads=c.H, group=c.Hq // c.H)[0] == \
-        "tq_decode_block_kernel"
+    kernel = tq.decode_kernel_names(c.D, c.kb, c.vb, num_kv_heads=c.H, group=c.Hq // c.H)[0]
+    assert kernel == ("tq_decode_mfma_kernel" if name.startswith("split") else "tq_decode_block_kernel")
     L = c.lens
     B, H, D = len(L), c.H, c.D
     last = (np.cumsum(L) - 1)[L > 0]  # row index of each sequence's new token

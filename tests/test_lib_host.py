@@ -141,9 +141,13 @@ def test_argument_validation_before_launch(lib):
     def deca(d, B=4, kn=P, ws_bytes=1 << 40, mb=7, pages=P):
         return so.tq_paged_decode_attention_append(ctypes.byref(d), P, kn, kn, pages, 100, P, mb, P, B,
                                                    100, 0.0, P, P, ws_bytes, None)
-    assert deca(_desc(lib, k_bits=8)) == E.TQ_ERR_UNSUPPORTED             # not a whole-block format
-    assert deca(_desc(lib, v_centroids=0x30000)) == E.TQ_ERR_UNSUPPORTED  # K4/V4 with two codebooks
+    # formats served by neither the block kernel nor the split kernel's staged instances
+    assert deca(_desc(lib, v_bits=3)) == E.TQ_ERR_UNSUPPORTED             # 3-bit values: vector kernel
+    assert deca(_desc(lib, head_dim=64, k_bits=2)) == E.TQ_ERR_UNSUPPORTED  # D = 64, 2-bit keys
+    assert deca(_desc(lib, k_bits=8, block_size=8)) == E.TQ_ERR_UNSUPPORTED  # runs of 16 split by blocks
     assert deca(_desc(lib, flags=1)) == E.TQ_ERR_UNSUPPORTED              # norm correction
+    assert deca(_desc(lib, k_bits=8, flags=2)) == E.TQ_ERR_UNSUPPORTED    # mean removal
+    assert deca(_desc(lib, flags=4, slot_stride=160)) == E.TQ_ERR_UNSUPPORTED  # QJL keys
     assert deca(_desc(lib, num_q_heads=72)) == E.TQ_ERR_UNSUPPORTED
     assert deca(_desc(lib), B=513) == E.TQ_ERR_UNSUPPORTED                # above TQ_APPEND_MAX_SEQS
     assert deca(_desc(lib), kn=None) == E.TQ_ERR_INVALID_ARG
