@@ -61,7 +61,7 @@ constexpr int kLutShift = 8;                   // table entries hold c * 2^8
 constexpr int kWShift = 13;                    // weights enter PV as w * 2^13 (below 2^15)
 constexpr float kThr = 2.0f;                   // lazy rescale threshold, log2 units
 constexpr float kSent = -1.0e30f;              // finite minus infinity of the running maxima
-constexpr int kMaxRuns = 384;                  // runs per unit (six lanes' worth of run rows)
+constexpr int kMaxRuns = 1024;                 // runs per unit (sixteen lanes' worth of run rows)
 constexpr int kPlanInts = 48;                  // LDS words of the work plan (3 per wave, 8 more)
 constexpr int kGrid = 256;                     // workgroups: one per compute unit of the MI355X
 

@@ -84,10 +84,11 @@ CASES = {
                        lens=list(np.random.default_rng(63).integers(1, 200, 400))),
     "blk32-long": dict(w=wl.Workload("blk32-long", 1, 1, 64, 8, 128, 3, 2, 0, values="student_t", seed=64),
                        lens=[20000]),
-    # balanced ranges whose pieces exceed one unit of 384 runs (an 813-run sequence among 255
-    # one-run ones: 407 runs per workgroup), and workgroups with over a hundred pieces
+    # balanced ranges whose pieces exceed one unit of 1024 runs (a 2400-run sequence among 255
+    # one-run ones may span at most three workgroups: 1201 runs per workgroup), and workgroups
+    # with over a hundred pieces
     "blk32-units": dict(w=wl.Workload("blk32-units", 1, 256, 64, 8, 128, 3, 2, 0, seed=65),
-                        lens=[16] * 100 + [13000] + [16] * 155),
+                        lens=[16] * 100 + [38400] + [16] * 155),
     "blk-units": dict(w=wl.Workload("blk-units", 1, 256, 32, 8, 128, 4, 4, 0, seed=66),
                       lens=[16] * 40 + [12999] + [16] * 215),
     # the largest sink count (128): sequences shorter than, equal to and longer than it
