@@ -42,6 +42,8 @@ CASES = [
     ("llama-g4", dict(w=wl.scaled(wl.WORKLOADS["llama3-8b"], num_seqs=3), lens=[1500, 777, 40])),
     ("mistral-sinks", dict(w=wl.scaled(wl.WORKLOADS["mistral-7b"], num_seqs=3), lens=[900, 3, 130])),
     ("ragged-g8", dict(w=wl.scaled(wl.WORKLOADS["ragged"], num_seqs=4), lens=[613, 64, 1, 300])),
+    # the matrix-core split kernel at D = 64, eight bits (the Qwen2.5-0.5B shape)
+    ("qwen-d64", dict(w=wl.scaled(wl.WORKLOADS["qwen2.5-0.5b"], num_seqs=3), lens=[4097, 1, 600])),
 ]
 
 
