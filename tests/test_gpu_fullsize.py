@@ -193,7 +193,7 @@ def test_full_size_sampled(name, layer, which, window, nc, nq):
               flush=True)
 
 
-FUSED = [("llama3-8b", 1), ("ragged", 5)]
+FUSED = [("llama3-8b", 1), ("ragged", 5), ("qwen2.5-0.5b", 7)]
 
 
 @pytest.mark.parametrize("name,layer", FUSED, ids=[f"{n}-L{l}" for n, l in FUSED])
@@ -215,7 +215,9 @@ def test_full_size_fused_append(name, layer):
     print(f"[fullsize] fused append {name} layer {layer} K{kb}/V{vb}: B={B} max_len={int(lens.max())}",
           flush=True)
     fmt = tq.LayerFormat(D, Hq, H, kb, vb, bs, 0)
-    assert tq.decode_kernel_names(D, kb, vb, False, H, Hq // H)[0] == "tq_decode_block_kernel"
+    # the block kernel (Llama, ragged) or the matrix-core split kernel's last split (Qwen) appends
+    assert tq.decode_kernel_names(D, kb, vb, False, H, Hq // H)[0] in ("tq_decode_block_kernel",
+                                                                       "tq_decode_mfma_kernel")
     ctx_pages = fmt.new_pages(num_blocks)
     bench.fill_layer(w, layer, fmt, ctx_pages, torch.from_numpy(ctx_np).cuda(), num_blocks, torch, tq, wl)
     new_k, new_v = bench.new_tokens(w, 1, wl)
