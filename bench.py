@@ -321,66 +321,145 @@ def stream_probe(torch, tq, w, reps=10):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_run(w, budget_s):
-    """The oracle as it stands, on a bounded sample: one layer, the first sequences in turn until
-    about `budget_s` seconds of decode work have been timed; pages built by the oracle itself."""
+CPU_MAX_TOKENS = 32769  # tokens of a sequence in the CPU sample: its first ones, up to one
+                        # Llama-shaped sequence (the oracle builds 8-bit pages about 13x slower
+                        # than 4-bit ones)
+
+
+def cpu_sample_layer(w):
+    """The first layer in the workload's main page format."""
+    return next(l for l in range(w.layers) if w.bits(l) == (w.k_bits, w.v_bits))
+
+
+def _oracle_sequence(w, b, before_decode=None):
+    """The first CPU_MAX_TOKENS tokens of sequence b (a shorter sequence of the same layer)
+    through the oracle as it stands: its pages built by the oracle's quantizer, then its decode.
+    `before_decode`, if given, is called between the two.  Returns (tokens, quantize seconds, rows,
+    decode start, decode end), times on the system-wide monotonic clock."""
     from oracle import attention as oatt
     from oracle import codebook as ocb
     from oracle import quantize as oq
     from packed_decode_attention_amd import workloads as wl
 
     lens = wl.seq_lens(w)
-    l = 0
+    l = cpu_sample_layer(w)
     kb, vb = w.bits(l)
     ck, cv = ocb.codebook(w.head_dim, kb), ocb.codebook(w.head_dim, vb)
     layer = dict(D=w.head_dim, H_kv=w.num_kv_heads, block_size=w.block_size, k_bits=kb, v_bits=vb, seed=0)
     q = wl.queries(w, l).numpy()
     sk, sv = wl.sinks(w, l)
-    sk = None if sk is None else sk.numpy()
-    sv = None if sv is None else sv.numpy()
+    L = min(int(lens[b]), CPU_MAX_TOKENS)
+    one = wl.scaled(w, num_seqs=1)
+    bt1, nblk = wl.block_tables(one, np.array([L]))
+    pages = np.zeros(nblk * w.block_size * w.num_kv_heads * oq.slot_bytes(w.head_dim, kb, vb), np.uint8)
+    k = wl.kv_values(w, l, L, "k").numpy()
+    v = wl.kv_values(w, l, L, "v").numpy()
+    slots = wl.token_slots(bt1, 0, np.arange(L), w.block_size)
+    clock = time.CLOCK_MONOTONIC
+    t0 = time.clock_gettime(clock)
+    oq.append_rows_fast(pages, k, v, slots, ck.boundaries32, cv.boundaries32, kb, vb, 0)
+    tq_s = time.clock_gettime(clock) - t0
+    if before_decode is not None:
+        before_decode()
+    t1 = time.clock_gettime(clock)
+    oatt.decode_attention(q[b:b + 1], pages, bt1, np.array([L]), layer, ck.centroids32, cv.centroids32,
+                          None if sk is None else sk.numpy()[b:b + 1],
+                          None if sv is None else sv.numpy()[b:b + 1], w.n_sink)
+    t2 = time.clock_gettime(clock)
+    return L, tq_s, L * w.num_kv_heads, t1, t2
+
+
+def _oracle_worker_init(barrier):
+    """One thread per worker process: BLAS and torch's CPU pool (the seeded input generators)."""
+    import threadpoolctl
+    import torch
+    torch.set_num_threads(1)
+    globals()["_pool_limits"] = threadpoolctl.threadpool_limits(limits=1)
+    globals()["_pool_barrier"] = barrier
+
+
+def _oracle_worker(name, b):
+    """One sequence in a worker: its pages, then a wait for every worker's pages, then its decode.
+    (A worker blocked at the barrier takes no other task, so the tasks go to distinct workers.)"""
+    from packed_decode_attention_amd import workloads as wl
+    return _oracle_sequence(wl.WORKLOADS[name], b, before_decode=_pool_barrier.wait)
+
+
+def cpu_baseline_run(w, budget_s):
+    """One thread: the first sequences in turn until about `budget_s` seconds of oracle work have
+    been timed."""
     tokens, t_dec, t_q, rows_q, seqs = 0, 0.0, 0.0, 0, []
     for b in range(w.num_seqs):
-        L = int(lens[b])
-        one = wl.scaled(w, num_seqs=1)
-        bt1, nblk = wl.block_tables(one, np.array([L]))
-        pages = np.zeros(nblk * w.block_size * w.num_kv_heads * oq.slot_bytes(w.head_dim, kb, vb), np.uint8)
-        k = wl.kv_values(w, l, L, "k").numpy()
-        v = wl.kv_values(w, l, L, "v").numpy()
-        slots = wl.token_slots(bt1, 0, np.arange(L), w.block_size)
-        t0 = time.perf_counter()
-        oq.append_rows_fast(pages, k, v, slots, ck.boundaries32, cv.boundaries32, kb, vb, 0)
-        t1 = time.perf_counter()
-        oatt.decode_attention(q[b:b + 1], pages, bt1, np.array([L]), layer, ck.centroids32, cv.centroids32,
-                              None if sk is None else sk[b:b + 1], None if sv is None else sv[b:b + 1], w.n_sink)
-        t2 = time.perf_counter()
-        t_q += t1 - t0
-        rows_q += L * w.num_kv_heads
-        t_dec += t2 - t1
+        L, tq_s, rows, d0, d1 = _oracle_sequence(w, b)
+        t_q += tq_s
+        rows_q += rows
+        t_dec += d1 - d0
         tokens += L
         seqs.append(b)
+        log(f"oracle, one thread: sequence {b} done ({L} tokens)")
         if t_dec + t_q > budget_s:
             break
     return tokens / t_dec, tokens, seqs, rows_q / t_q
 
 
+def cpu_host_threads():
+    """Logical CPUs this process may run on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_pool(w, workers):
+    """All host threads: one worker process per sequence, each on one thread, up to `workers`
+    sequences.  The workers build their pages, meet at a barrier, then decode side by side; the
+    rate is the sequences' tokens over the span from the first decode's start to the last one's
+    end."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+
+    seqs = list(range(min(workers, w.num_seqs)))
+    ctx = multiprocessing.get_context("spawn")  # fresh interpreters: nothing inherited from this one
+    barrier = ctx.Barrier(len(seqs), timeout=900)
+    from concurrent.futures import as_completed
+    res = []
+    with ProcessPoolExecutor(max_workers=len(seqs), mp_context=ctx, initializer=_oracle_worker_init,
+                             initargs=(barrier,)) as ex:
+        for f in as_completed([ex.submit(_oracle_worker, w.name, b) for b in seqs]):
+            res.append(f.result())
+            log(f"oracle, {len(seqs)} processes: {len(res)} of {len(seqs)} sequences done")
+    tokens = sum(r[0] for r in res)
+    span = max(r[4] for r in res) - min(r[3] for r in res)
+    rows = sum(r[2] for r in res)
+    q_rate = rows / max(r[1] for r in res)  # the page builds overlap too: rows over the longest
+    return tokens / span, tokens, seqs, len(seqs), q_rate
+
+
 def cpu_baseline(w, budget_s=12.0):
-    """The oracle timed twice on the host: with its BLAS pool at one thread, then at the pool's
-    full size.  Its per-sequence and per-head loops and its unpacking are Python on one thread in
-    both runs; only the BLAS calls use the pool."""
+    """The oracle timed on the host twice: on one thread, then with one worker process per
+    sequence on every host thread (up to 16).  Run before this process touches the GPU."""
     import threadpoolctl
-    with threadpoolctl.threadpool_limits(limits=1):
-        v1, tok1, seqs1, rq1 = cpu_baseline_run(w, budget_s)
-    vn, tokn, seqsn, rqn = cpu_baseline_run(w, budget_s)
-    threads = max([p["num_threads"] for p in threadpoolctl.threadpool_info()] + [1])
+    import torch
+    nt = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpoolctl.threadpool_limits(limits=1):
+            v1, tok1, seqs1, rq1 = cpu_baseline_run(w, budget_s)
+    finally:
+        torch.set_num_threads(nt)
+    vn, tokn, seqsn, procs, rqn = cpu_baseline_pool(w, cpu_host_threads())
+
     def sample(tokens, seqs, rows_rate):
-        return (f"layer 0 decode of sequences {seqs} ({tokens} KV tokens, {w.num_kv_heads} kv heads, "
+        return (f"layer {cpu_sample_layer(w)} (K{w.k_bits}/V{w.v_bits}) decode of the first {CPU_MAX_TOKENS} "
+                f"tokens at most of sequences {seqs} ({tokens} KV tokens, {w.num_kv_heads} kv heads, "
                 f"{w.num_q_heads} q heads) with the fp64 NumPy oracle; its quantize of the same rows ran at "
                 f"{rows_rate:.0f} rows/s")
-    return {"value": vn, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample(tokn, seqsn, rqn) + f"; BLAS pool of {threads} threads on a host with "
-                      f"{os.cpu_count()} logical CPUs (the Python loops run on one thread)",
+    return {"value": vn, "unit": "KV tokens/s", "cores": int(procs), "kind": "oracle",
+            "sample": sample(tokn, seqsn, rqn) + f"; {procs} worker processes of one thread each, one "
+                      f"sequence apiece, decoding side by side on a host with {os.cpu_count()} logical CPUs",
             "one_thread": {"value": v1, "unit": "KV tokens/s", "cores": 1,
-                           "sample": sample(tok1, seqs1, rq1) + "; BLAS pool limited to 1 thread"}}
+                           "sample": sample(tok1, seqs1, rq1) + "; one thread"}}
 
 
 def main():
@@ -429,6 +508,11 @@ def main():
     import packed_decode_attention_amd as tq
     from packed_decode_attention_amd import workloads as wl
 
+    cpu = None
+    if not (args.no_cpu_baseline or args.copy_probe or args.stream_probe):
+        # before the GPU is touched: the worker processes start as fresh interpreters
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl.WORKLOADS[args.workload], args.cpu_budget)
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
@@ -560,9 +644,8 @@ def main():
     }
     if args.graph:
         result["eager_ms_per_step"] = eager_ms_per_step
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
