@@ -660,20 +660,32 @@ template <> struct OpTable<4> { using E = uint2; static constexpr int N = 256, V
 template <> struct OpTable<3> { using E = uint2; static constexpr int N = 64, V = 2; };
 template <> struct OpTable<2> { using E = uint4; static constexpr int N = 256, V = 4; };
 
+// Thread tid builds entry tid (every table has at most one entry per thread of a workgroup): its
+// codebook values are loaded first (load_op_values), the entry is written once they are in
+// (store_op_entry), so the loads can be issued early.
 template <int BITS>
-__device__ __forceinline__ void build_op_table(typename OpTable<BITS>::E* t, const float* __restrict__ c,
-                                               int tid) {
+__device__ __forceinline__ void load_op_values(const float* __restrict__ c, int tid,
+                                               float (&x)[OpTable<BITS>::V]) {
   constexpr int V = OpTable<BITS>::V, M = (1 << BITS) - 1;
-  for (int e = tid; e < OpTable<BITS>::N; e += kWG) {
-    uint32_t hi[V], lo[V];
+  static_assert(OpTable<BITS>::N <= kWG, "one table entry per thread");
+  const int e = tid < OpTable<BITS>::N ? tid : 0;
 #pragma unroll
-    for (int v = 0; v < V; ++v) split_f16(ldexpf(c[(e >> (BITS * v)) & M], kLutShift), hi[v], lo[v]);
-    if constexpr (V == 1) t[e] = hi[0] | (lo[0] << 16);
-    if constexpr (V == 2) t[e] = make_uint2(hi[0] | (hi[1] << 16), lo[0] | (lo[1] << 16));
-    if constexpr (V == 4)
-      t[e] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), lo[0] | (lo[1] << 16),
+  for (int v = 0; v < V; ++v) x[v] = c[(e >> (BITS * v)) & M];
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_op_entry(typename OpTable<BITS>::E* t, const float (&x)[OpTable<BITS>::V],
+                                               int tid) {
+  constexpr int V = OpTable<BITS>::V;
+  if (tid >= OpTable<BITS>::N) return;
+  uint32_t hi[V], lo[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) split_f16(ldexpf(x[v], kLutShift), hi[v], lo[v]);
+  if constexpr (V == 1) t[tid] = hi[0] | (lo[0] << 16);
+  if constexpr (V == 2) t[tid] = make_uint2(hi[0] | (hi[1] << 16), lo[0] | (lo[1] << 16));
+  if constexpr (V == 4)
+    t[tid] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), lo[0] | (lo[1] << 16),
                         lo[2] | (lo[3] << 16));
-  }
 }
 
 // The other operand for four fp16 values given as x01 = x0 | x1 << 16 and x23 = x2 | x3 << 16.
@@ -880,6 +892,23 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   if (unit >= a.n_units) return;
   const int b = unit / a.max_split;
   const int split = unit - b * a.max_split;
+  const int tid = threadIdx.x;
+  // Loads that do not need the sequence length are issued before it arrives: this thread's
+  // codebook values for the operand tables, its query coordinates, and its entry of the block
+  // table from block split * chunk on (the split's first block unless sinks move its start; the
+  // entry is used only if it is).  All are in bounds: codes index their codebook, b < num_seqs,
+  // and the entry is read only below max_blocks of a block table that is present.
+  float kcv[OpTable<KB>::V], vcv[OpTable<VB>::V];
+  load_op_values<KB>(L.kc, tid, kcv);
+  load_op_values<VB>(L.vc, tid, vcv);
+  constexpr int LPH = D / 8;
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < LPH * G) qraw = *reinterpret_cast<const uint4*>(a.q + q_row(a, b, h, tid / LPH) * D + 8 * (tid % LPH));
+  auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
+  const int blk_pre = block_of(split * a.chunk);
+  const bool bt_pre_ok = a.bt != nullptr && blk_pre + tid < a.max_blocks;
+  const int32_t bt_pre = bt_pre_ok ? a.bt[(int64_t)b * a.max_blocks + blk_pre + tid] : 0;
+
   const int seq_len = a.seq_lens[b];
   const int ns = min(a.n_sink, seq_len);
   const int packed_end = seq_len - window_len(a, b, seq_len, ns);
@@ -904,14 +933,13 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   static_assert(!QJL || kXBytes >= 16 * D * 4, "room for the queries and the sketched queries");
   float(*s_part)[D + 2] = reinterpret_cast<float(*)[D + 2]>(s_x);  // [wave * H8 + head]
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t16 = lane & 15;
   const int q4 = lane >> 4;
 
-  build_op_table<KB>(s_ktab, L.kc, tid);
-  build_op_table<VB>(s_vtab, L.vc, tid);
+  store_op_entry<KB>(s_ktab, kcv, tid);
+  store_op_entry<VB>(s_vtab, vcv, tid);
   if (QJL && tid < 16) {  // entry e: fp16 +1 where bit i of e is set, else -1
     uint32_t hv[4];
 #pragma unroll
@@ -926,21 +954,29 @@ __global__ __launch_bounds__(kWG, 2) void tq_decode_mfma_kernel(DecodeArgs a) {
   const int p0 = max(split * a.chunk, UBLK ? (ns & ~15) : ns);
   const int p_end = min(split * a.chunk + a.chunk, packed_end);
   const bool any_rows = p_end > max(p0, ns);
-  auto block_of = [&](int p) { return a.bs_shift >= 0 ? (p >> a.bs_shift) : (p / L.bs); };
   const int blk0 = any_rows ? block_of(p0) : 0;
   const int blk_last = any_rows ? block_of(p_end - 1) : blk0;
   const int nblk = any_rows ? blk_last - blk0 + 1 : 0;
   const int32_t* btg = a.bt + (int64_t)b * a.max_blocks + blk0;
   const int64_t row_bytes = (int64_t)L.Hkv * L.stride;
-  for (int i = tid; i < nblk; i += kWG) s_boff[i] = (int64_t)btg[i] * L.bs * row_bytes;
+  for (int i = tid; i < nblk; i += kWG) {
+    const int32_t e = (i == tid && blk0 == blk_pre && bt_pre_ok) ? bt_pre : btg[i];
+    s_boff[i] = (int64_t)e * L.bs * row_bytes;
+  }
 
   // Rotated queries H (s * q): D/8 lanes of one DPP row per head, 8 coordinates per lane; the
   // largest |q'| of each head sets its power-of-two scale into fp16 range below.
-  constexpr int LPH = D / 8;
   if (tid < LPH * G) {
     const int g = tid / LPH, j = tid % LPH;
     float x[8];
-    load8_f16(a.q + q_row(a, b, h, g) * D + 8 * j, x);
+    {
+      const uint32_t w4[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = half_bits_to_float(w4[i] & 0xffffu);
+        x[2 * i + 1] = half_bits_to_float(w4[i] >> 16);
+      }
+    }
     if (kMean && L.mean) {
       float qs = 0.0f;
 #pragma unroll
